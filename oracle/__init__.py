@@ -1,0 +1,181 @@
+"""fp64 CPU oracle of the fused sparse-MLA attention step (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py``
+may import this package.  The product library never does, and the two share no code:
+this wrapper loads ``liboracle.so`` built from ``sparse_mla_oracle.c`` by plain gcc.
+
+The functions mirror the steps of the C file (each cites its passage there):
+``bf16_decode``, ``e4m3_decode``, ``e4m3_encode``, ``ue8m0_exponent``,
+``quantize_blocks``, ``rmsnorm``, ``rope`` and the whole step ``sparse_mla``.
+
+Parity pins: every function here is checked in ``tests/test_oracle_*.py`` against
+library routines (torch's CPU float8_e4m3fn cast, torch SDPA and rms_norm in fp64,
+the rotate-half routine of ``transformers``), closed forms and invariants.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sparse_mla_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+KV_E4M3_UE8M0 = 0
+KV_BF16 = 1
+
+
+def build(verbose: bool = False) -> str:
+    """Compile ``liboracle.so`` with gcc (fp64, OpenMP, no fast-math)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-fno-fast-math",
+           "-ffp-contract=off", "-o", _LIB_PATH + ".tmp", _SRC, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    lib.oracle_bf16_decode.restype = ctypes.c_double
+    lib.oracle_bf16_decode.argtypes = [ctypes.c_uint16]
+    lib.oracle_e4m3_decode.restype = ctypes.c_double
+    lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+    lib.oracle_e4m3_encode.argtypes = [ctypes.c_double]
+    lib.oracle_ue8m0_exponent.restype = ctypes.c_int
+    lib.oracle_ue8m0_exponent.argtypes = [ctypes.c_double]
+    lib.oracle_quantize_blocks.restype = None
+    lib.oracle_quantize_blocks.argtypes = [P, ctypes.c_int64, P, P]
+    lib.oracle_rmsnorm.restype = None
+    lib.oracle_rmsnorm.argtypes = [P, P, ctypes.c_int, ctypes.c_double, P]
+    lib.oracle_rope.restype = None
+    lib.oracle_rope.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double, ctypes.c_int]
+    lib.oracle_sparse_mla.restype = ctypes.c_int
+    lib.oracle_sparse_mla.argtypes = [P, P, P, P, P, P, P,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_double,
+                                      ctypes.c_double, P, P, P]
+    lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_num_threads.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def bf16_decode(bits) -> np.ndarray:
+    lib = _load()
+    b = np.asarray(bits, dtype=np.uint16)
+    return np.array([lib.oracle_bf16_decode(int(x)) for x in b.ravel()], dtype=np.float64).reshape(b.shape)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    lib = _load()
+    c = np.asarray(codes, dtype=np.uint8)
+    return np.array([lib.oracle_e4m3_decode(int(x)) for x in c.ravel()], dtype=np.float64).reshape(c.shape)
+
+
+def e4m3_encode(x) -> np.ndarray:
+    lib = _load()
+    v = np.asarray(x, dtype=np.float64)
+    return np.array([lib.oracle_e4m3_encode(float(z)) for z in v.ravel()], dtype=np.uint8).reshape(v.shape)
+
+
+def ue8m0_exponent(amax) -> np.ndarray:
+    lib = _load()
+    v = np.asarray(amax, dtype=np.float64)
+    return np.array([lib.oracle_ue8m0_exponent(float(z)) for z in v.ravel()], dtype=np.int32).reshape(v.shape)
+
+
+def quantize_blocks(o: np.ndarray):
+    """Block-32 UE8M0 + E4M3 quantization of ``o`` (last dim a multiple of 32).
+
+    Returns ``(codes u8 like o, scales u8 [..., d/32])``.
+    """
+    lib = _load()
+    o = np.ascontiguousarray(o, dtype=np.float64)
+    assert o.shape[-1] % 32 == 0
+    codes = np.empty(o.shape, dtype=np.uint8)
+    scales = np.empty(o.shape[:-1] + (o.shape[-1] // 32,), dtype=np.uint8)
+    lib.oracle_quantize_blocks(_ptr(o), o.size, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def rmsnorm(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
+    lib = _load()
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    y = np.empty_like(x)
+    lib.oracle_rmsnorm(_ptr(x), _ptr(w), x.shape[-1], float(eps), _ptr(y))
+    return y
+
+
+def rope(y: np.ndarray, rope_dim: int, pos: float, theta: float, direction: int = 1) -> np.ndarray:
+    """Rotate-half RoPE on the last ``rope_dim`` entries of a 1-D vector (copy)."""
+    lib = _load()
+    out = np.ascontiguousarray(y, dtype=np.float64).copy()
+    lib.oracle_rope(_ptr(out), out.shape[-1], int(rope_dim), float(pos), float(theta), int(direction))
+    return out
+
+
+def sparse_mla(q_bits: np.ndarray, kv_pool: np.ndarray, kv_scales: Optional[np.ndarray],
+               indices: np.ndarray, topk_length: np.ndarray, positions: np.ndarray,
+               norm_w: np.ndarray, *, sm_scale: float, eps: float, theta: float, rope_dim: int,
+               kv_format: int = KV_E4M3_UE8M0):
+    """The whole step for ``s_q`` tokens.
+
+    ``q_bits`` u16 [s_q, h, d] (bf16 bits); ``kv_pool`` u8 [n, d] (E4M3 codes) or u16
+    [n, d] (bf16 bits); ``kv_scales`` u8 [n, d/32] or None; ``indices`` i32 [s_q, topk];
+    ``topk_length`` / ``positions`` i32 [s_q]; ``norm_w`` [d].
+
+    Returns ``(o f64 [s_q, h, d], codes u8 [s_q, h, d], scales u8 [s_q, h, d/32])``.
+    Raises ``ValueError`` on an argument or index error.
+    """
+    lib = _load()
+    q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
+    s_q, h, d = q_bits.shape
+    kv_pool = np.ascontiguousarray(kv_pool)
+    n_rows = kv_pool.shape[0]
+    if kv_format == KV_E4M3_UE8M0:
+        assert kv_pool.dtype == np.uint8
+        kv_scales = np.ascontiguousarray(kv_scales, dtype=np.uint8)
+    else:
+        assert kv_pool.dtype == np.uint16
+        kv_scales = None
+    indices = np.ascontiguousarray(indices, dtype=np.int32)
+    topk = indices.shape[1] if indices.ndim == 2 else 0
+    topk_length = np.ascontiguousarray(topk_length, dtype=np.int32)
+    positions = np.ascontiguousarray(positions, dtype=np.int32)
+    norm_w = np.ascontiguousarray(norm_w, dtype=np.float64)
+    o = np.zeros((s_q, h, d), dtype=np.float64)
+    codes = np.zeros((s_q, h, d), dtype=np.uint8)
+    scales = np.zeros((s_q, h, d // 32), dtype=np.uint8)
+    rc = lib.oracle_sparse_mla(_ptr(q_bits), _ptr(kv_pool), _ptr(kv_scales), _ptr(indices),
+                               _ptr(topk_length), _ptr(positions), _ptr(norm_w),
+                               s_q, h, d, int(rope_dim), topk, n_rows, int(kv_format),
+                               float(sm_scale), float(eps), float(theta),
+                               _ptr(o), _ptr(codes), _ptr(scales))
+    if rc != 0:
+        raise ValueError(f"oracle_sparse_mla failed with code {rc}")
+    return o, codes, scales

@@ -1,0 +1,293 @@
+/*
+ * sparse_mla_oracle.c -- plain fp64 CPU oracle of the fused sparse-MLA attention step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, obviously-correct reference the
+ * GPU library is checked against.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load it; the product path never does.  It shares
+ * no code, header, table or constant with the GPU library: every step below is
+ * written from the definition it cites.
+ *
+ * What it computes (per query token t, per head h), following the pages:
+ *   [vLLM #56344 "Deepseek V41 Attention MegaKernel", Purpose, first bullet]
+ *     the fused step is: norm -> RoPE -> sparse attention -> inverse RoPE -> FP8 cast.
+ *   [vLLM #56344, Purpose, bug-fix bullet]
+ *     reads are capped at topk_length; entries beyond it are never dereferenced;
+ *     -1 marks an empty slot.
+ *   [vLLM #56344, Purpose, second bullet]
+ *     every token carries its own metadata row (positions, SWA + compressed indices).
+ *   [SGLang #39370 "[DSV4.1] Combine DSpark decode and prefill kernel optimizations",
+ *    Summary] the query norm is per head ("q_head_norm").
+ *   [vLLM #56344, Purpose] the KV cache row is 512 e4m3 bytes plus UE8M0 block
+ *     scales (528 B), shared as K and V by every head (MLA latent).
+ *   [SGLang #39370, commit note on the MXFP8 epilogue] UE8M0 block scales on the
+ *     output.
+ *
+ * Readings taken where the pages are silent (each is listed with its reason in the
+ * design notes of the repository):
+ *   - RMSNorm over the d dims of each head, eps inside the square root, one weight
+ *     vector norm_w[d] shared by all heads.
+ *   - RoPE is the rotate-half form on the last r dims: pairs (o0+i, o0+i+r/2),
+ *     o0 = d - r, angle p * base^(-2i/r).  Inverse RoPE rotates by the negated
+ *     angle at the same (query) position.  K rows are used as stored.
+ *   - Softmax over the valid entries J of the row; duplicates count once per entry;
+ *     an empty J gives o = 0.
+ *   - Output scale: the smallest power of two S = 2^(e-127), e in [0, 254], with
+ *     448 * S >= amax of the 32-element block; codes are round-to-nearest-even
+ *     OCP E4M3FN of o / S (so they never saturate).
+ *
+ * Formats written from their public definitions:
+ *   OCP 8-bit floating point specification, E4M3: bias 7, 3 mantissa bits,
+ *   subnormals, max normal 448 (0x7E), NaN = S.1111.111, no infinities.
+ *   bf16: the upper 16 bits of an IEEE-754 binary32.
+ *
+ * All arithmetic is double precision.  Parallel over tokens with OpenMP (the tokens
+ * are independent; each token's arithmetic is the same serial loop either way).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_ERR_ARG (-1)   /* bad sizes / scalars */
+#define ORACLE_ERR_INDEX (-2) /* a valid-prefix index outside [-1, n_rows) */
+#define ORACLE_ERR_NOMEM (-3)
+
+#define KV_E4M3_UE8M0 0
+#define KV_BF16 1
+
+#define BLOCK 32
+
+/* ---------------------------------------------------------------- decoders */
+
+/* bf16 bit pattern -> exact double (bf16 is the top half of a binary32). */
+double oracle_bf16_decode(uint16_t bits) {
+  uint32_t u = ((uint32_t)bits) << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* OCP E4M3FN code -> exact double.  NaN for S.1111.111. */
+double oracle_e4m3_decode(uint8_t code) {
+  int sign = (code >> 7) & 1;
+  int ex = (code >> 3) & 15;
+  int man = code & 7;
+  double v;
+  if (ex == 15 && man == 7) return NAN;
+  if (ex == 0)
+    v = ldexp((double)man, -9); /* subnormal: man/8 * 2^(1-7) */
+  else
+    v = ldexp(1.0 + man / 8.0, ex - 7);
+  return sign ? -v : v;
+}
+
+/* ---------------------------------------------------------------- encoders */
+
+/*
+ * Round-to-nearest-even onto the E4M3FN grid.  Requires |x| <= 448 (the caller's
+ * scale guarantees it); larger magnitudes saturate to +-448 (0x7E / 0xFE), which the
+ * path never produces.  The sign of x is kept, so a negative value that rounds to
+ * zero gives 0x80.
+ */
+uint8_t oracle_e4m3_encode(double x) {
+  uint8_t sign = (signbit(x) ? 0x80 : 0x00);
+  double a = fabs(x);
+  int k, E, code;
+  double q, n;
+  if (a == 0.0) return sign;
+  if (a >= 448.0) return (uint8_t)(sign | 0x7E);
+  frexp(a, &k);        /* a = f * 2^k, f in [0.5, 1)  ->  floor(log2 a) = k - 1 */
+  E = k - 1;
+  if (E < -6) E = -6;  /* below the smallest normal the quantum stays 2^-9 */
+  q = ldexp(1.0, E - 3);
+  n = nearbyint(a / q); /* a / q is exact (power-of-two divisor); default mode is RNE */
+  /* n in [0, 16]; n == 16 means the value rounded up to 2^(E+1). */
+  if (E == -6 && n < 8) {
+    code = (int)n; /* subnormal: mantissa n, exponent field 0 */
+  } else if (n == 16.0) {
+    code = ((E + 1 + 7) << 3);
+  } else {
+    code = ((E + 7) << 3) | ((int)n - 8);
+  }
+  if (code > 0x7E) code = 0x7E;
+  return (uint8_t)(sign | code);
+}
+
+/*
+ * UE8M0 exponent of a block: the smallest e in [0, 254] with 448 * 2^(e-127) >= amax.
+ * 448 * 2^E is exact in double for every E used here, so the comparison decides the
+ * exponent exactly (no log2 rounding).
+ */
+int oracle_ue8m0_exponent(double amax) {
+  int E, k;
+  if (!(amax > 0.0)) return 0; /* amax == 0 (or NaN): the clamp gives e = 0 */
+  frexp(amax, &k);
+  E = k - 1 - 9;               /* 448 * 2^E < amax here, since 448 < 2^9 */
+  while (ldexp(448.0, E) < amax) E++;
+  if (E + 127 < 0) return 0;
+  if (E + 127 > 254) return 254;
+  return E + 127;
+}
+
+/* Quantize n values (n a multiple of 32) in blocks of 32: scales[b] = e, codes = RNE(o / 2^(e-127)). */
+void oracle_quantize_blocks(const double* o, int64_t n, uint8_t* codes, uint8_t* scales) {
+  int64_t b, i;
+  for (b = 0; b < n / BLOCK; ++b) {
+    double amax = 0.0;
+    int e;
+    for (i = 0; i < BLOCK; ++i) {
+      double a = fabs(o[b * BLOCK + i]);
+      if (a > amax) amax = a;
+    }
+    e = oracle_ue8m0_exponent(amax);
+    scales[b] = (uint8_t)e;
+    for (i = 0; i < BLOCK; ++i) codes[b * BLOCK + i] = oracle_e4m3_encode(ldexp(o[b * BLOCK + i], 127 - e));
+  }
+}
+
+/* ---------------------------------------------------------------- q path */
+
+/* Per-head RMSNorm: y_i = x_i / sqrt(mean(x^2) + eps) * w_i. */
+void oracle_rmsnorm(const double* x, const double* w, int d, double eps, double* y) {
+  double ss = 0.0;
+  int i;
+  for (i = 0; i < d; ++i) ss += x[i] * x[i];
+  double inv = 1.0 / sqrt(ss / d + eps);
+  for (i = 0; i < d; ++i) y[i] = x[i] * inv * w[i];
+}
+
+/*
+ * Rotate-half RoPE on the last r dims of y (in place) at position pos.  direction = +1
+ * applies RoPE, direction = -1 applies its inverse (rotation by the negated angle).
+ */
+void oracle_rope(double* y, int d, int r, double pos, double base, int direction) {
+  int o0 = d - r, half = r / 2, i;
+  for (i = 0; i < half; ++i) {
+    double inv_freq = pow(base, -(2.0 * i) / (double)r);
+    double ang = (double)direction * pos * inv_freq;
+    double c = cos(ang), s = sin(ang);
+    double a = y[o0 + i], b = y[o0 + i + half];
+    y[o0 + i] = a * c - b * s;
+    y[o0 + i + half] = b * c + a * s;
+  }
+}
+
+/* ---------------------------------------------------------------- the step */
+
+/*
+ * Full step for s_q tokens.
+ *   q           bf16 bits [s_q][h][d]
+ *   kv_pool     kv_format 0: u8 E4M3 codes [n_rows][d];  1: bf16 bits [n_rows][d]
+ *   kv_scales   kv_format 0: u8 UE8M0 [n_rows][d/32];   1: unused (may be NULL)
+ *   indices     i32 [s_q][topk] rows of kv_pool, -1 = empty
+ *   topk_length i32 [s_q]: only entries j < min(topk_length, topk) are read
+ *   positions   i32 [s_q]
+ *   norm_w      f64 [d]
+ *   outputs: out_f64 [s_q][h][d] (pre-quant, after inverse RoPE), out_fp8 [s_q][h][d],
+ *            out_scales [s_q][h][d/32]; out_f64 may be NULL.
+ * Returns ORACLE_OK or a negative error.
+ */
+int oracle_sparse_mla(const uint16_t* q, const void* kv_pool, const uint8_t* kv_scales,
+                      const int32_t* indices, const int32_t* topk_length, const int32_t* positions,
+                      const double* norm_w, int s_q, int h, int d, int rope_dim, int topk,
+                      int64_t n_rows, int kv_format, double sm_scale, double eps, double theta,
+                      double* out_f64, uint8_t* out_fp8, uint8_t* out_scales) {
+  int t;
+  int status = ORACLE_OK;
+  if (s_q < 0 || h < 1 || d < 1 || d % BLOCK != 0 || rope_dim < 0 || rope_dim > d ||
+      rope_dim % 2 != 0 || topk < 0 || n_rows < 1 || (kv_format != KV_E4M3_UE8M0 && kv_format != KV_BF16))
+    return ORACLE_ERR_ARG;
+  if (kv_format == KV_E4M3_UE8M0 && kv_scales == NULL) return ORACLE_ERR_ARG;
+
+  /* validate the read prefix of every row first */
+  for (t = 0; t < s_q; ++t) {
+    int L = topk_length[t] < topk ? topk_length[t] : topk;
+    int j;
+    for (j = 0; j < L; ++j) {
+      int32_t r = indices[(int64_t)t * topk + j];
+      if (r < -1 || (int64_t)r >= n_rows) return ORACLE_ERR_INDEX;
+    }
+  }
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (t = 0; t < s_q; ++t) {
+    int L = topk_length[t] < topk ? topk_length[t] : topk;
+    int nv = 0, j, hh, i;
+    double pos = (double)positions[t];
+    /* rows of this token, decoded exactly: V[n][d] (K = V) */
+    double* V = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1) * (size_t)d);
+    double* x = (double*)malloc(sizeof(double) * (size_t)d);
+    double* y = (double*)malloc(sizeof(double) * (size_t)d);
+    double* s = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+    double* o = (double*)malloc(sizeof(double) * (size_t)d);
+    if (!V || !x || !y || !s || !o) {
+#pragma omp critical
+      status = ORACLE_ERR_NOMEM;
+      free(V); free(x); free(y); free(s); free(o);
+      continue;
+    }
+    /* valid set J: entries j < L holding a row id >= 0, one term per entry */
+    for (j = 0; j < L; ++j) {
+      int32_t r = indices[(int64_t)t * topk + j];
+      if (r < 0) continue;
+      for (i = 0; i < d; ++i) {
+        double v;
+        if (kv_format == KV_E4M3_UE8M0) {
+          const uint8_t* codes = (const uint8_t*)kv_pool;
+          int e = kv_scales[(int64_t)r * (d / BLOCK) + i / BLOCK];
+          v = oracle_e4m3_decode(codes[(int64_t)r * d + i]) * ldexp(1.0, e - 127);
+        } else {
+          const uint16_t* bits = (const uint16_t*)kv_pool;
+          v = oracle_bf16_decode(bits[(int64_t)r * d + i]);
+        }
+        V[(int64_t)nv * d + i] = v;
+      }
+      ++nv;
+    }
+    for (hh = 0; hh < h; ++hh) {
+      int64_t base = ((int64_t)t * h + hh) * d;
+      /* 1-3: decode q, per-head RMSNorm, RoPE at the token's position */
+      for (i = 0; i < d; ++i) x[i] = oracle_bf16_decode(q[base + i]);
+      oracle_rmsnorm(x, norm_w, d, eps, y);
+      oracle_rope(y, d, rope_dim, pos, theta, +1);
+      /* 4-6: softmax attention over the valid rows (exact two-pass softmax) */
+      for (i = 0; i < d; ++i) o[i] = 0.0;
+      if (nv > 0) {
+        double m = -INFINITY, l = 0.0;
+        for (j = 0; j < nv; ++j) {
+          double acc = 0.0;
+          for (i = 0; i < d; ++i) acc += y[i] * V[(int64_t)j * d + i];
+          s[j] = sm_scale * acc;
+          if (s[j] > m) m = s[j];
+        }
+        for (j = 0; j < nv; ++j) {
+          double p = exp(s[j] - m);
+          l += p;
+          for (i = 0; i < d; ++i) o[i] += p * V[(int64_t)j * d + i];
+        }
+        for (i = 0; i < d; ++i) o[i] /= l;
+      }
+      /* 7: inverse RoPE at the same position */
+      oracle_rope(o, d, rope_dim, pos, theta, -1);
+      /* 8: UE8M0 + E4M3 */
+      if (out_f64)
+        for (i = 0; i < d; ++i) out_f64[base + i] = o[i];
+      oracle_quantize_blocks(o, d, out_fp8 + base, out_scales + ((int64_t)t * h + hh) * (d / BLOCK));
+    }
+    free(V); free(x); free(y); free(s); free(o);
+  }
+  return status;
+}
+
+/* Number of OpenMP threads a parallel region of the oracle uses. */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

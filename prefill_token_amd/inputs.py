@@ -1,0 +1,194 @@
+"""Seeded synthetic inputs for the sparse-MLA step (shared by the tests, the oracle and the bench).
+
+This module holds no arithmetic of the step itself: it only draws random numbers and
+lays them out.  The KV pool producer (the KV-insert step, which sits before the path)
+is stood in for by the OCP MX v1.0 scale rule -- X = 2^(floor(log2 amax) - 8), E4M3
+elements saturated to +-448 -- with the E4M3 and bf16 roundings done by torch's
+library casts.  Neither the oracle nor the GPU library imports anything from here
+except through the arrays it returns.
+
+Workloads (shapes and distributions from the pages' kernel benchmark,
+[vLLM #56344 "Deepseek V41 Attention MegaKernel", Performance]: h_q = 64, topk 128
+SWA + 512 compressed, fp8_ds_mla KV rows of 512 E4M3 bytes + UE8M0 scales):
+
+  index  name             s_q   pools (SWA + compressed)     row
+  0      tiny             4     bf16 [256, 128]              48 distinct ids, 10 % -> -1
+  1      decode_sq1       1     8192 + 2048  fp8             128 SWA before pos + 512 comp, 10 % -> -1
+  2      decode_sq64      64    8192 + 2048  fp8             as decode_sq1
+  3      decode_sq1024    1024  65536 + 16384 fp8            as decode_sq1, L ~ U[64, 640], tail -> -1
+  4      prefill_sq2123   2123  8192 + 16384 fp8             causal 128 window incl. pos + 512 comp
+  5      decode_sq256     256   8192 + 2048  fp8             as decode_sq1 (the pages' s_q = 256 row)
+  6      prefill_sq184    184   8192 + 16384 fp8             as prefill_sq2123 (the pages' 184 row)
+
+Generation order per workload (numpy PCG64, seed 20260000 + index): positions, norm_w,
+q, pool latents, then per token the index row (compressed ids drawn without
+replacement, then the sentinel mask), then topk_length.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional
+
+import numpy as np
+import torch
+
+KV_E4M3_UE8M0 = 0
+KV_BF16 = 1
+
+SEED_BASE = 20260000
+
+
+@dataclass
+class Workload:
+    name: str
+    index: int
+    s_q: int
+    h: int
+    d: int
+    rope_dim: int
+    topk: int
+    n_swa: int
+    n_comp: int
+    kv_format: int
+    kind: str  # "tiny", "decode", "decode_ragged", "prefill"
+    sentinel_p: float
+    description: str
+
+    @property
+    def n_rows(self) -> int:
+        return self.n_swa + self.n_comp
+
+
+WORKLOADS: List[Workload] = [
+    Workload("tiny", 0, 4, 8, 128, 32, 48, 256, 0, KV_BF16, "tiny", 0.1,
+             "tiny: s_q=4, h_q=8, d=128 (32 rotary), bf16 pool [256,128], 48 ids/token, 10% -1"),
+    Workload("decode_sq1", 1, 1, 64, 512, 64, 640, 8192, 2048, KV_E4M3_UE8M0, "decode", 0.1,
+             "decode s_q=1, h_q=64, d=512 (64 rotary), topk 128 SWA + 512 compressed, fp8 pools 8192+2048"),
+    Workload("decode_sq64", 2, 64, 64, 512, 64, 640, 8192, 2048, KV_E4M3_UE8M0, "decode", 0.1,
+             "decode s_q=64, h_q=64, d=512 (64 rotary), topk 128 SWA + 512 compressed, fp8 pools 8192+2048"),
+    Workload("decode_sq1024", 3, 1024, 64, 512, 64, 640, 65536, 16384, KV_E4M3_UE8M0, "decode_ragged", 0.0,
+             "decode s_q=1024, h_q=64, d=512 (64 rotary), topk_length ~ U[64,640], fp8 pools 65536+16384"),
+    Workload("prefill_sq2123", 4, 2123, 64, 512, 64, 640, 8192, 16384, KV_E4M3_UE8M0, "prefill", 0.0,
+             "prefill s_q=2123 contiguous positions, h_q=64, d=512 (64 rotary), topk 640, fp8 pools 8192+16384"),
+    Workload("decode_sq256", 5, 256, 64, 512, 64, 640, 8192, 2048, KV_E4M3_UE8M0, "decode", 0.1,
+             "decode s_q=256, h_q=64, d=512 (64 rotary), topk 128 SWA + 512 compressed, fp8 pools 8192+2048"),
+    Workload("prefill_sq184", 6, 184, 64, 512, 64, 640, 8192, 16384, KV_E4M3_UE8M0, "prefill", 0.0,
+             "prefill s_q=184 contiguous positions, h_q=64, d=512 (64 rotary), topk 640, fp8 pools 8192+16384"),
+]
+BY_NAME: Dict[str, Workload] = {w.name: w for w in WORKLOADS}
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (torch's RNE cast) and return the bit patterns (u16)."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def bf16_values(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float32 values (a reinterpretation, exact)."""
+    return (np.asarray(bits, dtype=np.uint32) << 16).view(np.float32)
+
+
+def mx_pool(latents: np.ndarray):
+    """Stand-in KV producer: OCP MX scale per 32-block, E4M3 codes by torch's cast.
+
+    Returns ``(codes u8 [n, d], scales u8 [n, d/32])``.
+    """
+    n, d = latents.shape
+    blocks = latents.reshape(n, d // 32, 32).astype(np.float32)
+    amax = np.abs(blocks).max(axis=2)
+    _, k = np.frexp(amax)  # amax = f * 2^k, f in [0.5, 1)
+    X = np.where(amax > 0, k - 1 - 8, -127).astype(np.int32)
+    X = np.clip(X, -127, 127)
+    scaled = blocks / np.exp2(X.astype(np.float32))[..., None]
+    scaled = np.clip(scaled, -448.0, 448.0)
+    codes = torch.from_numpy(np.ascontiguousarray(scaled.reshape(n, d))).to(torch.float8_e4m3fn)
+    return codes.view(torch.uint8).numpy().copy(), (X + 127).astype(np.uint8)
+
+
+def _rng(index: int, seed: Optional[int]) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(SEED_BASE + index if seed is None else seed))
+
+
+def make(workload, seed: Optional[int] = None, s_q: Optional[int] = None) -> dict:
+    """Build the arrays of one workload.
+
+    ``workload`` is a name or an index; ``seed`` overrides the default seed; ``s_q``
+    overrides the token count (same recipe, fewer or more tokens).
+    """
+    w = BY_NAME[workload] if isinstance(workload, str) else WORKLOADS[workload]
+    rng = _rng(w.index, seed)
+    S = w.s_q if s_q is None else int(s_q)
+    h, d = w.h, w.d
+
+    # positions
+    if w.kind == "prefill":
+        off = int(rng.integers(0, 30000))
+        positions = (off + np.arange(S)).astype(np.int32)
+    else:
+        positions = rng.integers(0, 32768, size=S).astype(np.int32)
+    # norm weight ~ N(1, 0.1), held in fp32 at bf16-representable values
+    norm_w = bf16_values(bf16_bits(rng.normal(1.0, 0.1, size=d).astype(np.float32)))
+    # queries ~ N(0, 1) in bf16
+    q = bf16_bits(rng.standard_normal(size=(S, h, d), dtype=np.float32))
+    # pool
+    if w.kv_format == KV_BF16:
+        kv_pool = bf16_bits(rng.standard_normal(size=(w.n_rows, d), dtype=np.float32))
+        kv_scales = None
+    else:
+        lat = rng.standard_normal(size=(w.n_rows, d), dtype=np.float32)
+        kv_pool, kv_scales = mx_pool(lat)
+        del lat
+    # index rows
+    topk = w.topk
+    indices = np.full((S, topk), -1, dtype=np.int32)
+    if w.kind == "tiny":
+        for t in range(S):
+            indices[t] = rng.choice(w.n_rows, size=topk, replace=False)
+        mask = rng.random(size=(S, topk)) < w.sentinel_p
+        indices[mask] = -1
+        topk_length = np.full(S, topk, dtype=np.int32)
+    else:
+        n_win = 128
+        n_cmp = topk - n_win
+        if w.kind == "prefill":
+            win = positions[:, None] - (n_win - 1) + np.arange(n_win)[None, :]  # p-127 .. p
+        else:
+            win = positions[:, None] - n_win + np.arange(n_win)[None, :]  # p-128 .. p-1
+        indices[:, :n_win] = np.where(win >= 0, np.mod(win, w.n_swa), -1)
+        for t in range(S):
+            indices[t, n_win:] = w.n_swa + rng.choice(w.n_comp, size=n_cmp, replace=False)
+        if w.sentinel_p > 0:
+            mask = rng.random(size=(S, topk)) < w.sentinel_p
+            indices[mask] = -1
+        if w.kind == "decode_ragged":
+            topk_length = rng.integers(64, topk + 1, size=S).astype(np.int32)
+            cols = np.arange(topk)[None, :]
+            indices[cols >= topk_length[:, None]] = -1
+        else:
+            topk_length = np.full(S, topk, dtype=np.int32)
+    return dict(
+        name=w.name, description=w.description, s_q=S, h=h, d=d, rope_dim=w.rope_dim, topk=topk,
+        n_rows=w.n_rows, n_swa=w.n_swa, kv_format=w.kv_format,
+        sm_scale=1.0 / math.sqrt(d), eps=1e-6, theta=10000.0,
+        q=q, kv_pool=kv_pool, kv_scales=kv_scales, indices=indices,
+        topk_length=topk_length, positions=positions, norm_w=norm_w.astype(np.float32),
+    )
+
+
+def take_tokens(inp: dict, tokens) -> dict:
+    """The same inputs restricted to a subset of tokens (the pool is shared)."""
+    tokens = np.asarray(tokens, dtype=np.int64)
+    out = dict(inp)
+    for k in ("q", "indices", "topk_length", "positions"):
+        out[k] = np.ascontiguousarray(inp[k][tokens])
+    out["s_q"] = int(tokens.size)
+    return out
+
+
+def valid_rows(inp: dict) -> np.ndarray:
+    """Number of entries each token actually reads (j < topk_length and id >= 0)."""
+    L = np.minimum(inp["topk_length"], inp["topk"])
+    cols = np.arange(inp["topk"])[None, :]
+    return ((cols < L[:, None]) & (inp["indices"] >= 0)).sum(axis=1)
