@@ -1,0 +1,289 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused sparse-MLA step (sparse_mla_fwd) on one MI355X.
+
+A step is one sparse_mla_fwd call over one batch of seeded synthetic inputs, replayed
+from a HIP graph (inputs resident in HBM).  The headline workload is the s_q = 1 decode
+(h_q = 64, d = 512 with 64 rotary dims, topk 128 SWA + 512 compressed, E4M3 + UE8M0
+pools); the s_q = 64 / 256 / 1024 decodes and the 184 / 2123-token prefills are measured
+after the timed region and reported under "configs".
+
+Prints one JSON line:
+  value        tokens/s of the headline workload over the K timed steps (wall clock)
+  roofline     the headline call's compulsory HBM bytes / its mean duration (HIP events
+               on the launch stream) against 8 TB/s
+  cpu_baseline the fp64 oracle on a bounded sample of the same recipe, on the host cores
+  configs      per workload: us/call (warm and after a cache flush), tokens/s, HBM and
+               MFMA fractions
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import subprocess
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse_mla_fwd µs/call + tokens/s and % HBM/MFMA roofline at s_q=1/64/1024"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 / fp16 MFMA
+PAGES_US_SQ1 = 22.7            # pages' fused kernel at s_q = 1 (GB200, TP4, CUDA graph): context only
+EXTRA = ["decode_sq64", "decode_sq1024", "prefill_sq2123", "decode_sq256", "prefill_sq184"]
+FLUSH_BYTES = 512 << 20        # larger than the 256 MB MALL + 8 x 4 MB L2
+
+
+def upload(inp, torch, device):
+    t = {"q": torch.from_numpy(inp["q"].view(np.int16)).to(device).view(torch.bfloat16)}
+    t["kv_pool"] = torch.from_numpy(inp["kv_pool"]).to(device)
+    t["kv_scales"] = torch.from_numpy(inp["kv_scales"]).to(device)
+    for k in ("indices", "topk_length", "positions"):
+        t[k] = torch.from_numpy(np.ascontiguousarray(inp[k], dtype=np.int32)).to(device)
+    t["norm_w"] = torch.from_numpy(np.ascontiguousarray(inp["norm_w"], dtype=np.float32)).to(device)
+    return t
+
+
+def work_model(inp):
+    """Algorithmic flops and bytes of one call (valid entries only)."""
+    from prefill_token_amd import inputs
+
+    s_q, h, d = inp["q"].shape
+    nv = inputs.valid_rows(inp).astype(np.int64)
+    row_bytes = d + d // 32
+    flops = 4.0 * h * d * float(nv.sum())
+    L = np.minimum(inp["topk_length"], inp["topk"])
+    cols = np.arange(inp["topk"])[None, :]
+    valid = (cols < L[:, None]) & (inp["indices"] >= 0)
+    distinct = np.unique(inp["indices"][valid]).size
+    per_tok_fixed = 2 * h * d + 4 * inp["topk"] + 8 + h * d + h * d // 32
+    gathered = float(s_q * per_tok_fixed + row_bytes * nv.sum())
+    compulsory = float(s_q * per_tok_fixed + row_bytes * distinct)
+    return dict(flops=flops, gathered_bytes=gathered, compulsory_bytes=compulsory, valid_rows=int(nv.sum()),
+                distinct_rows=int(distinct))
+
+
+def measure(name, steps, warmup, torch, device, timed_steps=None):
+    """Time one workload; returns (result dict, wall seconds of the timed steps)."""
+    from prefill_token_amd import inputs, make_params, sparse_mla_fwd, sparse_mla_num_splits, sparse_mla_workspace_size
+
+    inp = inputs.make(name)
+    t = upload(inp, torch, device)
+    s_q, h, d = inp["q"].shape
+    out_fp8 = torch.empty((s_q, h, d), dtype=torch.uint8, device=device)
+    out_sc = torch.empty((s_q, h, d // 32), dtype=torch.uint8, device=device)
+    p = make_params(s_q=s_q, h_q=h, d=d, rope_dim=inp["rope_dim"], topk=inp["topk"], n_rows=inp["n_rows"],
+                    kv_format=inp["kv_format"], sm_scale=inp["sm_scale"])
+    ns = sparse_mla_num_splits(p)
+    need = sparse_mla_workspace_size(p)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+
+    def call():
+        sparse_mla_fwd(t["q"], t["kv_pool"], t["kv_scales"], t["indices"], t["topk_length"], t["positions"],
+                       t["norm_w"], out_fp8, out_sc, sm_scale=inp["sm_scale"], rope_dim=inp["rope_dim"],
+                       eps=inp["eps"], theta=inp["theta"], workspace=ws if need else None)
+
+    for _ in range(max(warmup, 1)):
+        call()
+    torch.cuda.synchronize()
+    eager_ref = (out_fp8.clone(), out_sc.clone())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    graph.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out_fp8, eager_ref[0]) and torch.equal(out_sc, eager_ref[1]), "graph replay differs"
+
+    n = timed_steps if timed_steps is not None else steps
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n):
+        ev[i][0].record(stream)
+        graph.replay()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+
+    # cold: flush the caches before each replay (outside the event pair)
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=device)
+    cold = []
+    for _ in range(max(5, min(steps, 20))):
+        flush.zero_()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        graph.replay()
+        b.record(stream)
+        b.synchronize()
+        cold.append(a.elapsed_time(b) * 1e3)
+    cold = np.array(cold)
+    del flush
+    assert torch.equal(out_fp8, eager_ref[0]), "replay after flush differs"
+
+    wm = work_model(inp)
+    mean_us = float(us.mean())
+    res = dict(
+        workload=name, description=inp["description"], s_q=s_q, num_splits=ns,
+        kernels="smla_main" + (" + smla_combine" if ns > 1 else ""),
+        us_per_call_mean=mean_us, us_per_call_median=float(np.median(us)),
+        us_per_call_p10=float(np.percentile(us, 10)), us_per_call_p90=float(np.percentile(us, 90)),
+        us_per_call_cold_median=float(np.median(cold)),
+        tokens_per_s=s_q / (mean_us * 1e-6), tokens_per_s_cold=s_q / (float(np.median(cold)) * 1e-6),
+        hbm_compulsory_GBs=wm["compulsory_bytes"] / (mean_us * 1e-6) / 1e9,
+        hbm_compulsory_frac=wm["compulsory_bytes"] / (mean_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        gather_effective_GBs=wm["gathered_bytes"] / (mean_us * 1e-6) / 1e9,
+        mfma_TFLOPs=wm["flops"] / (mean_us * 1e-6) / 1e12,
+        mfma_frac=wm["flops"] / (mean_us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS,
+        hbm_cold_frac=wm["compulsory_bytes"] / (float(np.median(cold)) * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        mfma_cold_frac=wm["flops"] / (float(np.median(cold)) * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS,
+        **wm,
+    )
+    return res, wall, n
+
+
+def cpu_baseline(seconds, torch, device):
+    """The oracle on a bounded sample of the headline recipe, all host threads."""
+    import oracle
+    from prefill_token_amd import inputs
+
+    sample_tokens = 64
+    inp = inputs.make("decode_sq1", seed=20261001, s_q=sample_tokens)
+    args = (inp["q"], inp["kv_pool"], inp["kv_scales"], inp["indices"], inp["topk_length"], inp["positions"],
+            inp["norm_w"])
+    kw = dict(sm_scale=inp["sm_scale"], eps=inp["eps"], theta=inp["theta"], rope_dim=inp["rope_dim"])
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        o, codes, scales = oracle.sparse_mla(*args, **kw)
+        reps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    # the same sample through the library, compared with the oracle (pre-quant error)
+    from prefill_token_amd import sparse_mla_fwd
+
+    t = upload(inp, torch, device)
+    out_fp8 = torch.empty(inp["q"].shape, dtype=torch.uint8, device=device)
+    out_sc = torch.empty(inp["q"].shape[:2] + (inp["d"] // 32,), dtype=torch.uint8, device=device)
+    out_f32 = torch.empty(inp["q"].shape, dtype=torch.float32, device=device)
+    sparse_mla_fwd(t["q"], t["kv_pool"], t["kv_scales"], t["indices"], t["topk_length"], t["positions"],
+                   t["norm_w"], out_fp8, out_sc, out_f32=out_f32, **kw)
+    torch.cuda.synchronize()
+    g = out_f32.cpu().numpy().astype(np.float64)
+    blk = o.reshape(*o.shape[:-1], -1, 32)
+    amax = np.abs(blk).max(-1)
+    err = np.abs(g.reshape(blk.shape) - blk).max(-1) / np.maximum(amax, 1e-300)
+    return {
+        "value": sample_tokens * reps / el, "unit": "tokens/s", "cores": min(oracle.num_threads(), sample_tokens),
+        "kind": "oracle",
+        "sample": f"{sample_tokens} decode tokens drawn with the decode s_q=1 recipe (same shapes, index mix "
+                  f"and distributions), {reps} repetition(s), {el:.1f} s",
+        "seconds": el, "gpu_vs_oracle_max_rel_block_err": float(err.max()),
+    }
+
+
+def host_info():
+    info = {"nproc": os.cpu_count(), "machine": platform.machine()}
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name"):
+                info["cpu_model"] = line.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    return info
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for fn in ("smla_kernels.hip", "smla_api.cpp", "smla_internal.h"):
+        with open(os.path.join(ROOT, "prefill_token_amd", "csrc", fn), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(digest):
+    """HBM bytes per call from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic_decode_sq1.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        if rec.get("source_digest") == digest:
+            return float(rec["hbm_bytes_per_call"])
+    except Exception:
+        pass
+    return None
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_sq1")
+    ap.add_argument("--extra", default=",".join(EXTRA), help="comma-separated workloads after the timed region")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build measures one GPU only: the step runs on a single MI355X and "
+                                   "has no multi-GPU path; run with --gpus 1"}), flush=True)
+        sys.exit(2)
+
+    import torch
+
+    from prefill_token_amd import _lib
+
+    _lib.load()  # fails loudly when the HIP library has not been built
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+
+    head, wall, n = measure(args.workload, args.steps, args.warmup, torch, device, timed_steps=args.steps)
+    configs = [head]
+    for name in [x for x in args.extra.split(",") if x and x != args.workload]:
+        r, _, _ = measure(name, args.steps, args.warmup, torch, device)
+        configs.append(r)
+        print(f"# {name}: {r['us_per_call_mean']:.2f} us/call, {r['tokens_per_s']:.4g} tok/s, "
+              f"HBM {100 * r['hbm_compulsory_frac']:.1f}%, MFMA {100 * r['mfma_frac']:.1f}%", file=sys.stderr,
+              flush=True)
+
+    digest = source_digest()
+    traffic = load_traffic(digest)
+    achieved = head["compulsory_bytes"] / (head["us_per_call_mean"] * 1e-6) / 1e9
+    roofline = {
+        "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+        "traffic": traffic, "kernel": head["kernels"], "scope": "whole sparse_mla_fwd call (HIP events on its stream)",
+        "bytes_per_call": head["compulsory_bytes"], "mean_us": head["us_per_call_mean"],
+    }
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.cpu_seconds, torch, device)
+    value = head["s_q"] * n / wall
+    out = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": n, "warmup": args.warmup,
+        "ms_per_step": wall / n * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": value / (1e6 / PAGES_US_SQ1),
+        "vs_baseline_note": "value / (1 / 22.7 us): the pages' fused kernel at s_q=1 on GB200 TP4 (context, "
+                            "another machine)",
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": head["description"], "name": head["workload"], "s_q": head["s_q"],
+                   "num_splits": head["num_splits"], "graph": True},
+        "roofline": roofline, "cpu_baseline": cpu, "configs": configs,
+        "device": torch.cuda.get_device_name(device), "host": host_info(), "source_digest": digest,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

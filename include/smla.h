@@ -1,0 +1,137 @@
+/*
+ * smla.h -- C ABI of the fused sparse-MLA attention step for AMD Instinct MI355X (gfx950).
+ *
+ * The operation [vLLM #56344 "Deepseek V41 Attention MegaKernel", Purpose, first
+ * bullet: the fused norm + RoPE + sparse-attention + inverse-RoPE + FP8-cast kernel]:
+ * for every query token t and head h,
+ *
+ *   1. x = q[t, h, :] (bf16); y = x / sqrt(mean(x^2) + eps) * norm_w   (per-head RMSNorm,
+ *      [SGLang #39370 "[DSV4.1] Combine DSpark decode and prefill kernel optimizations",
+ *      Summary: q_head_norm])
+ *   2. rotate-half RoPE on the last rope_dim dims of y at angle positions[t] * theta^(-2i/rope_dim)
+ *   3. J = { j < min(topk_length[t], topk) : indices[t, j] >= 0 }  -- entries at or beyond
+ *      topk_length are never read, -1 marks an empty slot
+ *      [vLLM #56344, Purpose, bug-fix bullet: reads capped at topk_length, -1 sentinels]
+ *   4. v_j = dequant(kv_pool[indices[t, j]]) -- one latent row per entry, used as both K
+ *      and V by every head (MLA), stored as 512 E4M3 bytes + one UE8M0 scale per 32
+ *      elements [vLLM #56344, Purpose: fp8 528 B rows]
+ *   5. o = sum_j softmax_j(sm_scale * <y, v_j>) v_j  (o = 0 when J is empty)
+ *   6. inverse RoPE (rotation by the negated angle) on the last rope_dim dims of o
+ *   7. per 32-element block: e = smallest integer in [0, 254] with 448 * 2^(e-127) >= max|o|,
+ *      out_scales = e, out_fp8 = round-to-nearest-even E4M3FN(o * 2^(127-e))
+ *      [SGLang #39370, commit note on the MXFP8 epilogue: UE8M0 block scales]
+ *
+ * Every decode or prefill token carries its own row of metadata (position, index row,
+ * length), so one call covers a flattened batch of tokens
+ * [vLLM #56344, Purpose, second bullet].
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers (HIP global memory) to contiguous
+ *     row-major arrays owned by the caller.  The library keeps no reference after
+ *     the call returns, allocates nothing and never synchronizes the device.
+ *   - The work is enqueued on params->stream (a hipStream_t; NULL = the null stream)
+ *     and completes asynchronously; the call may be captured in a HIP graph.
+ *   - Errors are reported by return code, never by exception or abort; the
+ *     thread-local message of the last failure is available from
+ *     sparse_mla_last_error().  Argument checks run on the host before any HIP call,
+ *     so a rejected call launches nothing.
+ */
+#ifndef SMLA_H
+#define SMLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SMLA_ABI_VERSION 1
+
+/* return codes */
+#define SMLA_OK 0
+#define SMLA_ERR_NULL 1  /* a required pointer is NULL */
+#define SMLA_ERR_SHAPE 2 /* unsupported d / rope_dim / h_q / topk combination */
+#define SMLA_ERR_VALUE 3 /* bad scalar (s_q < 0, n_rows < 1, non-finite or non-positive
+                            sm_scale / rms_eps / rope_theta, workspace too small,
+                            bad kv_format, num_splits out of range) */
+#define SMLA_ERR_HIP 4   /* a HIP launch failed */
+
+/* kv_pool formats */
+#define SMLA_KV_E4M3_UE8M0 0 /* kv_pool u8 [n_rows][d] E4M3FN codes, kv_scales u8 [n_rows][d/32] UE8M0 */
+#define SMLA_KV_BF16 1       /* kv_pool bf16 bits u16 [n_rows][d], kv_scales unused (may be NULL) */
+
+typedef struct smla_params {
+  int32_t s_q;      /* number of query tokens (0 = no-op) */
+  int32_t h_q;      /* heads per token, 1..64 */
+  int32_t d;        /* latent / head dim: 128 or 512 */
+  int32_t rope_dim; /* rotary dims at the end of each head: 0..d, a multiple of 16 */
+  int32_t topk;     /* row stride of `indices` (entries per token), 0..65536 */
+  int32_t kv_format;
+  int64_t n_rows;   /* rows in kv_pool (>= 1); every read index must lie in [-1, n_rows) */
+  float sm_scale;   /* softmax scale, finite and > 0 (typically 1/sqrt(d)) */
+  float rms_eps;    /* RMSNorm epsilon, finite and > 0 */
+  float rope_theta; /* RoPE base, finite and > 0 */
+  int32_t num_splits; /* 0 = automatic; else split each token's entries over this many
+                         workgroups (1..64) and combine */
+  float* out_f32;   /* optional f32 [s_q][h_q][d]: o after inverse RoPE, before the FP8
+                       cast (NULL = not written) */
+  void* workspace;  /* device scratch of >= sparse_mla_workspace_size(params) bytes, or
+                       NULL when that size is 0; contents need no initialization and
+                       are clobbered */
+  size_t workspace_bytes;
+  void* stream;     /* hipStream_t */
+} smla_params;
+
+/*
+ * The fused step (steps 1-7 above) for params->s_q tokens.
+ *
+ *   q           bf16 [s_q][h_q][d]            (device, read)
+ *   kv_pool     see kv_format                 (device, read)
+ *   kv_scales   u8 [n_rows][d/32] or NULL     (device, read)
+ *   indices     i32 [s_q][topk]               (device, read) -1 = empty slot; entries
+ *                                             j >= topk_length[t] are ignored whatever
+ *                                             they hold
+ *   topk_length i32 [s_q]                     (device, read) values > topk are capped at
+ *                                             topk, values <= 0 mean no entries
+ *   positions   i32 [s_q]                     (device, read) RoPE position of each token
+ *   norm_w      f32 [d]                       (device, read) RMSNorm weight
+ *   out_fp8     u8 [s_q][h_q][d]              (device, written) E4M3FN codes
+ *   out_scales  u8 [s_q][h_q][d/32]           (device, written) UE8M0 exponents
+ *   params      host pointer, read during the call only
+ *
+ * Preconditions not checked on the device (the values are in device memory): read
+ * indices lie in [-1, n_rows); kv_scales lie in [10, 246], the range in which every
+ * dequantized E4M3 value is a normal bf16 number (outside it, tiny values are rounded
+ * by the hardware conversion and huge ones overflow).
+ *
+ * Returns SMLA_OK, or SMLA_ERR_* with nothing launched (SMLA_ERR_HIP: a launch failed).
+ */
+int sparse_mla_fwd(const void* q, const void* kv_pool, const uint8_t* kv_scales,
+                   const int32_t* indices, const int32_t* topk_length, const int32_t* positions,
+                   const float* norm_w, uint8_t* out_fp8, uint8_t* out_scales,
+                   const smla_params* params);
+
+/*
+ * Bytes of device workspace sparse_mla_fwd needs for these parameters (0 when the
+ * call runs unsplit).  Depends on s_q, h_q, d, topk and num_splits only.  Returns 0
+ * for parameters sparse_mla_fwd would reject.
+ */
+size_t sparse_mla_workspace_size(const smla_params* params);
+
+/* The number of splits per token sparse_mla_fwd will use for these parameters (>= 1),
+   or 0 for parameters it would reject. */
+int sparse_mla_num_splits(const smla_params* params);
+
+/* Thread-local, NUL-terminated message describing the last failed call on this thread
+   ("" if none).  Valid until the next call on the same thread. */
+const char* sparse_mla_last_error(void);
+
+/* SMLA_ABI_VERSION of the loaded library. */
+int sparse_mla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SMLA_H */

@@ -1,0 +1,106 @@
+"""MI355X (gfx950) fused sparse-MLA attention step.
+
+The compute runs in ``libsmla.so`` (hand-written HIP kernels behind the C ABI of
+``include/smla.h``).  This module only marshals torch tensors (device memory) and the
+current HIP stream into that ABI; there is no other implementation to fall back on.
+
+    from prefill_token_amd import sparse_mla_fwd
+    sparse_mla_fwd(q, kv_pool, kv_scales, indices, topk_length, positions, norm_w,
+                   out_fp8, out_scales, sm_scale=..., rope_dim=64)
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+from . import _lib
+from ._lib import (SMLA_ERR_HIP, SMLA_ERR_NULL, SMLA_ERR_SHAPE, SMLA_ERR_VALUE, SMLA_KV_BF16,
+                   SMLA_KV_E4M3_UE8M0, SMLA_OK, LibraryMissing, SmlaParams, last_error)
+
+__all__ = [
+    "sparse_mla_fwd", "sparse_mla_workspace_size", "sparse_mla_num_splits", "sparse_mla_last_error",
+    "sparse_mla_abi_version", "make_params", "SmlaParams", "SmlaError", "LibraryMissing",
+    "SMLA_OK", "SMLA_ERR_NULL", "SMLA_ERR_SHAPE", "SMLA_ERR_VALUE", "SMLA_ERR_HIP",
+    "SMLA_KV_E4M3_UE8M0", "SMLA_KV_BF16",
+]
+
+
+class SmlaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"sparse_mla_fwd failed (code {code}): {msg}")
+        self.code = code
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def make_params(*, s_q: int, h_q: int, d: int, rope_dim: int, topk: int, n_rows: int, kv_format: int,
+                sm_scale: float, eps: float = 1e-6, theta: float = 1e4, num_splits: int = 0,
+                out_f32=None, workspace=None, stream=None) -> SmlaParams:
+    p = SmlaParams()
+    p.s_q, p.h_q, p.d, p.rope_dim, p.topk, p.kv_format = s_q, h_q, d, rope_dim, topk, kv_format
+    p.n_rows = n_rows
+    p.sm_scale, p.rms_eps, p.rope_theta = sm_scale, eps, theta
+    p.num_splits = num_splits
+    p.out_f32 = _ptr(out_f32)
+    p.workspace = _ptr(workspace)
+    p.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    p.stream = stream
+    return p
+
+
+def sparse_mla_workspace_size(params: SmlaParams) -> int:
+    return int(_lib.load().sparse_mla_workspace_size(ctypes.byref(params)))
+
+
+def sparse_mla_num_splits(params: SmlaParams) -> int:
+    return int(_lib.load().sparse_mla_num_splits(ctypes.byref(params)))
+
+
+def sparse_mla_last_error() -> str:
+    return last_error()
+
+
+def sparse_mla_abi_version() -> int:
+    return int(_lib.load().sparse_mla_abi_version())
+
+
+def sparse_mla_fwd(q, kv_pool, kv_scales, indices, topk_length, positions, norm_w, out_fp8, out_scales, *,
+                   sm_scale: float, rope_dim: int, eps: float = 1e-6, theta: float = 1e4, out_f32=None,
+                   workspace=None, num_splits: int = 0, stream=None) -> None:
+    """Enqueue the fused step on the current (or given) HIP stream.
+
+    q bf16 [s_q, h_q, d]; kv_pool uint8 / float8_e4m3fn [n, d] (E4M3 codes, with
+    kv_scales uint8 [n, d/32]) or bf16 [n, d] (kv_scales None); indices / topk_length /
+    positions int32; norm_w float32 [d]; out_fp8 uint8 / float8_e4m3fn [s_q, h_q, d];
+    out_scales uint8 [s_q, h_q, d/32]; out_f32 optional float32 [s_q, h_q, d].
+    ``workspace`` (a uint8 device tensor) is allocated here when the call needs one and
+    none is given.  Raises SmlaError with the library's message on failure.
+    """
+    import torch
+
+    s_q, h_q, d = q.shape
+    bf16_pool = kv_pool.dtype == torch.bfloat16
+    kv_format = SMLA_KV_BF16 if bf16_pool else SMLA_KV_E4M3_UE8M0
+    for name, t in (("q", q), ("kv_pool", kv_pool), ("indices", indices), ("topk_length", topk_length),
+                    ("positions", positions), ("norm_w", norm_w), ("out_fp8", out_fp8),
+                    ("out_scales", out_scales), ("kv_scales", kv_scales), ("out_f32", out_f32)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    topk = indices.shape[1] if indices.dim() == 2 else 0
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    params = make_params(s_q=s_q, h_q=h_q, d=d, rope_dim=rope_dim, topk=topk, n_rows=kv_pool.shape[0],
+                         kv_format=kv_format, sm_scale=sm_scale, eps=eps, theta=theta, num_splits=num_splits,
+                         out_f32=out_f32, workspace=workspace, stream=stream)
+    need = sparse_mla_workspace_size(params)
+    if need > 0 and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        params.workspace = _ptr(workspace)
+        params.workspace_bytes = need
+    rc = _lib.load().sparse_mla_fwd(_ptr(q), _ptr(kv_pool), _ptr(kv_scales), _ptr(indices), _ptr(topk_length),
+                                    _ptr(positions), _ptr(norm_w), _ptr(out_fp8), _ptr(out_scales),
+                                    ctypes.byref(params))
+    if rc != SMLA_OK:
+        raise SmlaError(rc, last_error())

@@ -1,0 +1,75 @@
+"""ctypes view of the C ABI declared in include/smla.h (argument marshalling only)."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsmla.so")
+
+SMLA_OK = 0
+SMLA_ERR_NULL = 1
+SMLA_ERR_SHAPE = 2
+SMLA_ERR_VALUE = 3
+SMLA_ERR_HIP = 4
+
+SMLA_KV_E4M3_UE8M0 = 0
+SMLA_KV_BF16 = 1
+
+
+class SmlaParams(ctypes.Structure):
+    """Mirror of ``smla_params`` (same field order and C layout)."""
+
+    _fields_ = [
+        ("s_q", ctypes.c_int32),
+        ("h_q", ctypes.c_int32),
+        ("d", ctypes.c_int32),
+        ("rope_dim", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
+        ("kv_format", ctypes.c_int32),
+        ("n_rows", ctypes.c_int64),
+        ("sm_scale", ctypes.c_float),
+        ("rms_eps", ctypes.c_float),
+        ("rope_theta", ctypes.c_float),
+        ("num_splits", ctypes.c_int32),
+        ("out_f32", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("stream", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+class LibraryMissing(RuntimeError):
+    pass
+
+
+def load() -> ctypes.CDLL:
+    """Load the in-tree libsmla.so; raises LibraryMissing if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise LibraryMissing(
+            f"{LIB_PATH} is missing: build it with `python -m prefill_token_amd.build` "
+            "(there is no fallback implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    lib.sparse_mla_fwd.restype = ctypes.c_int
+    lib.sparse_mla_fwd.argtypes = [P, P, P, P, P, P, P, P, P, ctypes.POINTER(SmlaParams)]
+    lib.sparse_mla_workspace_size.restype = ctypes.c_size_t
+    lib.sparse_mla_workspace_size.argtypes = [ctypes.POINTER(SmlaParams)]
+    lib.sparse_mla_num_splits.restype = ctypes.c_int
+    lib.sparse_mla_num_splits.argtypes = [ctypes.POINTER(SmlaParams)]
+    lib.sparse_mla_last_error.restype = ctypes.c_char_p
+    lib.sparse_mla_last_error.argtypes = []
+    lib.sparse_mla_abi_version.restype = ctypes.c_int
+    lib.sparse_mla_abi_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().sparse_mla_last_error().decode()

@@ -1,0 +1,140 @@
+// C ABI of the fused sparse-MLA step (declared in include/smla.h): argument checks on
+// the host, split selection, workspace sizing and error reporting.  All checks run
+// before any HIP call, so a rejected call enqueues nothing.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "smla.h"
+#include "smla_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+bool finite_pos(float x) { return isfinite(x) && x > 0.f; }
+
+// Shape/scalar checks shared by every entry point; returns SMLA_OK or an error code.
+int check_params(const smla_params* p) {
+  if (!p) return fail(SMLA_ERR_NULL, "params is NULL");
+  if (p->s_q < 0) return fail(SMLA_ERR_VALUE, "s_q must be >= 0 (got %d)", p->s_q);
+  if (p->n_rows < 1) return fail(SMLA_ERR_VALUE, "n_rows must be >= 1 (got %lld)", (long long)p->n_rows);
+  if (p->kv_format != SMLA_KV_E4M3_UE8M0 && p->kv_format != SMLA_KV_BF16)
+    return fail(SMLA_ERR_VALUE, "unknown kv_format %d", p->kv_format);
+  if (!finite_pos(p->sm_scale)) return fail(SMLA_ERR_VALUE, "sm_scale must be finite and > 0");
+  if (!finite_pos(p->rms_eps)) return fail(SMLA_ERR_VALUE, "rms_eps must be finite and > 0");
+  if (!finite_pos(p->rope_theta)) return fail(SMLA_ERR_VALUE, "rope_theta must be finite and > 0");
+  if (p->num_splits < 0 || p->num_splits > 64)
+    return fail(SMLA_ERR_VALUE, "num_splits must be in [0, 64] (got %d)", p->num_splits);
+  if (p->d != 128 && p->d != 512) return fail(SMLA_ERR_SHAPE, "d must be 128 or 512 (got %d)", p->d);
+  if (p->d == 512 && p->kv_format == SMLA_KV_BF16)
+    return fail(SMLA_ERR_SHAPE, "the bf16 pool is supported for d = 128 only");
+  if (p->h_q < 1 || p->h_q > 64) return fail(SMLA_ERR_SHAPE, "h_q must be in [1, 64] (got %d)", p->h_q);
+  if (p->rope_dim < 0 || p->rope_dim > p->d || p->rope_dim % 16 != 0)
+    return fail(SMLA_ERR_SHAPE, "rope_dim must be a multiple of 16 in [0, d] (got %d)", p->rope_dim);
+  if (p->topk < 0 || p->topk > 65536) return fail(SMLA_ERR_SHAPE, "topk must be in [0, 65536] (got %d)", p->topk);
+  if ((long long)p->s_q * p->topk > 0x7FFFFFFFLL)
+    return fail(SMLA_ERR_SHAPE, "s_q * topk must fit in int32");
+  if (p->s_q > 0x7FFFFFFF / 64) return fail(SMLA_ERR_SHAPE, "s_q too large");
+  return SMLA_OK;
+}
+
+int tiles_of(const smla_params* p) { return (p->topk + smla::kTileRows - 1) / smla::kTileRows; }
+
+// Splits per token: enough workgroups to cover the 256 compute units when few tokens
+// are in flight, never more splits than tiles.
+int choose_splits(const smla_params* p) {
+  const int tiles = tiles_of(p) > 0 ? tiles_of(p) : 1;
+  int ns = p->num_splits;
+  if (ns == 0) {
+    const int target = 256;
+    ns = p->s_q > 0 ? (target + p->s_q - 1) / p->s_q : 1;
+  }
+  if (ns > tiles) ns = tiles;
+  if (ns < 1) ns = 1;
+  return ns;
+}
+
+size_t workspace_bytes_for(const smla_params* p, int ns) {
+  if (ns <= 1) return 0;
+  return (size_t)p->s_q * (size_t)ns * smla::partial_floats(p->h_q, p->d) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int sparse_mla_abi_version(void) { return SMLA_ABI_VERSION; }
+
+const char* sparse_mla_last_error(void) { return g_last_error.c_str(); }
+
+int sparse_mla_num_splits(const smla_params* p) {
+  if (check_params(p) != SMLA_OK) return 0;
+  return choose_splits(p);
+}
+
+size_t sparse_mla_workspace_size(const smla_params* p) {
+  if (check_params(p) != SMLA_OK) return 0;
+  return workspace_bytes_for(p, choose_splits(p));
+}
+
+int sparse_mla_fwd(const void* q, const void* kv_pool, const uint8_t* kv_scales, const int32_t* indices,
+                   const int32_t* topk_length, const int32_t* positions, const float* norm_w, uint8_t* out_fp8,
+                   uint8_t* out_scales, const smla_params* p) {
+  g_last_error.clear();
+  int rc = check_params(p);
+  if (rc != SMLA_OK) return rc;
+  if (p->s_q == 0) return SMLA_OK;
+  if (!q || !kv_pool || !positions || !norm_w || !out_fp8 || !out_scales || !topk_length)
+    return fail(SMLA_ERR_NULL, "a required array pointer is NULL");
+  if (p->topk > 0 && !indices) return fail(SMLA_ERR_NULL, "indices is NULL");
+  if (p->kv_format == SMLA_KV_E4M3_UE8M0 && !kv_scales)
+    return fail(SMLA_ERR_NULL, "kv_scales is NULL for the E4M3 pool");
+  const int ns = choose_splits(p);
+  const size_t need = workspace_bytes_for(p, ns);
+  if (need > 0 && (!p->workspace || p->workspace_bytes < need))
+    return fail(SMLA_ERR_VALUE, "workspace of %zu bytes needed (got %zu)", need,
+                p->workspace ? p->workspace_bytes : (size_t)0);
+
+  smla::LaunchArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.kv_pool = kv_pool;
+  a.kv_scales = kv_scales;
+  a.indices = indices;
+  a.topk_length = topk_length;
+  a.positions = positions;
+  a.norm_w = norm_w;
+  a.out_fp8 = out_fp8;
+  a.out_scales = out_scales;
+  a.out_f32 = p->out_f32;
+  a.workspace = static_cast<float*>(p->workspace);
+  a.s_q = p->s_q;
+  a.h_q = p->h_q;
+  a.d = p->d;
+  a.rope_dim = p->rope_dim;
+  a.topk = p->topk;
+  a.kv_format = p->kv_format;
+  a.num_splits = ns;
+  a.n_rows = p->n_rows;
+  a.sm_scale = p->sm_scale;
+  a.rms_eps = p->rms_eps;
+  a.rope_theta = p->rope_theta;
+  a.stream = static_cast<hipStream_t>(p->stream);
+  const hipError_t e = smla::launch(a);
+  if (e != hipSuccess) return fail(SMLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return SMLA_OK;
+}
+
+}  // extern "C"

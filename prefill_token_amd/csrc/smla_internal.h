@@ -1,0 +1,37 @@
+// Internal launch interface between the C ABI layer and the gfx950 kernels.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace smla {
+
+struct LaunchArgs {
+  const uint16_t* q;          // bf16 bits [s_q][h_q][d]
+  const void* kv_pool;        // u8 E4M3 [n_rows][d] or bf16 bits [n_rows][d]
+  const uint8_t* kv_scales;   // u8 [n_rows][d/32] (E4M3 pool) or null
+  const int32_t* indices;     // [s_q][topk]
+  const int32_t* topk_length; // [s_q]
+  const int32_t* positions;   // [s_q]
+  const float* norm_w;        // [d]
+  uint8_t* out_fp8;           // [s_q][h_q][d]
+  uint8_t* out_scales;        // [s_q][h_q][d/32]
+  float* out_f32;             // [s_q][h_q][d] or null
+  float* workspace;           // partials when num_splits > 1
+  int s_q, h_q, d, rope_dim, topk, kv_format, num_splits;
+  int64_t n_rows;
+  float sm_scale, rms_eps, rope_theta;
+  hipStream_t stream;
+};
+
+// Rows of the index row processed per tile by one workgroup.
+constexpr int kTileRows = 64;
+
+// Workspace floats per (token, split): acc [h_q][d] + m [h_q] + l [h_q].
+inline size_t partial_floats(int h_q, int d) { return (size_t)h_q * (size_t)(d + 2); }
+
+// Enqueue the step; returns the HIP error of the first failed launch (hipSuccess if none).
+hipError_t launch(const LaunchArgs& a);
+
+}  // namespace smla

@@ -1,0 +1,766 @@
+// gfx950 (MI355X) kernels of the fused sparse-MLA attention step.
+//
+// The step [vLLM #56344 "Deepseek V41 Attention MegaKernel", Purpose]: per token,
+// per-head RMSNorm and RoPE on q, a gather of that token's own index rows from an
+// E4M3 + UE8M0 latent pool (K = V, shared by all heads), softmax attention, inverse
+// RoPE on the output and an E4M3 cast with UE8M0 block-32 scales.  Entries at or
+// beyond topk_length are never read and -1 marks an empty slot [same page, Purpose,
+// bug-fix bullet].
+//
+// Work decomposition (one 256-thread workgroup = 4 wave64 per token, or per token
+// split when few tokens are in flight):
+//   prologue   q[t] -> RMSNorm -> RoPE (angles in fp64) -> bf16 in LDS -> each wave
+//              keeps the B fragments of its 32 heads in registers for the whole token.
+//   per tile of 64 index entries (row ids prefetched two tiles ahead, raw rows one
+//   tile ahead into registers):
+//     QK^T     wave (a, c) computes S^T[32 rows c][32 heads a] with
+//              v_mfma_f32_32x32x16_bf16; the K fragments are read as E4M3 bytes from
+//              LDS and dequantized in registers by v_cvt_scalef32_pk_bf16_fp8 (exact
+//              for normal-range scales).
+//     V tile   the same raw rows are dequantized once into a transposed bf16 tile
+//              Vt[dim][row] (XOR-swizzled 16-byte chunks, conflict-free both ways).
+//     softmax  per-head tile max shared through LDS by the two row-halves; the
+//              running max is only raised when the tile max exceeds it by 2^8
+//              (lazy rescaling), P is rounded to bf16 and stored [head][row].
+//     P.V      wave w owns output dims [w*d/4, (w+1)*d/4) for all 64 heads
+//              (2 x d/128 accumulators of 32x32 in AGPRs).
+//   epilogue   o = acc / l -> LDS -> inverse RoPE -> per-32 amax -> UE8M0 exponent
+//              (integer test against 448 * 2^(e-127)) -> E4M3 by v_cvt_pk_fp8_f32 (RNE).
+//   split mode each workgroup writes (acc, m, l) for its share of the tiles; a second
+//              kernel combines the splits in split order and runs the same epilogue.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "smla_internal.h"
+
+namespace smla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int T = kTileRows;  // 64
+constexpr int NTHREADS = 256;
+constexpr int HP = 64;        // heads per workgroup (padded)
+
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+constexpr int align16(int x) { return (x + 15) & ~15; }
+
+template <int D, int EB>  // EB: pool element bytes (1 = E4M3 + UE8M0 scales, 2 = bf16)
+struct Cfg {
+  static constexpr int RB = D * EB;     // bytes per pool row
+  static constexpr int NCH = RB / 16;   // 16-byte chunks per row
+  static constexpr int CE = 16 / EB;    // elements per chunk
+  static constexpr int NSB = D / 32;    // UE8M0 bytes per row
+  // Raw tile: one DMA instruction (64 lanes x 16 B) moves G rows, lane i carrying chunk
+  // i / G of row i % G; the G rows are interleaved chunk by chunk, groups padded so that
+  // eight consecutive rows read at one chunk land in eight distinct 16-byte bank slots.
+  static constexpr int G = 1024 / RB;
+  static constexpr int GS = 1024 + 16 * G;
+  static constexpr int RAW_BYTES = (T / G) * GS;
+  static constexpr int SC_BYTES = (EB == 1) ? T * NSB : 16;
+  static constexpr int VT_BYTES = D * T * 2;  // [D][T] bf16, 128 B per dim
+  static constexpr int P_BYTES = HP * T * 2;  // [HP][T] bf16, 128 B per head
+  static constexpr int KS = D / 16;           // k-steps of the QK contraction
+  static constexpr int DQ = D / 4;            // P.V output dims per wave
+  static constexpr int NB = DQ / 32;          // 32-wide n-blocks per wave
+  static constexpr int OFF_RAW0 = 0;
+  static constexpr int OFF_RAW1 = OFF_RAW0 + RAW_BYTES;
+  static constexpr int OFF_SC0 = OFF_RAW1 + RAW_BYTES;
+  static constexpr int OFF_SC1 = OFF_SC0 + SC_BYTES;
+  static constexpr int OFF_VT = align16(OFF_SC1 + SC_BYTES);
+  static constexpr int OFF_P = OFF_VT + VT_BYTES;
+  static constexpr int LOOP_END = OFF_P + P_BYTES;
+  static constexpr int QS = D + 8;  // bf16 stride of the prologue q tile
+  static constexpr int Q_BYTES = HP * QS * 2;
+  static constexpr int OS = D + 4;  // f32 stride of the epilogue o tile
+  static constexpr int O_BYTES = HP * OS * 4;
+  static constexpr int BIG = align16(cmax(LOOP_END, cmax(Q_BYTES, O_BYTES)));
+  // small area: maxx[2][HP], alpha[HP], lsum[2][HP], cos[D/2], sin[D/2]
+  static constexpr int OFF_MAXX = BIG;
+  static constexpr int OFF_ALPHA = OFF_MAXX + 2 * HP * 4;
+  static constexpr int OFF_LSUM = OFF_ALPHA + HP * 4;
+  static constexpr int OFF_COS = OFF_LSUM + 2 * HP * 4;
+  static constexpr int OFF_SIN = OFF_COS + (D / 2) * 4;
+  static constexpr int SMEM = OFF_SIN + (D / 2) * 4;
+  static_assert(G >= 1 && G <= 8 && (T % G) == 0, "row size unsupported");
+  static_assert(SMEM <= 160 * 1024, "LDS budget");
+};
+
+// byte offset of chunk c of row r in a raw tile
+template <class C>
+__device__ __forceinline__ int raw_off(int r, int c) {
+  return (r / C::G) * C::GS + 16 * (C::G * c + r % C::G);
+}
+
+struct KArgs {
+  const uint16_t* q;
+  const uint8_t* pool;
+  const uint8_t* scales;
+  const int32_t* indices;
+  const int32_t* topk_length;
+  const int32_t* positions;
+  const float* norm_w;
+  uint8_t* out_fp8;
+  uint8_t* out_scales;
+  float* out_f32;
+  float* ws;
+  int s_q, h_q, rope_dim, topk, num_splits, tiles_per_split;
+  long long n_rows;
+  float sm_scale, rms_eps, rope_theta;
+};
+
+__device__ __forceinline__ uint32_t cvt_lo(uint32_t src, float sc) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src, sc, false));
+}
+__device__ __forceinline__ uint32_t cvt_hi(uint32_t src, float sc) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src, sc, true));
+}
+// UE8M0 byte -> the f32 scale operand (2^(e-127) carried in the exponent field)
+__device__ __forceinline__ float ue8m0_f32(uint32_t e) { return __builtin_bit_cast(float, e << 23); }
+
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ float bf16_f32(uint32_t h) { return __builtin_bit_cast(float, h << 16); }
+
+// XOR swizzle of the 16-byte chunk index in 128-byte LDS rows (Vt rows indexed by dim,
+// P rows indexed by head).  Eight consecutive rows get eight distinct slots (P.V reads);
+// rows 16c + e for the 4 x 8 chunk pattern of the V transpose also spread over all
+// slots (bits 3-5 of the row enter through r >> 3 and r >> 6).
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3) ^ (r >> 6)) & 7; }
+
+__device__ __forceinline__ size_t partial_floats_d(int h_q, int d) { return (size_t)h_q * (size_t)(d + 2); }
+
+// LDS DMA (global_load_lds_dword[x4]): every active lane writes its 4 / 16 bytes at
+// lds_base + 4*lane / 16*lane.  Issued from asm so that the compiler does not make its
+// own LDS reads wait for it; the tile loop waits (vmcnt 0) before the barrier that
+// publishes the data.  Vector loads retire in order, so the compiler's own vmcnt waits
+// stay correct (they can only over-wait).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// M0 is saved and restored around the DMA (the compiler reserves it for its own use).
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "v"(g), "s"(lds_base)
+      : "memory");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds_base) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "v"(g), "s"(lds_base)
+      : "memory");
+}
+
+// A zero the compiler cannot see through: lane-dependent address math derived from it
+// is recomputed where it is used instead of being hoisted (and kept live) across loops.
+__device__ __forceinline__ int opaque_zero() {
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return z;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Inverse RoPE + UE8M0/E4M3 quantization of heads [0, nheads) held in o_lds (f32,
+// row stride OSTR), writing global heads head0 + hl of token tok.  Each wave takes one
+// head at a time; lane l holds dims [EPL*l, EPL*l + EPL): the rotary partner comes from
+// lane l +- half/EPL and the 32-element block spans 32/EPL consecutive lanes.
+template <int D>
+__device__ void epilogue(const float* o_lds, int OSTR, int nheads, int head0, int tok, const KArgs& a,
+                         const float* cs, const float* sn) {
+  constexpr int EPL = D / 64;
+  constexpr int LPB = 32 / EPL;  // lanes per 32-element block
+  const int R = a.rope_dim, o0 = D - R, half = R / 2, lsh = half / EPL;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int hl = w; hl < nheads; hl += NTHREADS / 64) {
+    const float* orow = o_lds + hl * OSTR + EPL * lane;
+    float v[EPL];
+    if constexpr (EPL == 8) {
+      const float4 lo = *reinterpret_cast<const float4*>(orow);
+      const float4 hi = *reinterpret_cast<const float4*>(orow + 4);
+      v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+      v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+    } else {
+      const float2 p = *reinterpret_cast<const float2*>(orow);
+      v[0] = p.x; v[1] = p.y;
+    }
+    float r[EPL];
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const float up = __shfl(v[e], (lane + lsh) & 63);
+      const float dn = __shfl(v[e], (lane - lsh) & 63);
+      const int x = EPL * lane + e;
+      float val = v[e];
+      if (x >= o0) {
+        const int k = x - o0;
+        if (k < half) val = v[e] * cs[k] + up * sn[k];
+        else val = v[e] * cs[k - half] - dn * sn[k - half];
+      }
+      r[e] = val;
+      amax = fmaxf(amax, fabsf(val));
+    }
+#pragma unroll
+    for (int o = 1; o < LPB; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    const size_t g = ((size_t)tok * a.h_q + head0 + hl) * D + EPL * lane;
+    if (a.out_f32) {
+      if constexpr (EPL == 8) {
+        reinterpret_cast<float4*>(a.out_f32 + g)[0] = make_float4(r[0], r[1], r[2], r[3]);
+        reinterpret_cast<float4*>(a.out_f32 + g)[1] = make_float4(r[4], r[5], r[6], r[7]);
+      } else {
+        *reinterpret_cast<float2*>(a.out_f32 + g) = make_float2(r[0], r[1]);
+      }
+    }
+    // smallest e in [0, 254] with 448 * 2^(e-127) >= amax, decided on the f32 bits
+    const uint32_t bits = __builtin_bit_cast(uint32_t, amax);
+    int e = (int)(bits >> 23) - 8 + (((bits & 0x7FFFFFu) > 0x600000u) ? 1 : 0);
+    e = e < 0 ? 0 : (e > 254 ? 254 : e);
+    const int sh = 127 - e;
+    if constexpr (EPL == 8) {
+      uint32_t w0 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(r[0], sh), ldexpf(r[1], sh), 0, false);
+      w0 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(r[2], sh), ldexpf(r[3], sh), w0, true);
+      uint32_t w1 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(r[4], sh), ldexpf(r[5], sh), 0, false);
+      w1 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(r[6], sh), ldexpf(r[7], sh), w1, true);
+      *reinterpret_cast<uint2*>(a.out_fp8 + g) = make_uint2(w0, w1);
+    } else {
+      const uint32_t w0 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(r[0], sh), ldexpf(r[1], sh), 0, false);
+      *reinterpret_cast<uint16_t*>(a.out_fp8 + g) = (uint16_t)(w0 & 0xFFFFu);
+    }
+    if ((lane % LPB) == 0)
+      a.out_scales[((size_t)tok * a.h_q + head0 + hl) * (D / 32) + (EPL * lane) / 32] = (uint8_t)e;
+  }
+}
+
+// cos / sin of angle pos * theta^(-2i/R), i < R/2, computed in fp64
+__device__ __forceinline__ void rope_table(int pos, const KArgs& a, float* cs, float* sn) {
+  const int half = a.rope_dim / 2;
+  if ((int)threadIdx.x < half) {
+    const double lt = log2((double)a.rope_theta);
+    const double ang = (double)pos * exp2(-(2.0 * threadIdx.x / (double)a.rope_dim) * lt);
+    double s, c;
+    sincos(ang, &s, &c);
+    cs[threadIdx.x] = (float)c;
+    sn[threadIdx.x] = (float)s;
+  }
+}
+
+template <int D, int EB>
+__global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
+  using C = Cfg<D, EB>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM];
+  float* maxx = reinterpret_cast<float*>(smem + C::OFF_MAXX);
+  float* alpha_l = reinterpret_cast<float*>(smem + C::OFF_ALPHA);
+  float* lsum = reinterpret_cast<float*>(smem + C::OFF_LSUM);
+  float* cs = reinterpret_cast<float*>(smem + C::OFF_COS);
+  float* sn = reinterpret_cast<float*>(smem + C::OFF_SIN);
+  unsigned char* vt_l = smem + C::OFF_VT;
+  unsigned char* p_l = smem + C::OFF_P;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  const int qa = w >> 1, qc = w & 1;  // QK roles: head group, row half
+  const int ns = a.num_splits;
+  const int t = blockIdx.x / ns, split = blockIdx.x % ns;
+  const int pos = a.positions[t];
+
+  // ---------------- prologue: q -> RMSNorm -> RoPE -> bf16 (LDS) -> register fragments
+  rope_table(pos, a, cs, sn);
+  __syncthreads();
+  {
+    constexpr int EPL = D / 64;  // q elements per lane
+    unsigned short* qbf = reinterpret_cast<unsigned short*>(smem);
+    const int R = a.rope_dim, o0 = D - R, half = R / 2, lsh = half / EPL;
+    float wv[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) wv[e] = a.norm_w[EPL * lane + e];
+    // all 16 heads of this wave are loaded up front (one memory round trip)
+    using QV = typename std::conditional<EPL == 8, uint4, uint32_t>::type;
+    QV qraw[16];
+#pragma unroll
+    for (int hh = 0; hh < 16; ++hh) {
+      const int h = 16 * w + hh;
+      if (h < a.h_q) qraw[hh] = *reinterpret_cast<const QV*>(a.q + ((size_t)t * a.h_q + h) * D + EPL * lane);
+      else qraw[hh] = QV{};
+    }
+#pragma unroll
+    for (int hh = 0; hh < 16; ++hh) {
+      const int h = 16 * w + hh;
+      float x[EPL];
+      if constexpr (EPL == 8) {
+        const uint4 u = qraw[hh];
+        const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          x[2 * k] = bf16_f32(uu[k] & 0xFFFFu);
+          x[2 * k + 1] = bf16_f32(uu[k] >> 16);
+        }
+      } else {
+        const uint32_t u = qraw[hh];
+        x[0] = bf16_f32(u & 0xFFFFu);
+        x[1] = bf16_f32(u >> 16);
+      }
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) ss += x[e] * x[e];
+      ss = wave_sum(ss);
+      const float inv = 1.0f / sqrtf(ss / (float)D + a.rms_eps);
+      float y[EPL], yo[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) y[e] = x[e] * inv * wv[e];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float up = __shfl(y[e], (lane + lsh) & 63);
+        const float dn = __shfl(y[e], (lane - lsh) & 63);
+        const int xd = EPL * lane + e;
+        float r = y[e];
+        if (xd >= o0) {
+          const int k = xd - o0;
+          if (k < half) r = y[e] * cs[k] - up * sn[k];
+          else r = y[e] * cs[k - half] + dn * sn[k - half];
+        }
+        yo[e] = r;
+      }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qbf[h * C::QS + EPL * lane + e] = (unsigned short)bf16_rne(yo[e]);
+    }
+  }
+  __syncthreads();
+  // B fragments of Q^T for S^T = K Q^T.  The contraction order over dims is permuted to
+  // match the K reads: for the E4M3 pool step 2m+j, lane half h covers dims
+  // 32m + 16h + 8j + [0, 8) (one 16-byte read of K serves two steps); for the bf16 pool
+  // step ks, lane half h covers dims 16ks + 8h + [0, 8).
+  bf16x8 qf[C::KS];
+  {
+    const unsigned short* qrow = reinterpret_cast<const unsigned short*>(smem) + (32 * qa + lrow) * C::QS;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const int dim0 = (EB == 1) ? 32 * (ks >> 1) + 16 * lhalf + 8 * (ks & 1) : 16 * ks + 8 * lhalf;
+      qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + dim0);
+    }
+  }
+
+  // ---------------- tile range of this workgroup
+  const int lraw = a.topk_length[t];
+  const int lcap = lraw < 0 ? 0 : (lraw > a.topk ? a.topk : lraw);
+  const int ntile = (lcap + T - 1) / T;
+  const int tb = split * a.tiles_per_split;
+  const int te_raw = tb + a.tiles_per_split;
+  const int te = te_raw < ntile ? te_raw : ntile;
+  const int32_t* idx_t = a.indices + (size_t)t * a.topk;
+
+  // id of entry tile*64 + lane, or -1 when it is not read (beyond the length, a
+  // sentinel, or outside [0, n_rows))
+  auto load_ids = [&](int tile) -> int {
+    const int j = tile * T + lane;
+    int id = -1;
+    if (tile < te && j < lcap) id = idx_t[j];
+    return (id >= 0 && (long long)id < a.n_rows) ? id : -1;
+  };
+
+  // Enqueue the LDS DMA of one tile's rows (and scales) into raw / sc.  Rows that are not
+  // read keep stale LDS contents: the QK masks them and the V transpose zeroes them.
+  auto issue_tile = [&](int id_vec, unsigned char* raw, unsigned char* sc, int lane) {
+    constexpr int GPW = (T / C::G) / 4;  // DMA groups per wave
+#pragma unroll
+    for (int k = 0; k < GPW; ++k) {
+      const int gi = GPW * w + k;
+      const int row = C::G * gi + lane % C::G;
+      const int chunk = lane / C::G;
+      const int id = __shfl(id_vec, row);
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(raw + gi * C::GS));
+      if (id >= 0) dma16(a.pool + (size_t)id * C::RB + 16 * chunk, dst);
+    }
+    if constexpr (EB == 1) {
+      constexpr int WPR = C::NSB / 4;  // 4-byte scale words per row
+      const int f = 64 * w + lane;
+      const int row = f / WPR;
+      const int id = __shfl(id_vec, row & 63);
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(sc + 256 * w));
+      if (f < 64 * WPR && id >= 0) dma4(a.scales + (size_t)id * C::NSB + 4 * (f % WPR), dst);
+    }
+  };
+
+  f32x16 acc[2][C::NB];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sl2 = a.sm_scale * 1.4426950408889634f;
+
+  int id_cur = load_ids(tb);
+  int id_next = load_ids(tb + 1);
+  __syncthreads();  // every wave holds its q fragments: the q tile region may be reused
+  if (tb < te) issue_tile(id_cur, smem + C::OFF_RAW0, smem + C::OFF_SC0, lane);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA has landed
+
+  auto tile_step = [&](int tile, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
+    unsigned char* raw_l = smem + (BUF == 0 ? C::OFF_RAW0 : C::OFF_RAW1);
+    unsigned char* sc_l = smem + (BUF == 0 ? C::OFF_SC0 : C::OFF_SC1);
+    unsigned char* raw_n = smem + (BUF == 0 ? C::OFF_RAW1 : C::OFF_RAW0);
+    unsigned char* sc_n = smem + (BUF == 0 ? C::OFF_SC1 : C::OFF_SC0);
+    __syncthreads();  // B1: this tile's rows visible; Vt / P free
+    // lane-dependent values recomputed per tile (keeps them out of the live set)
+    const int tid = (int)threadIdx.x + opaque_zero();
+    const int lane = tid & 63, lrow = lane & 31, lhalf = lane >> 5;
+    const unsigned long long mask = __ballot(id_cur >= 0);
+    if (tile + 1 < te) issue_tile(id_next, raw_n, sc_n, lane);
+    const int id_next2 = load_ids(tile + 2);
+
+    // ---- QK^T: S^T[32 rows of half qc][32 heads of group qa]
+    f32x16 s;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = 0.f;
+    {
+      const int r = 32 * qc + lrow;
+      if constexpr (EB == 1) {
+        uint32_t scr[C::NSB / 4];
+#pragma unroll
+        for (int k = 0; k < C::NSB / 4; ++k) scr[k] = *reinterpret_cast<const uint32_t*>(sc_l + r * C::NSB + 4 * k);
+#pragma unroll
+        for (int m = 0; m < C::KS / 2; ++m) {  // dims [32m, 32m+32): scale block m
+          const uint4 rw = *reinterpret_cast<const uint4*>(raw_l + raw_off<C>(r, 2 * m + lhalf));
+          const float sc = ue8m0_f32((scr[m >> 2] >> (8 * (m & 3))) & 0xFFu);
+          const uint4 u0 = make_uint4(cvt_lo(rw.x, sc), cvt_hi(rw.x, sc), cvt_lo(rw.y, sc), cvt_hi(rw.y, sc));
+          const uint4 u1 = make_uint4(cvt_lo(rw.z, sc), cvt_hi(rw.z, sc), cvt_lo(rw.w, sc), cvt_hi(rw.w, sc));
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u0), qf[2 * m], s, 0, 0, 0);
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u1), qf[2 * m + 1], s, 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+          const bf16x8 A = *reinterpret_cast<const bf16x8*>(raw_l + raw_off<C>(r, 2 * ks + lhalf));
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qf[ks], s, 0, 0, 0);
+        }
+      }
+    }
+
+    // ---- V tile: raw rows -> Vt[dim][row] bf16 (transposed, swizzled); blocks of
+    // 4 rows x one 16-byte chunk; rows that are not read become zeros
+    constexpr int NBLK = (T / 4) * C::NCH;
+    for (int bb = tid; bb < NBLK; bb += NTHREADS) {
+      int q, c, rot;
+      if constexpr (C::NCH == 32) {
+        // lanes of an 8-lane group: 4 consecutive chunks x 2 quads read in rotated row
+        // order, so each read step touches 8 distinct bank slots
+        const int u = lane & 7, g8 = lane >> 3, j = bb / NTHREADS;
+        c = 4 * g8 + (u & 3);
+        q = 2 * (w + 4 * j) + (u >> 2);
+        rot = u >> 2;
+      } else {
+        q = bb / C::NCH;
+        c = bb % C::NCH;
+        rot = 0;
+      }
+      uint32_t pk[4][C::CE / 2];  // [row][element pair]
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int rr = (jj + rot) & 3;
+        const int row = 4 * q + rr;
+        const uint4 rw = *reinterpret_cast<const uint4*>(raw_l + raw_off<C>(row, c));
+        const bool valid = (mask >> row) & 1ull;
+        uint32_t v[C::CE / 2];
+        if constexpr (EB == 1) {
+          const float sc = ue8m0_f32(sc_l[row * C::NSB + (c >> 1)]);
+          v[0] = cvt_lo(rw.x, sc); v[1] = cvt_hi(rw.x, sc);
+          v[2] = cvt_lo(rw.y, sc); v[3] = cvt_hi(rw.y, sc);
+          v[4] = cvt_lo(rw.z, sc); v[5] = cvt_hi(rw.z, sc);
+          v[6] = cvt_lo(rw.w, sc); v[7] = cvt_hi(rw.w, sc);
+        } else {
+          v[0] = rw.x; v[1] = rw.y; v[2] = rw.z; v[3] = rw.w;
+        }
+#pragma unroll
+        for (int k = 0; k < C::CE / 2; ++k) {
+          // select the row slot with compile-time indices after rotation
+          const uint32_t val = valid ? v[k] : 0u;
+          if (rr == 0) pk[0][k] = val;
+          else if (rr == 1) pk[1][k] = val;
+          else if (rr == 2) pk[2][k] = val;
+          else pk[3][k] = val;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < C::CE; ++e) {
+        const int k = e >> 1;
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const uint2 o = make_uint2(__builtin_amdgcn_perm(pk[1][k], pk[0][k], sel),
+                                   __builtin_amdgcn_perm(pk[3][k], pk[2][k], sel));
+        const int n = C::CE * c + e;
+        *reinterpret_cast<uint2*>(vt_l + n * 128 + 16 * ((q >> 1) ^ swz(n)) + 8 * (q & 1)) = o;
+      }
+    }
+
+    // ---- softmax (part 1): tile max per head
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = 32 * qc + 8 * (i >> 2) + 4 * lhalf + (i & 3);
+      const bool v = (mask >> row) & 1ull;
+      s[i] = v ? s[i] * sl2 : -INFINITY;
+      mloc = fmaxf(mloc, s[i]);
+    }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    if (lhalf == 0) maxx[qc * HP + 32 * qa + lrow] = mloc;
+    __syncthreads();  // B2: maxima exchanged
+
+    // ---- softmax (part 2): running max (lazy), P in bf16, alpha
+    {
+      const float mt = fmaxf(mloc, maxx[(1 - qc) * HP + 32 * qa + lrow]);
+      float mnew = m_run;
+      if (mt > -INFINITY && (m_run == -INFINITY || mt > m_run + 8.0f)) mnew = mt;
+      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mnew);
+      m_run = mnew;
+      uint32_t pb[16];
+      float lp = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = (mnew == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[i] - mnew);
+        pb[i] = bf16_rne(p);
+        lp += bf16_f32(pb[i]);
+      }
+      l_run = l_run * alpha + lp;
+      const int head = 32 * qa + lrow;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint2 pw = make_uint2(pb[4 * g] | (pb[4 * g + 1] << 16), pb[4 * g + 2] | (pb[4 * g + 3] << 16));
+        *reinterpret_cast<uint2*>(p_l + head * 128 + 16 * ((4 * qc + g) ^ swz(head)) + 8 * lhalf) = pw;
+      }
+      if (qc == 0 && lhalf == 0) alpha_l[head] = alpha;
+    }
+    __syncthreads();  // B3: P and alpha visible
+
+    // ---- P.V: O[64 heads][dims of wave w]
+    {
+      bool need = false;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 v4 = *reinterpret_cast<const float4*>(alpha_l + 32 * mb + 8 * g + 4 * lhalf);
+          need |= (v4.x != 1.f) | (v4.y != 1.f) | (v4.z != 1.f) | (v4.w != 1.f);
+        }
+      if (__any(need)) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float4 v4 = *reinterpret_cast<const float4*>(alpha_l + 32 * mb + 8 * g + 4 * lhalf);
+#pragma unroll
+            for (int nb = 0; nb < C::NB; ++nb) {
+              acc[mb][nb][4 * g + 0] *= v4.x;
+              acc[mb][nb][4 * g + 1] *= v4.y;
+              acc[mb][nb][4 * g + 2] *= v4.z;
+              acc[mb][nb][4 * g + 3] *= v4.w;
+            }
+          }
+      }
+      const int d0 = C::DQ * w;
+#pragma unroll
+      for (int ks = 0; ks < T / 16; ++ks) {
+        const int ch = 2 * ks + lhalf;
+        bf16x8 A[2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const int h = 32 * mb + lrow;
+          A[mb] = *reinterpret_cast<const bf16x8*>(p_l + h * 128 + 16 * (ch ^ swz(h)));
+        }
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) {
+          const int n = d0 + 32 * nb + lrow;
+          const bf16x8 B = *reinterpret_cast<const bf16x8*>(vt_l + n * 128 + 16 * (ch ^ swz(n)));
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[mb], B, acc[mb][nb], 0, 0, 0);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile's DMA from this wave landed
+    id_cur = id_next;
+    id_next = id_next2;
+  };
+
+  for (int tile = tb; tile < te; tile += 2) {
+    tile_step(tile, std::integral_constant<int, 0>{});
+    if (tile + 1 < te) tile_step(tile + 1, std::integral_constant<int, 1>{});
+  }
+
+  // ---------------- finish: l per head, then normalize + epilogue, or write partials
+  {
+    const float lw = l_run + __shfl_xor(l_run, 32);
+    if (lhalf == 0) lsum[qc * HP + 32 * qa + lrow] = lw;
+    if (qc == 0 && lhalf == 0) maxx[32 * qa + lrow] = m_run;
+  }
+  __syncthreads();
+  const int d0 = C::DQ * w;
+  if (ns == 1) {
+    float* o_l = reinterpret_cast<float*>(smem);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int h = 32 * mb + 8 * (i >> 2) + 4 * lhalf + (i & 3);
+        const float lt = lsum[h] + lsum[HP + h];
+        const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) o_l[h * C::OS + d0 + 32 * nb + lrow] = acc[mb][nb][i] * inv;
+      }
+    __syncthreads();
+    epilogue<D>(o_l, C::OS, a.h_q, 0, t, a, cs, sn);
+  } else {
+    float* part = a.ws + ((size_t)t * ns + split) * partial_floats_d(a.h_q, D);
+    float* pm = part + (size_t)a.h_q * D;
+    float* pl = pm + a.h_q;
+    if (tid < a.h_q) {
+      pm[tid] = maxx[tid];
+      pl[tid] = lsum[tid] + lsum[HP + tid];
+    }
+    if (te > tb) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int h = 32 * mb + 8 * (i >> 2) + 4 * lhalf + (i & 3);
+          if (h < a.h_q) {
+#pragma unroll
+            for (int nb = 0; nb < C::NB; ++nb) part[(size_t)h * D + d0 + 32 * nb + lrow] = acc[mb][nb][i];
+          }
+        }
+    }
+  }
+}
+
+// Combine the splits of one token for 8 heads (in split order), then the epilogue.
+// All split statistics and accumulators are fetched with independent loads.
+template <int D>
+__global__ __launch_bounds__(NTHREADS) void smla_combine(KArgs a) {
+  constexpr int HC = 8, OSTR = D + 4, MAXS = 64;
+  __shared__ __attribute__((aligned(16))) float o_l[HC * OSTR];
+  __shared__ float cs[D / 2], sn[D / 2];
+  __shared__ float mm[HC][MAXS], ll[HC][MAXS], wgt[HC][MAXS];
+  __shared__ float den[HC];
+  const int t = blockIdx.x, h0 = HC * blockIdx.y;
+  const int nh = (a.h_q - h0) < HC ? (a.h_q - h0) : HC;
+  const int ns = a.num_splits;
+  const size_t pf = partial_floats_d(a.h_q, D);
+  const float* base = a.ws + (size_t)t * ns * pf;
+  rope_table(a.positions[t], a, cs, sn);
+  for (int f = threadIdx.x; f < HC * MAXS; f += NTHREADS) {
+    const int hl = f / MAXS, s = f % MAXS;
+    if (hl < nh && s < ns) {
+      const float* st = base + (size_t)s * pf + (size_t)a.h_q * D;
+      mm[hl][s] = st[h0 + hl];
+      ll[hl][s] = st[a.h_q + h0 + hl];
+    }
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < nh) {
+    const int hl = threadIdx.x;
+    float M = -INFINITY;
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, mm[hl][s]);
+    float dsum = 0.f;
+    for (int s = 0; s < ns; ++s) {
+      const float ms = mm[hl][s];
+      const float wv = (M == -INFINITY || ms == -INFINITY) ? 0.f : exp2f(ms - M);
+      wgt[hl][s] = wv;
+      dsum += wv * ll[hl][s];
+    }
+    den[hl] = dsum;
+  }
+  __syncthreads();
+  constexpr int Q4 = D / 4;
+  for (int f = threadIdx.x; f < nh * Q4; f += NTHREADS) {
+    const int hl = f / Q4, x4 = f % Q4;
+    const float* src = base + (size_t)(h0 + hl) * D + 4 * x4;
+    float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s0 = 0; s0 < ns; s0 += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        v[k] = (s0 + k < ns) ? *reinterpret_cast<const float4*>(src + (size_t)(s0 + k) * pf)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float wv = (s0 + k < ns) ? wgt[hl][s0 + k] : 0.f;
+        // a split that read nothing has an unwritten accumulator: select, never multiply
+        if (wv != 0.f) {
+          num.x += wv * v[k].x;
+          num.y += wv * v[k].y;
+          num.z += wv * v[k].z;
+          num.w += wv * v[k].w;
+        }
+      }
+    }
+    const float inv = den[hl] > 0.f ? 1.0f / den[hl] : 0.f;
+    *reinterpret_cast<float4*>(o_l + hl * OSTR + 4 * x4) =
+        make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv);
+  }
+  __syncthreads();
+  epilogue<D>(o_l, OSTR, nh, h0, t, a, cs, sn);
+}
+
+template <int D, int EB>
+hipError_t launch_t(const LaunchArgs& x, const KArgs& k) {
+  const int ns = x.num_splits;
+  hipLaunchKernelGGL((smla_main<D, EB>), dim3((unsigned)(x.s_q * ns)), dim3(NTHREADS), 0, x.stream, k);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ns == 1) return e;
+  hipLaunchKernelGGL((smla_combine<D>), dim3((unsigned)x.s_q, (unsigned)((x.h_q + 7) / 8)), dim3(NTHREADS), 0,
+                     x.stream, k);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch(const LaunchArgs& x) {
+  KArgs k;
+  k.q = x.q;
+  k.pool = static_cast<const uint8_t*>(x.kv_pool);
+  k.scales = x.kv_scales;
+  k.indices = x.indices;
+  k.topk_length = x.topk_length;
+  k.positions = x.positions;
+  k.norm_w = x.norm_w;
+  k.out_fp8 = x.out_fp8;
+  k.out_scales = x.out_scales;
+  k.out_f32 = x.out_f32;
+  k.ws = x.workspace;
+  k.s_q = x.s_q;
+  k.h_q = x.h_q;
+  k.rope_dim = x.rope_dim;
+  k.topk = x.topk;
+  k.num_splits = x.num_splits;
+  const int ntiles = (x.topk + kTileRows - 1) / kTileRows;
+  k.tiles_per_split = (ntiles + x.num_splits - 1) / x.num_splits;
+  if (k.tiles_per_split < 1) k.tiles_per_split = 1;
+  k.n_rows = x.n_rows;
+  k.sm_scale = x.sm_scale;
+  k.rms_eps = x.rms_eps;
+  k.rope_theta = x.rope_theta;
+  if (x.d == 512 && x.kv_format == 0) return launch_t<512, 1>(x, k);
+  if (x.d == 128 && x.kv_format == 0) return launch_t<128, 1>(x, k);
+  if (x.d == 128 && x.kv_format == 1) return launch_t<128, 2>(x, k);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace smla

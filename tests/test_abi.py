@@ -1,0 +1,144 @@
+"""The C ABI on the host (no GPU needed): the library loads, exports every function
+include/smla.h declares, and rejects bad arguments with the documented codes before
+any HIP call.  No call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import prefill_token_amd as smla
+from prefill_token_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from prefill_token_amd import build
+
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(sparse_mla_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert "sparse_mla_fwd" in names and len(names) >= 5
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version(lib):
+    assert smla.sparse_mla_abi_version() == 1
+
+
+def test_struct_layout_matches_header():
+    # int32 x6, int64, float x3, int32, pointers: offsets fixed by the C layout
+    P = smla.SmlaParams
+    assert P.n_rows.offset == 24 and P.sm_scale.offset == 32 and P.num_splits.offset == 44
+    assert P.out_f32.offset == 48 and P.stream.offset == 72 and ctypes.sizeof(P) == 80
+
+
+def good(**kw):
+    base = dict(s_q=4, h_q=64, d=512, rope_dim=64, topk=640, n_rows=10240, kv_format=0, sm_scale=0.0442)
+    base.update(kw)
+    return smla.make_params(**base)
+
+
+FAKE = 0x1000  # a non-null pointer the host never dereferences
+
+
+def call(lib, p, *, null=None, kv_scales=True):
+    ptrs = [FAKE] * 9
+    if not kv_scales:
+        ptrs[2] = None
+    if null is not None:
+        ptrs[null] = None
+    return lib.sparse_mla_fwd(*ptrs, ctypes.byref(p) if p is not None else None)
+
+
+def test_null_params(lib):
+    assert lib.sparse_mla_fwd(*([FAKE] * 9), None) == smla.SMLA_ERR_NULL
+    assert "params" in smla.sparse_mla_last_error()
+
+
+@pytest.mark.parametrize("which", [0, 1, 3, 4, 5, 6, 7, 8])
+def test_null_arrays(lib, which):
+    p = good(num_splits=1)
+    assert call(lib, p, null=which) == smla.SMLA_ERR_NULL
+
+
+def test_null_scales_for_fp8_pool(lib):
+    assert call(lib, good(num_splits=1), kv_scales=False) == smla.SMLA_ERR_NULL
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=256), smla.SMLA_ERR_SHAPE),
+    (dict(d=512, kv_format=1), smla.SMLA_ERR_SHAPE),
+    (dict(h_q=0), smla.SMLA_ERR_SHAPE),
+    (dict(h_q=65), smla.SMLA_ERR_SHAPE),
+    (dict(rope_dim=24), smla.SMLA_ERR_SHAPE),
+    (dict(rope_dim=528), smla.SMLA_ERR_SHAPE),
+    (dict(rope_dim=-16), smla.SMLA_ERR_SHAPE),
+    (dict(topk=-1), smla.SMLA_ERR_SHAPE),
+    (dict(topk=70000), smla.SMLA_ERR_SHAPE),
+    (dict(s_q=-1), smla.SMLA_ERR_VALUE),
+    (dict(n_rows=0), smla.SMLA_ERR_VALUE),
+    (dict(kv_format=7), smla.SMLA_ERR_VALUE),
+    (dict(sm_scale=0.0), smla.SMLA_ERR_VALUE),
+    (dict(sm_scale=float("nan")), smla.SMLA_ERR_VALUE),
+    (dict(sm_scale=float("inf")), smla.SMLA_ERR_VALUE),
+    (dict(eps=0.0), smla.SMLA_ERR_VALUE),
+    (dict(eps=-1e-6), smla.SMLA_ERR_VALUE),
+    (dict(theta=float("nan")), smla.SMLA_ERR_VALUE),
+    (dict(num_splits=-1), smla.SMLA_ERR_VALUE),
+    (dict(num_splits=65), smla.SMLA_ERR_VALUE),
+])
+def test_rejected_parameters(lib, kw, code):
+    p = good(**kw)
+    assert call(lib, p) == code
+    assert smla.sparse_mla_last_error() != ""
+    assert smla.sparse_mla_workspace_size(p) == 0 and smla.sparse_mla_num_splits(p) == 0
+
+
+def test_workspace_required_when_split(lib):
+    p = good(s_q=4)  # few tokens: automatic splitting needs a workspace
+    ns = smla.sparse_mla_num_splits(p)
+    assert ns > 1
+    need = smla.sparse_mla_workspace_size(p)
+    assert need == 4 * ns * 64 * (512 + 2) * 4
+    assert call(lib, p) == smla.SMLA_ERR_VALUE  # no workspace given
+    assert "workspace" in smla.sparse_mla_last_error()
+    p.workspace, p.workspace_bytes = FAKE, need - 1
+    assert call(lib, p) == smla.SMLA_ERR_VALUE
+
+
+def test_split_choice():
+    assert smla.sparse_mla_num_splits(good(s_q=1)) == 10   # one split per 64-entry tile
+    assert smla.sparse_mla_num_splits(good(s_q=2123)) == 1
+    assert smla.sparse_mla_num_splits(good(s_q=1, num_splits=3)) == 3
+    assert smla.sparse_mla_num_splits(good(s_q=1, num_splits=64)) == 10  # capped at the tile count
+    assert smla.sparse_mla_workspace_size(good(s_q=2123)) == 0
+
+
+def test_zero_tokens_is_a_noop(lib):
+    p = good(s_q=0)
+    assert lib.sparse_mla_fwd(*([None] * 9), ctypes.byref(p)) == smla.SMLA_OK
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(_lib.LibraryMissing):
+        _lib.load()

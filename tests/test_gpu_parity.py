@@ -1,0 +1,166 @@
+"""GPU parity: the HIP library through its C ABI against the fp64 oracle on the same
+seeded inputs (rules in tests/parity.py).
+
+Workloads: the tiny case and both small decode cases in full; the s_q = 1024 decode and
+the 2123-token prefill at full size in the benchmark's launch configuration, checked on
+sampled tokens the oracle computes one by one.  Edge cases: every tile boundary of
+topk_length, empty and all-sentinel rows, stale ids beyond topk_length pointing at rows
+that decode to NaN, duplicates, position 0, fewer heads, no rotary dims, the E4M3 pool at
+d = 128, the ends of the exact scale range, forced split counts, and bit-reproducibility.
+"""
+import numpy as np
+import pytest
+import torch
+
+from prefill_token_amd import inputs
+
+from parity import compare, run_gpu, run_oracle, to_device
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU containers
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+
+def check(inp, **kw):
+    gpu = run_gpu(inp, **kw)
+    ref = run_oracle(inp)
+    st = compare(gpu, ref)
+    print(inp["name"], kw, st, flush=True)
+    return gpu, ref, st
+
+
+def test_tiny():
+    check(inputs.make("tiny"))
+
+
+@pytest.mark.parametrize("seed", [None, 7])
+def test_decode_sq1(seed):
+    check(inputs.make("decode_sq1", seed=seed))
+
+
+def test_decode_sq64():
+    check(inputs.make("decode_sq64"))
+
+
+@pytest.mark.parametrize("ns", [1, 2, 3, 10])
+def test_decode_forced_splits(ns):
+    check(inputs.make("decode_sq64", seed=101, s_q=8), num_splits=ns)
+
+
+def _sampled(name, n_sample, seed=0):
+    inp = inputs.make(name)
+    dev = to_device(inp)
+    full = run_gpu(inp, dev_inputs=dev)                  # with out_f32
+    bench = run_gpu(inp, dev_inputs=dev, with_f32=False)  # the benchmark's launch configuration
+    assert np.array_equal(full["codes"], bench["codes"]) and np.array_equal(full["scales"], bench["scales"])
+    rng = np.random.default_rng(seed)
+    L = inp["topk_length"]
+    pick = set(rng.choice(inp["s_q"], size=n_sample, replace=False).tolist())
+    pick |= {0, inp["s_q"] - 1, int(np.argmin(L)), int(np.argmax(L))}
+    tok = np.array(sorted(pick))
+    sub = inputs.take_tokens(inp, tok)
+    ref = run_oracle(sub)
+    g = {k: v[tok] for k, v in full.items()}
+    st = compare(g, ref)
+    print(name, "sampled", len(tok), st, flush=True)
+
+
+def test_decode_sq1024_sampled():
+    _sampled("decode_sq1024", 60)
+
+
+def test_prefill_sq2123_sampled():
+    _sampled("prefill_sq2123", 40)
+
+
+def _decode_case(seed, s_q=8):
+    return inputs.make("decode_sq64", seed=seed, s_q=s_q)
+
+
+def test_topk_length_edges():
+    inp = _decode_case(11, s_q=10)
+    inp["topk_length"] = np.array([0, 1, 63, 64, 65, 127, 128, 639, 640, 5000], dtype=np.int32)
+    inp["indices"][inp["indices"] < 0] = 17  # no sentinels: the length alone decides
+    for ns in (0, 1, 4):
+        check(inp, num_splits=ns)
+
+
+def test_empty_and_sentinel_rows():
+    inp = _decode_case(12, s_q=4)
+    inp["indices"][0, :] = -1
+    inp["topk_length"][1] = 0
+    inp["indices"][2, :] = -1
+    inp["indices"][2, 300] = 5  # a single valid entry in the middle of the row
+    for ns in (0, 1):
+        gpu, ref, _ = check(inp, num_splits=ns)
+        assert (gpu["f32"][0] == 0).all() and (gpu["f32"][1] == 0).all()
+        assert (gpu["scales"][0] == 0).all() and ((gpu["codes"][0] & 0x7F) == 0).all()
+
+
+def test_stale_indices_point_at_nan_rows():
+    inp = _decode_case(13, s_q=4)
+    pool = inp["kv_pool"].copy()
+    pool[:16, :] = 0x7F  # rows 0..15 decode to NaN
+    inp["kv_pool"] = pool
+    idx = inp["indices"]
+    idx[(idx >= 0) & (idx < 16)] += 16
+    inp["topk_length"] = np.array([100, 37, 640, 0], dtype=np.int32)
+    for t, L in enumerate(inp["topk_length"]):
+        idx[t, L:] = np.arange(640 - L) % 16  # every entry past the length points at a NaN row
+    gpu, _, _ = check(inp)
+    assert np.isfinite(gpu["f32"]).all()
+
+
+def test_duplicates():
+    inp = _decode_case(14, s_q=3)
+    inp["indices"][:, 320:] = inp["indices"][:, 128:448]
+    check(inp)
+
+
+def test_position_zero_and_small():
+    inp = _decode_case(15, s_q=4)
+    inp["positions"] = np.array([0, 1, 2, 127], dtype=np.int32)
+    check(inp)
+
+
+@pytest.mark.parametrize("h", [1, 8, 16, 33, 48])
+def test_fewer_heads(h):
+    inp = _decode_case(16, s_q=3)
+    inp["q"] = np.ascontiguousarray(inp["q"][:, :h])
+    check(inp)
+
+
+def test_rope_dim_zero_and_full():
+    inp = _decode_case(17, s_q=3)
+    for r in (0, 512):
+        inp["rope_dim"] = r
+        check(inp)
+
+
+def test_fp8_pool_d128():
+    rng = np.random.default_rng(18)
+    inp = inputs.make("tiny")
+    pool, sc = inputs.mx_pool(rng.standard_normal((256, 128)).astype(np.float32))
+    inp.update(kv_pool=pool, kv_scales=sc, kv_format=inputs.KV_E4M3_UE8M0, name="tiny_fp8")
+    check(inp)
+
+
+@pytest.mark.parametrize("lo,hi", [(20, 20), (200, 200), (100, 140)])
+def test_scale_range_ends(lo, hi):
+    # pools far from unit scale (tiny and huge latents) within the range the f32
+    # scores and accumulators hold
+    inp = _decode_case(19, s_q=4)
+    rng = np.random.default_rng(lo + hi)
+    inp["kv_scales"] = rng.integers(lo, hi + 1, size=inp["kv_scales"].shape).astype(np.uint8)
+    check(inp)
+
+
+def test_bit_reproducible():
+    inp = _decode_case(20, s_q=16)
+    dev = to_device(inp)
+    for ns in (0, 1, 5):
+        a = run_gpu(inp, dev_inputs=dev, num_splits=ns)
+        b = run_gpu(inp, dev_inputs=dev, num_splits=ns)
+        for k in ("codes", "scales", "f32"):
+            assert a[k].tobytes() == b[k].tobytes(), (ns, k)
