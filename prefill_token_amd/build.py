@@ -24,6 +24,10 @@ HIPCC_FLAGS = [
     "-shared",
     # no packed fp32 VALU ops in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: the P.V accumulators are then rescaled in place by plain
+    # VALU multiplies (no AGPR round trips), and the AGPRs hold the q fragments the QK
+    # asm pins there
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
 ]
 

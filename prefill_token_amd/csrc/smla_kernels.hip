@@ -9,23 +9,27 @@
 //
 // Work decomposition (one 256-thread workgroup = 4 wave64 per token, or per token
 // split when few tokens are in flight):
-//   prologue   q[t] -> RMSNorm -> RoPE (angles in fp64) -> bf16 in LDS -> each wave
-//              keeps the B fragments of its 32 heads in registers for the whole token.
+//   prologue   q[t] -> RMSNorm -> RoPE (angles in fp64).  For the E4M3 pool q is split
+//              into two E4M3 terms (hi + lo) with their own UE8M0 scales per 32 dims
+//              (about 8 significant bits, finer than bf16); each QK wave keeps the
+//              fragments of its 32 heads in registers for the whole token.
 //   per tile of 64 index entries (row ids prefetched two tiles ahead, raw rows one
-//   tile ahead into registers):
-//     QK^T     wave (a, c) computes S^T[32 rows c][32 heads a] with
-//              v_mfma_f32_32x32x16_bf16; the K fragments are read as E4M3 bytes from
-//              LDS and dequantized in registers by v_cvt_scalef32_pk_bf16_fp8 (exact
-//              for normal-range scales).
-//     V tile   the same raw rows are dequantized once into a transposed bf16 tile
-//              Vt[dim][row] (XOR-swizzled 16-byte chunks, conflict-free both ways).
-//     softmax  per-head tile max shared through LDS by the two row-halves; the
-//              running max is only raised when the tile max exceeds it by 2^8
-//              (lazy rescaling), P is rounded to bf16 and stored [head][row].
+//   tile ahead by LDS DMA into a double buffer):
+//     QK^T     wave (a, c) computes S^T[32 rows of half c][32 heads of group a] with
+//              v_mfma_scale_f32_32x32x64_f8f6f4: K is the raw E4M3 row data with its
+//              UE8M0 block scales as the MFMA's A scales, q the hi / lo terms as B --
+//              no dequantization of K at all.  (bf16 pool: v_mfma_f32_32x32x16_bf16.)
+//     V tile   the same raw rows are dequantized once (v_cvt_scalef32_pk_bf16_fp8,
+//              exact) into a transposed bf16 tile Vt[dim][slot]; rows are stored in a
+//              slot order that makes both the transpose's reads and writes and the
+//              P.V reads bank-conflict free.
+//     softmax  per-head tile max shared through LDS by the two row halves; the running
+//              max is raised only when the tile max exceeds it by 2^8 (lazy rescale);
+//              P is rounded to bf16 (v_cvt_pk_bf16_f32) and stored [head][slot].
 //     P.V      wave w owns output dims [w*d/4, (w+1)*d/4) for all 64 heads
-//              (2 x d/128 accumulators of 32x32 in AGPRs).
+//              (v_mfma_f32_32x32x16_bf16, accumulators in AGPRs).
 //   epilogue   o = acc / l -> LDS -> inverse RoPE -> per-32 amax -> UE8M0 exponent
-//              (integer test against 448 * 2^(e-127)) -> E4M3 by v_cvt_pk_fp8_f32 (RNE).
+//              (integer test against 448 * 2^(e-127)) -> E4M3 by the scaled RNE convert.
 //   split mode each workgroup writes (acc, m, l) for its share of the tiles; a second
 //              kernel combines the splits in split order and runs the same epilogue.
 #include <hip/hip_runtime.h>
@@ -33,6 +37,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "smla_internal.h"
 
@@ -42,12 +47,25 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int T = kTileRows;  // 64
 constexpr int NTHREADS = 256;
 constexpr int HP = 64;        // heads per workgroup (padded)
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+// compile-time loop: f(std::integral_constant<int, i>) for i = 0 .. N-1
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 constexpr int align16(int x) { return (x + 15) & ~15; }
 
 template <int D, int EB>  // EB: pool element bytes (1 = E4M3 + UE8M0 scales, 2 = bf16)
@@ -65,18 +83,24 @@ struct Cfg {
   static constexpr int SC_BYTES = (EB == 1) ? T * NSB : 16;
   static constexpr int VT_BYTES = D * T * 2;  // [D][T] bf16, 128 B per dim
   static constexpr int P_BYTES = HP * T * 2;  // [HP][T] bf16, 128 B per head
-  static constexpr int KS = D / 16;           // k-steps of the QK contraction
+  static constexpr int KS = D / 16;           // k-steps of the bf16 QK contraction
+  static constexpr int KS8 = D / 64;          // k-steps of the E4M3 QK contraction
   static constexpr int DQ = D / 4;            // P.V output dims per wave
   static constexpr int NB = DQ / 32;          // 32-wide n-blocks per wave
   static constexpr int OFF_RAW0 = 0;
   static constexpr int OFF_RAW1 = OFF_RAW0 + RAW_BYTES;
   static constexpr int OFF_SC0 = OFF_RAW1 + RAW_BYTES;
   static constexpr int OFF_SC1 = OFF_SC0 + SC_BYTES;
-  static constexpr int OFF_VT = align16(OFF_SC1 + SC_BYTES);
+  static constexpr int RAW_END = align16(OFF_SC1 + SC_BYTES);
+  static constexpr int OFF_VT = RAW_END;
   static constexpr int OFF_P = OFF_VT + VT_BYTES;
   static constexpr int LOOP_END = OFF_P + P_BYTES;
-  static constexpr int QS = D + 8;  // bf16 stride of the prologue q tile
-  static constexpr int Q_BYTES = HP * QS * 2;
+  // prologue q tile: E4M3 pool -> two E4M3 terms [2][HP][QS8] + UE8M0 [2][HP][NSB];
+  // bf16 pool -> bf16 [HP][QS]
+  static constexpr int QS8 = D + 16;
+  static constexpr int OFF_QSC = 2 * HP * QS8;
+  static constexpr int QS = D + 8;
+  static constexpr int Q_BYTES = (EB == 1) ? OFF_QSC + 2 * HP * NSB : HP * QS * 2;
   static constexpr int OS = D + 4;  // f32 stride of the epilogue o tile
   static constexpr int O_BYTES = HP * OS * 4;
   static constexpr int BIG = align16(cmax(LOOP_END, cmax(Q_BYTES, O_BYTES)));
@@ -120,8 +144,28 @@ __device__ __forceinline__ uint32_t cvt_lo(uint32_t src, float sc) {
 __device__ __forceinline__ uint32_t cvt_hi(uint32_t src, float sc) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src, sc, true));
 }
-// UE8M0 byte -> the f32 scale operand (2^(e-127) carried in the exponent field)
+// UE8M0 byte -> the f32 scale operand of the scaled converts (the hardware reads the
+// exponent field as the E8M0 value, so e = 0 means 2^-127)
 __device__ __forceinline__ float ue8m0_f32(uint32_t e) { return __builtin_bit_cast(float, e << 23); }
+
+// smallest e in [0, 254] with 448 * 2^(e-127) >= amax (amax >= 0), decided on the f32 bits
+__device__ __forceinline__ int ue8m0_exp(float amax) {
+  const uint32_t bits = __builtin_bit_cast(uint32_t, amax);
+  int e = (int)(bits >> 23) - 8 + (((bits & 0x7FFFFFu) > 0x600000u) ? 1 : 0);
+  return e < 0 ? 0 : (e > 254 ? 254 : e);
+}
+
+// two f32 -> E4M3 codes (RNE) of x / 2^(e-127), into bytes 0-1 (hi = false) or 2-3
+__device__ __forceinline__ uint32_t enc2(uint32_t old, float x0, float x1, float sc, bool hi) {
+  s16x2 o = __builtin_bit_cast(s16x2, old);
+  o = hi ? __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, x0, x1, sc, true)
+         : __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, x0, x1, sc, false);
+  return __builtin_bit_cast(uint32_t, o);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
 
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
   uint32_t u = __builtin_bit_cast(uint32_t, f);
@@ -132,8 +176,8 @@ __device__ __forceinline__ float bf16_f32(uint32_t h) { return __builtin_bit_cas
 
 // XOR swizzle of the 16-byte chunk index in 128-byte LDS rows (Vt rows indexed by dim,
 // P rows indexed by head).  Eight consecutive rows get eight distinct slots (P.V reads);
-// rows 16c + e for the 4 x 8 chunk pattern of the V transpose also spread over all
-// slots (bits 3-5 of the row enter through r >> 3 and r >> 6).
+// rows 16c + e for the chunk pattern of the V transpose also spread over all slots
+// (bits 3-5 of the row enter through r >> 3 and r >> 6).
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3) ^ (r >> 6)) & 7; }
 
 __device__ __forceinline__ size_t partial_floats_d(int h_q, int d) { return (size_t)h_q * (size_t)(d + 2); }
@@ -172,6 +216,64 @@ __device__ __forceinline__ int opaque_zero() {
   return z;
 }
 
+// NST k-steps (64 dims each) of the E4M3 QK^T contraction, s (+)= sum_j K_j (q_hi,j + q_lo,j):
+// the scaled MFMAs run back to back (srcC = vdst of the previous one, which needs no
+// wait states), step j taking byte j of the scale registers.  Written as asm so that
+// the q fragments stay in AGPRs and s in VGPRs for the whole token (the compiler would
+// otherwise spill); all K fragments of the block are loaded before it.  The leading
+// s_nop covers a VALU write of an operand just before the block.
+template <int NST, bool FIRST>
+__device__ __forceinline__ void qk_block(f32x16& s, const i32x8* A, const i32x8* qh, const i32x8* ql, uint32_t ka,
+                                         uint32_t sh, uint32_t sl) {
+  static_assert(NST == 2 || NST == 4, "k-steps per block");
+  if constexpr (NST == 4 && FIRST) {
+    asm("s_nop 4\n\t"
+        "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %5, 0, %13, %14 op_sel_hi:[0,0,0]\n\t"
+        "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %9, %0, %13, %15 op_sel_hi:[0,0,0]\n\t"
+        "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %2, %6, %0, %13, %14 op_sel:[1,1,0] op_sel_hi:[0,0,0]\n\t"
+        "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %2, %10, %0, %13, %15 op_sel:[1,1,0] op_sel_hi:[0,0,0]\n\t"
+        "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %3, %7, %0, %13, %14 op_sel_hi:[1,1,0]\n\t"
+        "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %3, %11, %0, %13, %15 op_sel_hi:[1,1,0]\n\t"
+        "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %4, %8, %0, %13, %14 op_sel:[1,1,0] op_sel_hi:[1,1,0]\n\t"
+        "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %4, %12, %0, %13, %15 op_sel:[1,1,0] op_sel_hi:[1,1,0]"
+        : "=&v"(s)
+        : "v"(A[0]), "v"(A[1]), "v"(A[2]), "v"(A[3]), "a"(qh[0]), "a"(qh[1]), "a"(qh[2]), "a"(qh[3]), "a"(ql[0]), "a"(ql[1]), "a"(ql[2]), "a"(ql[3]), "v"(ka), "v"(sh), "v"(sl));
+  } else if constexpr (NST == 4) {
+    asm("s_nop 4\n\t"
+        "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %5, %0, %13, %14 op_sel_hi:[0,0,0]\n\t"
+        "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %9, %0, %13, %15 op_sel_hi:[0,0,0]\n\t"
+        "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %2, %6, %0, %13, %14 op_sel:[1,1,0] op_sel_hi:[0,0,0]\n\t"
+        "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %2, %10, %0, %13, %15 op_sel:[1,1,0] op_sel_hi:[0,0,0]\n\t"
+        "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %3, %7, %0, %13, %14 op_sel_hi:[1,1,0]\n\t"
+        "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %3, %11, %0, %13, %15 op_sel_hi:[1,1,0]\n\t"
+        "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %4, %8, %0, %13, %14 op_sel:[1,1,0] op_sel_hi:[1,1,0]\n\t"
+        "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %4, %12, %0, %13, %15 op_sel:[1,1,0] op_sel_hi:[1,1,0]"
+        : "+v"(s)
+        : "v"(A[0]), "v"(A[1]), "v"(A[2]), "v"(A[3]), "a"(qh[0]), "a"(qh[1]), "a"(qh[2]), "a"(qh[3]), "a"(ql[0]), "a"(ql[1]), "a"(ql[2]), "a"(ql[3]), "v"(ka), "v"(sh), "v"(sl));
+  } else if constexpr (FIRST) {
+    asm("s_nop 4\n\t"
+        "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %3, 0, %7, %8 op_sel_hi:[0,0,0]\n\t"
+        "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %5, %0, %7, %9 op_sel_hi:[0,0,0]\n\t"
+        "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %2, %4, %0, %7, %8 op_sel:[1,1,0] op_sel_hi:[0,0,0]\n\t"
+        "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %2, %6, %0, %7, %9 op_sel:[1,1,0] op_sel_hi:[0,0,0]"
+        : "=&v"(s)
+        : "v"(A[0]), "v"(A[1]), "a"(qh[0]), "a"(qh[1]), "a"(ql[0]), "a"(ql[1]), "v"(ka), "v"(sh), "v"(sl));
+  } else {
+    asm("s_nop 4\n\t"
+        "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %3, %0, %7, %8 op_sel_hi:[0,0,0]\n\t"
+        "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %5, %0, %7, %9 op_sel_hi:[0,0,0]\n\t"
+        "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %2, %4, %0, %7, %8 op_sel:[1,1,0] op_sel_hi:[0,0,0]\n\t"
+        "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %2, %6, %0, %7, %9 op_sel:[1,1,0] op_sel_hi:[0,0,0]"
+        : "+v"(s)
+        : "v"(A[0]), "v"(A[1]), "a"(qh[0]), "a"(qh[1]), "a"(ql[0]), "a"(ql[1]), "v"(ka), "v"(sh), "v"(sl));
+  }
+}
+// After the last QK step: 32 wait states before anything reads s (covers the
+// MFMA-write -> VALU/LDS-read and srcC WAR hazards of a 16-pass MFMA).
+__device__ __forceinline__ void qk_drain(f32x16& s) { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s)); }
+// keep a value in AGPRs from here on
+__device__ __forceinline__ void to_agpr(i32x8& x) { asm volatile("" : "+a"(x)); }
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
@@ -203,16 +305,19 @@ __device__ void epilogue(const float* o_lds, int OSTR, int nheads, int head0, in
     }
     float r[EPL];
     float amax = 0.f;
+    const bool rot = EPL * lane + EPL > o0;  // this lane holds rotary dims
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
       const float up = __shfl(v[e], (lane + lsh) & 63);
       const float dn = __shfl(v[e], (lane - lsh) & 63);
-      const int x = EPL * lane + e;
       float val = v[e];
-      if (x >= o0) {
-        const int k = x - o0;
-        if (k < half) val = v[e] * cs[k] + up * sn[k];
-        else val = v[e] * cs[k - half] - dn * sn[k - half];
+      if (rot) {
+        const int x = EPL * lane + e;
+        if (x >= o0) {
+          const int k = x - o0;
+          if (k < half) val = v[e] * cs[k] + up * sn[k];
+          else val = v[e] * cs[k - half] - dn * sn[k - half];
+        }
       }
       r[e] = val;
       amax = fmaxf(amax, fabsf(val));
@@ -228,19 +333,14 @@ __device__ void epilogue(const float* o_lds, int OSTR, int nheads, int head0, in
         *reinterpret_cast<float2*>(a.out_f32 + g) = make_float2(r[0], r[1]);
       }
     }
-    // smallest e in [0, 254] with 448 * 2^(e-127) >= amax, decided on the f32 bits
-    const uint32_t bits = __builtin_bit_cast(uint32_t, amax);
-    int e = (int)(bits >> 23) - 8 + (((bits & 0x7FFFFFu) > 0x600000u) ? 1 : 0);
-    e = e < 0 ? 0 : (e > 254 ? 254 : e);
-    const int sh = 127 - e;
+    const int e = ue8m0_exp(amax);
+    const float sc = ue8m0_f32((uint32_t)e);  // codes = RNE(o / 2^(e-127))
     if constexpr (EPL == 8) {
-      uint32_t w0 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(r[0], sh), ldexpf(r[1], sh), 0, false);
-      w0 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(r[2], sh), ldexpf(r[3], sh), w0, true);
-      uint32_t w1 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(r[4], sh), ldexpf(r[5], sh), 0, false);
-      w1 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(r[6], sh), ldexpf(r[7], sh), w1, true);
+      const uint32_t w0 = enc2(enc2(0u, r[0], r[1], sc, false), r[2], r[3], sc, true);
+      const uint32_t w1 = enc2(enc2(0u, r[4], r[5], sc, false), r[6], r[7], sc, true);
       *reinterpret_cast<uint2*>(a.out_fp8 + g) = make_uint2(w0, w1);
     } else {
-      const uint32_t w0 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(r[0], sh), ldexpf(r[1], sh), 0, false);
+      const uint32_t w0 = enc2(0u, r[0], r[1], sc, false);
       *reinterpret_cast<uint16_t*>(a.out_fp8 + g) = (uint16_t)(w0 & 0xFFFFu);
     }
     if ((lane % LPB) == 0)
@@ -258,6 +358,110 @@ __device__ __forceinline__ void rope_table(int pos, const KArgs& a, float* cs, f
     sincos(ang, &s, &c);
     cs[threadIdx.x] = (float)c;
     sn[threadIdx.x] = (float)s;
+  }
+}
+
+// q prologue: RMSNorm + RoPE of the 64 (padded) heads of token t into the LDS q tile
+// (two E4M3 terms + UE8M0 scales for the E4M3 pool, bf16 for the bf16 pool).  Wave w
+// handles heads 16w .. 16w+15, lane l dims [EPL*l, EPL*l + EPL).
+template <int D, int EB>
+__device__ void q_prologue(unsigned char* smem, int t, int lane, int w, const KArgs& a, const float* cs,
+                           const float* sn) {
+  using C = Cfg<D, EB>;
+  constexpr int EPL = D / 64;
+  const int R = a.rope_dim, o0 = D - R, half = R / 2, lsh = half / EPL;
+  float wv[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) wv[e] = a.norm_w[EPL * lane + e];
+  using QV = typename std::conditional<EPL == 8, uint4, uint32_t>::type;
+  QV qraw[16];  // all 16 heads of this wave are loaded up front (one memory round trip)
+#pragma unroll
+  for (int hh = 0; hh < 16; ++hh) {
+    const int h = 16 * w + hh;
+    if (h < a.h_q) qraw[hh] = *reinterpret_cast<const QV*>(a.q + ((size_t)t * a.h_q + h) * D + EPL * lane);
+    else qraw[hh] = QV{};
+  }
+  const bool rot = EPL * lane + EPL > o0;
+#pragma unroll  // fully: qraw is indexed by hh and must stay in registers
+  for (int hh = 0; hh < 16; ++hh) {
+    const int h = 16 * w + hh;
+    float x[EPL];
+    if constexpr (EPL == 8) {
+      const uint4 u = qraw[hh];
+      const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[2 * k] = bf16_f32(uu[k] & 0xFFFFu);
+        x[2 * k + 1] = bf16_f32(uu[k] >> 16);
+      }
+    } else {
+      const uint32_t u = qraw[hh];
+      x[0] = bf16_f32(u & 0xFFFFu);
+      x[1] = bf16_f32(u >> 16);
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) ss += x[e] * x[e];
+    ss = wave_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)D + a.rms_eps);
+    float y[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) y[e] = x[e] * inv * wv[e];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const float up = __shfl(y[e], (lane + lsh) & 63);
+      const float dn = __shfl(y[e], (lane - lsh) & 63);
+      if (rot) {
+        const int xd = EPL * lane + e;
+        if (xd >= o0) {
+          const int k = xd - o0;
+          if (k < half) y[e] = y[e] * cs[k] - up * sn[k];
+          else y[e] = y[e] * cs[k - half] + dn * sn[k - half];
+        }
+      }
+    }
+    if constexpr (EB == 1) {
+      // two E4M3 terms, each with a UE8M0 scale per 32 dims (32/EPL lanes)
+      constexpr int LPB = 32 / EPL;
+      unsigned char* qf8 = smem;
+      unsigned char* qsc = smem + C::OFF_QSC;
+#pragma unroll
+      for (int term = 0; term < 2; ++term) {
+        float amax = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(y[e]));
+#pragma unroll
+        for (int o = 1; o < LPB; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+        const int eq = ue8m0_exp(amax);
+        const float sc = ue8m0_f32((uint32_t)eq);
+        unsigned char* dst = qf8 + (term * HP + h) * C::QS8 + EPL * lane;
+        if constexpr (EPL == 8) {
+          const uint32_t w0 = enc2(enc2(0u, y[0], y[1], sc, false), y[2], y[3], sc, true);
+          const uint32_t w1 = enc2(enc2(0u, y[4], y[5], sc, false), y[6], y[7], sc, true);
+          *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+          if (term == 0) {  // residual for the second term
+            const f32x2 d0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w0, sc, false);
+            const f32x2 d1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w0, sc, true);
+            const f32x2 d2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w1, sc, false);
+            const f32x2 d3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w1, sc, true);
+            y[0] -= d0[0]; y[1] -= d0[1]; y[2] -= d1[0]; y[3] -= d1[1];
+            y[4] -= d2[0]; y[5] -= d2[1]; y[6] -= d3[0]; y[7] -= d3[1];
+          }
+        } else {
+          const uint32_t w0 = enc2(0u, y[0], y[1], sc, false);
+          *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(w0 & 0xFFFFu);
+          if (term == 0) {
+            const f32x2 d0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w0, sc, false);
+            y[0] -= d0[0]; y[1] -= d0[1];
+          }
+        }
+        if ((lane % LPB) == 0) qsc[(term * HP + h) * C::NSB + (EPL * lane) / 32] = (unsigned char)eq;
+      }
+    } else {
+      unsigned short* qbf = reinterpret_cast<unsigned short*>(smem);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qbf[h * C::QS + EPL * lane + e] = (unsigned short)bf16_rne(y[e]);
+    }
   }
 }
 
@@ -281,80 +485,53 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
   const int t = blockIdx.x / ns, split = blockIdx.x % ns;
   const int pos = a.positions[t];
 
-  // ---------------- prologue: q -> RMSNorm -> RoPE -> bf16 (LDS) -> register fragments
+  // ---------------- prologue
   rope_table(pos, a, cs, sn);
   __syncthreads();
-  {
-    constexpr int EPL = D / 64;  // q elements per lane
-    unsigned short* qbf = reinterpret_cast<unsigned short*>(smem);
-    const int R = a.rope_dim, o0 = D - R, half = R / 2, lsh = half / EPL;
-    float wv[EPL];
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) wv[e] = a.norm_w[EPL * lane + e];
-    // all 16 heads of this wave are loaded up front (one memory round trip)
-    using QV = typename std::conditional<EPL == 8, uint4, uint32_t>::type;
-    QV qraw[16];
-#pragma unroll
-    for (int hh = 0; hh < 16; ++hh) {
-      const int h = 16 * w + hh;
-      if (h < a.h_q) qraw[hh] = *reinterpret_cast<const QV*>(a.q + ((size_t)t * a.h_q + h) * D + EPL * lane);
-      else qraw[hh] = QV{};
-    }
-#pragma unroll
-    for (int hh = 0; hh < 16; ++hh) {
-      const int h = 16 * w + hh;
-      float x[EPL];
-      if constexpr (EPL == 8) {
-        const uint4 u = qraw[hh];
-        const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          x[2 * k] = bf16_f32(uu[k] & 0xFFFFu);
-          x[2 * k + 1] = bf16_f32(uu[k] >> 16);
-        }
-      } else {
-        const uint32_t u = qraw[hh];
-        x[0] = bf16_f32(u & 0xFFFFu);
-        x[1] = bf16_f32(u >> 16);
-      }
-      float ss = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) ss += x[e] * x[e];
-      ss = wave_sum(ss);
-      const float inv = 1.0f / sqrtf(ss / (float)D + a.rms_eps);
-      float y[EPL], yo[EPL];
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) y[e] = x[e] * inv * wv[e];
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        const float up = __shfl(y[e], (lane + lsh) & 63);
-        const float dn = __shfl(y[e], (lane - lsh) & 63);
-        const int xd = EPL * lane + e;
-        float r = y[e];
-        if (xd >= o0) {
-          const int k = xd - o0;
-          if (k < half) r = y[e] * cs[k] - up * sn[k];
-          else r = y[e] * cs[k - half] + dn * sn[k - half];
-        }
-        yo[e] = r;
-      }
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) qbf[h * C::QS + EPL * lane + e] = (unsigned short)bf16_rne(yo[e]);
-    }
-  }
+  q_prologue<D, EB>(smem, t, lane, w, a, cs, sn);
   __syncthreads();
-  // B fragments of Q^T for S^T = K Q^T.  The contraction order over dims is permuted to
-  // match the K reads: for the E4M3 pool step 2m+j, lane half h covers dims
-  // 32m + 16h + 8j + [0, 8) (one 16-byte read of K serves two steps); for the bf16 pool
-  // step ks, lane half h covers dims 16ks + 8h + [0, 8).
-  bf16x8 qf[C::KS];
-  {
+  // Q fragments (B operand of S^T = K Q^T) for the 32 heads of group qa.
+  //   E4M3 pool: k-step ks covers dims [64ks, 64ks+64); lane half h holds dims
+  //   64ks + 16h + [0,16) and 64ks + 32 + 16h + [0,16) of its head (the 32x32x64 f8
+  //   operand layout); the UE8M0 scale of block 2ks + h sits in byte ks % 4 of
+  //   qs8[term][ks / 4].
+  //   bf16 pool: step ks, lane half h holds dims 16ks + 8h + [0, 8).
+  i32x8 qf8[2][(EB == 1) ? C::KS8 : 1];
+  uint32_t qs8[2][(EB == 1) ? (C::KS8 + 3) / 4 : 1];
+  bf16x8 qbf[(EB == 2) ? C::KS : 1];
+  const uint32_t hsel = lhalf ? 0x07050301u : 0x06040200u;  // bytes 2j + h of 8
+  if constexpr (EB == 1) {
+#pragma unroll
+    for (int term = 0; term < 2; ++term) {
+      const unsigned char* qrow = smem + (term * HP + 32 * qa + lrow) * C::QS8 + 16 * lhalf;
+#pragma unroll
+      for (int ks = 0; ks < C::KS8; ++ks) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(qrow + 64 * ks);
+        const uint4 hi = *reinterpret_cast<const uint4*>(qrow + 64 * ks + 32);
+        qf8[term][ks] = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z,
+                                (int)hi.w};
+        to_agpr(qf8[term][ks]);
+      }
+      const unsigned char* srow = smem + C::OFF_QSC + (term * HP + 32 * qa + lrow) * C::NSB;
+      if constexpr (C::NSB >= 16) {
+        const uint4 s4 = *reinterpret_cast<const uint4*>(srow);
+        qs8[term][0] = __builtin_amdgcn_perm(s4.y, s4.x, hsel);
+        qs8[term][1] = __builtin_amdgcn_perm(s4.w, s4.z, hsel);
+      } else {
+        const uint32_t s1 = *reinterpret_cast<const uint32_t*>(srow);
+        qs8[term][0] = __builtin_amdgcn_perm(s1, s1, hsel);
+      }
+    }
+  } else {
     const unsigned short* qrow = reinterpret_cast<const unsigned short*>(smem) + (32 * qa + lrow) * C::QS;
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      const int dim0 = (EB == 1) ? 32 * (ks >> 1) + 16 * lhalf + 8 * (ks & 1) : 16 * ks + 8 * lhalf;
-      qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + dim0);
-    }
+    for (int ks = 0; ks < C::KS; ++ks) qbf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * lhalf);
+  }
+  __syncthreads();  // the q tile region is reused by the raw tiles below
+  {
+    // zero the raw tiles once: rows that are never loaded then read as finite values
+    uint4* z = reinterpret_cast<uint4*>(smem);
+    for (int i = tid; i < C::RAW_END / 16; i += NTHREADS) z[i] = make_uint4(0u, 0u, 0u, 0u);
   }
 
   // ---------------- tile range of this workgroup
@@ -376,7 +553,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
   };
 
   // Enqueue the LDS DMA of one tile's rows (and scales) into raw / sc.  Rows that are not
-  // read keep stale LDS contents: the QK masks them and the V transpose zeroes them.
+  // read keep older (finite) LDS contents: the QK masks them and P is zero for them.
   auto issue_tile = [&](int id_vec, unsigned char* raw, unsigned char* sc, int lane) {
     constexpr int GPW = (T / C::G) / 4;  // DMA groups per wave
 #pragma unroll
@@ -410,7 +587,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
 
   int id_cur = load_ids(tb);
   int id_next = load_ids(tb + 1);
-  __syncthreads();  // every wave holds its q fragments: the q tile region may be reused
+  __syncthreads();  // zeroing done before any DMA lands
   if (tb < te) issue_tile(id_cur, smem + C::OFF_RAW0, smem + C::OFF_SC0, lane);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA has landed
 
@@ -424,80 +601,80 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
     // lane-dependent values recomputed per tile (keeps them out of the live set)
     const int tid = (int)threadIdx.x + opaque_zero();
     const int lane = tid & 63, lrow = lane & 31, lhalf = lane >> 5;
+    const uint32_t hsel = lhalf ? 0x07050301u : 0x06040200u;
     const unsigned long long mask = __ballot(id_cur >= 0);
     if (tile + 1 < te) issue_tile(id_next, raw_n, sc_n, lane);
     const int id_next2 = load_ids(tile + 2);
 
     // ---- QK^T: S^T[32 rows of half qc][32 heads of group qa]
     f32x16 s;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = 0.f;
     {
       const int r = 32 * qc + lrow;
       if constexpr (EB == 1) {
-        uint32_t scr[C::NSB / 4];
-#pragma unroll
-        for (int k = 0; k < C::NSB / 4; ++k) scr[k] = *reinterpret_cast<const uint32_t*>(sc_l + r * C::NSB + 4 * k);
-#pragma unroll
-        for (int m = 0; m < C::KS / 2; ++m) {  // dims [32m, 32m+32): scale block m
-          const uint4 rw = *reinterpret_cast<const uint4*>(raw_l + raw_off<C>(r, 2 * m + lhalf));
-          const float sc = ue8m0_f32((scr[m >> 2] >> (8 * (m & 3))) & 0xFFu);
-          const uint4 u0 = make_uint4(cvt_lo(rw.x, sc), cvt_hi(rw.x, sc), cvt_lo(rw.y, sc), cvt_hi(rw.y, sc));
-          const uint4 u1 = make_uint4(cvt_lo(rw.z, sc), cvt_hi(rw.z, sc), cvt_lo(rw.w, sc), cvt_hi(rw.w, sc));
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u0), qf[2 * m], s, 0, 0, 0);
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u1), qf[2 * m + 1], s, 0, 0, 0);
+        uint32_t ksc[(C::KS8 + 3) / 4];  // UE8M0 of block 2ks + h in byte ks % 4
+        if constexpr (C::NSB >= 16) {
+          const uint4 s4 = *reinterpret_cast<const uint4*>(sc_l + r * C::NSB);
+          ksc[0] = __builtin_amdgcn_perm(s4.y, s4.x, hsel);
+          ksc[1] = __builtin_amdgcn_perm(s4.w, s4.z, hsel);
+        } else {
+          const uint32_t s1 = *reinterpret_cast<const uint32_t*>(sc_l + r * C::NSB);
+          ksc[0] = __builtin_amdgcn_perm(s1, s1, hsel);
         }
+        constexpr int NST = C::KS8 < 4 ? C::KS8 : 4;  // k-steps per scale word
+        static_for<C::KS8 / NST>([&](auto bc) {
+          constexpr int b = decltype(bc)::value;
+          i32x8 A[NST];
+#pragma unroll
+          for (int j = 0; j < NST; ++j) {
+            const int ks = NST * b + j;
+            const uint4 lo = *reinterpret_cast<const uint4*>(raw_l + raw_off<C>(r, 4 * ks + lhalf));
+            const uint4 hi = *reinterpret_cast<const uint4*>(raw_l + raw_off<C>(r, 4 * ks + 2 + lhalf));
+            A[j] = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          }
+          qk_block<NST, b == 0>(s, A, &qf8[0][NST * b], &qf8[1][NST * b], ksc[b], qs8[0][b], qs8[1][b]);
+        });
+        qk_drain(s);
       } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
           const bf16x8 A = *reinterpret_cast<const bf16x8*>(raw_l + raw_off<C>(r, 2 * ks + lhalf));
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qf[ks], s, 0, 0, 0);
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qbf[ks], s, 0, 0, 0);
         }
       }
     }
 
-    // ---- V tile: raw rows -> Vt[dim][row] bf16 (transposed, swizzled); blocks of
-    // 4 rows x one 16-byte chunk; rows that are not read become zeros
+    // ---- V tile: raw rows -> Vt[dim][slot] bf16.  A block is the 4 rows 8q + p + 2k
+    // (k = 0..3, slots 8q + 4p + k) of one 16-byte chunk c.
     constexpr int NBLK = (T / 4) * C::NCH;
     for (int bb = tid; bb < NBLK; bb += NTHREADS) {
-      int q, c, rot;
+      int q, p, c;
       if constexpr (C::NCH == 32) {
-        // lanes of an 8-lane group: 4 consecutive chunks x 2 quads read in rotated row
-        // order, so each read step touches 8 distinct bank slots
+        // an 8-lane group covers 4 consecutive chunks x both parities, so each read step
+        // touches 8 distinct bank slots and each write step 16 distinct 8-byte slots
         const int u = lane & 7, g8 = lane >> 3, j = bb / NTHREADS;
-        c = 4 * g8 + (u & 3);
-        q = 2 * (w + 4 * j) + (u >> 2);
-        rot = u >> 2;
+        c = 4 * g8 + (u >> 1);
+        p = u & 1;
+        q = w + 4 * j;
       } else {
-        q = bb / C::NCH;
-        c = bb % C::NCH;
-        rot = 0;
+        p = bb & 1;
+        c = (bb >> 1) % C::NCH;
+        q = (bb >> 1) / C::NCH;
       }
-      uint32_t pk[4][C::CE / 2];  // [row][element pair]
+      uint32_t pk[4][C::CE / 2];  // [k][element pair]
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int rr = (jj + rot) & 3;
-        const int row = 4 * q + rr;
+      for (int k = 0; k < 4; ++k) {
+        const int row = 8 * q + p + 2 * k;
         const uint4 rw = *reinterpret_cast<const uint4*>(raw_l + raw_off<C>(row, c));
-        const bool valid = (mask >> row) & 1ull;
-        uint32_t v[C::CE / 2];
         if constexpr (EB == 1) {
           const float sc = ue8m0_f32(sc_l[row * C::NSB + (c >> 1)]);
-          v[0] = cvt_lo(rw.x, sc); v[1] = cvt_hi(rw.x, sc);
-          v[2] = cvt_lo(rw.y, sc); v[3] = cvt_hi(rw.y, sc);
-          v[4] = cvt_lo(rw.z, sc); v[5] = cvt_hi(rw.z, sc);
-          v[6] = cvt_lo(rw.w, sc); v[7] = cvt_hi(rw.w, sc);
+          pk[k][0] = cvt_lo(rw.x, sc); pk[k][1] = cvt_hi(rw.x, sc);
+          pk[k][2] = cvt_lo(rw.y, sc); pk[k][3] = cvt_hi(rw.y, sc);
+          pk[k][4] = cvt_lo(rw.z, sc); pk[k][5] = cvt_hi(rw.z, sc);
+          pk[k][6] = cvt_lo(rw.w, sc); pk[k][7] = cvt_hi(rw.w, sc);
         } else {
-          v[0] = rw.x; v[1] = rw.y; v[2] = rw.z; v[3] = rw.w;
-        }
-#pragma unroll
-        for (int k = 0; k < C::CE / 2; ++k) {
-          // select the row slot with compile-time indices after rotation
-          const uint32_t val = valid ? v[k] : 0u;
-          if (rr == 0) pk[0][k] = val;
-          else if (rr == 1) pk[1][k] = val;
-          else if (rr == 2) pk[2][k] = val;
-          else pk[3][k] = val;
+          pk[k][0] = rw.x; pk[k][1] = rw.y; pk[k][2] = rw.z; pk[k][3] = rw.w;
         }
       }
 #pragma unroll
@@ -507,7 +684,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
         const uint2 o = make_uint2(__builtin_amdgcn_perm(pk[1][k], pk[0][k], sel),
                                    __builtin_amdgcn_perm(pk[3][k], pk[2][k], sel));
         const int n = C::CE * c + e;
-        *reinterpret_cast<uint2*>(vt_l + n * 128 + 16 * ((q >> 1) ^ swz(n)) + 8 * (q & 1)) = o;
+        *reinterpret_cast<uint2*>(vt_l + n * 128 + 16 * (q ^ swz(n)) + 8 * p) = o;
       }
     }
 
@@ -524,27 +701,32 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
     if (lhalf == 0) maxx[qc * HP + 32 * qa + lrow] = mloc;
     __syncthreads();  // B2: maxima exchanged
 
-    // ---- softmax (part 2): running max (lazy), P in bf16, alpha
+    // ---- softmax (part 2): running max (lazy), P in bf16 by slot, alpha
     {
       const float mt = fmaxf(mloc, maxx[(1 - qc) * HP + 32 * qa + lrow]);
       float mnew = m_run;
       if (mt > -INFINITY && (m_run == -INFINITY || mt > m_run + 8.0f)) mnew = mt;
       const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mnew);
       m_run = mnew;
-      uint32_t pb[16];
+      float p[16];
       float lp = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = (mnew == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[i] - mnew);
-        pb[i] = bf16_rne(p);
-        lp += bf16_f32(pb[i]);
+        p[i] = (mnew == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[i] - mnew);
+        lp += p[i];
       }
       l_run = l_run * alpha + lp;
       const int head = 32 * qa + lrow;
+      unsigned char* prow = p_l + head * 128;
+      const int sw = swz(head);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const uint2 pw = make_uint2(pb[4 * g] | (pb[4 * g + 1] << 16), pb[4 * g + 2] | (pb[4 * g + 3] << 16));
-        *reinterpret_cast<uint2*>(p_l + head * 128 + 16 * ((4 * qc + g) ^ swz(head)) + 8 * lhalf) = pw;
+        // rows 32qc + 8g + 4h + i -> slots 8(4qc + g) + 2h + {0, 1} (i = 0, 2) and
+        // 8(4qc + g) + 4 + 2h + {0, 1} (i = 1, 3)
+        const int q8 = 4 * qc + g;
+        unsigned char* cbase = prow + 16 * (q8 ^ sw) + 4 * lhalf;
+        *reinterpret_cast<uint32_t*>(cbase) = pack_bf16(p[4 * g + 0], p[4 * g + 2]);
+        *reinterpret_cast<uint32_t*>(cbase + 8) = pack_bf16(p[4 * g + 1], p[4 * g + 3]);
       }
       if (qc == 0 && lhalf == 0) alpha_l[head] = alpha;
     }
