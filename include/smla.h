@@ -29,6 +29,8 @@
  *   - All array pointers are DEVICE pointers (HIP global memory) to contiguous
  *     row-major arrays owned by the caller.  The library keeps no reference after
  *     the call returns, allocates nothing and never synchronizes the device.
+ *   - q, kv_pool, norm_w, out_fp8, out_f32 and the workspace must be 16-byte aligned,
+ *     kv_scales 4-byte aligned (SMLA_ERR_VALUE otherwise).
  *   - The work is enqueued on params->stream (a hipStream_t; NULL = the null stream)
  *     and completes asynchronously; the call may be captured in a HIP graph.
  *   - Errors are reported by return code, never by exception or abort; the
@@ -54,7 +56,8 @@ extern "C" {
 #define SMLA_ERR_SHAPE 2 /* unsupported d / rope_dim / h_q / topk combination */
 #define SMLA_ERR_VALUE 3 /* bad scalar (s_q < 0, n_rows < 1, non-finite or non-positive
                             sm_scale / rms_eps / rope_theta, workspace too small,
-                            bad kv_format, num_splits out of range) */
+                            bad kv_format, num_splits out of range) or a misaligned
+                            array pointer */
 #define SMLA_ERR_HIP 4   /* a HIP launch failed */
 
 /* kv_pool formats */

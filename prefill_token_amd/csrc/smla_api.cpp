@@ -102,6 +102,16 @@ int sparse_mla_fwd(const void* q, const void* kv_pool, const uint8_t* kv_scales,
   if (p->topk > 0 && !indices) return fail(SMLA_ERR_NULL, "indices is NULL");
   if (p->kv_format == SMLA_KV_E4M3_UE8M0 && !kv_scales)
     return fail(SMLA_ERR_NULL, "kv_scales is NULL for the E4M3 pool");
+  // vector loads / stores of 16 bytes (4 for the scale rows)
+  const struct {
+    const void* ptr;
+    uintptr_t align;
+    const char* name;
+  } al[] = {{q, 16, "q"}, {kv_pool, 16, "kv_pool"}, {kv_scales, 4, "kv_scales"}, {norm_w, 16, "norm_w"},
+            {out_fp8, 16, "out_fp8"}, {p->out_f32, 16, "out_f32"}, {p->workspace, 16, "workspace"}};
+  for (const auto& x : al)
+    if (reinterpret_cast<uintptr_t>(x.ptr) % x.align != 0)
+      return fail(SMLA_ERR_VALUE, "%s must be %u-byte aligned", x.name, (unsigned)x.align);
   const int ns = choose_splits(p);
   const size_t need = workspace_bytes_for(p, ns);
   if (need > 0 && (!p->workspace || p->workspace_bytes < need))

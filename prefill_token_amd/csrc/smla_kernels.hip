@@ -208,6 +208,12 @@ __device__ __forceinline__ void dma4(const void* g, uint32_t lds_base) {
       : "memory");
 }
 
+// lane permutation within rows of 16 lanes (DPP control CTRL), all lanes written
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
 // A zero the compiler cannot see through: lane-dependent address math derived from it
 // is recomputed where it is used instead of being hoisted (and kept live) across loops.
 __device__ __forceinline__ int opaque_zero() {
@@ -274,77 +280,61 @@ __device__ __forceinline__ void qk_drain(f32x16& s) { asm volatile("s_nop 7\n\ts
 // keep a value in AGPRs from here on
 __device__ __forceinline__ void to_agpr(i32x8& x) { asm volatile("" : "+a"(x)); }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
-// Inverse RoPE + UE8M0/E4M3 quantization of heads [0, nheads) held in o_lds (f32,
-// row stride OSTR), writing global heads head0 + hl of token tok.  Each wave takes one
-// head at a time; lane l holds dims [EPL*l, EPL*l + EPL): the rotary partner comes from
-// lane l +- half/EPL and the 32-element block spans 32/EPL consecutive lanes.
+// Inverse RoPE + UE8M0/E4M3 quantization of heads [0, nheads) held in o_lds (f32, row
+// stride OSTR), writing global heads head0 + hl of token tok.  One thread per (head,
+// 32-dim block), heads fastest across lanes: the block amax is lane-local and the
+// rotary partner dims (x +- rope_dim/2, same head) are read from the tile itself.
 template <int D>
 __device__ void epilogue(const float* o_lds, int OSTR, int nheads, int head0, int tok, const KArgs& a,
                          const float* cs, const float* sn) {
-  constexpr int EPL = D / 64;
-  constexpr int LPB = 32 / EPL;  // lanes per 32-element block
-  const int R = a.rope_dim, o0 = D - R, half = R / 2, lsh = half / EPL;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  for (int hl = w; hl < nheads; hl += NTHREADS / 64) {
-    const float* orow = o_lds + hl * OSTR + EPL * lane;
-    float v[EPL];
-    if constexpr (EPL == 8) {
-      const float4 lo = *reinterpret_cast<const float4*>(orow);
-      const float4 hi = *reinterpret_cast<const float4*>(orow + 4);
-      v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
-      v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
-    } else {
-      const float2 p = *reinterpret_cast<const float2*>(orow);
-      v[0] = p.x; v[1] = p.y;
-    }
-    float r[EPL];
-    float amax = 0.f;
-    const bool rot = EPL * lane + EPL > o0;  // this lane holds rotary dims
+  constexpr int NBK = D / 32;
+  const int R = a.rope_dim, o0 = D - R, half = R / 2;
+  for (int u = threadIdx.x; u < nheads * NBK; u += NTHREADS) {
+    const int hl = u % nheads, b = u / nheads;
+    const float* row = o_lds + hl * OSTR;
+    float v[32];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      const float up = __shfl(v[e], (lane + lsh) & 63);
-      const float dn = __shfl(v[e], (lane - lsh) & 63);
-      float val = v[e];
-      if (rot) {
-        const int x = EPL * lane + e;
+    for (int j = 0; j < 8; ++j) {
+      const float4 q4 = *reinterpret_cast<const float4*>(row + 32 * b + 4 * j);
+      v[4 * j] = q4.x; v[4 * j + 1] = q4.y; v[4 * j + 2] = q4.z; v[4 * j + 3] = q4.w;
+    }
+    if (32 * b + 32 > o0) {  // rotary dims in this block (chunks of 4 never straddle o0)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int x = 32 * b + 4 * j;
         if (x >= o0) {
           const int k = x - o0;
-          if (k < half) val = v[e] * cs[k] + up * sn[k];
-          else val = v[e] * cs[k - half] - dn * sn[k - half];
+          const bool lo = k < half;
+          const int kk = lo ? k : k - half;
+          const float4 pr = *reinterpret_cast<const float4*>(row + (lo ? x + half : x - half));
+          const float4 c4 = *reinterpret_cast<const float4*>(cs + kk);
+          const float4 s4 = *reinterpret_cast<const float4*>(sn + kk);
+          const float sg = lo ? 1.f : -1.f;
+          v[4 * j] = v[4 * j] * c4.x + sg * pr.x * s4.x;
+          v[4 * j + 1] = v[4 * j + 1] * c4.y + sg * pr.y * s4.y;
+          v[4 * j + 2] = v[4 * j + 2] * c4.z + sg * pr.z * s4.z;
+          v[4 * j + 3] = v[4 * j + 3] * c4.w + sg * pr.w * s4.w;
         }
       }
-      r[e] = val;
-      amax = fmaxf(amax, fabsf(val));
     }
+    float amax = 0.f;
 #pragma unroll
-    for (int o = 1; o < LPB; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-    const size_t g = ((size_t)tok * a.h_q + head0 + hl) * D + EPL * lane;
+    for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(v[e]));
+    const size_t g = ((size_t)tok * a.h_q + head0 + hl) * D + 32 * b;
     if (a.out_f32) {
-      if constexpr (EPL == 8) {
-        reinterpret_cast<float4*>(a.out_f32 + g)[0] = make_float4(r[0], r[1], r[2], r[3]);
-        reinterpret_cast<float4*>(a.out_f32 + g)[1] = make_float4(r[4], r[5], r[6], r[7]);
-      } else {
-        *reinterpret_cast<float2*>(a.out_f32 + g) = make_float2(r[0], r[1]);
-      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        reinterpret_cast<float4*>(a.out_f32 + g)[j] = make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
     }
     const int e = ue8m0_exp(amax);
     const float sc = ue8m0_f32((uint32_t)e);  // codes = RNE(o / 2^(e-127))
-    if constexpr (EPL == 8) {
-      const uint32_t w0 = enc2(enc2(0u, r[0], r[1], sc, false), r[2], r[3], sc, true);
-      const uint32_t w1 = enc2(enc2(0u, r[4], r[5], sc, false), r[6], r[7], sc, true);
-      *reinterpret_cast<uint2*>(a.out_fp8 + g) = make_uint2(w0, w1);
-    } else {
-      const uint32_t w0 = enc2(0u, r[0], r[1], sc, false);
-      *reinterpret_cast<uint16_t*>(a.out_fp8 + g) = (uint16_t)(w0 & 0xFFFFu);
-    }
-    if ((lane % LPB) == 0)
-      a.out_scales[((size_t)tok * a.h_q + head0 + hl) * (D / 32) + (EPL * lane) / 32] = (uint8_t)e;
+    uint32_t wd[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      wd[j] = enc2(enc2(0u, v[4 * j], v[4 * j + 1], sc, false), v[4 * j + 2], v[4 * j + 3], sc, true);
+    reinterpret_cast<uint4*>(a.out_fp8 + g)[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    reinterpret_cast<uint4*>(a.out_fp8 + g)[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
+    a.out_scales[((size_t)tok * a.h_q + head0 + hl) * NBK + b] = (uint8_t)e;
   }
 }
 
@@ -362,105 +352,146 @@ __device__ __forceinline__ void rope_table(int pos, const KArgs& a, float* cs, f
 }
 
 // q prologue: RMSNorm + RoPE of the 64 (padded) heads of token t into the LDS q tile
-// (two E4M3 terms + UE8M0 scales for the E4M3 pool, bf16 for the bf16 pool).  Wave w
-// handles heads 16w .. 16w+15, lane l dims [EPL*l, EPL*l + EPL).
+// (two E4M3 terms + UE8M0 scales for the E4M3 pool, bf16 for the bf16 pool).  One thread
+// per (head, 32-dim block), blocks fastest across lanes: the loads are contiguous per
+// head, the sum of squares is reduced over the head's D/32 adjacent lanes with DPP, and
+// the block amax of each term is lane-local.  The rotary partners (x +- rope_dim/2) are
+// exchanged through an f32 staging area at the start of the q tile region.  Also fills
+// the cos / sin table (between its loads and its use).
 template <int D, int EB>
-__device__ void q_prologue(unsigned char* smem, int t, int lane, int w, const KArgs& a, const float* cs,
-                           const float* sn) {
+__device__ void q_prologue(unsigned char* smem, int t, int pos, const KArgs& a, float* cs, float* sn) {
   using C = Cfg<D, EB>;
-  constexpr int EPL = D / 64;
-  const int R = a.rope_dim, o0 = D - R, half = R / 2, lsh = half / EPL;
-  float wv[EPL];
+  constexpr int NBK = D / 32;               // lanes per head
+  constexpr int NIT = HP * NBK / NTHREADS;  // units per thread
+  static_assert(NIT * NTHREADS == HP * NBK && NBK <= 16, "prologue mapping");
+  const int R = a.rope_dim, o0 = D - R, half = R / 2;
+  const int b = threadIdx.x % NBK;  // the same block in every unit of this thread
+  uint4 qraw[NIT][4];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) wv[e] = a.norm_w[EPL * lane + e];
-  using QV = typename std::conditional<EPL == 8, uint4, uint32_t>::type;
-  QV qraw[16];  // all 16 heads of this wave are loaded up front (one memory round trip)
+  for (int it = 0; it < NIT; ++it) {
+    const int h = (threadIdx.x + NTHREADS * it) / NBK;
+    const uint4* src = reinterpret_cast<const uint4*>(a.q + ((size_t)t * a.h_q + h) * D + 32 * b);
 #pragma unroll
-  for (int hh = 0; hh < 16; ++hh) {
-    const int h = 16 * w + hh;
-    if (h < a.h_q) qraw[hh] = *reinterpret_cast<const QV*>(a.q + ((size_t)t * a.h_q + h) * D + EPL * lane);
-    else qraw[hh] = QV{};
+    for (int j = 0; j < 4; ++j) qraw[it][j] = h < a.h_q ? src[j] : make_uint4(0u, 0u, 0u, 0u);
   }
-  const bool rot = EPL * lane + EPL > o0;
-#pragma unroll  // fully: qraw is indexed by hh and must stay in registers
-  for (int hh = 0; hh < 16; ++hh) {
-    const int h = 16 * w + hh;
-    float x[EPL];
-    if constexpr (EPL == 8) {
-      const uint4 u = qraw[hh];
-      const uint32_t uu[4] = {u.x, u.y, u.z, u.w};
+  float wv[32];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        x[2 * k] = bf16_f32(uu[k] & 0xFFFFu);
-        x[2 * k + 1] = bf16_f32(uu[k] >> 16);
-      }
-    } else {
-      const uint32_t u = qraw[hh];
-      x[0] = bf16_f32(u & 0xFFFFu);
-      x[1] = bf16_f32(u >> 16);
-    }
+  for (int j = 0; j < 8; ++j) {
+    const float4 w4 = *reinterpret_cast<const float4*>(a.norm_w + 32 * b + 4 * j);
+    wv[4 * j] = w4.x; wv[4 * j + 1] = w4.y; wv[4 * j + 2] = w4.z; wv[4 * j + 3] = w4.w;
+  }
+  rope_table(pos, a, cs, sn);  // overlaps the loads above
+
+  float* ystage = reinterpret_cast<float*>(smem);  // [HP][R] f32, rotary dims only
+  const bool rotb = 32 * b + 32 > o0;
+  float y[NIT][32];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int h = (threadIdx.x + NTHREADS * it) / NBK;
     float ss = 0.f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) ss += x[e] * x[e];
-    ss = wave_sum(ss);
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t uu[4] = {qraw[it][j].x, qraw[it][j].y, qraw[it][j].z, qraw[it][j].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        y[it][8 * j + 2 * k] = bf16_f32(uu[k] & 0xFFFFu);
+        y[it][8 * j + 2 * k + 1] = bf16_f32(uu[k] >> 16);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 32; ++e) ss += y[it][e] * y[it][e];
+    // sum over the NBK lanes of this head (a row of 16 lanes or a quad): lane pairs
+    // i^1, i^2 (quad_perm), then i <-> 7-i and i <-> 15-i (half / full row mirror), so
+    // that every lane adds the same two partial sums and ends with the same value
+    ss += dpp_f32<0xB1>(ss);
+    ss += dpp_f32<0x4E>(ss);
+    if constexpr (NBK == 16) {
+      ss += dpp_f32<0x141>(ss);
+      ss += dpp_f32<0x140>(ss);
+    }
     const float inv = 1.0f / sqrtf(ss / (float)D + a.rms_eps);
-    float y[EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) y[e] = x[e] * inv * wv[e];
+    for (int e = 0; e < 32; ++e) y[it][e] = y[it][e] * inv * wv[e];
+    if (rotb) {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      const float up = __shfl(y[e], (lane + lsh) & 63);
-      const float dn = __shfl(y[e], (lane - lsh) & 63);
-      if (rot) {
-        const int xd = EPL * lane + e;
-        if (xd >= o0) {
-          const int k = xd - o0;
-          if (k < half) y[e] = y[e] * cs[k] - up * sn[k];
-          else y[e] = y[e] * cs[k - half] + dn * sn[k - half];
+      for (int j = 0; j < 8; ++j) {
+        const int x = 32 * b + 4 * j;
+        if (x >= o0)
+          *reinterpret_cast<float4*>(ystage + h * R + (x - o0)) =
+              make_float4(y[it][4 * j], y[it][4 * j + 1], y[it][4 * j + 2], y[it][4 * j + 3]);
+      }
+    }
+  }
+  __syncthreads();  // staged rotary values and the cos / sin table visible
+  if (rotb) {
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int h = (threadIdx.x + NTHREADS * it) / NBK;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int x = 32 * b + 4 * j;
+        if (x >= o0) {
+          const int k = x - o0;
+          const bool lo = k < half;
+          const int kk = lo ? k : k - half;
+          const float4 pr = *reinterpret_cast<const float4*>(ystage + h * R + (lo ? k + half : k - half));
+          const float4 c4 = *reinterpret_cast<const float4*>(cs + kk);
+          const float4 s4 = *reinterpret_cast<const float4*>(sn + kk);
+          const float sg = lo ? -1.f : 1.f;  // forward rotation
+          y[it][4 * j] = y[it][4 * j] * c4.x + sg * pr.x * s4.x;
+          y[it][4 * j + 1] = y[it][4 * j + 1] * c4.y + sg * pr.y * s4.y;
+          y[it][4 * j + 2] = y[it][4 * j + 2] * c4.z + sg * pr.z * s4.z;
+          y[it][4 * j + 3] = y[it][4 * j + 3] * c4.w + sg * pr.w * s4.w;
         }
       }
     }
+  }
+  __syncthreads();  // staging reads done: the q tile below overwrites it
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int h = (threadIdx.x + NTHREADS * it) / NBK;
     if constexpr (EB == 1) {
-      // two E4M3 terms, each with a UE8M0 scale per 32 dims (32/EPL lanes)
-      constexpr int LPB = 32 / EPL;
+      // two E4M3 terms, each with its own UE8M0 scale per 32 dims
       unsigned char* qf8 = smem;
       unsigned char* qsc = smem + C::OFF_QSC;
 #pragma unroll
       for (int term = 0; term < 2; ++term) {
         float amax = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(y[e]));
-#pragma unroll
-        for (int o = 1; o < LPB; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+        for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(y[it][e]));
         const int eq = ue8m0_exp(amax);
         const float sc = ue8m0_f32((uint32_t)eq);
-        unsigned char* dst = qf8 + (term * HP + h) * C::QS8 + EPL * lane;
-        if constexpr (EPL == 8) {
-          const uint32_t w0 = enc2(enc2(0u, y[0], y[1], sc, false), y[2], y[3], sc, true);
-          const uint32_t w1 = enc2(enc2(0u, y[4], y[5], sc, false), y[6], y[7], sc, true);
-          *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
-          if (term == 0) {  // residual for the second term
-            const f32x2 d0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w0, sc, false);
-            const f32x2 d1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w0, sc, true);
-            const f32x2 d2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w1, sc, false);
-            const f32x2 d3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w1, sc, true);
-            y[0] -= d0[0]; y[1] -= d0[1]; y[2] -= d1[0]; y[3] -= d1[1];
-            y[4] -= d2[0]; y[5] -= d2[1]; y[6] -= d3[0]; y[7] -= d3[1];
-          }
-        } else {
-          const uint32_t w0 = enc2(0u, y[0], y[1], sc, false);
-          *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(w0 & 0xFFFFu);
-          if (term == 0) {
-            const f32x2 d0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w0, sc, false);
-            y[0] -= d0[0]; y[1] -= d0[1];
+        uint32_t wd[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          wd[j] = enc2(enc2(0u, y[it][4 * j], y[it][4 * j + 1], sc, false), y[it][4 * j + 2], y[it][4 * j + 3], sc,
+                       true);
+        uint4* dst = reinterpret_cast<uint4*>(qf8 + (term * HP + h) * C::QS8 + 32 * b);
+        dst[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+        dst[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
+        qsc[(term * HP + h) * C::NSB + b] = (unsigned char)eq;
+        if (term == 0) {  // residual for the second term
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const f32x2 d0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(wd[j], sc, false);
+            const f32x2 d1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(wd[j], sc, true);
+            y[it][4 * j] -= d0[0];
+            y[it][4 * j + 1] -= d0[1];
+            y[it][4 * j + 2] -= d1[0];
+            y[it][4 * j + 3] -= d1[1];
           }
         }
-        if ((lane % LPB) == 0) qsc[(term * HP + h) * C::NSB + (EPL * lane) / 32] = (unsigned char)eq;
       }
     } else {
-      unsigned short* qbf = reinterpret_cast<unsigned short*>(smem);
+      uint4* dst = reinterpret_cast<uint4*>(smem + (h * C::QS + 32 * b) * 2);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) qbf[h * C::QS + EPL * lane + e] = (unsigned short)bf16_rne(y[e]);
+      for (int j = 0; j < 4; ++j) {
+        uint32_t pk[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          pk[k] = bf16_rne(y[it][8 * j + 2 * k]) | (bf16_rne(y[it][8 * j + 2 * k + 1]) << 16);
+        dst[j] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      }
     }
   }
 }
@@ -486,9 +517,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
   const int pos = a.positions[t];
 
   // ---------------- prologue
-  rope_table(pos, a, cs, sn);
-  __syncthreads();
-  q_prologue<D, EB>(smem, t, lane, w, a, cs, sn);
+  q_prologue<D, EB>(smem, t, pos, a, cs, sn);
   __syncthreads();
   // Q fragments (B operand of S^T = K Q^T) for the 32 heads of group qa.
   //   E4M3 pool: k-step ks covers dims [64ks, 64ks+64); lane half h holds dims
@@ -543,35 +572,42 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
   const int te = te_raw < ntile ? te_raw : ntile;
   const int32_t* idx_t = a.indices + (size_t)t * a.topk;
 
-  // id of entry tile*64 + lane, or -1 when it is not read (beyond the length, a
-  // sentinel, or outside [0, n_rows))
-  auto load_ids = [&](int tile) -> int {
+  // Index entry tile*64 + lane, fetched one or two tiles before it is used.  The load
+  // is unconditional (clamped into the row) and its value is only looked at after the
+  // tile loop's own vmcnt(0): a compiler-generated wait for it would also wait for the
+  // row DMA issued in the same tile.
+  auto fetch_id = [&](int tile) -> int {
     const int j = tile * T + lane;
-    int id = -1;
-    if (tile < te && j < lcap) id = idx_t[j];
-    return (id >= 0 && (long long)id < a.n_rows) ? id : -1;
+    return a.topk > 0 ? idx_t[j < a.topk ? j : a.topk - 1] : -1;
+  };
+  // the id if entry tile*64 + lane is read, else -1 (beyond the length, a sentinel, or
+  // outside [0, n_rows))
+  auto valid_id = [&](int tile, int raw) -> int {
+    const int j = tile * T + lane;
+    return (tile < te && j < lcap && raw >= 0 && (long long)raw < a.n_rows) ? raw : -1;
   };
 
   // Enqueue the LDS DMA of one tile's rows (and scales) into raw / sc.  Rows that are not
   // read keep older (finite) LDS contents: the QK masks them and P is zero for them.
   auto issue_tile = [&](int id_vec, unsigned char* raw, unsigned char* sc, int lane) {
     constexpr int GPW = (T / C::G) / 4;  // DMA groups per wave
+    constexpr int WPR = C::NSB / 4;      // 4-byte scale words per row
+    // all row ids first (one round of cross-lane reads), then the DMA instructions
+    int id[GPW + 1];
+#pragma unroll
+    for (int k = 0; k < GPW; ++k) id[k] = __shfl(id_vec, C::G * (GPW * w + k) + lane % C::G);
+    const int f = 64 * w + lane;
+    if constexpr (EB == 1) id[GPW] = __shfl(id_vec, (f / WPR) & 63);
 #pragma unroll
     for (int k = 0; k < GPW; ++k) {
       const int gi = GPW * w + k;
-      const int row = C::G * gi + lane % C::G;
       const int chunk = lane / C::G;
-      const int id = __shfl(id_vec, row);
       const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(raw + gi * C::GS));
-      if (id >= 0) dma16(a.pool + (size_t)id * C::RB + 16 * chunk, dst);
+      if (id[k] >= 0) dma16(a.pool + (size_t)id[k] * C::RB + 16 * chunk, dst);
     }
     if constexpr (EB == 1) {
-      constexpr int WPR = C::NSB / 4;  // 4-byte scale words per row
-      const int f = 64 * w + lane;
-      const int row = f / WPR;
-      const int id = __shfl(id_vec, row & 63);
       const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(sc + 256 * w));
-      if (f < 64 * WPR && id >= 0) dma4(a.scales + (size_t)id * C::NSB + 4 * (f % WPR), dst);
+      if (f < 64 * WPR && id[GPW] >= 0) dma4(a.scales + (size_t)id[GPW] * C::NSB + 4 * (f % WPR), dst);
     }
   };
 
@@ -585,10 +621,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = a.sm_scale * 1.4426950408889634f;
 
-  int id_cur = load_ids(tb);
-  int id_next = load_ids(tb + 1);
+  int raw_cur = fetch_id(tb);
+  int raw_next = fetch_id(tb + 1);
   __syncthreads();  // zeroing done before any DMA lands
-  if (tb < te) issue_tile(id_cur, smem + C::OFF_RAW0, smem + C::OFF_SC0, lane);
+  if (tb < te) issue_tile(valid_id(tb, raw_cur), smem + C::OFF_RAW0, smem + C::OFF_SC0, lane);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA has landed
 
   auto tile_step = [&](int tile, auto bufc) {
@@ -602,9 +638,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
     const int tid = (int)threadIdx.x + opaque_zero();
     const int lane = tid & 63, lrow = lane & 31, lhalf = lane >> 5;
     const uint32_t hsel = lhalf ? 0x07050301u : 0x06040200u;
+    const int id_cur = valid_id(tile, raw_cur);
     const unsigned long long mask = __ballot(id_cur >= 0);
-    if (tile + 1 < te) issue_tile(id_next, raw_n, sc_n, lane);
-    const int id_next2 = load_ids(tile + 2);
+    if (tile + 1 < te) issue_tile(valid_id(tile + 1, raw_next), raw_n, sc_n, lane);
+    const int raw_next2 = fetch_id(tile + 2);
 
     // ---- QK^T: S^T[32 rows of half qc][32 heads of group qa]
     f32x16 s;
@@ -778,8 +815,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
       }
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile's DMA from this wave landed
-    id_cur = id_next;
-    id_next = id_next2;
+    raw_cur = raw_next;
+    raw_next = raw_next2;
   };
 
   for (int tile = tb; tile < te; tile += 2) {

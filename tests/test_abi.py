@@ -112,6 +112,21 @@ def test_rejected_parameters(lib, kw, code):
     assert smla.sparse_mla_workspace_size(p) == 0 and smla.sparse_mla_num_splits(p) == 0
 
 
+@pytest.mark.parametrize("which,off", [(0, 8), (1, 4), (2, 2), (6, 4), (7, 1)])
+def test_misaligned_pointers(lib, which, off):
+    p = good(num_splits=1)
+    ptrs = [FAKE] * 9
+    ptrs[which] = FAKE + off
+    assert lib.sparse_mla_fwd(*ptrs, ctypes.byref(p)) == smla.SMLA_ERR_VALUE
+    assert "aligned" in smla.sparse_mla_last_error()
+
+
+def test_misaligned_out_f32(lib):
+    p = good(num_splits=1)
+    p.out_f32 = FAKE + 4
+    assert call(lib, p) == smla.SMLA_ERR_VALUE
+
+
 def test_workspace_required_when_split(lib):
     p = good(s_q=4)  # few tokens: automatic splitting needs a workspace
     ns = smla.sparse_mla_num_splits(p)
