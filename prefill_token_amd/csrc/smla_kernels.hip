@@ -52,7 +52,9 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int T = kTileRows;  // 64
-constexpr int NTHREADS = 256;
+constexpr int NTHREADS = 512;  // main kernel: 8 waves, two per SIMD
+constexpr int NWAVES = NTHREADS / 64;
+constexpr int CTHREADS = 256;  // combine kernel
 constexpr int HP = 64;        // heads per workgroup (padded)
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
@@ -85,7 +87,10 @@ struct Cfg {
   static constexpr int P_BYTES = HP * T * 2;  // [HP][T] bf16, 128 B per head
   static constexpr int KS = D / 16;           // k-steps of the bf16 QK contraction
   static constexpr int KS8 = D / 64;          // k-steps of the E4M3 QK contraction
-  static constexpr int DQ = D / 4;            // P.V output dims per wave
+  static constexpr int KSW = KS / 2;          // ... per wave (each wave takes half the dims)
+  static constexpr int KSW8 = KS8 / 2;
+  static constexpr int PVW = (D / 32) < NWAVES ? (D / 32) : NWAVES;  // waves in P.V
+  static constexpr int DQ = D / PVW;          // P.V output dims per wave
   static constexpr int NB = DQ / 32;          // 32-wide n-blocks per wave
   static constexpr int OFF_RAW0 = 0;
   static constexpr int OFF_RAW1 = OFF_RAW0 + RAW_BYTES;
@@ -94,7 +99,8 @@ struct Cfg {
   static constexpr int RAW_END = align16(OFF_SC1 + SC_BYTES);
   static constexpr int OFF_VT = RAW_END;
   static constexpr int OFF_P = OFF_VT + VT_BYTES;
-  static constexpr int LOOP_END = OFF_P + P_BYTES;
+  static constexpr int OFF_SX = OFF_P + P_BYTES;  // partial S of the 4 S blocks, f32
+  static constexpr int LOOP_END = OFF_SX + 4 * 32 * 32 * 4;
   // prologue q tile: E4M3 pool -> two E4M3 terms [2][HP][QS8] + UE8M0 [2][HP][NSB];
   // bf16 pool -> bf16 [HP][QS]
   static constexpr int QS8 = D + 16;
@@ -111,7 +117,8 @@ struct Cfg {
   static constexpr int OFF_COS = OFF_LSUM + 2 * HP * 4;
   static constexpr int OFF_SIN = OFF_COS + (D / 2) * 4;
   static constexpr int SMEM = OFF_SIN + (D / 2) * 4;
-  static_assert(G >= 1 && G <= 8 && (T % G) == 0, "row size unsupported");
+  static_assert(G >= 1 && G <= 8 && (T % G) == 0 && ((T / G) % NWAVES) == 0, "row size unsupported");
+  static_assert(KSW8 == 1 || KSW8 == 2 || KSW8 == 4, "k-steps per wave");
   static_assert(SMEM <= 160 * 1024, "LDS budget");
 };
 
@@ -119,6 +126,21 @@ struct Cfg {
 template <class C>
 __device__ __forceinline__ int raw_off(int r, int c) {
   return (r / C::G) * C::GS + 16 * (C::G * c + r % C::G);
+}
+
+// The UE8M0 scales of the k-steps a wave owns (dim half qd) for one row or head: byte j
+// holds the scale of block 2(ks) + h, ks = KSW8*qd + j, h = lane half (hsel picks the
+// bytes 2j + h of the 8 block scales of the half).
+template <class C>
+__device__ __forceinline__ uint32_t scale_word(const unsigned char* row_scales, int qd, uint32_t hsel) {
+  if constexpr (C::NSB == 16) {
+    const uint2 s2 = *reinterpret_cast<const uint2*>(row_scales + 8 * qd);
+    return __builtin_amdgcn_perm(s2.y, s2.x, hsel);
+  } else {
+    static_assert(C::NSB == 4, "scale layout");
+    const uint32_t s1 = *reinterpret_cast<const uint32_t*>(row_scales);
+    return __builtin_amdgcn_perm(s1, s1, hsel) >> (8 * qd);
+  }
 }
 
 struct KArgs {
@@ -231,7 +253,7 @@ __device__ __forceinline__ int opaque_zero() {
 template <int NST, bool FIRST>
 __device__ __forceinline__ void qk_block(f32x16& s, const i32x8* A, const i32x8* qh, const i32x8* ql, uint32_t ka,
                                          uint32_t sh, uint32_t sl) {
-  static_assert(NST == 2 || NST == 4, "k-steps per block");
+  static_assert(NST == 1 || NST == 2 || NST == 4, "k-steps per block");
   if constexpr (NST == 4 && FIRST) {
     asm("s_nop 4\n\t"
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %5, 0, %13, %14 op_sel_hi:[0,0,0]\n\t"
@@ -244,7 +266,7 @@ __device__ __forceinline__ void qk_block(f32x16& s, const i32x8* A, const i32x8*
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %4, %12, %0, %13, %15 op_sel:[1,1,0] op_sel_hi:[1,1,0]"
         : "=&v"(s)
         : "v"(A[0]), "v"(A[1]), "v"(A[2]), "v"(A[3]), "a"(qh[0]), "a"(qh[1]), "a"(qh[2]), "a"(qh[3]), "a"(ql[0]), "a"(ql[1]), "a"(ql[2]), "a"(ql[3]), "v"(ka), "v"(sh), "v"(sl));
-  } else if constexpr (NST == 4) {
+  } else if constexpr (NST == 4 && !FIRST) {
     asm("s_nop 4\n\t"
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %5, %0, %13, %14 op_sel_hi:[0,0,0]\n\t"
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %9, %0, %13, %15 op_sel_hi:[0,0,0]\n\t"
@@ -256,7 +278,7 @@ __device__ __forceinline__ void qk_block(f32x16& s, const i32x8* A, const i32x8*
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %4, %12, %0, %13, %15 op_sel:[1,1,0] op_sel_hi:[1,1,0]"
         : "+v"(s)
         : "v"(A[0]), "v"(A[1]), "v"(A[2]), "v"(A[3]), "a"(qh[0]), "a"(qh[1]), "a"(qh[2]), "a"(qh[3]), "a"(ql[0]), "a"(ql[1]), "a"(ql[2]), "a"(ql[3]), "v"(ka), "v"(sh), "v"(sl));
-  } else if constexpr (FIRST) {
+  } else if constexpr (NST == 2 && FIRST) {
     asm("s_nop 4\n\t"
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %3, 0, %7, %8 op_sel_hi:[0,0,0]\n\t"
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %5, %0, %7, %9 op_sel_hi:[0,0,0]\n\t"
@@ -264,7 +286,7 @@ __device__ __forceinline__ void qk_block(f32x16& s, const i32x8* A, const i32x8*
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %2, %6, %0, %7, %9 op_sel:[1,1,0] op_sel_hi:[0,0,0]"
         : "=&v"(s)
         : "v"(A[0]), "v"(A[1]), "a"(qh[0]), "a"(qh[1]), "a"(ql[0]), "a"(ql[1]), "v"(ka), "v"(sh), "v"(sl));
-  } else {
+  } else if constexpr (NST == 2 && !FIRST) {
     asm("s_nop 4\n\t"
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %3, %0, %7, %8 op_sel_hi:[0,0,0]\n\t"
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %5, %0, %7, %9 op_sel_hi:[0,0,0]\n\t"
@@ -272,6 +294,18 @@ __device__ __forceinline__ void qk_block(f32x16& s, const i32x8* A, const i32x8*
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %2, %6, %0, %7, %9 op_sel:[1,1,0] op_sel_hi:[0,0,0]"
         : "+v"(s)
         : "v"(A[0]), "v"(A[1]), "a"(qh[0]), "a"(qh[1]), "a"(ql[0]), "a"(ql[1]), "v"(ka), "v"(sh), "v"(sl));
+  } else if constexpr (NST == 1 && FIRST) {
+    asm("s_nop 4\n\t"
+        "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %4, %5 op_sel_hi:[0,0,0]\n\t"
+        "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %3, %0, %4, %6 op_sel_hi:[0,0,0]"
+        : "=&v"(s)
+        : "v"(A[0]), "a"(qh[0]), "a"(ql[0]), "v"(ka), "v"(sh), "v"(sl));
+  } else if constexpr (NST == 1 && !FIRST) {
+    asm("s_nop 4\n\t"
+        "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %4, %5 op_sel_hi:[0,0,0]\n\t"
+        "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %3, %0, %4, %6 op_sel_hi:[0,0,0]"
+        : "+v"(s)
+        : "v"(A[0]), "a"(qh[0]), "a"(ql[0]), "v"(ka), "v"(sh), "v"(sl));
   }
 }
 // After the last QK step: 32 wait states before anything reads s (covers the
@@ -284,12 +318,12 @@ __device__ __forceinline__ void to_agpr(i32x8& x) { asm volatile("" : "+a"(x)); 
 // stride OSTR), writing global heads head0 + hl of token tok.  One thread per (head,
 // 32-dim block), heads fastest across lanes: the block amax is lane-local and the
 // rotary partner dims (x +- rope_dim/2, same head) are read from the tile itself.
-template <int D>
+template <int D, int NT>
 __device__ void epilogue(const float* o_lds, int OSTR, int nheads, int head0, int tok, const KArgs& a,
                          const float* cs, const float* sn) {
   constexpr int NBK = D / 32;
   const int R = a.rope_dim, o0 = D - R, half = R / 2;
-  for (int u = threadIdx.x; u < nheads * NBK; u += NTHREADS) {
+  for (int u = threadIdx.x; u < nheads * NBK; u += NT) {
     const int hl = u % nheads, b = u / nheads;
     const float* row = o_lds + hl * OSTR;
     float v[32];
@@ -362,8 +396,10 @@ template <int D, int EB>
 __device__ void q_prologue(unsigned char* smem, int t, int pos, const KArgs& a, float* cs, float* sn) {
   using C = Cfg<D, EB>;
   constexpr int NBK = D / 32;               // lanes per head
-  constexpr int NIT = HP * NBK / NTHREADS;  // units per thread
-  static_assert(NIT * NTHREADS == HP * NBK && NBK <= 16, "prologue mapping");
+  constexpr int NU = HP * NBK;                           // units
+  constexpr int NIT = (NU + NTHREADS - 1) / NTHREADS;    // units per thread
+  static_assert((NU % NTHREADS == 0 || NU < NTHREADS) && NU % 64 == 0 && NBK <= 16, "prologue mapping");
+  const bool act = (int)threadIdx.x < NU;  // whole waves idle when NU < NTHREADS
   const int R = a.rope_dim, o0 = D - R, half = R / 2;
   const int b = threadIdx.x % NBK;  // the same block in every unit of this thread
   uint4 qraw[NIT][4];
@@ -372,7 +408,7 @@ __device__ void q_prologue(unsigned char* smem, int t, int pos, const KArgs& a, 
     const int h = (threadIdx.x + NTHREADS * it) / NBK;
     const uint4* src = reinterpret_cast<const uint4*>(a.q + ((size_t)t * a.h_q + h) * D + 32 * b);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) qraw[it][j] = h < a.h_q ? src[j] : make_uint4(0u, 0u, 0u, 0u);
+    for (int j = 0; j < 4; ++j) qraw[it][j] = (act && h < a.h_q) ? src[j] : make_uint4(0u, 0u, 0u, 0u);
   }
   float wv[32];
 #pragma unroll
@@ -383,7 +419,7 @@ __device__ void q_prologue(unsigned char* smem, int t, int pos, const KArgs& a, 
   rope_table(pos, a, cs, sn);  // overlaps the loads above
 
   float* ystage = reinterpret_cast<float*>(smem);  // [HP][R] f32, rotary dims only
-  const bool rotb = 32 * b + 32 > o0;
+  const bool rotb = act && 32 * b + 32 > o0;
   float y[NIT][32];
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
@@ -449,6 +485,7 @@ __device__ void q_prologue(unsigned char* smem, int t, int pos, const KArgs& a, 
   __syncthreads();  // staging reads done: the q tile below overwrites it
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
+    if (!act) break;
     const int h = (threadIdx.x + NTHREADS * it) / NBK;
     if constexpr (EB == 1) {
       // two E4M3 terms, each with its own UE8M0 scale per 32 dims
@@ -511,7 +548,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int lrow = lane & 31, lhalf = lane >> 5;
-  const int qa = w >> 1, qc = w & 1;  // QK roles: head group, row half
+  // QK roles: head group qa, row half qc, dim half qd.  Waves w and w + 4 share a SIMD
+  // and hold the two dim halves of the same S block.
+  const int qa = w & 1, qc = (w >> 1) & 1, qd = w >> 2;
   const int ns = a.num_splits;
   const int t = blockIdx.x / ns, split = blockIdx.x % ns;
   const int pos = a.positions[t];
@@ -519,42 +558,36 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
   // ---------------- prologue
   q_prologue<D, EB>(smem, t, pos, a, cs, sn);
   __syncthreads();
-  // Q fragments (B operand of S^T = K Q^T) for the 32 heads of group qa.
+  // Q fragments (B operand of S^T = K Q^T) of the 32 heads of group qa over dim half qd.
   //   E4M3 pool: k-step ks covers dims [64ks, 64ks+64); lane half h holds dims
   //   64ks + 16h + [0,16) and 64ks + 32 + 16h + [0,16) of its head (the 32x32x64 f8
-  //   operand layout); the UE8M0 scale of block 2ks + h sits in byte ks % 4 of
-  //   qs8[term][ks / 4].
+  //   operand layout); the UE8M0 scale of block 2ks + h sits in byte ks - KSW8*qd of
+  //   qs8[term].
   //   bf16 pool: step ks, lane half h holds dims 16ks + 8h + [0, 8).
-  i32x8 qf8[2][(EB == 1) ? C::KS8 : 1];
-  uint32_t qs8[2][(EB == 1) ? (C::KS8 + 3) / 4 : 1];
-  bf16x8 qbf[(EB == 2) ? C::KS : 1];
+  i32x8 qf8[2][(EB == 1) ? C::KSW8 : 1];
+  uint32_t qs8[2];
+  bf16x8 qbf[(EB == 2) ? C::KSW : 1];
   const uint32_t hsel = lhalf ? 0x07050301u : 0x06040200u;  // bytes 2j + h of 8
   if constexpr (EB == 1) {
 #pragma unroll
     for (int term = 0; term < 2; ++term) {
       const unsigned char* qrow = smem + (term * HP + 32 * qa + lrow) * C::QS8 + 16 * lhalf;
 #pragma unroll
-      for (int ks = 0; ks < C::KS8; ++ks) {
+      for (int j = 0; j < C::KSW8; ++j) {
+        const int ks = C::KSW8 * qd + j;
         const uint4 lo = *reinterpret_cast<const uint4*>(qrow + 64 * ks);
         const uint4 hi = *reinterpret_cast<const uint4*>(qrow + 64 * ks + 32);
-        qf8[term][ks] = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z,
-                                (int)hi.w};
-        to_agpr(qf8[term][ks]);
+        qf8[term][j] = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z,
+                               (int)hi.w};
+        to_agpr(qf8[term][j]);
       }
-      const unsigned char* srow = smem + C::OFF_QSC + (term * HP + 32 * qa + lrow) * C::NSB;
-      if constexpr (C::NSB >= 16) {
-        const uint4 s4 = *reinterpret_cast<const uint4*>(srow);
-        qs8[term][0] = __builtin_amdgcn_perm(s4.y, s4.x, hsel);
-        qs8[term][1] = __builtin_amdgcn_perm(s4.w, s4.z, hsel);
-      } else {
-        const uint32_t s1 = *reinterpret_cast<const uint32_t*>(srow);
-        qs8[term][0] = __builtin_amdgcn_perm(s1, s1, hsel);
-      }
+      qs8[term] = scale_word<C>(smem + C::OFF_QSC + (term * HP + 32 * qa + lrow) * C::NSB, qd, hsel);
     }
   } else {
     const unsigned short* qrow = reinterpret_cast<const unsigned short*>(smem) + (32 * qa + lrow) * C::QS;
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) qbf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * lhalf);
+    for (int j = 0; j < C::KSW; ++j)
+      qbf[j] = *reinterpret_cast<const bf16x8*>(qrow + 16 * (C::KSW * qd + j) + 8 * lhalf);
   }
   __syncthreads();  // the q tile region is reused by the raw tiles below
   {
@@ -590,8 +623,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
   // Enqueue the LDS DMA of one tile's rows (and scales) into raw / sc.  Rows that are not
   // read keep older (finite) LDS contents: the QK masks them and P is zero for them.
   auto issue_tile = [&](int id_vec, unsigned char* raw, unsigned char* sc, int lane) {
-    constexpr int GPW = (T / C::G) / 4;  // DMA groups per wave
-    constexpr int WPR = C::NSB / 4;      // 4-byte scale words per row
+    constexpr int GPW = (T / C::G) / NWAVES;  // DMA groups per wave
+    constexpr int WPR = C::NSB / 4;           // 4-byte scale words per row
     // all row ids first (one round of cross-lane reads), then the DMA instructions
     int id[GPW + 1];
 #pragma unroll
@@ -606,8 +639,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
       if (id[k] >= 0) dma16(a.pool + (size_t)id[k] * C::RB + 16 * chunk, dst);
     }
     if constexpr (EB == 1) {
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(sc + 256 * w));
-      if (f < 64 * WPR && id[GPW] >= 0) dma4(a.scales + (size_t)id[GPW] * C::NSB + 4 * (f % WPR), dst);
+      if (w < WPR) {
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(sc + 256 * w));
+        if (id[GPW] >= 0) dma4(a.scales + (size_t)id[GPW] * C::NSB + 4 * (f % WPR), dst);
+      }
     }
   };
 
@@ -633,7 +668,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
     unsigned char* sc_l = smem + (BUF == 0 ? C::OFF_SC0 : C::OFF_SC1);
     unsigned char* raw_n = smem + (BUF == 0 ? C::OFF_RAW1 : C::OFF_RAW0);
     unsigned char* sc_n = smem + (BUF == 0 ? C::OFF_SC1 : C::OFF_SC0);
-    __syncthreads();  // B1: this tile's rows visible; Vt / P free
+    __syncthreads();  // B1: this tile's rows visible; Vt / P / partial S free
     // lane-dependent values recomputed per tile (keeps them out of the live set)
     const int tid = (int)threadIdx.x + opaque_zero();
     const int lane = tid & 63, lrow = lane & 31, lhalf = lane >> 5;
@@ -643,103 +678,122 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
     if (tile + 1 < te) issue_tile(valid_id(tile + 1, raw_next), raw_n, sc_n, lane);
     const int raw_next2 = fetch_id(tile + 2);
 
-    // ---- QK^T: S^T[32 rows of half qc][32 heads of group qa]
+    // ---- QK^T: partial S^T[32 rows of half qc][32 heads of group qa] over dim half qd
     f32x16 s;
-    {
+    auto qk = [&]() {
       const int r = 32 * qc + lrow;
       if constexpr (EB == 1) {
-        uint32_t ksc[(C::KS8 + 3) / 4];  // UE8M0 of block 2ks + h in byte ks % 4
-        if constexpr (C::NSB >= 16) {
-          const uint4 s4 = *reinterpret_cast<const uint4*>(sc_l + r * C::NSB);
-          ksc[0] = __builtin_amdgcn_perm(s4.y, s4.x, hsel);
-          ksc[1] = __builtin_amdgcn_perm(s4.w, s4.z, hsel);
-        } else {
-          const uint32_t s1 = *reinterpret_cast<const uint32_t*>(sc_l + r * C::NSB);
-          ksc[0] = __builtin_amdgcn_perm(s1, s1, hsel);
-        }
-        constexpr int NST = C::KS8 < 4 ? C::KS8 : 4;  // k-steps per scale word
-        static_for<C::KS8 / NST>([&](auto bc) {
-          constexpr int b = decltype(bc)::value;
-          i32x8 A[NST];
+        const uint32_t ksc = scale_word<C>(sc_l + r * C::NSB, qd, hsel);
+        i32x8 A[C::KSW8];
 #pragma unroll
-          for (int j = 0; j < NST; ++j) {
-            const int ks = NST * b + j;
-            const uint4 lo = *reinterpret_cast<const uint4*>(raw_l + raw_off<C>(r, 4 * ks + lhalf));
-            const uint4 hi = *reinterpret_cast<const uint4*>(raw_l + raw_off<C>(r, 4 * ks + 2 + lhalf));
-            A[j] = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-          }
-          qk_block<NST, b == 0>(s, A, &qf8[0][NST * b], &qf8[1][NST * b], ksc[b], qs8[0][b], qs8[1][b]);
-        });
+        for (int j = 0; j < C::KSW8; ++j) {
+          const int ks = C::KSW8 * qd + j;
+          const uint4 lo = *reinterpret_cast<const uint4*>(raw_l + raw_off<C>(r, 4 * ks + lhalf));
+          const uint4 hi = *reinterpret_cast<const uint4*>(raw_l + raw_off<C>(r, 4 * ks + 2 + lhalf));
+          A[j] = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+        qk_block<C::KSW8, true>(s, A, qf8[0], qf8[1], ksc, qs8[0], qs8[1]);
         qk_drain(s);
       } else {
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-          const bf16x8 A = *reinterpret_cast<const bf16x8*>(raw_l + raw_off<C>(r, 2 * ks + lhalf));
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qbf[ks], s, 0, 0, 0);
+        for (int j = 0; j < C::KSW; ++j) {
+          const bf16x8 A =
+              *reinterpret_cast<const bf16x8*>(raw_l + raw_off<C>(r, 2 * (C::KSW * qd + j) + lhalf));
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qbf[j], s, 0, 0, 0);
         }
       }
-    }
+    };
 
     // ---- V tile: raw rows -> Vt[dim][slot] bf16.  A block is the 4 rows 8q + p + 2k
     // (k = 0..3, slots 8q + 4p + k) of one 16-byte chunk c.
-    constexpr int NBLK = (T / 4) * C::NCH;
-    for (int bb = tid; bb < NBLK; bb += NTHREADS) {
-      int q, p, c;
-      if constexpr (C::NCH == 32) {
-        // an 8-lane group covers 4 consecutive chunks x both parities, so each read step
-        // touches 8 distinct bank slots and each write step 16 distinct 8-byte slots
-        const int u = lane & 7, g8 = lane >> 3, j = bb / NTHREADS;
-        c = 4 * g8 + (u >> 1);
-        p = u & 1;
-        q = w + 4 * j;
-      } else {
-        p = bb & 1;
-        c = (bb >> 1) % C::NCH;
-        q = (bb >> 1) / C::NCH;
-      }
-      uint32_t pk[4][C::CE / 2];  // [k][element pair]
+    auto vtrans = [&]() {
+      constexpr int NBLK = (T / 4) * C::NCH;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int row = 8 * q + p + 2 * k;
-        const uint4 rw = *reinterpret_cast<const uint4*>(raw_l + raw_off<C>(row, c));
-        if constexpr (EB == 1) {
-          const float sc = ue8m0_f32(sc_l[row * C::NSB + (c >> 1)]);
-          pk[k][0] = cvt_lo(rw.x, sc); pk[k][1] = cvt_hi(rw.x, sc);
-          pk[k][2] = cvt_lo(rw.y, sc); pk[k][3] = cvt_hi(rw.y, sc);
-          pk[k][4] = cvt_lo(rw.z, sc); pk[k][5] = cvt_hi(rw.z, sc);
-          pk[k][6] = cvt_lo(rw.w, sc); pk[k][7] = cvt_hi(rw.w, sc);
+      for (int bb0 = 0; bb0 < NBLK; bb0 += NTHREADS) {
+        const int bb = bb0 + tid;
+        if (NBLK % NTHREADS != 0 && bb >= NBLK) break;
+        int q, p, c;
+        if constexpr (C::NCH == 32) {
+          // an 8-lane group covers 4 consecutive chunks x both parities, so each read
+          // step touches 8 distinct bank slots and each write step 16 distinct 8-byte slots
+          const int u = lane & 7, g8 = lane >> 3;
+          c = 4 * g8 + (u >> 1);
+          p = u & 1;
+          q = w + NWAVES * (bb0 / NTHREADS);
         } else {
-          pk[k][0] = rw.x; pk[k][1] = rw.y; pk[k][2] = rw.z; pk[k][3] = rw.w;
+          p = bb & 1;
+          c = (bb >> 1) % C::NCH;
+          q = (bb >> 1) / C::NCH;
+        }
+        uint32_t pk[4][C::CE / 2];  // [k][element pair]
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int row = 8 * q + p + 2 * k;
+          const uint4 rw = *reinterpret_cast<const uint4*>(raw_l + raw_off<C>(row, c));
+          if constexpr (EB == 1) {
+            const float sc = ue8m0_f32(sc_l[row * C::NSB + (c >> 1)]);
+            pk[k][0] = cvt_lo(rw.x, sc); pk[k][1] = cvt_hi(rw.x, sc);
+            pk[k][2] = cvt_lo(rw.y, sc); pk[k][3] = cvt_hi(rw.y, sc);
+            pk[k][4] = cvt_lo(rw.z, sc); pk[k][5] = cvt_hi(rw.z, sc);
+            pk[k][6] = cvt_lo(rw.w, sc); pk[k][7] = cvt_hi(rw.w, sc);
+          } else {
+            pk[k][0] = rw.x; pk[k][1] = rw.y; pk[k][2] = rw.z; pk[k][3] = rw.w;
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < C::CE; ++e) {
+          const int k = e >> 1;
+          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+          const uint2 o = make_uint2(__builtin_amdgcn_perm(pk[1][k], pk[0][k], sel),
+                                     __builtin_amdgcn_perm(pk[3][k], pk[2][k], sel));
+          const int n = C::CE * c + e;
+          *reinterpret_cast<uint2*>(vt_l + n * 128 + 16 * (q ^ swz(n)) + 8 * p) = o;
         }
       }
-#pragma unroll
-      for (int e = 0; e < C::CE; ++e) {
-        const int k = e >> 1;
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        const uint2 o = make_uint2(__builtin_amdgcn_perm(pk[1][k], pk[0][k], sel),
-                                   __builtin_amdgcn_perm(pk[3][k], pk[2][k], sel));
-        const int n = C::CE * c + e;
-        *reinterpret_cast<uint2*>(vt_l + n * 128 + 16 * (q ^ swz(n)) + 8 * p) = o;
-      }
+    };
+
+    // the two waves of a SIMD run the halves in opposite order: one issues MFMAs while
+    // the other converts
+    if (qd == 0) {
+      qk();
+      vtrans();
+    } else {
+      vtrans();
+      qk();
     }
 
-    // ---- softmax (part 1): tile max per head
-    float mloc = -INFINITY;
+    // ---- partial S exchange: the dim-half-1 wave hands its partial to its partner
+    float* sx = reinterpret_cast<float*>(smem + C::OFF_SX) + (w & 3) * 1024;
+    if (qd == 1) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = 32 * qc + 8 * (i >> 2) + 4 * lhalf + (i & 3);
-      const bool v = (mask >> row) & 1ull;
-      s[i] = v ? s[i] * sl2 : -INFINITY;
-      mloc = fmaxf(mloc, s[i]);
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<float4*>(sx + 4 * (64 * j + lane)) = make_float4(s[4 * j], s[4 * j + 1], s[4 * j + 2], s[4 * j + 3]);
     }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    if (lhalf == 0) maxx[qc * HP + 32 * qa + lrow] = mloc;
+    __syncthreads();  // B2a: partial S visible
+    float mloc = -INFINITY;
+    if (qd == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 v = *reinterpret_cast<const float4*>(sx + 4 * (64 * j + lane));
+        s[4 * j] += v.x; s[4 * j + 1] += v.y; s[4 * j + 2] += v.z; s[4 * j + 3] += v.w;
+      }
+      // ---- softmax (part 1): tile max per head
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 32 * qc + 8 * (i >> 2) + 4 * lhalf + (i & 3);
+        const bool v = (mask >> row) & 1ull;
+        s[i] = v ? s[i] * sl2 : -INFINITY;
+        mloc = fmaxf(mloc, s[i]);
+      }
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+      if (lhalf == 0) maxx[qc * HP + 32 * qa + lrow] = mloc;
+    }
     __syncthreads();  // B2: maxima exchanged
 
     // ---- softmax (part 2): running max (lazy), P in bf16 by slot, alpha
-    {
+    if (qd == 0) {
       const float mt = fmaxf(mloc, maxx[(1 - qc) * HP + 32 * qa + lrow]);
       float mnew = m_run;
       if (mt > -INFINITY && (m_run == -INFINITY || mt > m_run + 8.0f)) mnew = mt;
@@ -770,7 +824,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
     __syncthreads();  // B3: P and alpha visible
 
     // ---- P.V: O[64 heads][dims of wave w]
-    {
+    if (w < C::PVW) {
       bool need = false;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
@@ -825,7 +879,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
   }
 
   // ---------------- finish: l per head, then normalize + epilogue, or write partials
-  {
+  if (qd == 0) {
     const float lw = l_run + __shfl_xor(l_run, 32);
     if (lhalf == 0) lsum[qc * HP + 32 * qa + lrow] = lw;
     if (qc == 0 && lhalf == 0) maxx[32 * qa + lrow] = m_run;
@@ -834,18 +888,20 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
   const int d0 = C::DQ * w;
   if (ns == 1) {
     float* o_l = reinterpret_cast<float*>(smem);
+    if (w < C::PVW) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int h = 32 * mb + 8 * (i >> 2) + 4 * lhalf + (i & 3);
-        const float lt = lsum[h] + lsum[HP + h];
-        const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+        for (int i = 0; i < 16; ++i) {
+          const int h = 32 * mb + 8 * (i >> 2) + 4 * lhalf + (i & 3);
+          const float lt = lsum[h] + lsum[HP + h];
+          const float inv = lt > 0.f ? 1.0f / lt : 0.f;
 #pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) o_l[h * C::OS + d0 + 32 * nb + lrow] = acc[mb][nb][i] * inv;
-      }
+          for (int nb = 0; nb < C::NB; ++nb) o_l[h * C::OS + d0 + 32 * nb + lrow] = acc[mb][nb][i] * inv;
+        }
+    }
     __syncthreads();
-    epilogue<D>(o_l, C::OS, a.h_q, 0, t, a, cs, sn);
+    epilogue<D, NTHREADS>(o_l, C::OS, a.h_q, 0, t, a, cs, sn);
   } else {
     float* part = a.ws + ((size_t)t * ns + split) * partial_floats_d(a.h_q, D);
     float* pm = part + (size_t)a.h_q * D;
@@ -854,7 +910,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
       pm[tid] = maxx[tid];
       pl[tid] = lsum[tid] + lsum[HP + tid];
     }
-    if (te > tb) {
+    if (te > tb && w < C::PVW) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -872,7 +928,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
 // Combine the splits of one token for 8 heads (in split order), then the epilogue.
 // All split statistics and accumulators are fetched with independent loads.
 template <int D>
-__global__ __launch_bounds__(NTHREADS) void smla_combine(KArgs a) {
+__global__ __launch_bounds__(CTHREADS) void smla_combine(KArgs a) {
   constexpr int HC = 8, OSTR = D + 4, MAXS = 64;
   __shared__ __attribute__((aligned(16))) float o_l[HC * OSTR];
   __shared__ float cs[D / 2], sn[D / 2];
@@ -884,7 +940,7 @@ __global__ __launch_bounds__(NTHREADS) void smla_combine(KArgs a) {
   const size_t pf = partial_floats_d(a.h_q, D);
   const float* base = a.ws + (size_t)t * ns * pf;
   rope_table(a.positions[t], a, cs, sn);
-  for (int f = threadIdx.x; f < HC * MAXS; f += NTHREADS) {
+  for (int f = threadIdx.x; f < HC * MAXS; f += CTHREADS) {
     const int hl = f / MAXS, s = f % MAXS;
     if (hl < nh && s < ns) {
       const float* st = base + (size_t)s * pf + (size_t)a.h_q * D;
@@ -908,7 +964,7 @@ __global__ __launch_bounds__(NTHREADS) void smla_combine(KArgs a) {
   }
   __syncthreads();
   constexpr int Q4 = D / 4;
-  for (int f = threadIdx.x; f < nh * Q4; f += NTHREADS) {
+  for (int f = threadIdx.x; f < nh * Q4; f += CTHREADS) {
     const int hl = f / Q4, x4 = f % Q4;
     const float* src = base + (size_t)(h0 + hl) * D + 4 * x4;
     float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -935,7 +991,7 @@ __global__ __launch_bounds__(NTHREADS) void smla_combine(KArgs a) {
         make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv);
   }
   __syncthreads();
-  epilogue<D>(o_l, OSTR, nh, h0, t, a, cs, sn);
+  epilogue<D, CTHREADS>(o_l, OSTR, nh, h0, t, a, cs, sn);
 }
 
 template <int D, int EB>
@@ -944,7 +1000,7 @@ hipError_t launch_t(const LaunchArgs& x, const KArgs& k) {
   hipLaunchKernelGGL((smla_main<D, EB>), dim3((unsigned)(x.s_q * ns)), dim3(NTHREADS), 0, x.stream, k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ns == 1) return e;
-  hipLaunchKernelGGL((smla_combine<D>), dim3((unsigned)x.s_q, (unsigned)((x.h_q + 7) / 8)), dim3(NTHREADS), 0,
+  hipLaunchKernelGGL((smla_combine<D>), dim3((unsigned)x.s_q, (unsigned)((x.h_q + 7) / 8)), dim3(CTHREADS), 0,
                      x.stream, k);
   return hipGetLastError();
 }
