@@ -16,6 +16,13 @@ Prints one JSON line:
                MFMA fractions
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Counter helpers (for the HBM traffic figure, see profiles/):
+  python bench.py --copy-probe MIB    plain device-to-device copies of MIB MiB (the
+                                      reference kernel for FETCH_SIZE / WRITE_SIZE)
+  python bench.py --traffic-from DIR  turn the four rocprofv3 --pmc CSVs under DIR
+                                      (fetch/, write/, copy_fetch/, copy_write/) into
+                                      profiles/traffic_decode_sq1.json
 """
 from __future__ import annotations
 
@@ -225,6 +232,67 @@ def load_traffic(digest):
     return None
 
 
+COPY_PROBE_REPS = 8
+
+
+def copy_probe(mib):
+    """A plain device copy of known size, for scaling the memory counters."""
+    import torch
+
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(COPY_PROBE_REPS):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "reps": COPY_PROBE_REPS}), flush=True)
+
+
+def _counter_rows(folder, counter):
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {folder}")
+    rows = []
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def traffic_from(folder, copy_mib):
+    """HBM bytes per sparse_mla_fwd call at decode s_q = 1 from rocprofv3 --pmc runs:
+    the median FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of each of its kernels, each
+    scaled by (known bytes / counter reading) of a plain copy of copy_mib MiB."""
+    out = {"source_digest": source_digest(), "workload": "decode_sq1", "copy_probe_mib": copy_mib, "kernels": {}}
+    total = 0.0
+    for counter, sub, csub in (("FETCH_SIZE", "fetch", "copy_fetch"), ("WRITE_SIZE", "write", "copy_write")):
+        crow = [v for k, v in _counter_rows(os.path.join(folder, csub), counter) if "copy" in k.lower()]
+        if not crow:
+            raise SystemExit(f"no copy kernel rows for {counter}")
+        factor = (copy_mib * 1024.0) / float(np.median(crow))
+        out[f"{counter}_copy_factor"] = factor
+        rows = _counter_rows(os.path.join(folder, sub), counter)
+        for kname in ("smla_main", "smla_combine"):
+            vals = [v for k, v in rows if kname in k]
+            if not vals:
+                continue
+            kib = float(np.median(vals))
+            out["kernels"].setdefault(kname, {})[counter + "_KiB_median"] = kib
+            out["kernels"][kname]["dispatches"] = len(vals)
+            total += kib * factor * 1024.0
+    out["hbm_bytes_per_call"] = total
+    path = os.path.join(ROOT, "profiles", "traffic_decode_sq1.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -234,7 +302,15 @@ def main():
     ap.add_argument("--extra", default=",".join(EXTRA), help="comma-separated workloads after the timed region")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB")
+    ap.add_argument("--traffic-from", default="", metavar="DIR")
     args = ap.parse_args()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
+    if args.traffic_from:
+        traffic_from(args.traffic_from, 256)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this build measures one GPU only: the step runs on a single MI355X and "
@@ -276,7 +352,9 @@ def main():
         "vs_baseline": value / (1e6 / PAGES_US_SQ1),
         "vs_baseline_note": "value / (1 / 22.7 us): the pages' fused kernel at s_q=1 on GB200 TP4 (context, "
                             "another machine)",
-        "dtype": "bf16", "data": "synthetic",
+        "dtype": "e4m3+bf16", "data": "synthetic",
+        "dtype_note": "QK^T on E4M3 MFMAs (q split into two E4M3 terms with UE8M0 scales), P.V on bf16 "
+                      "MFMAs, f32 accumulation and softmax",
         "config": {"workload": head["description"], "name": head["workload"], "s_q": head["s_q"],
                    "num_splits": head["num_splits"], "graph": True},
         "roofline": roofline, "cpu_baseline": cpu, "configs": configs,
