@@ -1,8 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark of the fused sparse-MLA step (sparse_mla_fwd) on one MI355X.
 
-A step is one sparse_mla_fwd call over one batch of seeded synthetic inputs, replayed
-from a HIP graph (inputs resident in HBM).  The headline workload is the s_q = 1 decode
+A step is one sparse_mla_fwd call over one batch of seeded synthetic inputs (inputs
+resident in HBM).  The timed steps are replays of a HIP graph holding 10 back-to-back
+calls, so a step's time is the GPU's and not the host's graph-launch latency (which is
+reported separately as us_per_call_single_graph_median).  The headline workload is the s_q = 1 decode
 (h_q = 64, d = 512 with 64 rotary dims, topk 128 SWA + 512 compressed, E4M3 + UE8M0
 pools); the s_q = 64 / 256 / 1024 decodes and the 184 / 2123-token prefills are measured
 after the timed region and reported under "configs".
@@ -47,6 +49,7 @@ MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 / fp16 MFMA
 PAGES_US_SQ1 = 22.7            # pages' fused kernel at s_q = 1 (GB200, TP4, CUDA graph): context only
 EXTRA = ["decode_sq64", "decode_sq1024", "prefill_sq2123", "decode_sq256", "prefill_sq184"]
 FLUSH_BYTES = 512 << 20        # larger than the 256 MB MALL + 8 x 4 MB L2
+CALLS_PER_GRAPH = 10           # timed replays hold this many back-to-back calls
 
 
 def upload(inp, torch, device):
@@ -102,25 +105,47 @@ def measure(name, steps, warmup, torch, device, timed_steps=None):
         call()
     torch.cuda.synchronize()
     eager_ref = (out_fp8.clone(), out_sc.clone())
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
+    graph1 = torch.cuda.CUDAGraph()  # one call: launch-inclusive and cold timings
+    with torch.cuda.graph(graph1):
         call()
-    graph.replay()
-    torch.cuda.synchronize()
-    assert torch.equal(out_fp8, eager_ref[0]) and torch.equal(out_sc, eager_ref[1]), "graph replay differs"
+    graphg = torch.cuda.CUDAGraph()  # CALLS_PER_GRAPH back-to-back calls: the timed steps
+    with torch.cuda.graph(graphg):
+        for _ in range(CALLS_PER_GRAPH):
+            call()
+    for g in (graph1, graphg):
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_fp8, eager_ref[0]) and torch.equal(out_sc, eager_ref[1]), "graph replay differs"
 
-    n = timed_steps if timed_steps is not None else steps
+    n = max(1, timed_steps if timed_steps is not None else steps)
+    reps, rem = divmod(n, CALLS_PER_GRAPH)
+    plan = [(graphg, CALLS_PER_GRAPH)] * reps
+    if rem:  # exactly n calls: the remainder runs as one shorter graph
+        graphr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graphr):
+            for _ in range(rem):
+                call()
+        plan.append((graphr, rem))
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in plan]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(n):
-        ev[i][0].record(stream)
-        graph.replay()
-        ev[i][1].record(stream)
+    for (g, _), (a, b) in zip(plan, ev):
+        a.record(stream)
+        g.replay()
+        b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    us = np.concatenate([np.full(k, a.elapsed_time(b) * 1e3 / k) for (_, k), (a, b) in zip(plan, ev)])
+
+    # one call per replay: includes the graph launch latency of a lone call
+    ev1 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+    for a, b in ev1:
+        a.record(stream)
+        graph1.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    us1 = np.array([a.elapsed_time(b) * 1e3 for a, b in ev1])
 
     # cold: flush the caches before each replay (outside the event pair)
     flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=device)
@@ -129,7 +154,7 @@ def measure(name, steps, warmup, torch, device, timed_steps=None):
         flush.zero_()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        graph.replay()
+        graph1.replay()
         b.record(stream)
         b.synchronize()
         cold.append(a.elapsed_time(b) * 1e3)
@@ -145,6 +170,7 @@ def measure(name, steps, warmup, torch, device, timed_steps=None):
         us_per_call_mean=mean_us, us_per_call_median=float(np.median(us)),
         us_per_call_p10=float(np.percentile(us, 10)), us_per_call_p90=float(np.percentile(us, 90)),
         us_per_call_cold_median=float(np.median(cold)),
+        us_per_call_single_graph_median=float(np.median(us1)), calls_per_graph=CALLS_PER_GRAPH,
         tokens_per_s=s_q / (mean_us * 1e-6), tokens_per_s_cold=s_q / (float(np.median(cold)) * 1e-6),
         hbm_compulsory_GBs=wm["compulsory_bytes"] / (mean_us * 1e-6) / 1e9,
         hbm_compulsory_frac=wm["compulsory_bytes"] / (mean_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
@@ -296,7 +322,7 @@ def traffic_from(folder, copy_mib):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_sq1")
     ap.add_argument("--extra", default=",".join(EXTRA), help="comma-separated workloads after the timed region")

@@ -24,9 +24,8 @@ HIPCC_FLAGS = [
     "-shared",
     # no packed fp32 VALU ops in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA results in VGPRs: the P.V accumulators are then rescaled in place by plain
-    # VALU multiplies (no AGPR round trips), and the AGPRs hold the q fragments the QK
-    # asm pins there
+    # MFMA results in VGPRs: with two waves per SIMD every register a wave has is a
+    # VGPR, and the P.V accumulators are rescaled in place by plain VALU multiplies
     "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
 ]

@@ -7,31 +7,35 @@
 // beyond topk_length are never read and -1 marks an empty slot [same page, Purpose,
 // bug-fix bullet].
 //
-// Work decomposition (one 256-thread workgroup = 4 wave64 per token, or per token
-// split when few tokens are in flight):
-//   prologue   q[t] -> RMSNorm -> RoPE (angles in fp64).  For the E4M3 pool q is split
-//              into two E4M3 terms (hi + lo) with their own UE8M0 scales per 32 dims
-//              (about 8 significant bits, finer than bf16); each QK wave keeps the
-//              fragments of its 32 heads in registers for the whole token.
+// Work decomposition: one 512-thread workgroup (8 wave64, two per SIMD) per token, or
+// per token split when few tokens are in flight.
+//   prologue   one thread per (head, 32-dim block): q -> RMSNorm -> RoPE (angles in
+//              fp64) -> times sm_scale*log2(e).  For the E4M3 pool q is split into two
+//              E4M3 terms (hi + lo) with their own UE8M0 scales per 32 dims (about 8
+//              significant bits); each wave keeps the fragments of its 32 heads x 256
+//              dims in VGPRs for the whole token.
 //   per tile of 64 index entries (row ids prefetched two tiles ahead, raw rows one
 //   tile ahead by LDS DMA into a double buffer):
-//     QK^T     wave (a, c) computes S^T[32 rows of half c][32 heads of group a] with
-//              v_mfma_scale_f32_32x32x64_f8f6f4: K is the raw E4M3 row data with its
-//              UE8M0 block scales as the MFMA's A scales, q the hi / lo terms as B --
-//              no dequantization of K at all.  (bf16 pool: v_mfma_f32_32x32x16_bf16.)
+//     QK^T     wave (a, c, d) computes the partial S^T[32 rows of half c][32 heads of
+//              group a] over dim half d with v_mfma_scale_f32_32x32x64_f8f6f4: K is the
+//              raw E4M3 row data with its UE8M0 block scales as the MFMA's A scales, q
+//              the hi / lo terms as B -- no dequantization of K at all.  (bf16 pool:
+//              v_mfma_f32_32x32x16_bf16.)  The two dim halves meet through LDS.
 //     V tile   the same raw rows are dequantized once (v_cvt_scalef32_pk_bf16_fp8,
 //              exact) into a transposed bf16 tile Vt[dim][slot]; rows are stored in a
 //              slot order that makes both the transpose's reads and writes and the
-//              P.V reads bank-conflict free.
+//              P.V reads bank-conflict free.  The two waves of a SIMD run QK and the
+//              V tile in opposite orders so that MFMA and VALU work overlap.
 //     softmax  per-head tile max shared through LDS by the two row halves; the running
 //              max is raised only when the tile max exceeds it by 2^8 (lazy rescale);
 //              P is rounded to bf16 (v_cvt_pk_bf16_f32) and stored [head][slot].
-//     P.V      wave w owns output dims [w*d/4, (w+1)*d/4) for all 64 heads
-//              (v_mfma_f32_32x32x16_bf16, accumulators in AGPRs).
+//     P.V      wave w owns output dims [64w, 64w + 64) for all 64 heads
+//              (v_mfma_f32_32x32x16_bf16, accumulators in VGPRs).
 //   epilogue   o = acc / l -> LDS -> inverse RoPE -> per-32 amax -> UE8M0 exponent
 //              (integer test against 448 * 2^(e-127)) -> E4M3 by the scaled RNE convert.
 //   split mode each workgroup writes (acc, m, l) for its share of the tiles; a second
-//              kernel combines the splits in split order and runs the same epilogue.
+//              kernel combines the splits of each (token, head) in split order and runs
+//              the same epilogue.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -54,7 +58,7 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 constexpr int T = kTileRows;  // 64
 constexpr int NTHREADS = 512;  // main kernel: 8 waves, two per SIMD
 constexpr int NWAVES = NTHREADS / 64;
-constexpr int CTHREADS = 256;  // combine kernel
+constexpr int CTHREADS = 128;  // combine kernel: one (token, head) per workgroup
 constexpr int HP = 64;        // heads per workgroup (padded)
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
@@ -109,17 +113,23 @@ struct Cfg {
   static constexpr int Q_BYTES = (EB == 1) ? OFF_QSC + 2 * HP * NSB : HP * QS * 2;
   static constexpr int OS = D + 4;  // f32 stride of the epilogue o tile
   static constexpr int O_BYTES = HP * OS * 4;
-  static constexpr int BIG = align16(cmax(LOOP_END, cmax(Q_BYTES, O_BYTES)));
+  // the prologue's q tile sits after the raw tiles, so the first tile's DMA can land
+  // while the prologue runs
+  static constexpr int OFF_Q = RAW_END;
+  static constexpr int OFF_W = OFF_Q + align16(Q_BYTES);  // prologue: norm_w f32 [D]
+  static constexpr int BIG = align16(cmax(LOOP_END, cmax(OFF_Q + Q_BYTES, O_BYTES)));
   // small area: maxx[2][HP], alpha[HP], lsum[2][HP], cos[D/2], sin[D/2]
   static constexpr int OFF_MAXX = BIG;
   static constexpr int OFF_ALPHA = OFF_MAXX + 2 * HP * 4;
   static constexpr int OFF_LSUM = OFF_ALPHA + HP * 4;
   static constexpr int OFF_COS = OFF_LSUM + 2 * HP * 4;
   static constexpr int OFF_SIN = OFF_COS + (D / 2) * 4;
-  static constexpr int SMEM = OFF_SIN + (D / 2) * 4;
+  static constexpr int OFF_FLAG = OFF_SIN + (D / 2) * 4;  // rescale flags of the 2 head groups
+  static constexpr int SMEM = OFF_FLAG + 16;
   static_assert(G >= 1 && G <= 8 && (T % G) == 0 && ((T / G) % NWAVES) == 0, "row size unsupported");
   static_assert(KSW8 == 1 || KSW8 == 2 || KSW8 == 4, "k-steps per wave");
   static_assert(SMEM <= 160 * 1024, "LDS budget");
+  static_assert(OFF_W + D * 4 <= LOOP_END && HP * D * 4 <= OFF_W, "prologue areas");
 };
 
 // byte offset of chunk c of row r in a raw tile
@@ -247,9 +257,8 @@ __device__ __forceinline__ int opaque_zero() {
 // NST k-steps (64 dims each) of the E4M3 QK^T contraction, s (+)= sum_j K_j (q_hi,j + q_lo,j):
 // the scaled MFMAs run back to back (srcC = vdst of the previous one, which needs no
 // wait states), step j taking byte j of the scale registers.  Written as asm so that
-// the q fragments stay in AGPRs and s in VGPRs for the whole token (the compiler would
-// otherwise spill); all K fragments of the block are loaded before it.  The leading
-// s_nop covers a VALU write of an operand just before the block.
+// the chain stays back to back with all K fragments of the block loaded before it.  The
+// leading s_nop covers a VALU write of an operand just before the block.
 template <int NST, bool FIRST>
 __device__ __forceinline__ void qk_block(f32x16& s, const i32x8* A, const i32x8* qh, const i32x8* ql, uint32_t ka,
                                          uint32_t sh, uint32_t sl) {
@@ -265,7 +274,7 @@ __device__ __forceinline__ void qk_block(f32x16& s, const i32x8* A, const i32x8*
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %4, %8, %0, %13, %14 op_sel:[1,1,0] op_sel_hi:[1,1,0]\n\t"
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %4, %12, %0, %13, %15 op_sel:[1,1,0] op_sel_hi:[1,1,0]"
         : "=&v"(s)
-        : "v"(A[0]), "v"(A[1]), "v"(A[2]), "v"(A[3]), "a"(qh[0]), "a"(qh[1]), "a"(qh[2]), "a"(qh[3]), "a"(ql[0]), "a"(ql[1]), "a"(ql[2]), "a"(ql[3]), "v"(ka), "v"(sh), "v"(sl));
+        : "v"(A[0]), "v"(A[1]), "v"(A[2]), "v"(A[3]), "v"(qh[0]), "v"(qh[1]), "v"(qh[2]), "v"(qh[3]), "v"(ql[0]), "v"(ql[1]), "v"(ql[2]), "v"(ql[3]), "v"(ka), "v"(sh), "v"(sl));
   } else if constexpr (NST == 4 && !FIRST) {
     asm("s_nop 4\n\t"
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %5, %0, %13, %14 op_sel_hi:[0,0,0]\n\t"
@@ -277,7 +286,7 @@ __device__ __forceinline__ void qk_block(f32x16& s, const i32x8* A, const i32x8*
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %4, %8, %0, %13, %14 op_sel:[1,1,0] op_sel_hi:[1,1,0]\n\t"
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %4, %12, %0, %13, %15 op_sel:[1,1,0] op_sel_hi:[1,1,0]"
         : "+v"(s)
-        : "v"(A[0]), "v"(A[1]), "v"(A[2]), "v"(A[3]), "a"(qh[0]), "a"(qh[1]), "a"(qh[2]), "a"(qh[3]), "a"(ql[0]), "a"(ql[1]), "a"(ql[2]), "a"(ql[3]), "v"(ka), "v"(sh), "v"(sl));
+        : "v"(A[0]), "v"(A[1]), "v"(A[2]), "v"(A[3]), "v"(qh[0]), "v"(qh[1]), "v"(qh[2]), "v"(qh[3]), "v"(ql[0]), "v"(ql[1]), "v"(ql[2]), "v"(ql[3]), "v"(ka), "v"(sh), "v"(sl));
   } else if constexpr (NST == 2 && FIRST) {
     asm("s_nop 4\n\t"
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %3, 0, %7, %8 op_sel_hi:[0,0,0]\n\t"
@@ -285,7 +294,7 @@ __device__ __forceinline__ void qk_block(f32x16& s, const i32x8* A, const i32x8*
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %2, %4, %0, %7, %8 op_sel:[1,1,0] op_sel_hi:[0,0,0]\n\t"
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %2, %6, %0, %7, %9 op_sel:[1,1,0] op_sel_hi:[0,0,0]"
         : "=&v"(s)
-        : "v"(A[0]), "v"(A[1]), "a"(qh[0]), "a"(qh[1]), "a"(ql[0]), "a"(ql[1]), "v"(ka), "v"(sh), "v"(sl));
+        : "v"(A[0]), "v"(A[1]), "v"(qh[0]), "v"(qh[1]), "v"(ql[0]), "v"(ql[1]), "v"(ka), "v"(sh), "v"(sl));
   } else if constexpr (NST == 2 && !FIRST) {
     asm("s_nop 4\n\t"
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %3, %0, %7, %8 op_sel_hi:[0,0,0]\n\t"
@@ -293,26 +302,24 @@ __device__ __forceinline__ void qk_block(f32x16& s, const i32x8* A, const i32x8*
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %2, %4, %0, %7, %8 op_sel:[1,1,0] op_sel_hi:[0,0,0]\n\t"
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %2, %6, %0, %7, %9 op_sel:[1,1,0] op_sel_hi:[0,0,0]"
         : "+v"(s)
-        : "v"(A[0]), "v"(A[1]), "a"(qh[0]), "a"(qh[1]), "a"(ql[0]), "a"(ql[1]), "v"(ka), "v"(sh), "v"(sl));
+        : "v"(A[0]), "v"(A[1]), "v"(qh[0]), "v"(qh[1]), "v"(ql[0]), "v"(ql[1]), "v"(ka), "v"(sh), "v"(sl));
   } else if constexpr (NST == 1 && FIRST) {
     asm("s_nop 4\n\t"
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %4, %5 op_sel_hi:[0,0,0]\n\t"
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %3, %0, %4, %6 op_sel_hi:[0,0,0]"
         : "=&v"(s)
-        : "v"(A[0]), "a"(qh[0]), "a"(ql[0]), "v"(ka), "v"(sh), "v"(sl));
+        : "v"(A[0]), "v"(qh[0]), "v"(ql[0]), "v"(ka), "v"(sh), "v"(sl));
   } else if constexpr (NST == 1 && !FIRST) {
     asm("s_nop 4\n\t"
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %4, %5 op_sel_hi:[0,0,0]\n\t"
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %3, %0, %4, %6 op_sel_hi:[0,0,0]"
         : "+v"(s)
-        : "v"(A[0]), "a"(qh[0]), "a"(ql[0]), "v"(ka), "v"(sh), "v"(sl));
+        : "v"(A[0]), "v"(qh[0]), "v"(ql[0]), "v"(ka), "v"(sh), "v"(sl));
   }
 }
 // After the last QK step: 32 wait states before anything reads s (covers the
 // MFMA-write -> VALU/LDS-read and srcC WAR hazards of a 16-pass MFMA).
 __device__ __forceinline__ void qk_drain(f32x16& s) { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s)); }
-// keep a value in AGPRs from here on
-__device__ __forceinline__ void to_agpr(i32x8& x) { asm volatile("" : "+a"(x)); }
 
 // Inverse RoPE + UE8M0/E4M3 quantization of heads [0, nheads) held in o_lds (f32, row
 // stride OSTR), writing global heads head0 + hl of token tok.  One thread per (head,
@@ -374,14 +381,63 @@ __device__ void epilogue(const float* o_lds, int OSTR, int nheads, int head0, in
 
 // cos / sin of angle pos * theta^(-2i/R), i < R/2, computed in fp64
 __device__ __forceinline__ void rope_table(int pos, const KArgs& a, float* cs, float* sn) {
-  const int half = a.rope_dim / 2;
-  if ((int)threadIdx.x < half) {
+  // entry i is computed by lane i / nw of wave i % nw: spread over the waves
+  const int half = a.rope_dim / 2, nw = blockDim.x / 64;
+  for (int i = (threadIdx.x & 63) * nw + (threadIdx.x >> 6); i < half; i += blockDim.x) {
     const double lt = log2((double)a.rope_theta);
-    const double ang = (double)pos * exp2(-(2.0 * threadIdx.x / (double)a.rope_dim) * lt);
+    const double ang = (double)pos * exp2(-(2.0 * i / (double)a.rope_dim) * lt);
     double s, c;
     sincos(ang, &s, &c);
-    cs[threadIdx.x] = (float)c;
-    sn[threadIdx.x] = (float)s;
+    cs[i] = (float)c;
+    sn[i] = (float)s;
+  }
+}
+
+// Rotary pairing of the prologue (uniform per call): the partner of dim x is x +- r/2.
+//   ROT_NONE  r = 0
+//   ROT_LANE  r/2 a power-of-two multiple of 32 and the rotary slice aligned to 2*(r/64)
+//             blocks: the partner is the same element of the lane (block) b ^ (r/64)
+//   ROT_STAGE anything else: exchanged through an f32 staging area in LDS
+enum { ROT_NONE = 0, ROT_LANE = 1, ROT_STAGE = 2 };
+__host__ __device__ inline int rot_mode(int d, int r) {
+  if (r == 0) return ROT_NONE;
+  const int half = r / 2, o0 = d - r;
+  if (half % 32 == 0 && o0 % 32 == 0) {
+    const int dist = half / 32;
+    if ((dist & (dist - 1)) == 0 && (o0 / 32) % (2 * dist) == 0) return ROT_LANE;
+  }
+  return ROT_STAGE;
+}
+
+// Forward RoPE with the partner in lane ^ DIST (ROT_LANE): rb is the lane's block index
+// within the rotary slice (negative outside it); the first DIST blocks take
+// y*c - partner*s, the next DIST y*c + partner*s.  Every lane runs the cross-lane reads.
+template <int DIST, int NIT>
+__device__ __forceinline__ void rot_lane(float (&y)[NIT][32], bool rotb, int rb, const float* cs, const float* sn) {
+  const float sg = (rb >= 0 && rb < DIST) ? -1.f : 1.f;
+  const int kk0 = 32 * (rb & (DIST - 1));  // cos / sin index of element 0
+  float pr[NIT][32];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it)
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      if constexpr (DIST == 1) pr[it][e] = dpp_f32<0xB1>(y[it][e]);
+      else if constexpr (DIST == 2) pr[it][e] = dpp_f32<0x4E>(y[it][e]);
+      else
+        pr[it][e] = __builtin_bit_cast(
+            float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, y[it][e]), 0x1F | (DIST << 10)));
+    }
+  if (rotb) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float4 c4 = *reinterpret_cast<const float4*>(cs + kk0 + 4 * j);
+      const float4 s4 = *reinterpret_cast<const float4*>(sn + kk0 + 4 * j);
+      const float c[4] = {c4.x, c4.y, c4.z, c4.w}, sv[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+      for (int it = 0; it < NIT; ++it)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[it][4 * j + e] = y[it][4 * j + e] * c[e] + sg * pr[it][4 * j + e] * sv[e];
+    }
   }
 }
 
@@ -389,18 +445,21 @@ __device__ __forceinline__ void rope_table(int pos, const KArgs& a, float* cs, f
 // (two E4M3 terms + UE8M0 scales for the E4M3 pool, bf16 for the bf16 pool).  One thread
 // per (head, 32-dim block), blocks fastest across lanes: the loads are contiguous per
 // head, the sum of squares is reduced over the head's D/32 adjacent lanes with DPP, and
-// the block amax of each term is lane-local.  The rotary partners (x +- rope_dim/2) are
-// exchanged through an f32 staging area at the start of the q tile region.  Also fills
-// the cos / sin table (between its loads and its use).
-template <int D, int EB>
-__device__ void q_prologue(unsigned char* smem, int t, int pos, const KArgs& a, float* cs, float* sn) {
+// the block amax of each term is lane-local.  norm_w is read once into LDS.  The
+// rotary partners come from another lane (ROT_LANE) or through the f32 staging area
+// ystage (ROT_STAGE).  The q tile goes to OFF_Q.  Also fills the cos / sin table, and
+// calls after_loads() (every thread, once) as soon as the q loads are in flight.
+template <int D, int EB, class Hook>
+__device__ void q_prologue(unsigned char* smem, int t, int pos, const KArgs& a, float* cs, float* sn,
+                           float* ystage, Hook&& after_loads) {
   using C = Cfg<D, EB>;
-  constexpr int NBK = D / 32;               // lanes per head
-  constexpr int NU = HP * NBK;                           // units
-  constexpr int NIT = (NU + NTHREADS - 1) / NTHREADS;    // units per thread
+  constexpr int NBK = D / 32;                           // lanes per head
+  constexpr int NU = HP * NBK;                          // units
+  constexpr int NIT = (NU + NTHREADS - 1) / NTHREADS;   // units per thread
   static_assert((NU % NTHREADS == 0 || NU < NTHREADS) && NU % 64 == 0 && NBK <= 16, "prologue mapping");
   const bool act = (int)threadIdx.x < NU;  // whole waves idle when NU < NTHREADS
   const int R = a.rope_dim, o0 = D - R, half = R / 2;
+  const int mode = rot_mode(D, R);
   const int b = threadIdx.x % NBK;  // the same block in every unit of this thread
   uint4 qraw[NIT][4];
 #pragma unroll
@@ -410,20 +469,24 @@ __device__ void q_prologue(unsigned char* smem, int t, int pos, const KArgs& a, 
 #pragma unroll
     for (int j = 0; j < 4; ++j) qraw[it][j] = (act && h < a.h_q) ? src[j] : make_uint4(0u, 0u, 0u, 0u);
   }
+  float* wsh = reinterpret_cast<float*>(smem + C::OFF_W);
+  float4 wload = make_float4(0.f, 0.f, 0.f, 0.f);
+  if ((int)threadIdx.x < D / 4) wload = reinterpret_cast<const float4*>(a.norm_w)[threadIdx.x];
+  after_loads();
+  rope_table(pos, a, cs, sn);  // overlaps the loads above
+  if ((int)threadIdx.x < D / 4) reinterpret_cast<float4*>(wsh)[threadIdx.x] = wload;
+  __syncthreads();  // norm_w and the cos / sin table visible
   float wv[32];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const float4 w4 = *reinterpret_cast<const float4*>(a.norm_w + 32 * b + 4 * j);
+    const float4 w4 = reinterpret_cast<const float4*>(wsh)[8 * b + j];
     wv[4 * j] = w4.x; wv[4 * j + 1] = w4.y; wv[4 * j + 2] = w4.z; wv[4 * j + 3] = w4.w;
   }
-  rope_table(pos, a, cs, sn);  // overlaps the loads above
 
-  float* ystage = reinterpret_cast<float*>(smem);  // [HP][R] f32, rotary dims only
-  const bool rotb = act && 32 * b + 32 > o0;
+  const bool rotb = act && 32 * b + 32 > o0;  // this lane's block holds rotary dims
   float y[NIT][32];
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
-    const int h = (threadIdx.x + NTHREADS * it) / NBK;
     float ss = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -445,52 +508,68 @@ __device__ void q_prologue(unsigned char* smem, int t, int pos, const KArgs& a, 
       ss += dpp_f32<0x141>(ss);
       ss += dpp_f32<0x140>(ss);
     }
-    const float inv = 1.0f / sqrtf(ss / (float)D + a.rms_eps);
+    // the softmax scale (in log2 units) rides on q: the scores come out ready for exp2
+    const float inv = (a.sm_scale * 1.4426950408889634f) / sqrtf(ss / (float)D + a.rms_eps);
 #pragma unroll
     for (int e = 0; e < 32; ++e) y[it][e] = y[it][e] * inv * wv[e];
-    if (rotb) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int x = 32 * b + 4 * j;
-        if (x >= o0)
-          *reinterpret_cast<float4*>(ystage + h * R + (x - o0)) =
-              make_float4(y[it][4 * j], y[it][4 * j + 1], y[it][4 * j + 2], y[it][4 * j + 3]);
-      }
-    }
   }
-  __syncthreads();  // staged rotary values and the cos / sin table visible
-  if (rotb) {
+
+  if (mode == ROT_LANE) {
+    const int dist = half / 32;
+    const int rb = b - o0 / 32;  // block index within the rotary slice
+    if (dist == 1) rot_lane<1, NIT>(y, rotb, rb, cs, sn);
+    else if (dist == 2) rot_lane<2, NIT>(y, rotb, rb, cs, sn);
+    else if (dist == 4) rot_lane<4, NIT>(y, rotb, rb, cs, sn);
+    else rot_lane<8, NIT>(y, rotb, rb, cs, sn);
+  } else if (mode == ROT_STAGE) {
+    // ystage: [HP][R] f32 of the rotary dims (chunks of 4 never straddle o0 or o0 + r/2)
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       const int h = (threadIdx.x + NTHREADS * it) / NBK;
+      if (rotb) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int x = 32 * b + 4 * j;
-        if (x >= o0) {
-          const int k = x - o0;
-          const bool lo = k < half;
-          const int kk = lo ? k : k - half;
-          const float4 pr = *reinterpret_cast<const float4*>(ystage + h * R + (lo ? k + half : k - half));
-          const float4 c4 = *reinterpret_cast<const float4*>(cs + kk);
-          const float4 s4 = *reinterpret_cast<const float4*>(sn + kk);
-          const float sg = lo ? -1.f : 1.f;  // forward rotation
-          y[it][4 * j] = y[it][4 * j] * c4.x + sg * pr.x * s4.x;
-          y[it][4 * j + 1] = y[it][4 * j + 1] * c4.y + sg * pr.y * s4.y;
-          y[it][4 * j + 2] = y[it][4 * j + 2] * c4.z + sg * pr.z * s4.z;
-          y[it][4 * j + 3] = y[it][4 * j + 3] * c4.w + sg * pr.w * s4.w;
+        for (int j = 0; j < 8; ++j) {
+          const int x = 32 * b + 4 * j;
+          if (x >= o0)
+            *reinterpret_cast<float4*>(ystage + h * R + (x - o0)) =
+                make_float4(y[it][4 * j], y[it][4 * j + 1], y[it][4 * j + 2], y[it][4 * j + 3]);
         }
       }
     }
+    __syncthreads();  // staged rotary values visible
+    if (rotb) {
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int h = (threadIdx.x + NTHREADS * it) / NBK;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int x = 32 * b + 4 * j;
+          if (x >= o0) {
+            const int k = x - o0;
+            const bool lo = k < half;
+            const int kk = lo ? k : k - half;
+            const float4 pr = *reinterpret_cast<const float4*>(ystage + h * R + (lo ? k + half : k - half));
+            const float4 c4 = *reinterpret_cast<const float4*>(cs + kk);
+            const float4 s4 = *reinterpret_cast<const float4*>(sn + kk);
+            const float sg = lo ? -1.f : 1.f;  // forward rotation
+            y[it][4 * j] = y[it][4 * j] * c4.x + sg * pr.x * s4.x;
+            y[it][4 * j + 1] = y[it][4 * j + 1] * c4.y + sg * pr.y * s4.y;
+            y[it][4 * j + 2] = y[it][4 * j + 2] * c4.z + sg * pr.z * s4.z;
+            y[it][4 * j + 3] = y[it][4 * j + 3] * c4.w + sg * pr.w * s4.w;
+          }
+        }
+      }
+    }
+    __syncthreads();  // staging reads done: the q tile below may overwrite it
   }
-  __syncthreads();  // staging reads done: the q tile below overwrites it
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
     if (!act) break;
     const int h = (threadIdx.x + NTHREADS * it) / NBK;
     if constexpr (EB == 1) {
       // two E4M3 terms, each with its own UE8M0 scale per 32 dims
-      unsigned char* qf8 = smem;
-      unsigned char* qsc = smem + C::OFF_QSC;
+      unsigned char* qf8 = smem + C::OFF_Q;
+      unsigned char* qsc = smem + C::OFF_Q + C::OFF_QSC;
 #pragma unroll
       for (int term = 0; term < 2; ++term) {
         float amax = 0.f;
@@ -520,7 +599,7 @@ __device__ void q_prologue(unsigned char* smem, int t, int pos, const KArgs& a, 
         }
       }
     } else {
-      uint4* dst = reinterpret_cast<uint4*>(smem + (h * C::QS + 32 * b) * 2);
+      uint4* dst = reinterpret_cast<uint4*>(smem + C::OFF_Q + (h * C::QS + 32 * b) * 2);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         uint32_t pk[4];
@@ -539,6 +618,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM];
   float* maxx = reinterpret_cast<float*>(smem + C::OFF_MAXX);
   float* alpha_l = reinterpret_cast<float*>(smem + C::OFF_ALPHA);
+  int* flag_l = reinterpret_cast<int*>(smem + C::OFF_FLAG);
   float* lsum = reinterpret_cast<float*>(smem + C::OFF_LSUM);
   float* cs = reinterpret_cast<float*>(smem + C::OFF_COS);
   float* sn = reinterpret_cast<float*>(smem + C::OFF_SIN);
@@ -554,47 +634,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
   const int ns = a.num_splits;
   const int t = blockIdx.x / ns, split = blockIdx.x % ns;
   const int pos = a.positions[t];
-
-  // ---------------- prologue
-  q_prologue<D, EB>(smem, t, pos, a, cs, sn);
-  __syncthreads();
-  // Q fragments (B operand of S^T = K Q^T) of the 32 heads of group qa over dim half qd.
-  //   E4M3 pool: k-step ks covers dims [64ks, 64ks+64); lane half h holds dims
-  //   64ks + 16h + [0,16) and 64ks + 32 + 16h + [0,16) of its head (the 32x32x64 f8
-  //   operand layout); the UE8M0 scale of block 2ks + h sits in byte ks - KSW8*qd of
-  //   qs8[term].
-  //   bf16 pool: step ks, lane half h holds dims 16ks + 8h + [0, 8).
-  i32x8 qf8[2][(EB == 1) ? C::KSW8 : 1];
-  uint32_t qs8[2];
-  bf16x8 qbf[(EB == 2) ? C::KSW : 1];
-  const uint32_t hsel = lhalf ? 0x07050301u : 0x06040200u;  // bytes 2j + h of 8
-  if constexpr (EB == 1) {
-#pragma unroll
-    for (int term = 0; term < 2; ++term) {
-      const unsigned char* qrow = smem + (term * HP + 32 * qa + lrow) * C::QS8 + 16 * lhalf;
-#pragma unroll
-      for (int j = 0; j < C::KSW8; ++j) {
-        const int ks = C::KSW8 * qd + j;
-        const uint4 lo = *reinterpret_cast<const uint4*>(qrow + 64 * ks);
-        const uint4 hi = *reinterpret_cast<const uint4*>(qrow + 64 * ks + 32);
-        qf8[term][j] = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z,
-                               (int)hi.w};
-        to_agpr(qf8[term][j]);
-      }
-      qs8[term] = scale_word<C>(smem + C::OFF_QSC + (term * HP + 32 * qa + lrow) * C::NSB, qd, hsel);
-    }
-  } else {
-    const unsigned short* qrow = reinterpret_cast<const unsigned short*>(smem) + (32 * qa + lrow) * C::QS;
-#pragma unroll
-    for (int j = 0; j < C::KSW; ++j)
-      qbf[j] = *reinterpret_cast<const bf16x8*>(qrow + 16 * (C::KSW * qd + j) + 8 * lhalf);
-  }
-  __syncthreads();  // the q tile region is reused by the raw tiles below
-  {
-    // zero the raw tiles once: rows that are never loaded then read as finite values
-    uint4* z = reinterpret_cast<uint4*>(smem);
-    for (int i = tid; i < C::RAW_END / 16; i += NTHREADS) z[i] = make_uint4(0u, 0u, 0u, 0u);
-  }
 
   // ---------------- tile range of this workgroup
   const int lraw = a.topk_length[t];
@@ -646,6 +685,63 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
     }
   };
 
+  // ---------------- prologue
+  // The first tile's row DMA is issued as soon as the q loads are in flight, into raw
+  // tiles zeroed first (rows that are never loaded must read as finite values); the q
+  // tile sits above the raw tiles.  A rotary slice that needs the staging area (at
+  // offset 0) makes the DMA wait for the prologue.
+  int raw_cur = fetch_id(tb);
+  int raw_next = fetch_id(tb + 1);
+  {
+    uint4* z = reinterpret_cast<uint4*>(smem);
+    for (int i = tid; i < C::RAW_END / 16; i += NTHREADS) z[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  const bool early = rot_mode(D, a.rope_dim) != ROT_STAGE;  // no staging area needed
+  float* ystage = reinterpret_cast<float*>(smem);
+  q_prologue<D, EB>(smem, t, pos, a, cs, sn, ystage, [&]() {
+    if (early) {
+      __syncthreads();  // zeroing done before any DMA lands
+      if (tb < te) issue_tile(valid_id(tb, raw_cur), smem + C::OFF_RAW0, smem + C::OFF_SC0, lane);
+    }
+  });
+  __syncthreads();
+  // Q fragments (B operand of S^T = K Q^T) of the 32 heads of group qa over dim half qd.
+  //   E4M3 pool: k-step ks covers dims [64ks, 64ks+64); lane half h holds dims
+  //   64ks + 16h + [0,16) and 64ks + 32 + 16h + [0,16) of its head (the 32x32x64 f8
+  //   operand layout); the UE8M0 scale of block 2ks + h sits in byte ks - KSW8*qd of
+  //   qs8[term].
+  //   bf16 pool: step ks, lane half h holds dims 16ks + 8h + [0, 8).
+  i32x8 qf8[2][(EB == 1) ? C::KSW8 : 1];
+  uint32_t qs8[2];
+  bf16x8 qbf[(EB == 2) ? C::KSW : 1];
+  const uint32_t hsel = lhalf ? 0x07050301u : 0x06040200u;  // bytes 2j + h of 8
+  if constexpr (EB == 1) {
+#pragma unroll
+    for (int term = 0; term < 2; ++term) {
+      const unsigned char* qrow = smem + C::OFF_Q + (term * HP + 32 * qa + lrow) * C::QS8 + 16 * lhalf;
+#pragma unroll
+      for (int j = 0; j < C::KSW8; ++j) {
+        const int ks = C::KSW8 * qd + j;
+        const uint4 lo = *reinterpret_cast<const uint4*>(qrow + 64 * ks);
+        const uint4 hi = *reinterpret_cast<const uint4*>(qrow + 64 * ks + 32);
+        qf8[term][j] = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z,
+                               (int)hi.w};
+      }
+      qs8[term] = scale_word<C>(smem + C::OFF_Q + C::OFF_QSC + (term * HP + 32 * qa + lrow) * C::NSB, qd, hsel);
+    }
+  } else {
+    const unsigned short* qrow = reinterpret_cast<const unsigned short*>(smem + C::OFF_Q) + (32 * qa + lrow) * C::QS;
+#pragma unroll
+    for (int j = 0; j < C::KSW; ++j)
+      qbf[j] = *reinterpret_cast<const bf16x8*>(qrow + 16 * (C::KSW * qd + j) + 8 * lhalf);
+  }
+  if (!early) {
+    __syncthreads();  // staging (at offset 0) read; zero the raw tiles again
+    uint4* z = reinterpret_cast<uint4*>(smem);
+    for (int i = tid; i < C::RAW_END / 16; i += NTHREADS) z[i] = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+    if (tb < te) issue_tile(valid_id(tb, raw_cur), smem + C::OFF_RAW0, smem + C::OFF_SC0, lane);
+  }
   f32x16 acc[2][C::NB];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
@@ -654,13 +750,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
-  const float sl2 = a.sm_scale * 1.4426950408889634f;
 
-  int raw_cur = fetch_id(tb);
-  int raw_next = fetch_id(tb + 1);
-  __syncthreads();  // zeroing done before any DMA lands
-  if (tb < te) issue_tile(valid_id(tb, raw_cur), smem + C::OFF_RAW0, smem + C::OFF_SC0, lane);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA has landed
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's first-tile DMA has landed
 
   auto tile_step = [&](int tile, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
@@ -710,46 +801,74 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
     // (k = 0..3, slots 8q + 4p + k) of one 16-byte chunk c.
     auto vtrans = [&]() {
       constexpr int NBLK = (T / 4) * C::NCH;
+      if constexpr (C::NCH == 32 && C::G == 2 && EB == 1) {
+        // one block per thread.  An 8-lane group covers 4 consecutive chunks x both
+        // parities, so each read step touches 8 distinct bank slots and each write step
+        // 16 distinct 8-byte slots.  Rows 8q + p + 2k sit in group 4q + k at parity p.
+        static_assert(NBLK == NTHREADS, "one V block per thread");
+        const int u = lane & 7, g8 = lane >> 3;
+        const int c = 4 * g8 + (u >> 1), p = u & 1, q = w;
+        const unsigned char* rbase = raw_l + 4 * q * C::GS + 16 * (2 * c + p);
+        const unsigned char* sbase = sc_l + (8 * q + p) * C::NSB + (c >> 1);
+        uint4 rw[4];
+        uint32_t sb[4];
 #pragma unroll
-      for (int bb0 = 0; bb0 < NBLK; bb0 += NTHREADS) {
-        const int bb = bb0 + tid;
-        if (NBLK % NTHREADS != 0 && bb >= NBLK) break;
-        int q, p, c;
-        if constexpr (C::NCH == 32) {
-          // an 8-lane group covers 4 consecutive chunks x both parities, so each read
-          // step touches 8 distinct bank slots and each write step 16 distinct 8-byte slots
-          const int u = lane & 7, g8 = lane >> 3;
-          c = 4 * g8 + (u >> 1);
-          p = u & 1;
-          q = w + NWAVES * (bb0 / NTHREADS);
-        } else {
-          p = bb & 1;
-          c = (bb >> 1) % C::NCH;
-          q = (bb >> 1) / C::NCH;
+        for (int k = 0; k < 4; ++k) {  // all loads first, one wait
+          rw[k] = *reinterpret_cast<const uint4*>(rbase + k * C::GS);
+          sb[k] = sbase[2 * k * C::NSB];
         }
-        uint32_t pk[4][C::CE / 2];  // [k][element pair]
+        uint32_t pk[4][8];  // [k][element pair]
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const int row = 8 * q + p + 2 * k;
-          const uint4 rw = *reinterpret_cast<const uint4*>(raw_l + raw_off<C>(row, c));
-          if constexpr (EB == 1) {
-            const float sc = ue8m0_f32(sc_l[row * C::NSB + (c >> 1)]);
-            pk[k][0] = cvt_lo(rw.x, sc); pk[k][1] = cvt_hi(rw.x, sc);
-            pk[k][2] = cvt_lo(rw.y, sc); pk[k][3] = cvt_hi(rw.y, sc);
-            pk[k][4] = cvt_lo(rw.z, sc); pk[k][5] = cvt_hi(rw.z, sc);
-            pk[k][6] = cvt_lo(rw.w, sc); pk[k][7] = cvt_hi(rw.w, sc);
-          } else {
-            pk[k][0] = rw.x; pk[k][1] = rw.y; pk[k][2] = rw.z; pk[k][3] = rw.w;
-          }
+          const float sc = ue8m0_f32(sb[k]);
+          pk[k][0] = cvt_lo(rw[k].x, sc); pk[k][1] = cvt_hi(rw[k].x, sc);
+          pk[k][2] = cvt_lo(rw[k].y, sc); pk[k][3] = cvt_hi(rw[k].y, sc);
+          pk[k][4] = cvt_lo(rw[k].z, sc); pk[k][5] = cvt_hi(rw[k].z, sc);
+          pk[k][6] = cvt_lo(rw[k].w, sc); pk[k][7] = cvt_hi(rw[k].w, sc);
         }
+        // dim n = 16c + e: swz(n) = (e & 7) ^ (e >> 3) ^ K0 with K0 = (2c ^ (c >> 2)) & 7,
+        // so the 16-byte slot is (q ^ K0) ^ E(e), E(e) = (e & 7) ^ (e >> 3)
+        const int q0 = q ^ ((2 * c ^ (c >> 2)) & 7);
+        unsigned char* wbase = vt_l + 2048 * c + 8 * p;
 #pragma unroll
-        for (int e = 0; e < C::CE; ++e) {
+        for (int e = 0; e < 16; ++e) {
           const int k = e >> 1;
           const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
           const uint2 o = make_uint2(__builtin_amdgcn_perm(pk[1][k], pk[0][k], sel),
                                      __builtin_amdgcn_perm(pk[3][k], pk[2][k], sel));
-          const int n = C::CE * c + e;
-          *reinterpret_cast<uint2*>(vt_l + n * 128 + 16 * (q ^ swz(n)) + 8 * p) = o;
+          const int E = (e & 7) ^ (e >> 3);
+          *reinterpret_cast<uint2*>(wbase + 128 * e + 16 * (q0 ^ E)) = o;
+        }
+      } else {
+#pragma unroll
+        for (int bb0 = 0; bb0 < NBLK; bb0 += NTHREADS) {
+          const int bb = bb0 + tid;
+          if (NBLK % NTHREADS != 0 && bb >= NBLK) break;
+          const int p = bb & 1, c = (bb >> 1) % C::NCH, q = (bb >> 1) / C::NCH;
+          uint32_t pk[4][C::CE / 2];  // [k][element pair]
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int row = 8 * q + p + 2 * k;
+            const uint4 rw = *reinterpret_cast<const uint4*>(raw_l + raw_off<C>(row, c));
+            if constexpr (EB == 1) {
+              const float sc = ue8m0_f32(sc_l[row * C::NSB + (c >> 1)]);
+              pk[k][0] = cvt_lo(rw.x, sc); pk[k][1] = cvt_hi(rw.x, sc);
+              pk[k][2] = cvt_lo(rw.y, sc); pk[k][3] = cvt_hi(rw.y, sc);
+              pk[k][4] = cvt_lo(rw.z, sc); pk[k][5] = cvt_hi(rw.z, sc);
+              pk[k][6] = cvt_lo(rw.w, sc); pk[k][7] = cvt_hi(rw.w, sc);
+            } else {
+              pk[k][0] = rw.x; pk[k][1] = rw.y; pk[k][2] = rw.z; pk[k][3] = rw.w;
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < C::CE; ++e) {
+            const int k = e >> 1;
+            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+            const uint2 o = make_uint2(__builtin_amdgcn_perm(pk[1][k], pk[0][k], sel),
+                                       __builtin_amdgcn_perm(pk[3][k], pk[2][k], sel));
+            const int n = C::CE * c + e;
+            *reinterpret_cast<uint2*>(vt_l + n * 128 + 16 * (q ^ swz(n)) + 8 * p) = o;
+          }
         }
       }
     };
@@ -779,12 +898,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
         const float4 v = *reinterpret_cast<const float4*>(sx + 4 * (64 * j + lane));
         s[4 * j] += v.x; s[4 * j + 1] += v.y; s[4 * j + 2] += v.z; s[4 * j + 3] += v.w;
       }
-      // ---- softmax (part 1): tile max per head
+      // ---- softmax (part 1): tile max per head.  s is already in log2 units (q carries
+      // sm_scale * log2(e)).  Row 32qc + 8g + 4h + j of value i = 4g + j is valid iff
+      // its bit is set in the tile mask: the per-lane condition is built on the scalar
+      // unit (lanes 0-31 take bit r, lanes 32-63 bit r + 4) and applied by one select.
+      const uint32_t mw = (uint32_t)(mask >> (32 * qc));
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int row = 32 * qc + 8 * (i >> 2) + 4 * lhalf + (i & 3);
-        const bool v = (mask >> row) & 1ull;
-        s[i] = v ? s[i] * sl2 : -INFINITY;
+        const int r = 8 * (i >> 2) + (i & 3);
+        const unsigned long long lm = (((mw >> r) & 1u) ? 0x00000000FFFFFFFFull : 0ull) |
+                                      (((mw >> (r + 4)) & 1u) ? 0xFFFFFFFF00000000ull : 0ull);
+        s[i] = __builtin_amdgcn_inverse_ballot_w64(lm) ? s[i] : -INFINITY;
         mloc = fmaxf(mloc, s[i]);
       }
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
@@ -798,12 +922,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
       float mnew = m_run;
       if (mt > -INFINITY && (m_run == -INFINITY || mt > m_run + 8.0f)) mnew = mt;
       const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mnew);
+      // the accumulators need rescaling only where a finite running max was raised
+      const bool raised = __any(m_run != -INFINITY && mnew != m_run);
       m_run = mnew;
+      const float msafe = (mnew == -INFINITY) ? 0.f : mnew;  // masked scores are -inf: p = 0
       float p[16];
       float lp = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        p[i] = (mnew == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[i] - mnew);
+        p[i] = __builtin_amdgcn_exp2f(s[i] - msafe);
         lp += p[i];
       }
       l_run = l_run * alpha + lp;
@@ -820,20 +947,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
         *reinterpret_cast<uint32_t*>(cbase + 8) = pack_bf16(p[4 * g + 1], p[4 * g + 3]);
       }
       if (qc == 0 && lhalf == 0) alpha_l[head] = alpha;
+      if (qc == 0 && lane == 0) flag_l[qa] = raised ? 1 : 0;
     }
     __syncthreads();  // B3: P and alpha visible
 
     // ---- P.V: O[64 heads][dims of wave w]
     if (w < C::PVW) {
-      bool need = false;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float4 v4 = *reinterpret_cast<const float4*>(alpha_l + 32 * mb + 8 * g + 4 * lhalf);
-          need |= (v4.x != 1.f) | (v4.y != 1.f) | (v4.z != 1.f) | (v4.w != 1.f);
-        }
-      if (__any(need)) {
+      const int2 fl = *reinterpret_cast<const int2*>(flag_l);
+      if (__builtin_amdgcn_readfirstlane(fl.x | fl.y)) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -925,59 +1046,55 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
   }
 }
 
-// Combine the splits of one token for 8 heads (in split order), then the epilogue.
-// All split statistics and accumulators are fetched with independent loads.
+// Combine the splits of one (token, head): o = sum_s w_s acc_s / sum_s w_s l_s with
+// w_s = 2^(m_s - M), M = max_s m_s, in split order, then the epilogue.  One memory
+// round trip: every thread issues the loads of its 4 dims for all splits (16 at a
+// time) together with the split statistics, and the cos / sin table is computed while
+// they are in flight.  A split that read nothing has weight 0 and its accumulator
+// (never written) is not used.
 template <int D>
 __global__ __launch_bounds__(CTHREADS) void smla_combine(KArgs a) {
-  constexpr int HC = 8, OSTR = D + 4, MAXS = 64;
-  __shared__ __attribute__((aligned(16))) float o_l[HC * OSTR];
-  __shared__ float cs[D / 2], sn[D / 2];
-  __shared__ float mm[HC][MAXS], ll[HC][MAXS], wgt[HC][MAXS];
-  __shared__ float den[HC];
-  const int t = blockIdx.x, h0 = HC * blockIdx.y;
-  const int nh = (a.h_q - h0) < HC ? (a.h_q - h0) : HC;
+  constexpr int OSTR = D + 4, MAXS = 64, SCH = 16;
+  __shared__ __attribute__((aligned(16))) float o_l[OSTR];
+  __shared__ __attribute__((aligned(16))) float cs[D / 2], sn[D / 2];
+  __shared__ float mm[MAXS], ll[MAXS];
+  const int t = blockIdx.x, h = blockIdx.y;
   const int ns = a.num_splits;
   const size_t pf = partial_floats_d(a.h_q, D);
   const float* base = a.ws + (size_t)t * ns * pf;
+  const int f = threadIdx.x;  // float4 index within the head's D dims
+  const bool act = f < D / 4;
+  float4 v[SCH];
+#pragma unroll
+  for (int k = 0; k < SCH; ++k)
+    v[k] = (act && k < ns) ? *reinterpret_cast<const float4*>(base + (size_t)k * pf + (size_t)h * D + 4 * f)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+  if ((int)threadIdx.x < ns) {
+    const float* st = base + (size_t)threadIdx.x * pf + (size_t)a.h_q * D;
+    mm[threadIdx.x] = st[h];
+    ll[threadIdx.x] = st[a.h_q + h];
+  }
   rope_table(a.positions[t], a, cs, sn);
-  for (int f = threadIdx.x; f < HC * MAXS; f += CTHREADS) {
-    const int hl = f / MAXS, s = f % MAXS;
-    if (hl < nh && s < ns) {
-      const float* st = base + (size_t)s * pf + (size_t)a.h_q * D;
-      mm[hl][s] = st[h0 + hl];
-      ll[hl][s] = st[a.h_q + h0 + hl];
-    }
-  }
   __syncthreads();
-  if ((int)threadIdx.x < nh) {
-    const int hl = threadIdx.x;
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, mm[hl][s]);
-    float dsum = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const float ms = mm[hl][s];
-      const float wv = (M == -INFINITY || ms == -INFINITY) ? 0.f : exp2f(ms - M);
-      wgt[hl][s] = wv;
-      dsum += wv * ll[hl][s];
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, mm[s]);
+  float den = 0.f;
+  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < ns; s0 += SCH) {
+    if (s0 > 0) {
+#pragma unroll
+      for (int k = 0; k < SCH; ++k)
+        v[k] = (act && s0 + k < ns)
+                   ? *reinterpret_cast<const float4*>(base + (size_t)(s0 + k) * pf + (size_t)h * D + 4 * f)
+                   : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    den[hl] = dsum;
-  }
-  __syncthreads();
-  constexpr int Q4 = D / 4;
-  for (int f = threadIdx.x; f < nh * Q4; f += CTHREADS) {
-    const int hl = f / Q4, x4 = f % Q4;
-    const float* src = base + (size_t)(h0 + hl) * D + 4 * x4;
-    float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s0 = 0; s0 < ns; s0 += 8) {
-      float4 v[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        v[k] = (s0 + k < ns) ? *reinterpret_cast<const float4*>(src + (size_t)(s0 + k) * pf)
-                             : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float wv = (s0 + k < ns) ? wgt[hl][s0 + k] : 0.f;
-        // a split that read nothing has an unwritten accumulator: select, never multiply
+    for (int k = 0; k < SCH; ++k) {
+      if (s0 + k < ns) {
+        const float ms = mm[s0 + k];
+        const float wv = (M == -INFINITY || ms == -INFINITY) ? 0.f : exp2f(ms - M);
+        den += wv * ll[s0 + k];
+        // select, never multiply: a split with weight 0 may hold an unwritten accumulator
         if (wv != 0.f) {
           num.x += wv * v[k].x;
           num.y += wv * v[k].y;
@@ -986,12 +1103,11 @@ __global__ __launch_bounds__(CTHREADS) void smla_combine(KArgs a) {
         }
       }
     }
-    const float inv = den[hl] > 0.f ? 1.0f / den[hl] : 0.f;
-    *reinterpret_cast<float4*>(o_l + hl * OSTR + 4 * x4) =
-        make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv);
   }
+  const float inv = den > 0.f ? 1.0f / den : 0.f;
+  if (act) *reinterpret_cast<float4*>(o_l + 4 * f) = make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv);
   __syncthreads();
-  epilogue<D, CTHREADS>(o_l, OSTR, nh, h0, t, a, cs, sn);
+  epilogue<D, CTHREADS>(o_l, OSTR, 1, h, t, a, cs, sn);
 }
 
 template <int D, int EB>
@@ -1000,8 +1116,7 @@ hipError_t launch_t(const LaunchArgs& x, const KArgs& k) {
   hipLaunchKernelGGL((smla_main<D, EB>), dim3((unsigned)(x.s_q * ns)), dim3(NTHREADS), 0, x.stream, k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ns == 1) return e;
-  hipLaunchKernelGGL((smla_combine<D>), dim3((unsigned)x.s_q, (unsigned)((x.h_q + 7) / 8)), dim3(CTHREADS), 0,
-                     x.stream, k);
+  hipLaunchKernelGGL((smla_combine<D>), dim3((unsigned)x.s_q, (unsigned)x.h_q), dim3(CTHREADS), 0, x.stream, k);
   return hipGetLastError();
 }
 
