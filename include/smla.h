@@ -53,7 +53,8 @@ extern "C" {
 /* return codes */
 #define SMLA_OK 0
 #define SMLA_ERR_NULL 1  /* a required pointer is NULL */
-#define SMLA_ERR_SHAPE 2 /* unsupported d / rope_dim / h_q / topk combination */
+#define SMLA_ERR_SHAPE 2 /* unsupported d / rope_dim / h_q / topk combination, or a
+                            pool of 4 GiB or more */
 #define SMLA_ERR_VALUE 3 /* bad scalar (s_q < 0, n_rows < 1, non-finite or non-positive
                             sm_scale / rms_eps / rope_theta, workspace too small,
                             bad kv_format, num_splits out of range) or a misaligned
@@ -71,7 +72,9 @@ typedef struct smla_params {
   int32_t rope_dim; /* rotary dims at the end of each head: 0..d, a multiple of 16 */
   int32_t topk;     /* row stride of `indices` (entries per token), 0..65536 */
   int32_t kv_format;
-  int64_t n_rows;   /* rows in kv_pool (>= 1); every read index must lie in [-1, n_rows) */
+  int64_t n_rows;   /* rows in kv_pool (>= 1); every read index must lie in [-1, n_rows).
+                       The pool is addressed with 32-bit byte offsets: n_rows * row bytes
+                       must stay below 4 GiB - 16 (SMLA_ERR_SHAPE otherwise) */
   float sm_scale;   /* softmax scale, finite and > 0 (typically 1/sqrt(d)) */
   float rms_eps;    /* RMSNorm epsilon, finite and > 0 */
   float rope_theta; /* RoPE base, finite and > 0 */

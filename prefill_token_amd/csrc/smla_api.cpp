@@ -48,6 +48,11 @@ int check_params(const smla_params* p) {
   if ((long long)p->s_q * p->topk > 0x7FFFFFFFLL)
     return fail(SMLA_ERR_SHAPE, "s_q * topk must fit in int32");
   if (p->s_q > 0x7FFFFFFF / 64) return fail(SMLA_ERR_SHAPE, "s_q too large");
+  // rows are gathered at 32-bit byte offsets into the pool (and its scales)
+  const long long row_bytes = (long long)p->d * (p->kv_format == SMLA_KV_BF16 ? 2 : 1);
+  if (p->n_rows > 0xFFFFFFF0LL / row_bytes)
+    return fail(SMLA_ERR_SHAPE, "kv_pool must be smaller than 4 GiB (n_rows %lld x %lld bytes)",
+                (long long)p->n_rows, row_bytes);
   return SMLA_OK;
 }
 

@@ -38,6 +38,8 @@
 //              the same epilogue.
 #include <hip/hip_runtime.h>
 #include <math.h>
+
+#include <cmath>
 #include <stdint.h>
 
 #include <type_traits>
@@ -129,7 +131,7 @@ struct Cfg {
   static_assert(G >= 1 && G <= 8 && (T % G) == 0 && ((T / G) % NWAVES) == 0, "row size unsupported");
   static_assert(KSW8 == 1 || KSW8 == 2 || KSW8 == 4, "k-steps per wave");
   static_assert(SMEM <= 160 * 1024, "LDS budget");
-  static_assert(OFF_W + D * 4 <= LOOP_END && HP * D * 4 <= OFF_W, "prologue areas");
+  static_assert(OFF_W + D * 4 <= LOOP_END && HP * (D + 4) * 4 <= OFF_W, "prologue areas");
 };
 
 // byte offset of chunk c of row r in a raw tile
@@ -168,6 +170,7 @@ struct KArgs {
   int s_q, h_q, rope_dim, topk, num_splits, tiles_per_split;
   long long n_rows;
   float sm_scale, rms_eps, rope_theta;
+  double log2_theta;  // log2(rope_theta), computed on the host
 };
 
 __device__ __forceinline__ uint32_t cvt_lo(uint32_t src, float sc) {
@@ -214,29 +217,35 @@ __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3) ^ (r >> 6)) & 7
 
 __device__ __forceinline__ size_t partial_floats_d(int h_q, int d) { return (size_t)h_q * (size_t)(d + 2); }
 
-// LDS DMA (global_load_lds_dword[x4]): every active lane writes its 4 / 16 bytes at
-// lds_base + 4*lane / 16*lane.  Issued from asm so that the compiler does not make its
-// own LDS reads wait for it; the tile loop waits (vmcnt 0) before the barrier that
-// publishes the data.  Vector loads retire in order, so the compiler's own vmcnt waits
-// stay correct (they can only over-wait).
+// LDS DMA (buffer_load_dword[x4] ... lds): every lane writes its 4 / 16 bytes at
+// lds_base + 4*lane / 16*lane, read at byte offset voff of a buffer resource.  An
+// offset at or beyond the resource's size reads as zeros, which is how entries that are
+// not read (sentinels, beyond the length) become zero rows without a branch.  Issued
+// from asm so that the compiler does not make its own LDS reads wait for it; the tile
+// loop waits (vmcnt 0) before the barrier that publishes the data.  Vector loads retire
+// in order, so the compiler's own vmcnt waits stay correct (they can only over-wait).
+// M0 is saved and restored around the DMA (the compiler reserves it for its own use).
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
-// M0 is saved and restored around the DMA (the compiler reserves it for its own use).
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
+constexpr uint32_t kNoRow = 0xFFFFFFF0u;  // an offset past every resource: zeros
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void dma16(uint32_t voff, __amdgpu_buffer_rsrc_t rsrc, uint32_t lds_base) {
   uint32_t save;
   asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds\n\ts_mov_b32 m0, %0"
       : "=&s"(save)
-      : "v"(g), "s"(lds_base)
+      : "v"(voff), "s"(rsrc), "s"(lds_base)
       : "memory");
 }
-__device__ __forceinline__ void dma4(const void* g, uint32_t lds_base) {
+__device__ __forceinline__ void dma4(uint32_t voff, __amdgpu_buffer_rsrc_t rsrc, uint32_t lds_base) {
   uint32_t save;
   asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds\n\ts_mov_b32 m0, %0"
       : "=&s"(save)
-      : "v"(g), "s"(lds_base)
+      : "v"(voff), "s"(rsrc), "s"(lds_base)
       : "memory");
 }
 
@@ -381,63 +390,19 @@ __device__ void epilogue(const float* o_lds, int OSTR, int nheads, int head0, in
 
 // cos / sin of angle pos * theta^(-2i/R), i < R/2, computed in fp64
 __device__ __forceinline__ void rope_table(int pos, const KArgs& a, float* cs, float* sn) {
-  // entry i is computed by lane i / nw of wave i % nw: spread over the waves
+  // angle pos * theta^(-2i/r) in fp64, reduced to [-pi, pi] in fp64 (Cody-Waite with a
+  // two-part 2*pi: |n| < 2^13, so n * hi is exact in the fma), then sin / cos in fp32
+  // of the reduced angle.  Entry i is computed by lane i / nw of wave i % nw.
+  constexpr double kInv2Pi = 0.15915494309189535, k2PiHi = 6.283185307179586, k2PiLo = 2.4492935982947064e-16;
   const int half = a.rope_dim / 2, nw = blockDim.x / 64;
   for (int i = (threadIdx.x & 63) * nw + (threadIdx.x >> 6); i < half; i += blockDim.x) {
-    const double lt = log2((double)a.rope_theta);
-    const double ang = (double)pos * exp2(-(2.0 * i / (double)a.rope_dim) * lt);
-    double s, c;
-    sincos(ang, &s, &c);
-    cs[i] = (float)c;
-    sn[i] = (float)s;
-  }
-}
-
-// Rotary pairing of the prologue (uniform per call): the partner of dim x is x +- r/2.
-//   ROT_NONE  r = 0
-//   ROT_LANE  r/2 a power-of-two multiple of 32 and the rotary slice aligned to 2*(r/64)
-//             blocks: the partner is the same element of the lane (block) b ^ (r/64)
-//   ROT_STAGE anything else: exchanged through an f32 staging area in LDS
-enum { ROT_NONE = 0, ROT_LANE = 1, ROT_STAGE = 2 };
-__host__ __device__ inline int rot_mode(int d, int r) {
-  if (r == 0) return ROT_NONE;
-  const int half = r / 2, o0 = d - r;
-  if (half % 32 == 0 && o0 % 32 == 0) {
-    const int dist = half / 32;
-    if ((dist & (dist - 1)) == 0 && (o0 / 32) % (2 * dist) == 0) return ROT_LANE;
-  }
-  return ROT_STAGE;
-}
-
-// Forward RoPE with the partner in lane ^ DIST (ROT_LANE): rb is the lane's block index
-// within the rotary slice (negative outside it); the first DIST blocks take
-// y*c - partner*s, the next DIST y*c + partner*s.  Every lane runs the cross-lane reads.
-template <int DIST, int NIT>
-__device__ __forceinline__ void rot_lane(float (&y)[NIT][32], bool rotb, int rb, const float* cs, const float* sn) {
-  const float sg = (rb >= 0 && rb < DIST) ? -1.f : 1.f;
-  const int kk0 = 32 * (rb & (DIST - 1));  // cos / sin index of element 0
-  float pr[NIT][32];
-#pragma unroll
-  for (int it = 0; it < NIT; ++it)
-#pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      if constexpr (DIST == 1) pr[it][e] = dpp_f32<0xB1>(y[it][e]);
-      else if constexpr (DIST == 2) pr[it][e] = dpp_f32<0x4E>(y[it][e]);
-      else
-        pr[it][e] = __builtin_bit_cast(
-            float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, y[it][e]), 0x1F | (DIST << 10)));
-    }
-  if (rotb) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float4 c4 = *reinterpret_cast<const float4*>(cs + kk0 + 4 * j);
-      const float4 s4 = *reinterpret_cast<const float4*>(sn + kk0 + 4 * j);
-      const float c[4] = {c4.x, c4.y, c4.z, c4.w}, sv[4] = {s4.x, s4.y, s4.z, s4.w};
-#pragma unroll
-      for (int it = 0; it < NIT; ++it)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) y[it][4 * j + e] = y[it][4 * j + e] * c[e] + sg * pr[it][4 * j + e] * sv[e];
-    }
+    const double ang = (double)pos * exp2(-(2.0 * i / (double)a.rope_dim) * a.log2_theta);
+    const double n = rint(ang * kInv2Pi);
+    const double r = fma(-n, k2PiLo, fma(-n, k2PiHi, ang));
+    float s, c;
+    sincosf((float)r, &s, &c);
+    cs[i] = c;
+    sn[i] = s;
   }
 }
 
@@ -445,10 +410,11 @@ __device__ __forceinline__ void rot_lane(float (&y)[NIT][32], bool rotb, int rb,
 // (two E4M3 terms + UE8M0 scales for the E4M3 pool, bf16 for the bf16 pool).  One thread
 // per (head, 32-dim block), blocks fastest across lanes: the loads are contiguous per
 // head, the sum of squares is reduced over the head's D/32 adjacent lanes with DPP, and
-// the block amax of each term is lane-local.  norm_w is read once into LDS.  The
-// rotary partners come from another lane (ROT_LANE) or through the f32 staging area
-// ystage (ROT_STAGE).  The q tile goes to OFF_Q.  Also fills the cos / sin table, and
-// calls after_loads() (every thread, once) as soon as the q loads are in flight.
+// the block amax of each term is lane-local.  norm_w is read once into LDS.  RoPE runs
+// densely through the f32 staging area ystage ([HP][R + 4]): the lanes holding rotary
+// dims stage them, every thread rotates four (dim, dim + r/2) pairs, and the lanes read
+// their rotated dims back.  The q tile goes to OFF_Q.  Also fills the cos / sin table,
+// and calls after_loads() (every thread, once) as soon as the q loads are in flight.
 template <int D, int EB, class Hook>
 __device__ void q_prologue(unsigned char* smem, int t, int pos, const KArgs& a, float* cs, float* sn,
                            float* ystage, Hook&& after_loads) {
@@ -458,8 +424,7 @@ __device__ void q_prologue(unsigned char* smem, int t, int pos, const KArgs& a, 
   constexpr int NIT = (NU + NTHREADS - 1) / NTHREADS;   // units per thread
   static_assert((NU % NTHREADS == 0 || NU < NTHREADS) && NU % 64 == 0 && NBK <= 16, "prologue mapping");
   const bool act = (int)threadIdx.x < NU;  // whole waves idle when NU < NTHREADS
-  const int R = a.rope_dim, o0 = D - R, half = R / 2;
-  const int mode = rot_mode(D, R);
+  const int R = a.rope_dim, o0 = D - R, half = R / 2, RS = R + 4;
   const int b = threadIdx.x % NBK;  // the same block in every unit of this thread
   uint4 qraw[NIT][4];
 #pragma unroll
@@ -509,34 +474,42 @@ __device__ void q_prologue(unsigned char* smem, int t, int pos, const KArgs& a, 
       ss += dpp_f32<0x140>(ss);
     }
     // the softmax scale (in log2 units) rides on q: the scores come out ready for exp2
-    const float inv = (a.sm_scale * 1.4426950408889634f) / sqrtf(ss / (float)D + a.rms_eps);
+    const float inv = (a.sm_scale * 1.4426950408889634f) * __builtin_amdgcn_rsqf(ss / (float)D + a.rms_eps);
 #pragma unroll
     for (int e = 0; e < 32; ++e) y[it][e] = y[it][e] * inv * wv[e];
   }
 
-  if (mode == ROT_LANE) {
-    const int dist = half / 32;
-    const int rb = b - o0 / 32;  // block index within the rotary slice
-    if (dist == 1) rot_lane<1, NIT>(y, rotb, rb, cs, sn);
-    else if (dist == 2) rot_lane<2, NIT>(y, rotb, rb, cs, sn);
-    else if (dist == 4) rot_lane<4, NIT>(y, rotb, rb, cs, sn);
-    else rot_lane<8, NIT>(y, rotb, rb, cs, sn);
-  } else if (mode == ROT_STAGE) {
-    // ystage: [HP][R] f32 of the rotary dims (chunks of 4 never straddle o0 or o0 + r/2)
+  if (R > 0) {
+    // stage the rotary dims (chunks of 4 never straddle o0 or o0 + r/2)
+    if (rotb) {
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const int h = (threadIdx.x + NTHREADS * it) / NBK;
-      if (rotb) {
+      for (int it = 0; it < NIT; ++it) {
+        const int h = (threadIdx.x + NTHREADS * it) / NBK;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int x = 32 * b + 4 * j;
           if (x >= o0)
-            *reinterpret_cast<float4*>(ystage + h * R + (x - o0)) =
+            *reinterpret_cast<float4*>(ystage + h * RS + (x - o0)) =
                 make_float4(y[it][4 * j], y[it][4 * j + 1], y[it][4 * j + 2], y[it][4 * j + 3]);
         }
       }
     }
     __syncthreads();  // staged rotary values visible
+    // forward rotation of the pairs (k, k + r/2), four consecutive k per step
+    const int q4 = half / 4;
+    for (int u = threadIdx.x; u < HP * q4; u += NTHREADS) {
+      const int h = u / q4, k = 4 * (u % q4);
+      float* row = ystage + h * RS;
+      const float4 lo = *reinterpret_cast<const float4*>(row + k);
+      const float4 hi = *reinterpret_cast<const float4*>(row + k + half);
+      const float4 c4 = *reinterpret_cast<const float4*>(cs + k);
+      const float4 s4 = *reinterpret_cast<const float4*>(sn + k);
+      *reinterpret_cast<float4*>(row + k) = make_float4(lo.x * c4.x - hi.x * s4.x, lo.y * c4.y - hi.y * s4.y,
+                                                        lo.z * c4.z - hi.z * s4.z, lo.w * c4.w - hi.w * s4.w);
+      *reinterpret_cast<float4*>(row + k + half) = make_float4(hi.x * c4.x + lo.x * s4.x, hi.y * c4.y + lo.y * s4.y,
+                                                               hi.z * c4.z + lo.z * s4.z, hi.w * c4.w + lo.w * s4.w);
+    }
+    __syncthreads();  // rotated values visible
     if (rotb) {
 #pragma unroll
       for (int it = 0; it < NIT; ++it) {
@@ -545,17 +518,8 @@ __device__ void q_prologue(unsigned char* smem, int t, int pos, const KArgs& a, 
         for (int j = 0; j < 8; ++j) {
           const int x = 32 * b + 4 * j;
           if (x >= o0) {
-            const int k = x - o0;
-            const bool lo = k < half;
-            const int kk = lo ? k : k - half;
-            const float4 pr = *reinterpret_cast<const float4*>(ystage + h * R + (lo ? k + half : k - half));
-            const float4 c4 = *reinterpret_cast<const float4*>(cs + kk);
-            const float4 s4 = *reinterpret_cast<const float4*>(sn + kk);
-            const float sg = lo ? -1.f : 1.f;  // forward rotation
-            y[it][4 * j] = y[it][4 * j] * c4.x + sg * pr.x * s4.x;
-            y[it][4 * j + 1] = y[it][4 * j + 1] * c4.y + sg * pr.y * s4.y;
-            y[it][4 * j + 2] = y[it][4 * j + 2] * c4.z + sg * pr.z * s4.z;
-            y[it][4 * j + 3] = y[it][4 * j + 3] * c4.w + sg * pr.w * s4.w;
+            const float4 v = *reinterpret_cast<const float4*>(ystage + h * RS + (x - o0));
+            y[it][4 * j] = v.x; y[it][4 * j + 1] = v.y; y[it][4 * j + 2] = v.z; y[it][4 * j + 3] = v.w;
           }
         }
       }
@@ -570,12 +534,19 @@ __device__ void q_prologue(unsigned char* smem, int t, int pos, const KArgs& a, 
       // two E4M3 terms, each with its own UE8M0 scale per 32 dims
       unsigned char* qf8 = smem + C::OFF_Q;
       unsigned char* qsc = smem + C::OFF_Q + C::OFF_QSC;
+      int eq = 0;
 #pragma unroll
       for (int term = 0; term < 2; ++term) {
-        float amax = 0.f;
+        if (term == 0) {
+          float amax = 0.f;
 #pragma unroll
-        for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(y[it][e]));
-        const int eq = ue8m0_exp(amax);
+          for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(y[it][e]));
+          eq = ue8m0_exp(amax);
+        } else {
+          // the residual of an RNE E4M3 code is at most 16 of its scale units (half an
+          // ulp of the top binade): 2^-4 of the first scale holds it unsaturated
+          eq = eq >= 4 ? eq - 4 : 0;
+        }
         const float sc = ue8m0_f32((uint32_t)eq);
         uint32_t wd[8];
 #pragma unroll
@@ -660,7 +631,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
   };
 
   // Enqueue the LDS DMA of one tile's rows (and scales) into raw / sc.  Rows that are not
-  // read keep older (finite) LDS contents: the QK masks them and P is zero for them.
+  // read come in as zeros (an out-of-range offset): the QK masks them and P is zero.
+  const __amdgpu_buffer_rsrc_t pool_rs = buf_rsrc(a.pool, (uint32_t)(a.n_rows * C::RB));
+  const __amdgpu_buffer_rsrc_t scale_rs = buf_rsrc(a.scales, (uint32_t)(a.n_rows * C::NSB));
   auto issue_tile = [&](int id_vec, unsigned char* raw, unsigned char* sc, int lane) {
     constexpr int GPW = (T / C::G) / NWAVES;  // DMA groups per wave
     constexpr int WPR = C::NSB / 4;           // 4-byte scale words per row
@@ -675,34 +648,27 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
       const int gi = GPW * w + k;
       const int chunk = lane / C::G;
       const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(raw + gi * C::GS));
-      if (id[k] >= 0) dma16(a.pool + (size_t)id[k] * C::RB + 16 * chunk, dst);
+      dma16(id[k] >= 0 ? (uint32_t)id[k] * C::RB + 16 * chunk : kNoRow, pool_rs, dst);
     }
     if constexpr (EB == 1) {
       if (w < WPR) {
         const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(sc + 256 * w));
-        if (id[GPW] >= 0) dma4(a.scales + (size_t)id[GPW] * C::NSB + 4 * (f % WPR), dst);
+        dma4(id[GPW] >= 0 ? (uint32_t)id[GPW] * C::NSB + 4 * (f % WPR) : kNoRow, scale_rs, dst);
       }
     }
   };
 
   // ---------------- prologue
-  // The first tile's row DMA is issued as soon as the q loads are in flight, into raw
-  // tiles zeroed first (rows that are never loaded must read as finite values); the q
-  // tile sits above the raw tiles.  A rotary slice that needs the staging area (at
-  // offset 0) makes the DMA wait for the prologue.
+  // The first tile's row DMA is issued as soon as the q loads are in flight; the q tile
+  // sits above the raw tiles.  A rotary slice too long for the staging area there is
+  // staged at offset 0 instead, and the DMA waits for the prologue.
   int raw_cur = fetch_id(tb);
   int raw_next = fetch_id(tb + 1);
-  {
-    uint4* z = reinterpret_cast<uint4*>(smem);
-    for (int i = tid; i < C::RAW_END / 16; i += NTHREADS) z[i] = make_uint4(0u, 0u, 0u, 0u);
-  }
-  const bool early = rot_mode(D, a.rope_dim) != ROT_STAGE;  // no staging area needed
-  float* ystage = reinterpret_cast<float*>(smem);
+  // the rotary staging sits above the raw tiles when it fits below norm_w
+  const bool early = C::RAW_END + HP * (a.rope_dim + 4) * 4 <= C::OFF_W;
+  float* ystage = reinterpret_cast<float*>(smem + (early ? C::RAW_END : 0));
   q_prologue<D, EB>(smem, t, pos, a, cs, sn, ystage, [&]() {
-    if (early) {
-      __syncthreads();  // zeroing done before any DMA lands
-      if (tb < te) issue_tile(valid_id(tb, raw_cur), smem + C::OFF_RAW0, smem + C::OFF_SC0, lane);
-    }
+    if (early && tb < te) issue_tile(valid_id(tb, raw_cur), smem + C::OFF_RAW0, smem + C::OFF_SC0, lane);
   });
   __syncthreads();
   // Q fragments (B operand of S^T = K Q^T) of the 32 heads of group qa over dim half qd.
@@ -736,10 +702,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
       qbf[j] = *reinterpret_cast<const bf16x8*>(qrow + 16 * (C::KSW * qd + j) + 8 * lhalf);
   }
   if (!early) {
-    __syncthreads();  // staging (at offset 0) read; zero the raw tiles again
-    uint4* z = reinterpret_cast<uint4*>(smem);
-    for (int i = tid; i < C::RAW_END / 16; i += NTHREADS) z[i] = make_uint4(0u, 0u, 0u, 0u);
-    __syncthreads();
+    __syncthreads();  // staging (at offset 0) read before the DMA lands there
     if (tb < te) issue_tile(valid_id(tb, raw_cur), smem + C::OFF_RAW0, smem + C::OFF_SC0, lane);
   }
   f32x16 acc[2][C::NB];
@@ -1147,6 +1110,7 @@ hipError_t launch(const LaunchArgs& x) {
   k.sm_scale = x.sm_scale;
   k.rms_eps = x.rms_eps;
   k.rope_theta = x.rope_theta;
+  k.log2_theta = std::log2((double)x.rope_theta);
   if (x.d == 512 && x.kv_format == 0) return launch_t<512, 1>(x, k);
   if (x.d == 128 && x.kv_format == 0) return launch_t<128, 1>(x, k);
   if (x.d == 128 && x.kv_format == 1) return launch_t<128, 2>(x, k);

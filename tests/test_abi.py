@@ -93,6 +93,7 @@ def test_null_scales_for_fp8_pool(lib):
     (dict(rope_dim=-16), smla.SMLA_ERR_SHAPE),
     (dict(topk=-1), smla.SMLA_ERR_SHAPE),
     (dict(topk=70000), smla.SMLA_ERR_SHAPE),
+    (dict(n_rows=(1 << 32) // 512), smla.SMLA_ERR_SHAPE),  # a 4 GiB pool
     (dict(s_q=-1), smla.SMLA_ERR_VALUE),
     (dict(n_rows=0), smla.SMLA_ERR_VALUE),
     (dict(kv_format=7), smla.SMLA_ERR_VALUE),
