@@ -118,7 +118,7 @@ struct Cfg {
   // the prologue's q tile sits after the raw tiles, so the first tile's DMA can land
   // while the prologue runs
   static constexpr int OFF_Q = RAW_END;
-  static constexpr int OFF_W = OFF_Q + align16(Q_BYTES);  // prologue: norm_w f32 [D]
+  static constexpr int OFF_W = OFF_Q + align16(Q_BYTES);  // prologue: norm_w f32, 36 per block
   static constexpr int BIG = align16(cmax(LOOP_END, cmax(OFF_Q + Q_BYTES, O_BYTES)));
   // small area: maxx[2][HP], alpha[HP], lsum[2][HP], cos[D/2], sin[D/2]
   static constexpr int OFF_MAXX = BIG;
@@ -131,7 +131,7 @@ struct Cfg {
   static_assert(G >= 1 && G <= 8 && (T % G) == 0 && ((T / G) % NWAVES) == 0, "row size unsupported");
   static_assert(KSW8 == 1 || KSW8 == 2 || KSW8 == 4, "k-steps per wave");
   static_assert(SMEM <= 160 * 1024, "LDS budget");
-  static_assert(OFF_W + D * 4 <= LOOP_END && HP * (D + 4) * 4 <= OFF_W, "prologue areas");
+  static_assert(OFF_W + (D / 32) * 36 * 4 <= LOOP_END && HP * (D + 4) * 4 <= OFF_W, "prologue areas");
 };
 
 // byte offset of chunk c of row r in a raw tile
@@ -273,7 +273,7 @@ __device__ __forceinline__ void qk_block(f32x16& s, const i32x8* A, const i32x8*
                                          uint32_t sh, uint32_t sl) {
   static_assert(NST == 1 || NST == 2 || NST == 4, "k-steps per block");
   if constexpr (NST == 4 && FIRST) {
-    asm("s_nop 4\n\t"
+    asm volatile("s_nop 4\n\t"
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %5, 0, %13, %14 op_sel_hi:[0,0,0]\n\t"
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %9, %0, %13, %15 op_sel_hi:[0,0,0]\n\t"
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %2, %6, %0, %13, %14 op_sel:[1,1,0] op_sel_hi:[0,0,0]\n\t"
@@ -285,7 +285,7 @@ __device__ __forceinline__ void qk_block(f32x16& s, const i32x8* A, const i32x8*
         : "=&v"(s)
         : "v"(A[0]), "v"(A[1]), "v"(A[2]), "v"(A[3]), "v"(qh[0]), "v"(qh[1]), "v"(qh[2]), "v"(qh[3]), "v"(ql[0]), "v"(ql[1]), "v"(ql[2]), "v"(ql[3]), "v"(ka), "v"(sh), "v"(sl));
   } else if constexpr (NST == 4 && !FIRST) {
-    asm("s_nop 4\n\t"
+    asm volatile("s_nop 4\n\t"
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %5, %0, %13, %14 op_sel_hi:[0,0,0]\n\t"
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %9, %0, %13, %15 op_sel_hi:[0,0,0]\n\t"
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %2, %6, %0, %13, %14 op_sel:[1,1,0] op_sel_hi:[0,0,0]\n\t"
@@ -297,7 +297,7 @@ __device__ __forceinline__ void qk_block(f32x16& s, const i32x8* A, const i32x8*
         : "+v"(s)
         : "v"(A[0]), "v"(A[1]), "v"(A[2]), "v"(A[3]), "v"(qh[0]), "v"(qh[1]), "v"(qh[2]), "v"(qh[3]), "v"(ql[0]), "v"(ql[1]), "v"(ql[2]), "v"(ql[3]), "v"(ka), "v"(sh), "v"(sl));
   } else if constexpr (NST == 2 && FIRST) {
-    asm("s_nop 4\n\t"
+    asm volatile("s_nop 4\n\t"
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %3, 0, %7, %8 op_sel_hi:[0,0,0]\n\t"
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %5, %0, %7, %9 op_sel_hi:[0,0,0]\n\t"
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %2, %4, %0, %7, %8 op_sel:[1,1,0] op_sel_hi:[0,0,0]\n\t"
@@ -305,7 +305,7 @@ __device__ __forceinline__ void qk_block(f32x16& s, const i32x8* A, const i32x8*
         : "=&v"(s)
         : "v"(A[0]), "v"(A[1]), "v"(qh[0]), "v"(qh[1]), "v"(ql[0]), "v"(ql[1]), "v"(ka), "v"(sh), "v"(sl));
   } else if constexpr (NST == 2 && !FIRST) {
-    asm("s_nop 4\n\t"
+    asm volatile("s_nop 4\n\t"
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %3, %0, %7, %8 op_sel_hi:[0,0,0]\n\t"
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %5, %0, %7, %9 op_sel_hi:[0,0,0]\n\t"
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %2, %4, %0, %7, %8 op_sel:[1,1,0] op_sel_hi:[0,0,0]\n\t"
@@ -313,13 +313,13 @@ __device__ __forceinline__ void qk_block(f32x16& s, const i32x8* A, const i32x8*
         : "+v"(s)
         : "v"(A[0]), "v"(A[1]), "v"(qh[0]), "v"(qh[1]), "v"(ql[0]), "v"(ql[1]), "v"(ka), "v"(sh), "v"(sl));
   } else if constexpr (NST == 1 && FIRST) {
-    asm("s_nop 4\n\t"
+    asm volatile("s_nop 4\n\t"
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %4, %5 op_sel_hi:[0,0,0]\n\t"
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %3, %0, %4, %6 op_sel_hi:[0,0,0]"
         : "=&v"(s)
         : "v"(A[0]), "v"(qh[0]), "v"(ql[0]), "v"(ka), "v"(sh), "v"(sl));
   } else if constexpr (NST == 1 && !FIRST) {
-    asm("s_nop 4\n\t"
+    asm volatile("s_nop 4\n\t"
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %4, %5 op_sel_hi:[0,0,0]\n\t"
         "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %3, %0, %4, %6 op_sel_hi:[0,0,0]"
         : "+v"(s)
@@ -439,12 +439,14 @@ __device__ void q_prologue(unsigned char* smem, int t, int pos, const KArgs& a, 
   if ((int)threadIdx.x < D / 4) wload = reinterpret_cast<const float4*>(a.norm_w)[threadIdx.x];
   after_loads();
   rope_table(pos, a, cs, sn);  // overlaps the loads above
-  if ((int)threadIdx.x < D / 4) reinterpret_cast<float4*>(wsh)[threadIdx.x] = wload;
+  // block b of norm_w at 36 * b floats: the 16 lanes of a head read 16 distinct banks
+  if ((int)threadIdx.x < D / 4)
+    *reinterpret_cast<float4*>(wsh + 36 * (threadIdx.x / 8) + 4 * (threadIdx.x % 8)) = wload;
   __syncthreads();  // norm_w and the cos / sin table visible
   float wv[32];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const float4 w4 = reinterpret_cast<const float4*>(wsh)[8 * b + j];
+    const float4 w4 = *reinterpret_cast<const float4*>(wsh + 36 * b + 4 * j);
     wv[4 * j] = w4.x; wv[4 * j + 1] = w4.y; wv[4 * j + 2] = w4.z; wv[4 * j + 3] = w4.w;
   }
 
@@ -729,7 +731,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
     const uint32_t hsel = lhalf ? 0x07050301u : 0x06040200u;
     const int id_cur = valid_id(tile, raw_cur);
     const unsigned long long mask = __ballot(id_cur >= 0);
-    if (tile + 1 < te) issue_tile(valid_id(tile + 1, raw_next), raw_n, sc_n, lane);
+    const int id_next = valid_id(tile + 1, raw_next);
     const int raw_next2 = fetch_id(tile + 2);
 
     // ---- QK^T: partial S^T[32 rows of half qc][32 heads of group qa] over dim half qd
@@ -747,7 +749,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
           A[j] = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         }
         qk_block<C::KSW8, true>(s, A, qf8[0], qf8[1], ksc, qs8[0], qs8[1]);
-        qk_drain(s);
       } else {
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[i] = 0.f;
@@ -836,15 +837,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
       }
     };
 
-    // the two waves of a SIMD run the halves in opposite order: one issues MFMAs while
-    // the other converts
+    // The two waves of a SIMD run the halves in opposite order: one issues MFMAs while
+    // the other converts.  The next tile's DMA goes out between the halves, after the
+    // MFMA chain (qd 0) or the conversion (qd 1) has been issued.
     if (qd == 0) {
       qk();
+      if (tile + 1 < te) issue_tile(id_next, raw_n, sc_n, lane);
       vtrans();
     } else {
       vtrans();
+      if (tile + 1 < te) issue_tile(id_next, raw_n, sc_n, lane);
       qk();
     }
+    if constexpr (EB == 1) qk_drain(s);  // the MFMA chain's results before any read of s
 
     // ---- partial S exchange: the dim-half-1 wave hands its partial to its partner
     float* sx = reinterpret_cast<float*>(smem + C::OFF_SX) + (w & 3) * 1024;
@@ -979,7 +984,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
         for (int i = 0; i < 16; ++i) {
           const int h = 32 * mb + 8 * (i >> 2) + 4 * lhalf + (i & 3);
           const float lt = lsum[h] + lsum[HP + h];
-          const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+          const float inv = lt > 0.f ? __builtin_amdgcn_rcpf(lt) : 0.f;
 #pragma unroll
           for (int nb = 0; nb < C::NB; ++nb) o_l[h * C::OS + d0 + 32 * nb + lrow] = acc[mb][nb][i] * inv;
         }
