@@ -791,17 +791,25 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
           pk[k][6] = cvt_lo(rw[k].w, sc); pk[k][7] = cvt_hi(rw[k].w, sc);
         }
         // dim n = 16c + e: swz(n) = (e & 7) ^ (e >> 3) ^ K0 with K0 = (2c ^ (c >> 2)) & 7,
-        // so the 16-byte slot is (q ^ K0) ^ E(e), E(e) = (e & 7) ^ (e >> 3)
-        const int q0 = q ^ ((2 * c ^ (c >> 2)) & 7);
-        unsigned char* wbase = vt_l + 2048 * c + 8 * p;
+        // so the 16-byte slot is (q ^ K0) ^ E(e), E(e) = (e & 7) ^ (e >> 3).  In write
+        // step e, lanes with f = 1 (8-lane groups 2, 3 of each half wave) write element
+        // e ^ 1 instead: dim rows of both parities are written at once, so a half wave's
+        // 256 bytes cover all 64 banks.  (f only flips bit 0 of the element: the register
+        // pair e >> 1 stays the same, the byte selector and the row change.)
+        const int f = (g8 >> 1) & 1;
+        const int q0 = q ^ ((2 * c ^ (c >> 2)) & 7) ^ f;
+        const uint32_t sel_even = f ? 0x07060302u : 0x05040100u;  // element e ^ f, e even
+        const uint32_t sel_odd = f ? 0x05040100u : 0x07060302u;   // e odd
+        unsigned char* wb_even = vt_l + 2048 * c + 8 * p + 128 * f;   // row 16c + (e ^ f)
+        unsigned char* wb_odd = vt_l + 2048 * c + 8 * p - 128 * f;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int k = e >> 1;
-          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+          const uint32_t sel = (e & 1) ? sel_odd : sel_even;
           const uint2 o = make_uint2(__builtin_amdgcn_perm(pk[1][k], pk[0][k], sel),
                                      __builtin_amdgcn_perm(pk[3][k], pk[2][k], sel));
           const int E = (e & 7) ^ (e >> 3);
-          *reinterpret_cast<uint2*>(wbase + 128 * e + 16 * (q0 ^ E)) = o;
+          *reinterpret_cast<uint2*>(((e & 1) ? wb_odd : wb_even) + 128 * e + 16 * (q0 ^ E)) = o;
         }
       } else {
 #pragma unroll
