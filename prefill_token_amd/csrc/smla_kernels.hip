@@ -78,6 +78,7 @@ constexpr int align16(int x) { return (x + 15) & ~15; }
 
 template <int D, int EB>  // EB: pool element bytes (1 = E4M3 + UE8M0 scales, 2 = bf16)
 struct Cfg {
+  static constexpr int kD = D, kEB = EB;
   static constexpr int RB = D * EB;     // bytes per pool row
   static constexpr int NCH = RB / 16;   // 16-byte chunks per row
   static constexpr int CE = 16 / EB;    // elements per chunk
@@ -415,10 +416,10 @@ __device__ __forceinline__ void rope_table(int pos, const KArgs& a, float* cs, f
 // dims stage them, every thread rotates four (dim, dim + r/2) pairs, and the lanes read
 // their rotated dims back.  The q tile goes to OFF_Q.  Also fills the cos / sin table,
 // and calls after_loads() (every thread, once) as soon as the q loads are in flight.
-template <int D, int EB, class Hook>
+template <class C, class Hook>
 __device__ void q_prologue(unsigned char* smem, int t, int pos, const KArgs& a, float* cs, float* sn,
                            float* ystage, Hook&& after_loads) {
-  using C = Cfg<D, EB>;
+  constexpr int D = C::kD, EB = C::kEB;
   constexpr int NBK = D / 32;                           // lanes per head
   constexpr int NU = HP * NBK;                          // units
   constexpr int NIT = (NU + NTHREADS - 1) / NTHREADS;   // units per thread
@@ -669,7 +670,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
   // the rotary staging sits above the raw tiles when it fits below norm_w
   const bool early = C::RAW_END + HP * (a.rope_dim + 4) * 4 <= C::OFF_W;
   float* ystage = reinterpret_cast<float*>(smem + (early ? C::RAW_END : 0));
-  q_prologue<D, EB>(smem, t, pos, a, cs, sn, ystage, [&]() {
+  q_prologue<C>(smem, t, pos, a, cs, sn, ystage, [&]() {
     if (early && tb < te) issue_tile(valid_id(tb, raw_cur), smem + C::OFF_RAW0, smem + C::OFF_SC0, lane);
   });
   __syncthreads();
@@ -1022,6 +1023,487 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Warp-specialized kernel for d = 512 with the E4M3 pool (the production shape).
+//
+// The eight waves split into two roles, one wave of each per SIMD:
+//   QK waves (w = 0..3, head group qa = w & 1, row half qc = w >> 1) hold q for their
+//     32 heads over all 512 dims in VGPRs and compute S^T[32 rows][32 heads] of a tile
+//     with 16 scaled E4M3 MFMAs, then the softmax of that block.
+//   P.V waves (w = 4..7) own output dims [128v, 128v + 128) for all 64 heads and a
+//     private bf16 V tile Vt[128 dims][64 slots].  In each k-step of 16 slots they read P
+//     and Vt for the previous tile, issue its 8 MFMAs and then dequantize the same 16
+//     slots of the current tile into Vt (the reads of the k-step are complete by then),
+//     so their conversion work runs under their own and the QK wave's MFMAs.
+// Iteration i: QK waves compute S and P of tile i, P.V waves P.V of tile i - 1 and the V
+// tile of tile i; one barrier per iteration.  The softmax is taken against the running
+// max of the previous tiles: a QK wave flags its head group when its block max exceeds
+// that max by more than 2^8.  The flags are read after the barrier; if any is set
+// (always on the first tile), the QK waves merge the block maxima of both row halves,
+// raise the running max, rewrite P from the scores they still hold and publish the
+// accumulator rescale, and a second barrier lets the P.V waves go on.  The running max
+// is therefore the same lazily raised max as in the generic kernel.
+struct WsCfg {
+  static constexpr int kD = 512, kEB = 1;
+  static constexpr int D = kD;
+  static constexpr int RB = D, NCH = D / 16, NSB = D / 32, G = 1024 / RB;
+  static constexpr int GS = 1024 + 16 * G;
+  static constexpr int RAW_BYTES = (T / G) * GS;
+  static constexpr int SC_BYTES = T * NSB;
+  static constexpr int VW = 128;                    // dims per P.V wave
+  static constexpr int VTW_BYTES = VW * T * 2;      // one P.V wave's Vt
+  static constexpr int P_BYTES = HP * T * 2;
+  static constexpr int OFF_RAW0 = 0;
+  static constexpr int OFF_RAW1 = RAW_BYTES;
+  static constexpr int OFF_SC0 = 2 * RAW_BYTES;
+  static constexpr int OFF_SC1 = OFF_SC0 + SC_BYTES;
+  static constexpr int OFF_VT = align16(OFF_SC1 + SC_BYTES);
+  static constexpr int OFF_P0 = OFF_VT + 4 * VTW_BYTES;
+  static constexpr int OFF_P1 = OFF_P0 + P_BYTES;
+  static constexpr int LOOP_END = OFF_P1 + P_BYTES;
+  // prologue: the q tile (two E4M3 terms + UE8M0) over the Vt / P area, norm_w after it;
+  // the rotary staging in the second raw tile while the first one's DMA lands
+  static constexpr int QS8 = D + 16;
+  static constexpr int OFF_QSC = 2 * HP * QS8;
+  static constexpr int QS = D + 8;
+  static constexpr int Q_BYTES = OFF_QSC + 2 * HP * NSB;
+  static constexpr int OFF_Q = OFF_VT;
+  static constexpr int OFF_W = OFF_Q + align16(Q_BYTES);
+  static constexpr int OS = D + 4;
+  static constexpr int O_BYTES = HP * OS * 4;
+  static constexpr int BIG = align16(cmax(LOOP_END, cmax(OFF_W + NSB * 36 * 4, O_BYTES)));
+  // small area: block maxima [2 tiles][2 row halves][HP], alpha [HP], lsum [2][HP],
+  // flags (overflow [2 tiles][4 QK waves], rescale [2 head groups]), cos, sin
+  static constexpr int OFF_MAXX = BIG;
+  static constexpr int OFF_ALPHA = OFF_MAXX + 4 * HP * 4;
+  static constexpr int OFF_LSUM = OFF_ALPHA + HP * 4;
+  static constexpr int OFF_FLAG = OFF_LSUM + 2 * HP * 4;
+  static constexpr int OFF_COS = OFF_FLAG + 64;
+  static constexpr int OFF_SIN = OFF_COS + (D / 2) * 4;
+  static constexpr int SMEM = OFF_SIN + (D / 2) * 4;
+  static_assert(G == 2 && NSB == 16, "layout written for 512-byte rows");
+  static_assert(SMEM <= 160 * 1024, "LDS budget");
+  static_assert(HP * (D + 4) * 4 <= OFF_W, "rotary staging at offset 0 stays below norm_w");
+};
+
+__global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
+  using C = WsCfg;
+  constexpr int D = C::D;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM];
+  float* maxx = reinterpret_cast<float*>(smem + C::OFF_MAXX);
+  float* alpha_l = reinterpret_cast<float*>(smem + C::OFF_ALPHA);
+  int* flag_l = reinterpret_cast<int*>(smem + C::OFF_FLAG);
+  float* lsum = reinterpret_cast<float*>(smem + C::OFF_LSUM);
+  float* cs = reinterpret_cast<float*>(smem + C::OFF_COS);
+  float* sn = reinterpret_cast<float*>(smem + C::OFF_SIN);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  const int ns = a.num_splits;
+  const int t = blockIdx.x / ns, split = blockIdx.x % ns;
+  const int pos = a.positions[t];
+
+  const int lraw = a.topk_length[t];
+  const int lcap = lraw < 0 ? 0 : (lraw > a.topk ? a.topk : lraw);
+  const int ntile = (lcap + T - 1) / T;
+  const int tb = split * a.tiles_per_split;
+  const int te_raw = tb + a.tiles_per_split;
+  const int te = te_raw < ntile ? te_raw : ntile;
+  const int n = te > tb ? te - tb : 0;
+  const int32_t* idx_t = a.indices + (size_t)t * a.topk;
+
+  auto fetch_id = [&](int tile) -> int {
+    const int j = tile * T + lane;
+    return a.topk > 0 ? idx_t[j < a.topk ? j : a.topk - 1] : -1;
+  };
+  auto valid_id = [&](int tile, int raw) -> int {
+    const int j = tile * T + lane;
+    return (tile < te && j < lcap && raw >= 0 && (long long)raw < a.n_rows) ? raw : -1;
+  };
+  const __amdgpu_buffer_rsrc_t pool_rs = buf_rsrc(a.pool, (uint32_t)(a.n_rows * C::RB));
+  const __amdgpu_buffer_rsrc_t scale_rs = buf_rsrc(a.scales, (uint32_t)(a.n_rows * C::NSB));
+  // One part of the LDS DMA of a tile: part k < 4 moves DMA group 4w + k (two rows, one
+  // 1 KB instruction; the rows' ids come from two lanes by readlane), part 4 the scale
+  // rows of 16 ids (waves 0-3, one shuffle).  Rows that are not read come in as zeros.
+  constexpr int GPW = (T / C::G) / NWAVES;
+  static_assert(GPW == 4, "four row DMAs per wave");
+  auto dma_part = [&](int k, int id_vec, unsigned char* raw, unsigned char* sc, int lane) {
+    if (k < GPW) {
+      const int gi = GPW * w + k;
+      const int i0 = __builtin_amdgcn_readlane(id_vec, 2 * gi), i1 = __builtin_amdgcn_readlane(id_vec, 2 * gi + 1);
+      const int id = (lane & 1) ? i1 : i0;
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(raw + gi * C::GS));
+      dma16(id >= 0 ? (uint32_t)id * C::RB + 16 * (lane >> 1) : kNoRow, pool_rs, dst);
+    } else if (w < C::NSB / 4) {
+      constexpr int WPR = C::NSB / 4;
+      const int f = 64 * w + lane;
+      const int id = __shfl(id_vec, (f / WPR) & 63);
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(sc + 256 * w));
+      dma4(id >= 0 ? (uint32_t)id * C::NSB + 4 * (f % WPR) : kNoRow, scale_rs, dst);
+    }
+  };
+  auto issue_tile = [&](int id_vec, unsigned char* raw, unsigned char* sc, int lane) {
+#pragma unroll
+    for (int k = 0; k <= GPW; ++k) dma_part(k, id_vec, raw, sc, lane);
+  };
+  auto raw_buf = [&](int i) { return smem + ((i & 1) ? C::OFF_RAW1 : C::OFF_RAW0); };
+  auto sc_buf = [&](int i) { return smem + ((i & 1) ? C::OFF_SC1 : C::OFF_SC0); };
+  auto p_buf = [&](int i) { return smem + ((i & 1) ? C::OFF_P1 : C::OFF_P0); };
+
+  // ---------------- prologue (all waves)
+  int raw_cur = fetch_id(tb);
+  int raw_next = fetch_id(tb + 1);
+  const bool early = HP * (a.rope_dim + 4) * 4 <= C::RAW_BYTES;
+  float* ystage = reinterpret_cast<float*>(smem + (early ? C::OFF_RAW1 : 0));
+  q_prologue<C>(smem, t, pos, a, cs, sn, ystage, [&]() {
+    if (early && n > 0) issue_tile(valid_id(tb, raw_cur), raw_buf(0), sc_buf(0), lane);
+  });
+  __syncthreads();  // q tile complete
+  if (!early && n > 0) issue_tile(valid_id(tb, raw_cur), raw_buf(0), sc_buf(0), lane);
+
+  f32x16 acc[2][4];   // P.V waves: O[64 heads][128 dims]
+  float m_run = -INFINITY, l_run = 0.f;  // QK waves: per head (lane & 31 of group qa)
+
+  if (w < 4) {
+    // =============================== QK waves
+    const int qa = w & 1, qc = w >> 1;
+    const uint32_t hsel = lhalf ? 0x07050301u : 0x06040200u;
+    // q of the 32 heads of group qa, all 8 k-steps: lane half h holds dims 64ks + 16h +
+    // [0,16) and 64ks + 32 + 16h + [0,16); byte j of qs[term][k] scales k-step 4k + j
+    i32x8 qf[2][8];
+    uint32_t qs[2][2];
+#pragma unroll
+    for (int term = 0; term < 2; ++term) {
+      const unsigned char* qrow = smem + C::OFF_Q + (term * HP + 32 * qa + lrow) * C::QS8 + 16 * lhalf;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(qrow + 64 * ks);
+        const uint4 hi = *reinterpret_cast<const uint4*>(qrow + 64 * ks + 32);
+        qf[term][ks] = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+      const unsigned char* qsr = smem + C::OFF_Q + C::OFF_QSC + (term * HP + 32 * qa + lrow) * C::NSB;
+      qs[term][0] = scale_word<C>(qsr, 0, hsel);
+      qs[term][1] = scale_word<C>(qsr, 1, hsel);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's share of the first tile landed
+    __syncthreads();  // B0: q tile read (the P.V waves overwrite it), first tile visible
+
+    f32x16 s;          // scores of the last tile, kept for a rewrite of its P
+    float l_pend = 0.f;
+    for (int it = 0; it <= n; ++it) {
+      const int tile = tb + it;
+      const int lane = ((int)threadIdx.x + opaque_zero()) & 63, lrow = lane & 31, lhalf = lane >> 5;
+      const int head = 32 * qa + lrow;
+      const bool do_qk = it < n;
+      // K rows of this tile first: their latency covers the flag check below
+      const int r = 32 * qc + lrow;
+      i32x8 A[8];
+      uint32_t ksc0 = 0, ksc1 = 0;
+      if (do_qk) {
+        const unsigned char* raw_l = raw_buf(it);
+        const unsigned char* sc_l = sc_buf(it);
+        const uint32_t hsel = lhalf ? 0x07050301u : 0x06040200u;
+        ksc0 = scale_word<C>(sc_l + r * C::NSB, 0, hsel);
+        ksc1 = scale_word<C>(sc_l + r * C::NSB, 1, hsel);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const uint4 lo = *reinterpret_cast<const uint4*>(raw_l + raw_off<C>(r, 4 * ks + lhalf));
+          const uint4 hi = *reinterpret_cast<const uint4*>(raw_l + raw_off<C>(r, 4 * ks + 2 + lhalf));
+          A[ks] = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+      }
+      if (it > 0) {
+        const int4 fl = *reinterpret_cast<const int4*>(flag_l + 4 * ((it - 1) & 1));
+        if (__builtin_amdgcn_readfirstlane(fl.x | fl.y | fl.z | fl.w)) {
+          // slow path for tile it - 1: merge the block maxima, raise the running max
+          const float* mx = maxx + 2 * HP * ((it - 1) & 1);
+          const float mt = fmaxf(mx[head], mx[HP + head]);
+          float mnew = m_run;
+          if (mt > -INFINITY && (m_run == -INFINITY || mt > m_run + 8.0f)) mnew = mt;
+          const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mnew);
+          const bool raised = __any(m_run != -INFINITY && mnew != m_run);
+          m_run = mnew;
+          const float msafe = (mnew == -INFINITY) ? 0.f : mnew;
+          float p[16];
+          float lp = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            p[i] = __builtin_amdgcn_exp2f(s[i] - msafe);
+            lp += p[i];
+          }
+          l_run = l_run * alpha + lp;
+          unsigned char* prow = p_buf(it - 1) + head * 128;
+          const int sw = swz(head);
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<uint2*>(prow + 16 * ((4 * qc + g) ^ sw) + 8 * lhalf) =
+                make_uint2(pack_bf16(p[4 * g], p[4 * g + 1]), pack_bf16(p[4 * g + 2], p[4 * g + 3]));
+          if (qc == 0 && lhalf == 0) alpha_l[head] = alpha;
+          if (qc == 0 && lane == 0) flag_l[8 + qa] = raised ? 1 : 0;
+          __syncthreads();  // B': P and alpha rewritten
+        } else {
+          l_run += l_pend;
+        }
+      }
+      const int id_cur = valid_id(tile, raw_cur);
+      const unsigned long long mask = __ballot(id_cur >= 0);
+      const int id_next = valid_id(tile + 1, raw_next);
+      const int raw_next2 = fetch_id(tile + 2);
+
+      if (do_qk) {
+        qk_block<4, true>(s, A, qf[0], qf[1], ksc0, qs[0][0], qs[1][0]);
+        qk_block<4, false>(s, A + 4, qf[0] + 4, qf[1] + 4, ksc1, qs[0][1], qs[1][1]);
+      }
+      // the next tile's DMA goes out while the MFMA chain runs
+      if (it + 1 < n) issue_tile(id_next, raw_buf(it + 1), sc_buf(it + 1), lane);
+      if (do_qk) {
+        qk_drain(s);
+        // mask (row 32qc + 8g + 4h + j holds value 4g + j), block max over the 32 rows
+        const uint32_t mw = (uint32_t)(mask >> (32 * qc));
+        float lm = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int rr = 8 * (i >> 2) + (i & 3);
+          const unsigned long long lmk = (((mw >> rr) & 1u) ? 0x00000000FFFFFFFFull : 0ull) |
+                                         (((mw >> (rr + 4)) & 1u) ? 0xFFFFFFFF00000000ull : 0ull);
+          s[i] = __builtin_amdgcn_inverse_ballot_w64(lmk) ? s[i] : -INFINITY;
+          lm = fmaxf(lm, s[i]);
+        }
+        lm = fmaxf(lm, __shfl_xor(lm, 32));
+        // P against the running max; exact unless the flag below sends the tile to the
+        // slow path, which rewrites it
+        const float msafe = (m_run == -INFINITY) ? 0.f : m_run;
+        float p[16];
+        float lp = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          p[i] = __builtin_amdgcn_exp2f(s[i] - msafe);
+          lp += p[i];
+        }
+        l_pend = lp;
+        unsigned char* prow = p_buf(it) + head * 128;
+        const int sw = swz(head);
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<uint2*>(prow + 16 * ((4 * qc + g) ^ sw) + 8 * lhalf) =
+              make_uint2(pack_bf16(p[4 * g], p[4 * g + 1]), pack_bf16(p[4 * g + 2], p[4 * g + 3]));
+        if (lhalf == 0) maxx[2 * HP * (it & 1) + qc * HP + head] = lm;
+        const bool over = __any(lm > m_run + 8.0f);
+        if (lane == 0) flag_l[4 * (it & 1) + w] = over ? 1 : 0;
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile's DMA from this wave landed
+      raw_cur = raw_next;
+      raw_next = raw_next2;
+      __syncthreads();  // end of iteration
+    }
+  } else {
+    // =============================== P.V waves
+    const int v = w - 4;
+    unsigned char* vt = smem + C::OFF_VT + v * C::VTW_BYTES;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();  // B0
+
+    // one iteration: P.V of tile it - 1 (PV) and / or the V tile of tile it (VT)
+    auto pv_iter = [&](const int it, auto pv_c, auto vt_c) __attribute__((always_inline)) {
+      const int tile = tb + it;
+      const int lane = ((int)threadIdx.x + opaque_zero()) & 63, lrow = lane & 31, lhalf = lane >> 5;
+      const unsigned char* p_l = p_buf(it - 1);
+      const unsigned char* raw_l = raw_buf(it);
+      const unsigned char* sc_l = sc_buf(it);
+      // Address bases.  Row n of Vt (dim) or P (head) is 128 bytes, its 16-byte chunk ch
+      // stored at chunk ch ^ swz(n).  For the P.V reads n = 32b + lrow (b = n-block or
+      // m-block) and ch = 2ks + lhalf, so the stored chunk is nu ^ (2ks ^ kb(b)) with the
+      // lane part nu = swz(lrow) ^ lhalf and kb(b) = 4(b & 1) ^ (b >> 1): eight lane offsets
+      // rd[c] = 128 lrow + 16 (nu ^ c) cover every read, the rest is an immediate.
+      const int nu = (lrow & 7) ^ (lrow >> 3) ^ lhalf;
+      uint32_t rd[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) rd[c] = 128 * lrow + 16 * (nu ^ c);
+      // V tile roles: lane = 8c' + j converts rows 16ks + 2j, 16ks + 2j + 1 (one DMA group,
+      // adjacent 16-byte pieces) of chunk 8v + c' (tile dims 16c' .. 16c' + 15 of this
+      // wave).  Dim n = 16c' + e takes the two slots at chunk 2ks + (j >> 2) of its row,
+      // stored at chunk lam ^ (2ks ^ E(e)) with lam = K0(c') ^ (j >> 2), K0(c') = (2c' ^
+      // (c' >> 2)) & 7, E(e) = (e & 7) ^ (e >> 3): lane offsets wr0 + 16 (lam ^ c), plus 128 e.
+      const int j = lane & 7, cl = lane >> 3;
+      const int lam = ((2 * cl) ^ (cl >> 2) ^ (j >> 2)) & 7;
+      const uint32_t wr0 = 2048 * cl + 4 * (j & 3);
+      const uint32_t rsrc = (uint32_t)(j * C::GS + 32 * cl);  // + group 8ks, + chunk 8v
+      const uint32_t ssrc = (uint32_t)(32 * j);               // + 256 ks + 4v
+      const int raw_next2 = fetch_id(tile + 2);
+      bf16x8 Ap[2], Bv[4];
+      uint4 ra[2], rb[2];
+      uint32_t wa[2], wb[2];
+      auto load_p = [&](int ks) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          Ap[mb] = *reinterpret_cast<const bf16x8*>(p_l + 4096 * mb + rd[(2 * ks) ^ (4 * mb)]);
+      };
+      auto load_v = [&](int ks) {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          Bv[nb] = *reinterpret_cast<const bf16x8*>(vt + 4096 * nb + rd[(2 * ks) ^ (4 * (nb & 1)) ^ (nb >> 1)]);
+      };
+      auto load_vt = [&](int ks, int u) {
+        const unsigned char* src = raw_l + rsrc + 8 * ks * C::GS + 256 * v;
+        ra[u] = *reinterpret_cast<const uint4*>(src);
+        rb[u] = *reinterpret_cast<const uint4*>(src + 16);
+        const unsigned char* ssp = sc_l + ssrc + 256 * ks + 4 * v;
+        wa[u] = *reinterpret_cast<const uint32_t*>(ssp);
+        wb[u] = *reinterpret_cast<const uint32_t*>(ssp + C::NSB);
+      };
+      constexpr bool PV = decltype(pv_c)::value, VT = decltype(vt_c)::value;
+      {
+        // first k-step's operands before the flag check (P is read again if the slow
+        // path rewrites it)
+        if constexpr (PV) {
+          load_p(0);
+          load_v(0);
+        }
+        if constexpr (VT) load_vt(0, 0);
+        if constexpr (PV) {
+          const int4 fl = *reinterpret_cast<const int4*>(flag_l + 4 * ((it - 1) & 1));
+          if (__builtin_amdgcn_readfirstlane(fl.x | fl.y | fl.z | fl.w)) {
+            __syncthreads();  // B': P and alpha rewritten
+            load_p(0);
+            const int2 rf = *reinterpret_cast<const int2*>(flag_l + 8);
+            if (__builtin_amdgcn_readfirstlane(rf.x | rf.y)) {
+#pragma unroll
+              for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                  const float4 v4 = *reinterpret_cast<const float4*>(alpha_l + 32 * mb + 8 * g + 4 * lhalf);
+#pragma unroll
+                  for (int nb = 0; nb < 4; ++nb) {
+                    acc[mb][nb][4 * g + 0] *= v4.x;
+                    acc[mb][nb][4 * g + 1] *= v4.y;
+                    acc[mb][nb][4 * g + 2] *= v4.z;
+                    acc[mb][nb][4 * g + 3] *= v4.w;
+                  }
+                }
+            }
+          }
+        }
+        const int id_next = valid_id(tile + 1, raw_next);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int u = ks & 1;
+          // one of this wave's row DMAs for the next tile per k-step (zero rows past the
+          // end of the range)
+          if constexpr (VT) dma_part(ks, id_next, raw_buf(it + 1), sc_buf(it + 1), lane);
+          if (VT && ks + 1 < 4) load_vt(ks + 1, u ^ 1);
+          if constexpr (PV) {
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+              for (int mb = 0; mb < 2; ++mb)
+                acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ap[mb], Bv[nb], acc[mb][nb], 0, 0, 0);
+            // next k-step's operands, read while this k-step's MFMAs and conversion run
+            if (ks + 1 < 4) {
+              load_p(ks + 1);
+              load_v(ks + 1);
+            }
+          }
+          if constexpr (VT) {
+            const int bsh = 8 * (cl >> 1);
+            const float sa = ue8m0_f32((wa[u] >> bsh) & 0xFFu), sb = ue8m0_f32((wb[u] >> bsh) & 0xFFu);
+            const uint4 xa = ra[u], xb = rb[u];
+            const uint32_t pa[8] = {cvt_lo(xa.x, sa), cvt_hi(xa.x, sa), cvt_lo(xa.y, sa), cvt_hi(xa.y, sa),
+                                    cvt_lo(xa.z, sa), cvt_hi(xa.z, sa), cvt_lo(xa.w, sa), cvt_hi(xa.w, sa)};
+            const uint32_t pb[8] = {cvt_lo(xb.x, sb), cvt_hi(xb.x, sb), cvt_lo(xb.y, sb), cvt_hi(xb.y, sb),
+                                    cvt_lo(xb.z, sb), cvt_hi(xb.z, sb), cvt_lo(xb.w, sb), cvt_hi(xb.w, sb)};
+            // (the reads of this k-step's slots were issued before: LDS ops of a wave are
+            // processed in order)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int k = e >> 1;
+              const uint32_t val = __builtin_amdgcn_perm(pb[k], pa[k], (e & 1) ? 0x07060302u : 0x05040100u);
+              const int c = (2 * ks) ^ (e & 7) ^ (e >> 3);
+              *reinterpret_cast<uint32_t*>(vt + wr0 + 16 * (lam ^ c) + 128 * e) = val;
+            }
+          }
+          if constexpr (PV && VT) {
+            // spread the conversion and the LDS traffic between the 8 MFMAs
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+              __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+              __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);  // DS write
+            }
+          }
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      raw_cur = raw_next;
+      raw_next = raw_next2;
+      __syncthreads();  // end of iteration
+    };
+    // the first and last iterations are separate straight-line copies
+    if (n == 0) {
+      pv_iter(0, std::false_type{}, std::false_type{});
+    } else {
+      pv_iter(0, std::false_type{}, std::true_type{});
+      for (int it = 1; it < n; ++it) pv_iter(it, std::true_type{}, std::true_type{});
+      pv_iter(n, std::true_type{}, std::false_type{});
+    }
+  }
+
+  // ---------------- finish
+  if (w < 4) {
+    const int qa = w & 1, qc = w >> 1;
+    const float lw = l_run + __shfl_xor(l_run, 32);
+    if (lhalf == 0) lsum[qc * HP + 32 * qa + lrow] = lw;
+    if (qc == 0 && lhalf == 0) maxx[32 * qa + lrow] = m_run;
+  }
+  __syncthreads();
+  if (ns == 1) {
+    float* o_l = reinterpret_cast<float*>(smem);
+    if (w >= 4) {
+      const int d0 = C::VW * (w - 4);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int h = 32 * mb + 8 * (i >> 2) + 4 * lhalf + (i & 3);
+          const float lt = lsum[h] + lsum[HP + h];
+          const float inv = lt > 0.f ? __builtin_amdgcn_rcpf(lt) : 0.f;
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) o_l[h * C::OS + d0 + 32 * nb + lrow] = acc[mb][nb][i] * inv;
+        }
+    }
+    __syncthreads();
+    epilogue<D, NTHREADS>(o_l, C::OS, a.h_q, 0, t, a, cs, sn);
+  } else {
+    float* part = a.ws + ((size_t)t * ns + split) * partial_floats_d(a.h_q, D);
+    float* pm = part + (size_t)a.h_q * D;
+    float* pl = pm + a.h_q;
+    if (tid < a.h_q) {
+      pm[tid] = maxx[tid];
+      pl[tid] = lsum[tid] + lsum[HP + tid];
+    }
+    if (n > 0 && w >= 4) {
+      const int d0 = C::VW * (w - 4);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int h = 32 * mb + 8 * (i >> 2) + 4 * lhalf + (i & 3);
+          if (h < a.h_q) {
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) part[(size_t)h * D + d0 + 32 * nb + lrow] = acc[mb][nb][i];
+          }
+        }
+    }
+  }
+}
+
 // Combine the splits of one (token, head): o = sum_s w_s acc_s / sum_s w_s l_s with
 // w_s = 2^(m_s - M), M = max_s m_s, in split order, then the epilogue.  One memory
 // round trip: every thread issues the loads of its 4 dims for all splits (16 at a
@@ -1089,7 +1571,10 @@ __global__ __launch_bounds__(CTHREADS) void smla_combine(KArgs a) {
 template <int D, int EB>
 hipError_t launch_t(const LaunchArgs& x, const KArgs& k) {
   const int ns = x.num_splits;
-  hipLaunchKernelGGL((smla_main<D, EB>), dim3((unsigned)(x.s_q * ns)), dim3(NTHREADS), 0, x.stream, k);
+  if constexpr (D == 512 && EB == 1)
+    hipLaunchKernelGGL(smla_ws, dim3((unsigned)(x.s_q * ns)), dim3(NTHREADS), 0, x.stream, k);
+  else
+    hipLaunchKernelGGL((smla_main<D, EB>), dim3((unsigned)(x.s_q * ns)), dim3(NTHREADS), 0, x.stream, k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ns == 1) return e;
   hipLaunchKernelGGL((smla_combine<D>), dim3((unsigned)x.s_q, (unsigned)x.h_q), dim3(CTHREADS), 0, x.stream, k);
