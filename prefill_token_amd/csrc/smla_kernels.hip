@@ -1024,17 +1024,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Warp-specialized kernel for d = 512 with the E4M3 pool (the production shape).
+// Persistent warp-specialized kernel for d = 512, rope_dim 0 or 64, E4M3 pool (the
+// production shape).
 //
-// The eight waves split into two roles, one wave of each per SIMD:
+// Each workgroup walks the work items (token, split) blockIdx.x, blockIdx.x + gridDim.x,
+// ...  The eight waves split into two roles, one wave of each per SIMD:
 //   QK waves (w = 0..3, head group qa = w & 1, row half qc = w >> 1) hold q for their
 //     32 heads over all 512 dims in VGPRs and compute S^T[32 rows][32 heads] of a tile
 //     with 16 scaled E4M3 MFMAs, then the softmax of that block.
 //   P.V waves (w = 4..7) own output dims [128v, 128v + 128) for all 64 heads and a
-//     private bf16 V tile Vt[128 dims][64 slots].  In each k-step of 16 slots they read P
-//     and Vt for the previous tile, issue its 8 MFMAs and then dequantize the same 16
-//     slots of the current tile into Vt (the reads of the k-step are complete by then),
-//     so their conversion work runs under their own and the QK wave's MFMAs.
+//     private bf16 V tile Vt[128 dims][64 slots].  In each k-step of 16 slots they issue
+//     the 8 MFMAs of the previous tile and dequantize the same 16 slots of the current
+//     tile into Vt, interleaved so that the conversion runs under the MFMAs.
 // Iteration i: QK waves compute S and P of tile i, P.V waves P.V of tile i - 1 and the V
 // tile of tile i; one barrier per iteration.  The softmax is taken against the running
 // max of the previous tiles: a QK wave flags its head group when its block max exceeds
@@ -1043,6 +1044,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
 // raise the running max, rewrite P from the scores they still hold and publish the
 // accumulator rescale, and a second barrier lets the P.V waves go on.  The running max
 // is therefore the same lazily raised max as in the generic kernel.
+// Between items: the P.V waves run the epilogue of the finished item from registers
+// through a private staging area, while the QK waves issue the next item's first tile DMA
+// and run its q prologue into a q tile over the V-tile area, from which they then load
+// their fragments.
 struct WsCfg {
   static constexpr int kD = 512, kEB = 1;
   static constexpr int D = kD;
@@ -1061,29 +1066,29 @@ struct WsCfg {
   static constexpr int OFF_P0 = OFF_VT + 4 * VTW_BYTES;
   static constexpr int OFF_P1 = OFF_P0 + P_BYTES;
   static constexpr int LOOP_END = OFF_P1 + P_BYTES;
-  // prologue: the q tile (two E4M3 terms + UE8M0) over the Vt / P area, norm_w after it;
-  // the rotary staging in the second raw tile while the first one's DMA lands
-  static constexpr int QS8 = D + 16;
-  static constexpr int OFF_QSC = 2 * HP * QS8;
-  static constexpr int QS = D + 8;
-  static constexpr int Q_BYTES = OFF_QSC + 2 * HP * NSB;
-  static constexpr int OFF_Q = OFF_VT;
-  static constexpr int OFF_W = OFF_Q + align16(Q_BYTES);
-  static constexpr int OS = D + 4;
-  static constexpr int O_BYTES = HP * OS * 4;
-  static constexpr int BIG = align16(cmax(LOOP_END, cmax(OFF_W + NSB * 36 * 4, O_BYTES)));
-  // small area: block maxima [2 tiles][2 row halves][HP], alpha [HP], lsum [2][HP],
-  // flags (overflow [2 tiles][4 QK waves], rescale [2 head groups]), cos, sin
-  static constexpr int OFF_MAXX = BIG;
-  static constexpr int OFF_ALPHA = OFF_MAXX + 4 * HP * 4;
-  static constexpr int OFF_LSUM = OFF_ALPHA + HP * 4;
-  static constexpr int OFF_FLAG = OFF_LSUM + 2 * HP * 4;
-  static constexpr int OFF_COS = OFF_FLAG + 64;
-  static constexpr int OFF_SIN = OFF_COS + (D / 2) * 4;
-  static constexpr int SMEM = OFF_SIN + (D / 2) * 4;
+  // between items: the q tile [2 terms][HP][512 B] (16-byte chunk c of head h stored at
+  // c ^ (h & 15)) over the V tiles, its UE8M0 scales [2][HP][16] in P0, the P.V waves'
+  // epilogue staging (16 heads x 128 dims f32 each, rows padded to 132 floats) in the
+  // second raw tile
+  static constexpr int OFF_QT = OFF_VT;
+  static constexpr int OFF_QSC = OFF_P0;
+  static constexpr int EST_STRIDE = VW + 4;  // floats
+  static constexpr int EST_BYTES = 16 * EST_STRIDE * 4;
+  static constexpr int OFF_EST = OFF_RAW1;
+  // small area
+  static constexpr int OFF_MAXX = LOOP_END;                // [2 tiles][2 row halves][HP]
+  static constexpr int OFF_ALPHA = OFF_MAXX + 4 * HP * 4;  // [HP]
+  static constexpr int OFF_LSUM = OFF_ALPHA + HP * 4;      // [2 row halves][HP]
+  static constexpr int OFF_MFIN = OFF_LSUM + 2 * HP * 4;   // [HP]
+  static constexpr int OFF_FLAG = OFF_MFIN + HP * 4;       // overflow [2 tiles][4], rescale [2]
+  static constexpr int OFF_ROPE = OFF_FLAG + 64;           // per wave: cos[32], -sin[32], sin[32]
+  static constexpr int OFF_NW = OFF_ROPE + NWAVES * 96 * 4; // norm_w, block b at 36 b floats
+  static constexpr int OFF_IFREQ = OFF_NW + (D / 32) * 36 * 4;  // theta^(-2i/r), i < 32, fp64
+  static constexpr int SMEM = OFF_IFREQ + 32 * 8;
   static_assert(G == 2 && NSB == 16, "layout written for 512-byte rows");
   static_assert(SMEM <= 160 * 1024, "LDS budget");
-  static_assert(HP * (D + 4) * 4 <= OFF_W, "rotary staging at offset 0 stays below norm_w");
+  static_assert(2 * HP * 512 <= 4 * VTW_BYTES && 2 * HP * 16 <= P_BYTES && 4 * EST_BYTES <= RAW_BYTES,
+                "item transition areas");
 };
 
 __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
@@ -1094,137 +1099,370 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
   float* alpha_l = reinterpret_cast<float*>(smem + C::OFF_ALPHA);
   int* flag_l = reinterpret_cast<int*>(smem + C::OFF_FLAG);
   float* lsum = reinterpret_cast<float*>(smem + C::OFF_LSUM);
-  float* cs = reinterpret_cast<float*>(smem + C::OFF_COS);
-  float* sn = reinterpret_cast<float*>(smem + C::OFF_SIN);
+  float* mfin = reinterpret_cast<float*>(smem + C::OFF_MFIN);
+  // The kernel arguments used only between items, re-read from the kernarg segment
+  // where they are needed (an opaque pointer), so that they are not held in registers
+  // across the tile loops.
+  auto karg = [&]() -> const __attribute__((address_space(4))) KArgs& {
+    const __attribute__((address_space(4))) KArgs* p =
+        (const __attribute__((address_space(4))) KArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(p));
+    return *p;
+  };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lrow = lane & 31, lhalf = lane >> 5;
   const int ns = a.num_splits;
-  const int t = blockIdx.x / ns, split = blockIdx.x % ns;
-  const int pos = a.positions[t];
+  const int total = a.s_q * ns;
+  const bool rot = a.rope_dim > 0;  // 0 or 64 on this path
+  float* rtab = reinterpret_cast<float*>(smem + C::OFF_ROPE) + 96 * w;  // this wave's table
 
-  const int lraw = a.topk_length[t];
-  const int lcap = lraw < 0 ? 0 : (lraw > a.topk ? a.topk : lraw);
-  const int ntile = (lcap + T - 1) / T;
-  const int tb = split * a.tiles_per_split;
-  const int te_raw = tb + a.tiles_per_split;
-  const int te = te_raw < ntile ? te_raw : ntile;
-  const int n = te > tb ? te - tb : 0;
-  const int32_t* idx_t = a.indices + (size_t)t * a.topk;
-
-  auto fetch_id = [&](int tile) -> int {
-    const int j = tile * T + lane;
-    return a.topk > 0 ? idx_t[j < a.topk ? j : a.topk - 1] : -1;
+  struct Item {
+    int t, pos, lcap, tb, te, n;
   };
-  auto valid_id = [&](int tile, int raw) -> int {
-    const int j = tile * T + lane;
-    return (tile < te && j < lcap && raw >= 0 && (long long)raw < a.n_rows) ? raw : -1;
+  auto info = [&](int item) {
+    Item I;
+    I.t = item / ns;
+    const int split = item % ns;
+    I.pos = a.positions[I.t];
+    const int lraw = a.topk_length[I.t];
+    I.lcap = lraw < 0 ? 0 : (lraw > a.topk ? a.topk : lraw);
+    const int ntile = (I.lcap + T - 1) / T;
+    I.tb = split * a.tiles_per_split;
+    const int te_raw = I.tb + a.tiles_per_split;
+    I.te = te_raw < ntile ? te_raw : ntile;
+    I.n = I.te > I.tb ? I.te - I.tb : 0;
+    return I;
+  };
+  // Index entry tile*64 + lane, fetched before it is used (clamped into the row); its
+  // value is only looked at after a vmcnt(0) wait of the tile loop.
+  auto fetch_id = [&](const Item& I, int tile) -> int {
+    const int j = tile * T + (((int)threadIdx.x + opaque_zero()) & 63);
+    return a.topk > 0 ? a.indices[(size_t)I.t * a.topk + (j < a.topk ? j : a.topk - 1)] : -1;
+  };
+  // the id if entry tile*64 + lane is read, else -1 (beyond the length, a sentinel, or
+  // outside [0, n_rows))
+  auto valid_id = [&](const Item& I, int tile, int raw) -> int {
+    const int j = tile * T + (((int)threadIdx.x + opaque_zero()) & 63);
+    return (tile < I.te && j < I.lcap && raw >= 0 && (long long)raw < a.n_rows) ? raw : -1;
   };
   const __amdgpu_buffer_rsrc_t pool_rs = buf_rsrc(a.pool, (uint32_t)(a.n_rows * C::RB));
   const __amdgpu_buffer_rsrc_t scale_rs = buf_rsrc(a.scales, (uint32_t)(a.n_rows * C::NSB));
-  // One part of the LDS DMA of a tile: part k < 4 moves DMA group 4w + k (two rows, one
-  // 1 KB instruction; the rows' ids come from two lanes by readlane), part 4 the scale
-  // rows of 16 ids (waves 0-3, one shuffle).  Rows that are not read come in as zeros.
-  constexpr int GPW = (T / C::G) / NWAVES;
-  static_assert(GPW == 4, "four row DMAs per wave");
-  auto dma_part = [&](int k, int id_vec, unsigned char* raw, unsigned char* sc, int lane) {
-    if (k < GPW) {
-      const int gi = GPW * w + k;
+  // One part of the LDS DMA of a tile, as if issued by wave vw: part k < 4 moves DMA group
+  // 4vw + k (two rows, one 1 KB instruction; the rows' ids come from two lanes by
+  // readlane), part 4 the scale rows of 16 ids (vw < 4, one shuffle).  Rows that are not
+  // read come in as zeros.
+  auto dma_part = [&](int k, int vw, int id_vec, unsigned char* raw, unsigned char* sc) {
+    const int lane = ((int)threadIdx.x + opaque_zero()) & 63;
+    if (k < 4) {
+      const int gi = 4 * vw + k;
       const int i0 = __builtin_amdgcn_readlane(id_vec, 2 * gi), i1 = __builtin_amdgcn_readlane(id_vec, 2 * gi + 1);
       const int id = (lane & 1) ? i1 : i0;
       const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(raw + gi * C::GS));
       dma16(id >= 0 ? (uint32_t)id * C::RB + 16 * (lane >> 1) : kNoRow, pool_rs, dst);
-    } else if (w < C::NSB / 4) {
-      constexpr int WPR = C::NSB / 4;
-      const int f = 64 * w + lane;
-      const int id = __shfl(id_vec, (f / WPR) & 63);
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(sc + 256 * w));
-      dma4(id >= 0 ? (uint32_t)id * C::NSB + 4 * (f % WPR) : kNoRow, scale_rs, dst);
+    } else {
+      const int f = 64 * vw + lane;
+      const int id = __shfl(id_vec, (f / 4) & 63);
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(sc + 256 * vw));
+      dma4(id >= 0 ? (uint32_t)id * C::NSB + 4 * (f % 4) : kNoRow, scale_rs, dst);
     }
-  };
-  auto issue_tile = [&](int id_vec, unsigned char* raw, unsigned char* sc, int lane) {
-#pragma unroll
-    for (int k = 0; k <= GPW; ++k) dma_part(k, id_vec, raw, sc, lane);
   };
   auto raw_buf = [&](int i) { return smem + ((i & 1) ? C::OFF_RAW1 : C::OFF_RAW0); };
   auto sc_buf = [&](int i) { return smem + ((i & 1) ? C::OFF_SC1 : C::OFF_SC0); };
   auto p_buf = [&](int i) { return smem + ((i & 1) ? C::OFF_P1 : C::OFF_P0); };
 
-  // ---------------- prologue (all waves)
-  int raw_cur = fetch_id(tb);
-  int raw_next = fetch_id(tb + 1);
-  const bool early = HP * (a.rope_dim + 4) * 4 <= C::RAW_BYTES;
-  float* ystage = reinterpret_cast<float*>(smem + (early ? C::OFF_RAW1 : 0));
-  q_prologue<C>(smem, t, pos, a, cs, sn, ystage, [&]() {
-    if (early && n > 0) issue_tile(valid_id(tb, raw_cur), raw_buf(0), sc_buf(0), lane);
-  });
-  __syncthreads();  // q tile complete
-  if (!early && n > 0) issue_tile(valid_id(tb, raw_cur), raw_buf(0), sc_buf(0), lane);
+  // ---------------- q prologue of an item (QK waves, in two steps)
+  // Thread tid < 256 handles block b = tid & 15 (32 dims) of heads (tid >> 4) + 16k,
+  // k = 0..3: a row of 16 lanes holds one head, whose sum of squares is reduced with DPP.
+  auto q_load = [&](const Item& I, uint4 (&x)[4][4]) {
+    // lane-dependent values are recomputed in each phase (opaque_zero) instead of being
+    // hoisted out of the item loop and kept live across it
+    const int tid = (int)threadIdx.x + opaque_zero(), qb = tid & 15;
+    const auto& K = karg();
+    const uint16_t* qp = K.q;
+    const int hq = K.h_q;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int head = (tid >> 4) + 16 * k;
+      const uint4* src = reinterpret_cast<const uint4*>(qp + ((size_t)I.t * hq + head) * D + 32 * qb);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[k][j] = head < hq ? src[j] : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  // cos / sin of angle pos * theta^(-2i/64), i < 32: the angle in fp64 (the inverse
+  // frequencies are computed once per workgroup), reduced to [-pi, pi] (Cody-Waite with a
+  // two-part 2*pi), then the hardware sine / cosine of the reduced angle in revolutions;
+  // lane i of every wave computes entry i of the wave's own table (cos, -sin, sin).
+  const double* ifreq = reinterpret_cast<const double*>(smem + C::OFF_IFREQ);
+  auto rope_tab = [&](const Item& I) {
+    const int lane = ((int)threadIdx.x + opaque_zero()) & 63;
+    if (rot && lane < 32) {
+      constexpr double kInv2Pi = 0.15915494309189535, k2PiHi = 6.283185307179586, k2PiLo = 2.4492935982947064e-16;
+      const double ang = (double)I.pos * ifreq[lane];
+      const double nn = rint(ang * kInv2Pi);
+      const double r = fma(-nn, k2PiLo, fma(-nn, k2PiHi, ang));
+      const float rev = (float)(r * kInv2Pi);  // in [-1/2, 1/2]
+      const float sv = __builtin_amdgcn_sinf(rev), cv = __builtin_amdgcn_cosf(rev);
+      rtab[lane] = cv;
+      rtab[32 + lane] = -sv;
+      rtab[64 + lane] = sv;
+    }
+  };
+  // RMSNorm (f32), times sm_scale * log2(e) (the scores come out ready for exp2), RoPE on
+  // dims 448..511 (blocks 14 and 15 swap values through DPP), then two E4M3 terms with
+  // their own UE8M0 scales per block into the q tile
+  auto q_units = [&](const uint4 (&x)[4][4]) {
+    const int tid = (int)threadIdx.x + opaque_zero(), qb = tid & 15;
+    const auto& K = karg();
+    const float qscale = K.sm_scale * 1.4426950408889634f, eps = K.rms_eps;
+    float wv[32];
+    const float* nw = reinterpret_cast<const float*>(smem + C::OFF_NW) + 36 * qb;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float4 w4 = *reinterpret_cast<const float4*>(nw + 4 * j);
+      wv[4 * j] = w4.x; wv[4 * j + 1] = w4.y; wv[4 * j + 2] = w4.z; wv[4 * j + 3] = w4.w;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int head = (tid >> 4) + 16 * k;
+      float y[32];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t uu[4] = {x[k][j].x, x[k][j].y, x[k][j].z, x[k][j].w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          y[8 * j + 2 * m] = bf16_f32(uu[m] & 0xFFFFu);
+          y[8 * j + 2 * m + 1] = bf16_f32(uu[m] >> 16);
+        }
+      }
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) ss += y[e] * y[e];
+      // lane pairs i^1, i^2, then i <-> 7-i, i <-> 15-i: every lane of the row ends with
+      // the same sum
+      ss += dpp_f32<0xB1>(ss);
+      ss += dpp_f32<0x4E>(ss);
+      ss += dpp_f32<0x141>(ss);
+      ss += dpp_f32<0x140>(ss);
+      const float inv = qscale * __builtin_amdgcn_rsqf(ss / (float)D + eps);
+#pragma unroll
+      for (int e = 0; e < 32; ++e) y[e] = y[e] * inv * wv[e];
+      if (rot && qb >= 14) {
+        // (448 + e, 480 + e) pairs: block 14 takes y c - y' s, block 15 y c + y' s
+        const float* st = rtab + (qb == 14 ? 32 : 64);
+#pragma unroll
+        for (int q4 = 0; q4 < 8; ++q4) {
+          const float4 c4 = *reinterpret_cast<const float4*>(rtab + 4 * q4);
+          const float4 s4 = *reinterpret_cast<const float4*>(st + 4 * q4);
+          const float cc[4] = {c4.x, c4.y, c4.z, c4.w}, sv[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const int e = 4 * q4 + m;
+            const float pe = dpp_f32<0xB4>(y[e]);  // quad_perm [0,1,3,2]: lanes 14 <-> 15
+            y[e] = __builtin_fmaf(pe, sv[m], y[e] * cc[m]);
+          }
+        }
+      }
+      unsigned char* qt = smem + C::OFF_QT + head * 512;
+      unsigned char* qsc = smem + C::OFF_QSC + head * 16 + qb;
+      const int sw = head & 15;
+      float amax = 0.f;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(y[e]));
+      int eq = ue8m0_exp(amax);
+#pragma unroll
+      for (int term = 0; term < 2; ++term) {
+        const float sc = ue8m0_f32((uint32_t)eq);
+        uint32_t wd[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          wd[j] = enc2(enc2(0u, y[4 * j], y[4 * j + 1], sc, false), y[4 * j + 2], y[4 * j + 3], sc, true);
+        unsigned char* row = qt + term * HP * 512;
+        *reinterpret_cast<uint4*>(row + 16 * ((2 * qb) ^ sw)) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+        *reinterpret_cast<uint4*>(row + 16 * ((2 * qb + 1) ^ sw)) = make_uint4(wd[4], wd[5], wd[6], wd[7]);
+        qsc[term * HP * 16] = (unsigned char)eq;
+        if (term == 0) {
+          // residual for the second term; an RNE E4M3 code is off by at most 16 of its
+          // scale units, so 2^-4 of the first scale holds the residual unsaturated
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const f32x2 d0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(wd[j], sc, false);
+            const f32x2 d1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(wd[j], sc, true);
+            y[4 * j] -= d0[0];
+            y[4 * j + 1] -= d0[1];
+            y[4 * j + 2] -= d1[0];
+            y[4 * j + 3] -= d1[1];
+          }
+          eq = eq >= 4 ? eq - 4 : 0;
+        }
+      }
+    }
+  };
 
-  f32x16 acc[2][4];   // P.V waves: O[64 heads][128 dims]
-  float m_run = -INFINITY, l_run = 0.f;  // QK waves: per head (lane & 31 of group qa)
+  // norm_w into LDS once (block b at 36 b floats: the 16 lanes of a head read 16 distinct
+  // banks)
+  if (tid < D / 4) {
+    const float4 w4 = reinterpret_cast<const float4*>(a.norm_w)[tid];
+    *reinterpret_cast<float4*>(smem + C::OFF_NW + 4 * (36 * (tid / 8) + 4 * (tid % 8))) = w4;
+  }
+  if (rot && tid >= 448 && tid < 480) {  // inverse frequencies theta^(-2i/r) in fp64
+    const int i = tid - 448;
+    reinterpret_cast<double*>(smem + C::OFF_IFREQ)[i] = exp2(-(2.0 * i / (double)a.rope_dim) * a.log2_theta);
+  }
+  __syncthreads();
 
   if (w < 4) {
     // =============================== QK waves
     const int qa = w & 1, qc = w >> 1;
-    const uint32_t hsel = lhalf ? 0x07050301u : 0x06040200u;
-    // q of the 32 heads of group qa, all 8 k-steps: lane half h holds dims 64ks + 16h +
-    // [0,16) and 64ks + 32 + 16h + [0,16); byte j of qs[term][k] scales k-step 4k + j
-    i32x8 qf[2][8];
-    uint32_t qs[2][2];
+    int item = blockIdx.x;
+    Item I = info(item);
+    int raw_cur, raw_next;
+    // an item's prologue (its ids and q loads already issued): first-tile DMA (all of it),
+    // cos / sin table, q tile
+    auto transition = [&](const uint4 (&x)[4][4]) {
+      if (I.n > 0) {
+        const int id0 = valid_id(I, I.tb, raw_cur);
 #pragma unroll
-    for (int term = 0; term < 2; ++term) {
-      const unsigned char* qrow = smem + C::OFF_Q + (term * HP + 32 * qa + lrow) * C::QS8 + 16 * lhalf;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const uint4 lo = *reinterpret_cast<const uint4*>(qrow + 64 * ks);
-        const uint4 hi = *reinterpret_cast<const uint4*>(qrow + 64 * ks + 32);
-        qf[term][ks] = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        for (int k = 0; k < 4; ++k) {
+          dma_part(k, w, id0, raw_buf(0), sc_buf(0));
+          dma_part(k, w + 4, id0, raw_buf(0), sc_buf(0));
+        }
+        dma_part(4, w, id0, raw_buf(0), sc_buf(0));
       }
-      const unsigned char* qsr = smem + C::OFF_Q + C::OFF_QSC + (term * HP + 32 * qa + lrow) * C::NSB;
-      qs[term][0] = scale_word<C>(qsr, 0, hsel);
-      qs[term][1] = scale_word<C>(qsr, 1, hsel);
+      rope_tab(I);
+      q_units(x);
+    };
+    {
+      raw_cur = fetch_id(I, I.tb);
+      raw_next = fetch_id(I, I.tb + 1);
+      uint4 x[4][4];
+      q_load(I, x);
+      transition(x);
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's share of the first tile landed
-    __syncthreads();  // B0: q tile read (the P.V waves overwrite it), first tile visible
-
-    f32x16 s;          // scores of the last tile, kept for a rewrite of its P
-    float l_pend = 0.f;
-    for (int it = 0; it <= n; ++it) {
-      const int tile = tb + it;
+    while (true) {
+      __syncthreads();  // B_A: q tile complete
       const int lane = ((int)threadIdx.x + opaque_zero()) & 63, lrow = lane & 31, lhalf = lane >> 5;
-      const int head = 32 * qa + lrow;
-      const bool do_qk = it < n;
-      // K rows of this tile first: their latency covers the flag check below
-      const int r = 32 * qc + lrow;
-      i32x8 A[8];
-      uint32_t ksc0 = 0, ksc1 = 0;
-      if (do_qk) {
-        const unsigned char* raw_l = raw_buf(it);
-        const unsigned char* sc_l = sc_buf(it);
-        const uint32_t hsel = lhalf ? 0x07050301u : 0x06040200u;
-        ksc0 = scale_word<C>(sc_l + r * C::NSB, 0, hsel);
-        ksc1 = scale_word<C>(sc_l + r * C::NSB, 1, hsel);
+      const uint32_t hsel = lhalf ? 0x07050301u : 0x06040200u;
+      // q of the 32 heads of group qa, all 8 k-steps: lane half h holds dims 64ks + 16h +
+      // [0,16) and 64ks + 32 + 16h + [0,16); byte j of qs[term][k] scales k-step 4k + j
+      i32x8 qf[2][8];
+      uint32_t qs[2][2];
+      {
+        const int head = 32 * qa + lrow, sw = head & 15;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const uint4 lo = *reinterpret_cast<const uint4*>(raw_l + raw_off<C>(r, 4 * ks + lhalf));
-          const uint4 hi = *reinterpret_cast<const uint4*>(raw_l + raw_off<C>(r, 4 * ks + 2 + lhalf));
-          A[ks] = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        for (int term = 0; term < 2; ++term) {
+          const unsigned char* row = smem + C::OFF_QT + (term * HP + head) * 512;
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks) {
+            const uint4 lo = *reinterpret_cast<const uint4*>(row + 16 * ((4 * ks + lhalf) ^ sw));
+            const uint4 hi = *reinterpret_cast<const uint4*>(row + 16 * ((4 * ks + 2 + lhalf) ^ sw));
+            qf[term][ks] = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          }
+          const unsigned char* qsr = smem + C::OFF_QSC + (term * HP + head) * 16;
+          qs[term][0] = scale_word<C>(qsr, 0, hsel);
+          qs[term][1] = scale_word<C>(qsr, 1, hsel);
         }
       }
-      if (it > 0) {
-        const int4 fl = *reinterpret_cast<const int4*>(flag_l + 4 * ((it - 1) & 1));
-        if (__builtin_amdgcn_readfirstlane(fl.x | fl.y | fl.z | fl.w)) {
-          // slow path for tile it - 1: merge the block maxima, raise the running max
-          const float* mx = maxx + 2 * HP * ((it - 1) & 1);
-          const float mt = fmaxf(mx[head], mx[HP + head]);
-          float mnew = m_run;
-          if (mt > -INFINITY && (m_run == -INFINITY || mt > m_run + 8.0f)) mnew = mt;
-          const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mnew);
-          const bool raised = __any(m_run != -INFINITY && mnew != m_run);
-          m_run = mnew;
-          const float msafe = (mnew == -INFINITY) ? 0.f : mnew;
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // the first tile landed
+      __syncthreads();  // B_B: q tile read (the P.V waves overwrite it), first tile visible
+
+      const int n = I.n;
+      const int next = item + (int)gridDim.x;
+      float m_run = -INFINITY, l_run = 0.f, l_pend = 0.f;
+      f32x16 s;  // scores of the last tile, kept for a rewrite of its P
+      // flag check for tile it - 1 (it >= 1): the slow path merges the block maxima,
+      // raises the running max and rewrites P
+      auto check = [&](const int it) __attribute__((always_inline)) {
+        const int lane = ((int)threadIdx.x + opaque_zero()) & 63, lrow = lane & 31, lhalf = lane >> 5;
+        const int head = 32 * qa + lrow;
+        {
+          const int4 fl = *reinterpret_cast<const int4*>(flag_l + 4 * ((it - 1) & 1));
+          if (__builtin_amdgcn_readfirstlane(fl.x | fl.y | fl.z | fl.w)) {
+            // slow path for tile it - 1: merge the block maxima, raise the running max
+            const float* mx = maxx + 2 * HP * ((it - 1) & 1);
+            const float mt = fmaxf(mx[head], mx[HP + head]);
+            float mnew = m_run;
+            if (mt > -INFINITY && (m_run == -INFINITY || mt > m_run + 8.0f)) mnew = mt;
+            const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mnew);
+            const bool raised = __any(m_run != -INFINITY && mnew != m_run);
+            m_run = mnew;
+            const float msafe = (mnew == -INFINITY) ? 0.f : mnew;
+            float p[16];
+            float lp = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              p[i] = __builtin_amdgcn_exp2f(s[i] - msafe);
+              lp += p[i];
+            }
+            l_run = l_run * alpha + lp;
+            unsigned char* prow = p_buf(it - 1) + head * 128;
+            const int sw = swz(head);
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+              *reinterpret_cast<uint2*>(prow + 16 * ((4 * qc + g) ^ sw) + 8 * lhalf) =
+                  make_uint2(pack_bf16(p[4 * g], p[4 * g + 1]), pack_bf16(p[4 * g + 2], p[4 * g + 3]));
+            if (qc == 0 && lhalf == 0) alpha_l[head] = alpha;
+            if (qc == 0 && lane == 0) flag_l[8 + qa] = raised ? 1 : 0;
+            __syncthreads();  // B': P and alpha rewritten
+          } else {
+            l_run += l_pend;
+          }
+        }
+      };
+      for (int it = 0; it < n; ++it) {
+        const int tile = I.tb + it;
+        const int lane = ((int)threadIdx.x + opaque_zero()) & 63, lrow = lane & 31, lhalf = lane >> 5;
+        const int head = 32 * qa + lrow;
+        const int r = 32 * qc + lrow;
+        i32x8 A[8];
+        uint32_t ksc0 = 0, ksc1 = 0;
+        auto load_a = [&](int ks0) {
+          const unsigned char* raw_l = raw_buf(it);
+#pragma unroll
+          for (int ks = ks0; ks < ks0 + 4; ++ks) {
+            const uint4 lo = *reinterpret_cast<const uint4*>(raw_l + raw_off<C>(r, 4 * ks + lhalf));
+            const uint4 hi = *reinterpret_cast<const uint4*>(raw_l + raw_off<C>(r, 4 * ks + 2 + lhalf));
+            A[ks] = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          }
+        };
+        if (it > 0) check(it);
+        const int id_cur = valid_id(I, tile, raw_cur);
+        const unsigned long long mask = __ballot(id_cur >= 0);
+        const int id_next = valid_id(I, tile + 1, raw_next);
+        const int raw_next2 = fetch_id(I, tile + 2);
+        // the next tile's DMA (the row DMAs queue behind the P.V waves' MFMAs meanwhile)
+        if (it + 1 < n) {
+#pragma unroll
+          for (int k = 0; k <= 4; ++k) dma_part(k, w, id_next, raw_buf(it + 1), sc_buf(it + 1));
+        }
+        {
+          const unsigned char* sc_l = sc_buf(it);
+          const uint32_t hsel = lhalf ? 0x07050301u : 0x06040200u;
+          ksc0 = scale_word<C>(sc_l + r * C::NSB, 0, hsel);
+          ksc1 = scale_word<C>(sc_l + r * C::NSB, 1, hsel);
+          load_a(0);
+          load_a(4);
+          qk_block<4, true>(s, A, qf[0], qf[1], ksc0, qs[0][0], qs[1][0]);
+          qk_block<4, false>(s, A + 4, qf[0] + 4, qf[1] + 4, ksc1, qs[0][1], qs[1][1]);
+        }
+        {
+          qk_drain(s);
+          // mask (row 32qc + 8g + 4h + j holds value 4g + j), block max over the 32 rows
+          const uint32_t mw = (uint32_t)(mask >> (32 * qc));
+          float lm = -INFINITY;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int rr = 8 * (i >> 2) + (i & 3);
+            const unsigned long long lmk = (((mw >> rr) & 1u) ? 0x00000000FFFFFFFFull : 0ull) |
+                                           (((mw >> (rr + 4)) & 1u) ? 0xFFFFFFFF00000000ull : 0ull);
+            s[i] = __builtin_amdgcn_inverse_ballot_w64(lmk) ? s[i] : -INFINITY;
+            lm = fmaxf(lm, s[i]);
+          }
+          lm = fmaxf(lm, __shfl_xor(lm, 32));
+          // P against the running max; exact unless the flag below sends the tile to the
+          // slow path, which rewrites it
+          const float msafe = (m_run == -INFINITY) ? 0.f : m_run;
           float p[16];
           float lp = 0.f;
 #pragma unroll
@@ -1232,136 +1470,129 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
             p[i] = __builtin_amdgcn_exp2f(s[i] - msafe);
             lp += p[i];
           }
-          l_run = l_run * alpha + lp;
-          unsigned char* prow = p_buf(it - 1) + head * 128;
+          l_pend = lp;
+          unsigned char* prow = p_buf(it) + head * 128;
           const int sw = swz(head);
 #pragma unroll
           for (int g = 0; g < 4; ++g)
             *reinterpret_cast<uint2*>(prow + 16 * ((4 * qc + g) ^ sw) + 8 * lhalf) =
                 make_uint2(pack_bf16(p[4 * g], p[4 * g + 1]), pack_bf16(p[4 * g + 2], p[4 * g + 3]));
-          if (qc == 0 && lhalf == 0) alpha_l[head] = alpha;
-          if (qc == 0 && lane == 0) flag_l[8 + qa] = raised ? 1 : 0;
-          __syncthreads();  // B': P and alpha rewritten
-        } else {
-          l_run += l_pend;
+          if (lhalf == 0) maxx[2 * HP * (it & 1) + qc * HP + head] = lm;
+          const bool over = __any(lm > m_run + 8.0f);
+          if (lane == 0) flag_l[4 * (it & 1) + w] = over ? 1 : 0;
         }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile's DMA from this wave landed
+        raw_cur = raw_next;
+        raw_next = raw_next2;
+        __syncthreads();  // end of iteration
       }
-      const int id_cur = valid_id(tile, raw_cur);
-      const unsigned long long mask = __ballot(id_cur >= 0);
-      const int id_next = valid_id(tile + 1, raw_next);
-      const int raw_next2 = fetch_id(tile + 2);
-
-      if (do_qk) {
-        qk_block<4, true>(s, A, qf[0], qf[1], ksc0, qs[0][0], qs[1][0]);
-        qk_block<4, false>(s, A + 4, qf[0] + 4, qf[1] + 4, ksc1, qs[0][1], qs[1][1]);
-      }
-      // the next tile's DMA goes out while the MFMA chain runs
-      if (it + 1 < n) issue_tile(id_next, raw_buf(it + 1), sc_buf(it + 1), lane);
-      if (do_qk) {
-        qk_drain(s);
-        // mask (row 32qc + 8g + 4h + j holds value 4g + j), block max over the 32 rows
-        const uint32_t mw = (uint32_t)(mask >> (32 * qc));
-        float lm = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int rr = 8 * (i >> 2) + (i & 3);
-          const unsigned long long lmk = (((mw >> rr) & 1u) ? 0x00000000FFFFFFFFull : 0ull) |
-                                         (((mw >> (rr + 4)) & 1u) ? 0xFFFFFFFF00000000ull : 0ull);
-          s[i] = __builtin_amdgcn_inverse_ballot_w64(lmk) ? s[i] : -INFINITY;
-          lm = fmaxf(lm, s[i]);
+      // last iteration (P.V of the last tile on the other waves): final check, the item's
+      // row sums and max for the epilogue, and the next item's ids, which stay in flight
+      // into the next item's prologue
+      uint4 x[4][4];
+      uint32_t touch0 = 0, touch1 = 0;
+      {
+        if (n > 0) check(n);
+        const int lane = ((int)threadIdx.x + opaque_zero()) & 63, lrow = lane & 31, lhalf = lane >> 5;
+        const int head = 32 * qa + lrow;
+        const float lw = l_run + __shfl_xor(l_run, 32);
+        if (lhalf == 0) lsum[qc * HP + head] = lw;
+        if (qc == 0 && lhalf == 0) mfin[head] = m_run;
+        if (next < total) {
+          I = info(next);
+          raw_cur = fetch_id(I, I.tb);
+          raw_next = fetch_id(I, I.tb + 1);
+          // touch the next item's q rows into the L2 (256 B per lane); the registers stay
+          // reserved until the prologue's own q loads have been waited for
+          const int tq = 64 * w + lane;
+          if (tq / 4 < a.h_q) {
+            const uint16_t* qn = a.q + ((size_t)I.t * a.h_q) * D + 128 * tq;
+            asm volatile("global_load_dword %0, %1, off" : "=v"(touch0) : "v"(qn) : "memory");
+            asm volatile("global_load_dword %0, %1, off offset:128" : "=v"(touch1) : "v"(qn) : "memory");
+          }
         }
-        lm = fmaxf(lm, __shfl_xor(lm, 32));
-        // P against the running max; exact unless the flag below sends the tile to the
-        // slow path, which rewrites it
-        const float msafe = (m_run == -INFINITY) ? 0.f : m_run;
-        float p[16];
-        float lp = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          p[i] = __builtin_amdgcn_exp2f(s[i] - msafe);
-          lp += p[i];
-        }
-        l_pend = lp;
-        unsigned char* prow = p_buf(it) + head * 128;
-        const int sw = swz(head);
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          *reinterpret_cast<uint2*>(prow + 16 * ((4 * qc + g) ^ sw) + 8 * lhalf) =
-              make_uint2(pack_bf16(p[4 * g], p[4 * g + 1]), pack_bf16(p[4 * g + 2], p[4 * g + 3]));
-        if (lhalf == 0) maxx[2 * HP * (it & 1) + qc * HP + head] = lm;
-        const bool over = __any(lm > m_run + 8.0f);
-        if (lane == 0) flag_l[4 * (it & 1) + w] = over ? 1 : 0;
+        __syncthreads();  // end of the last iteration
       }
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile's DMA from this wave landed
-      raw_cur = raw_next;
-      raw_next = raw_next2;
-      __syncthreads();  // end of iteration
+      item = next;
+      if (item >= total) break;
+      q_load(I, x);
+      transition(x);  // waits for the q loads, and so for the touch loads before them
+      asm volatile("" ::"v"(touch0), "v"(touch1));
     }
   } else {
     // =============================== P.V waves
     const int v = w - 4;
     unsigned char* vt = smem + C::OFF_VT + v * C::VTW_BYTES;
+    int item = blockIdx.x;
+    Item I = info(item);
+    rope_tab(I);  // this wave's table, for the epilogue's inverse RoPE
+    while (true) {
+      __syncthreads();  // B_A
+      __syncthreads();  // B_B
+      const int n = I.n;
+      f32x16 acc[2][4];  // O[64 heads][128 dims]
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();  // B0
-
-    // one iteration: P.V of tile it - 1 (PV) and / or the V tile of tile it (VT)
-    auto pv_iter = [&](const int it, auto pv_c, auto vt_c) __attribute__((always_inline)) {
-      const int tile = tb + it;
-      const int lane = ((int)threadIdx.x + opaque_zero()) & 63, lrow = lane & 31, lhalf = lane >> 5;
-      const unsigned char* p_l = p_buf(it - 1);
-      const unsigned char* raw_l = raw_buf(it);
-      const unsigned char* sc_l = sc_buf(it);
-      // Address bases.  Row n of Vt (dim) or P (head) is 128 bytes, its 16-byte chunk ch
-      // stored at chunk ch ^ swz(n).  For the P.V reads n = 32b + lrow (b = n-block or
-      // m-block) and ch = 2ks + lhalf, so the stored chunk is nu ^ (2ks ^ kb(b)) with the
-      // lane part nu = swz(lrow) ^ lhalf and kb(b) = 4(b & 1) ^ (b >> 1): eight lane offsets
-      // rd[c] = 128 lrow + 16 (nu ^ c) cover every read, the rest is an immediate.
-      const int nu = (lrow & 7) ^ (lrow >> 3) ^ lhalf;
-      uint32_t rd[8];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) rd[c] = 128 * lrow + 16 * (nu ^ c);
-      // V tile roles: lane = 8c' + j converts rows 16ks + 2j, 16ks + 2j + 1 (one DMA group,
-      // adjacent 16-byte pieces) of chunk 8v + c' (tile dims 16c' .. 16c' + 15 of this
-      // wave).  Dim n = 16c' + e takes the two slots at chunk 2ks + (j >> 2) of its row,
-      // stored at chunk lam ^ (2ks ^ E(e)) with lam = K0(c') ^ (j >> 2), K0(c') = (2c' ^
-      // (c' >> 2)) & 7, E(e) = (e & 7) ^ (e >> 3): lane offsets wr0 + 16 (lam ^ c), plus 128 e.
-      const int j = lane & 7, cl = lane >> 3;
-      const int lam = ((2 * cl) ^ (cl >> 2) ^ (j >> 2)) & 7;
-      const uint32_t wr0 = 2048 * cl + 4 * (j & 3);
-      const uint32_t rsrc = (uint32_t)(j * C::GS + 32 * cl);  // + group 8ks, + chunk 8v
-      const uint32_t ssrc = (uint32_t)(32 * j);               // + 256 ks + 4v
-      const int raw_next2 = fetch_id(tile + 2);
-      bf16x8 Ap[2], Bv[4];
-      uint4 ra[2], rb[2];
-      uint32_t wa[2], wb[2];
-      auto load_p = [&](int ks) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-          Ap[mb] = *reinterpret_cast<const bf16x8*>(p_l + 4096 * mb + rd[(2 * ks) ^ (4 * mb)]);
-      };
-      auto load_v = [&](int ks) {
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
-          Bv[nb] = *reinterpret_cast<const bf16x8*>(vt + 4096 * nb + rd[(2 * ks) ^ (4 * (nb & 1)) ^ (nb >> 1)]);
-      };
-      auto load_vt = [&](int ks, int u) {
-        const unsigned char* src = raw_l + rsrc + 8 * ks * C::GS + 256 * v;
-        ra[u] = *reinterpret_cast<const uint4*>(src);
-        rb[u] = *reinterpret_cast<const uint4*>(src + 16);
-        const unsigned char* ssp = sc_l + ssrc + 256 * ks + 4 * v;
-        wa[u] = *reinterpret_cast<const uint32_t*>(ssp);
-        wb[u] = *reinterpret_cast<const uint32_t*>(ssp + C::NSB);
-      };
-      constexpr bool PV = decltype(pv_c)::value, VT = decltype(vt_c)::value;
-      {
-        // first k-step's operands before the flag check (P is read again if the slow
-        // path rewrites it)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
+      int raw_next = fetch_id(I, I.tb + 1);
+
+      // one iteration: P.V of tile it - 1 (PV) and / or the V tile of tile it (VT)
+      auto pv_iter = [&](const int it, auto pv_c, auto vt_c) __attribute__((always_inline)) {
+        constexpr bool PV = decltype(pv_c)::value, VT = decltype(vt_c)::value;
+        const int tile = I.tb + it;
+        const int lane = ((int)threadIdx.x + opaque_zero()) & 63, lrow = lane & 31, lhalf = lane >> 5;
+        const unsigned char* p_l = p_buf(it - 1);
+        const unsigned char* raw_l = raw_buf(it);
+        const unsigned char* sc_l = sc_buf(it);
+        // Address bases.  Row n of Vt (dim) or P (head) is 128 bytes, its 16-byte chunk ch
+        // stored at chunk ch ^ swz(n).  For the P.V reads n = 32b + lrow (b = n-block or
+        // m-block) and ch = 2ks + lhalf, so the stored chunk is nu ^ (2ks ^ kb(b)) with the
+        // lane part nu = swz(lrow) ^ lhalf and kb(b) = 4(b & 1) ^ (b >> 1): eight lane offsets
+        // rd[c] = 128 lrow + 16 (nu ^ c) cover every read, the rest is an immediate.
+        const int nu = (lrow & 7) ^ (lrow >> 3) ^ lhalf;
+        uint32_t rd[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) rd[c] = 128 * lrow + 16 * (nu ^ c);
+        // V tile roles: lane = 8c' + j converts rows 16ks + 2j, 16ks + 2j + 1 (one DMA group,
+        // adjacent 16-byte pieces) of chunk 8v + c' (tile dims 16c' .. 16c' + 15 of this
+        // wave).  Dim n = 16c' + e takes the two slots at chunk 2ks + (j >> 2) of its row,
+        // stored at chunk lam ^ (2ks ^ E(e)) with lam = K0(c') ^ (j >> 2), K0(c') = (2c' ^
+        // (c' >> 2)) & 7, E(e) = (e & 7) ^ (e >> 3): lane offsets wr0 + 16 (lam ^ c), plus 128 e.
+        const int j = lane & 7, cl = lane >> 3;
+        const int lam = ((2 * cl) ^ (cl >> 2) ^ (j >> 2)) & 7;
+        const uint32_t wr0 = 2048 * cl + 4 * (j & 3);
+        const uint32_t rsrc = (uint32_t)(j * C::GS + 32 * cl);  // + group 8ks, + chunk 8v
+        const uint32_t ssrc = (uint32_t)(32 * j);               // + 256 ks + 4v
+        const int raw_next2 = fetch_id(I, tile + 2);
+        // operands double-buffered by k-step parity: the reads of k-step ks + 1 go out at
+        // the start of k-step ks, a full k-step of MFMAs ahead of their use
+        bf16x8 Ap[2][2], Bv[2][4];
+        uint4 ra[2], rb[2];
+        uint32_t wa[2], wb[2];
+        auto load_p = [&](int ks) {
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+            Ap[ks & 1][mb] = *reinterpret_cast<const bf16x8*>(p_l + 4096 * mb + rd[(2 * ks) ^ (4 * mb)]);
+        };
+        auto load_v = [&](int ks) {
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+            Bv[ks & 1][nb] =
+                *reinterpret_cast<const bf16x8*>(vt + 4096 * nb + rd[(2 * ks) ^ (4 * (nb & 1)) ^ (nb >> 1)]);
+        };
+        auto load_vt = [&](int ks, int u) {
+          const unsigned char* src = raw_l + rsrc + 8 * ks * C::GS + 256 * v;
+          ra[u] = *reinterpret_cast<const uint4*>(src);
+          rb[u] = *reinterpret_cast<const uint4*>(src + 16);
+          const unsigned char* ssp = sc_l + ssrc + 256 * ks + 4 * v;
+          wa[u] = *reinterpret_cast<const uint32_t*>(ssp);
+          wb[u] = *reinterpret_cast<const uint32_t*>(ssp + C::NSB);
+        };
+        // first k-step's operands before the flag check (P is read again if the slow path
+        // rewrites it)
         if constexpr (PV) {
           load_p(0);
           load_v(0);
@@ -1390,25 +1621,26 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
             }
           }
         }
-        const int id_next = valid_id(tile + 1, raw_next);
+        const int id_next = valid_id(I, tile + 1, raw_next);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           const int u = ks & 1;
+          __builtin_amdgcn_sched_barrier(0);
+          // next k-step's operands first
+          if (VT && ks + 1 < 4) load_vt(ks + 1, u ^ 1);
+          if (PV && ks + 1 < 4) {
+            load_p(ks + 1);
+            load_v(ks + 1);
+          }
           // one of this wave's row DMAs for the next tile per k-step (zero rows past the
           // end of the range)
-          if constexpr (VT) dma_part(ks, id_next, raw_buf(it + 1), sc_buf(it + 1), lane);
-          if (VT && ks + 1 < 4) load_vt(ks + 1, u ^ 1);
+          if constexpr (VT) dma_part(ks, w, id_next, raw_buf(it + 1), sc_buf(it + 1));
           if constexpr (PV) {
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
               for (int mb = 0; mb < 2; ++mb)
-                acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ap[mb], Bv[nb], acc[mb][nb], 0, 0, 0);
-            // next k-step's operands, read while this k-step's MFMAs and conversion run
-            if (ks + 1 < 4) {
-              load_p(ks + 1);
-              load_v(ks + 1);
-            }
+                acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ap[u][mb], Bv[u][nb], acc[mb][nb], 0, 0, 0);
           }
           if constexpr (VT) {
             const int bsh = 8 * (cl >> 1);
@@ -1429,77 +1661,149 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
             }
           }
           if constexpr (PV && VT) {
-            // spread the conversion and the LDS traffic between the 8 MFMAs
+            // the conversion and its LDS writes spread between the 8 MFMAs
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
               __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
               __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
-              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
               __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);  // DS write
             }
           }
         }
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        raw_next = raw_next2;
+        __syncthreads();  // end of iteration
+      };
+      // the first and last iterations are separate straight-line copies
+      if (n == 0) {
+        pv_iter(0, std::false_type{}, std::false_type{});
+      } else {
+        pv_iter(0, std::false_type{}, std::true_type{});
+        for (int it = 1; it < n; ++it) pv_iter(it, std::true_type{}, std::true_type{});
+        pv_iter(n, std::true_type{}, std::false_type{});
       }
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-      raw_cur = raw_next;
-      raw_next = raw_next2;
-      __syncthreads();  // end of iteration
-    };
-    // the first and last iterations are separate straight-line copies
-    if (n == 0) {
-      pv_iter(0, std::false_type{}, std::false_type{});
-    } else {
-      pv_iter(0, std::false_type{}, std::true_type{});
-      for (int it = 1; it < n; ++it) pv_iter(it, std::true_type{}, std::true_type{});
-      pv_iter(n, std::true_type{}, std::false_type{});
-    }
-  }
 
-  // ---------------- finish
-  if (w < 4) {
-    const int qa = w & 1, qc = w >> 1;
-    const float lw = l_run + __shfl_xor(l_run, 32);
-    if (lhalf == 0) lsum[qc * HP + 32 * qa + lrow] = lw;
-    if (qc == 0 && lhalf == 0) maxx[32 * qa + lrow] = m_run;
-  }
-  __syncthreads();
-  if (ns == 1) {
-    float* o_l = reinterpret_cast<float*>(smem);
-    if (w >= 4) {
-      const int d0 = C::VW * (w - 4);
+      // ---- finish of the item; the next item's q loads go out first
+      const int next = item + (int)gridDim.x;
+      const bool more = next < total;
+      Item In = I;
+      if (more) In = info(next);
+      const int lane = ((int)threadIdx.x + opaque_zero()) & 63, lrow = lane & 31, lhalf = lane >> 5;
+      const auto& K = karg();
+      const int hq = K.h_q;
+      if (ns == 1) {
+        // normalize in registers (row sums of the lane's 32 heads: four float4 per half),
+        // then per pass 16 heads x 128 dims through the staging area (rows of 132 floats:
+        // the 16 heads of a read step fall in 16 distinct bank quads): lane (hl = lane & 15,
+        // block 4v + (lane >> 4)) runs inverse RoPE, block amax, UE8M0 exponent and E4M3 codes
+        uint8_t* out_fp8 = K.out_fp8;
+        uint8_t* out_scales = K.out_scales;
+        float* out_f32 = K.out_f32;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int h = 32 * mb + 8 * (i >> 2) + 4 * lhalf + (i & 3);
-          const float lt = lsum[h] + lsum[HP + h];
-          const float inv = lt > 0.f ? __builtin_amdgcn_rcpf(lt) : 0.f;
+          for (int g = 0; g < 4; ++g) {
+            const int h0 = 32 * mb + 8 * g + 4 * lhalf;
+            const float4 la = *reinterpret_cast<const float4*>(lsum + h0);
+            const float4 lb = *reinterpret_cast<const float4*>(lsum + HP + h0);
+            const float lt[4] = {la.x + lb.x, la.y + lb.y, la.z + lb.z, la.w + lb.w};
 #pragma unroll
-          for (int nb = 0; nb < 4; ++nb) o_l[h * C::OS + d0 + 32 * nb + lrow] = acc[mb][nb][i] * inv;
-        }
-    }
-    __syncthreads();
-    epilogue<D, NTHREADS>(o_l, C::OS, a.h_q, 0, t, a, cs, sn);
-  } else {
-    float* part = a.ws + ((size_t)t * ns + split) * partial_floats_d(a.h_q, D);
-    float* pm = part + (size_t)a.h_q * D;
-    float* pl = pm + a.h_q;
-    if (tid < a.h_q) {
-      pm[tid] = maxx[tid];
-      pl[tid] = lsum[tid] + lsum[HP + tid];
-    }
-    if (n > 0 && w >= 4) {
-      const int d0 = C::VW * (w - 4);
+            for (int jj = 0; jj < 4; ++jj) {
+              const float inv = lt[jj] > 0.f ? __builtin_amdgcn_rcpf(lt[jj]) : 0.f;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+              for (int nb = 0; nb < 4; ++nb) acc[mb][nb][4 * g + jj] *= inv;
+            }
+          }
+        float* est = reinterpret_cast<float*>(smem + C::OFF_EST + v * C::EST_BYTES);
+        const int hl_u = lane & 15, blk = lane >> 4, gb = 4 * v + blk;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int h = 32 * mb + 8 * (i >> 2) + 4 * lhalf + (i & 3);
-          if (h < a.h_q) {
+        for (int pass = 0; pass < 4; ++pass) {
+          const int mb = pass >> 1, hb = 16 * (pass & 1);
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) part[(size_t)h * D + d0 + 32 * nb + lrow] = acc[mb][nb][i];
+          for (int g2 = 0; g2 < 2; ++g2)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const int i = 4 * (2 * (pass & 1) + g2) + jj;
+              const int hl = 8 * g2 + 4 * lhalf + jj;
+#pragma unroll
+              for (int nb = 0; nb < 4; ++nb) est[hl * C::EST_STRIDE + 32 * nb + lrow] = acc[mb][nb][i];
+            }
+          const int h = 32 * mb + hb + hl_u;
+          const float* row = est + hl_u * C::EST_STRIDE;
+          float vv[32];
+#pragma unroll
+          for (int q4 = 0; q4 < 8; ++q4) {
+            const float4 f4 = *reinterpret_cast<const float4*>(row + 32 * blk + 4 * q4);
+            vv[4 * q4] = f4.x; vv[4 * q4 + 1] = f4.y; vv[4 * q4 + 2] = f4.z; vv[4 * q4 + 3] = f4.w;
+          }
+          if (rot && gb >= 14) {
+            // inverse rotation of (448 + e, 480 + e): block 14 takes o c + o' s, block 15
+            // o c - o' s
+            const float* st = rtab + (gb == 14 ? 64 : 32);
+#pragma unroll
+            for (int q4 = 0; q4 < 8; ++q4) {
+              const float4 f4 = *reinterpret_cast<const float4*>(row + 32 * (blk ^ 1) + 4 * q4);
+              const float4 c4 = *reinterpret_cast<const float4*>(rtab + 4 * q4);
+              const float4 s4 = *reinterpret_cast<const float4*>(st + 4 * q4);
+              const float pr[4] = {f4.x, f4.y, f4.z, f4.w}, cc[4] = {c4.x, c4.y, c4.z, c4.w},
+                          sv[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+              for (int m = 0; m < 4; ++m) {
+                const int e = 4 * q4 + m;
+                vv[e] = __builtin_fmaf(pr[m], sv[m], vv[e] * cc[m]);
+              }
+            }
+          }
+          float amax = 0.f;
+#pragma unroll
+          for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(vv[e]));
+          if (h < hq) {
+            const size_t g = ((size_t)I.t * hq + h) * D + 32 * gb;
+            if (out_f32) {
+#pragma unroll
+              for (int q4 = 0; q4 < 8; ++q4)
+                reinterpret_cast<float4*>(out_f32 + g)[q4] =
+                    make_float4(vv[4 * q4], vv[4 * q4 + 1], vv[4 * q4 + 2], vv[4 * q4 + 3]);
+            }
+            const int e8 = ue8m0_exp(amax);
+            const float sc = ue8m0_f32((uint32_t)e8);  // codes = RNE(o / 2^(e-127))
+            uint32_t wd[8];
+#pragma unroll
+            for (int q4 = 0; q4 < 8; ++q4)
+              wd[q4] = enc2(enc2(0u, vv[4 * q4], vv[4 * q4 + 1], sc, false), vv[4 * q4 + 2], vv[4 * q4 + 3], sc, true);
+            reinterpret_cast<uint4*>(out_fp8 + g)[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+            reinterpret_cast<uint4*>(out_fp8 + g)[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
+            out_scales[((size_t)I.t * hq + h) * (D / 32) + gb] = (uint8_t)e8;
           }
         }
+      } else {
+        // this split's (acc, m, l) for the combine kernel
+        const int split = item % ns;
+        float* part = K.ws + ((size_t)I.t * ns + split) * partial_floats_d(hq, D);
+        float* pm = part + (size_t)hq * D;
+        float* pl = pm + hq;
+        if (v == 0 && lane < hq) {
+          pm[lane] = mfin[lane];
+          pl[lane] = lsum[lane] + lsum[HP + lane];
+        }
+        if (n > 0) {
+          const int d0 = C::VW * v;
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int h = 32 * mb + 8 * (i >> 2) + 4 * lhalf + (i & 3);
+              if (h < hq) {
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) part[(size_t)h * D + d0 + 32 * nb + lrow] = acc[mb][nb][i];
+              }
+            }
+        }
+      }
+      if (!more) break;
+      item = next;
+      I = In;
+      rope_tab(I);
     }
   }
 }
@@ -1568,13 +1872,29 @@ __global__ __launch_bounds__(CTHREADS) void smla_combine(KArgs a) {
   epilogue<D, CTHREADS>(o_l, OSTR, 1, h, t, a, cs, sn);
 }
 
+// compute units of the current device (one persistent workgroup each)
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 template <int D, int EB>
 hipError_t launch_t(const LaunchArgs& x, const KArgs& k) {
   const int ns = x.num_splits;
-  if constexpr (D == 512 && EB == 1)
-    hipLaunchKernelGGL(smla_ws, dim3((unsigned)(x.s_q * ns)), dim3(NTHREADS), 0, x.stream, k);
-  else
-    hipLaunchKernelGGL((smla_main<D, EB>), dim3((unsigned)(x.s_q * ns)), dim3(NTHREADS), 0, x.stream, k);
+  const int items = x.s_q * ns;
+  if (D == 512 && EB == 1 && (x.rope_dim == 0 || x.rope_dim == 64)) {
+    const int cus = device_cus();
+    hipLaunchKernelGGL(smla_ws, dim3((unsigned)(items < cus ? items : cus)), dim3(NTHREADS), 0, x.stream, k);
+  } else {
+    hipLaunchKernelGGL((smla_main<D, EB>), dim3((unsigned)items), dim3(NTHREADS), 0, x.stream, k);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ns == 1) return e;
   hipLaunchKernelGGL((smla_combine<D>), dim3((unsigned)x.s_q, (unsigned)x.h_q), dim3(CTHREADS), 0, x.stream, k);
