@@ -1622,6 +1622,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
           }
         }
         const int id_next = valid_id(I, tile + 1, raw_next);
+        // the k-step loop at raised wave priority: when both waves of a SIMD are ready,
+        // this wave's MFMA / conversion stream goes first (the QK wave is then usually
+        // waiting on its own MFMA chain)
+        __builtin_amdgcn_s_setprio(2);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           const int u = ks & 1;
@@ -1670,6 +1674,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
             }
           }
         }
+        __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_s_waitcnt(0x0F70);
         raw_next = raw_next2;
         __syncthreads();  // end of iteration
