@@ -1172,10 +1172,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
   auto sc_buf = [&](int i) { return smem + ((i & 1) ? C::OFF_SC1 : C::OFF_SC0); };
   auto p_buf = [&](int i) { return smem + ((i & 1) ? C::OFF_P1 : C::OFF_P0); };
 
-  // ---------------- q prologue of an item (QK waves, in two steps)
-  // Thread tid < 256 handles block b = tid & 15 (32 dims) of heads (tid >> 4) + 16k,
-  // k = 0..3: a row of 16 lanes holds one head, whose sum of squares is reduced with DPP.
-  auto q_load = [&](const Item& I, uint4 (&x)[4][4]) {
+  // ---------------- q prologue of an item (in two steps)
+  // With NU units per thread, thread tid handles block b = tid & 15 (32 dims) of heads
+  // (tid >> 4) + (64 / NU) k, k < NU: a row of 16 lanes holds one head, whose sum of
+  // squares is reduced with DPP.  Between items the QK waves run it alone (NU = 4); the
+  // first item of a workgroup is split over all eight waves (NU = 2).
+  auto q_load = [&](const Item& I, auto nu_c, uint4 (&x)[4][4]) {
+    constexpr int NU = decltype(nu_c)::value;
     // lane-dependent values are recomputed in each phase (opaque_zero) instead of being
     // hoisted out of the item loop and kept live across it
     const int tid = (int)threadIdx.x + opaque_zero(), qb = tid & 15;
@@ -1183,8 +1186,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
     const uint16_t* qp = K.q;
     const int hq = K.h_q;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int head = (tid >> 4) + 16 * k;
+    for (int k = 0; k < NU; ++k) {
+      const int head = (tid >> 4) + (64 / NU) * k;
       const uint4* src = reinterpret_cast<const uint4*>(qp + ((size_t)I.t * hq + head) * D + 32 * qb);
 #pragma unroll
       for (int j = 0; j < 4; ++j) x[k][j] = head < hq ? src[j] : make_uint4(0u, 0u, 0u, 0u);
@@ -1212,7 +1215,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
   // RMSNorm (f32), times sm_scale * log2(e) (the scores come out ready for exp2), RoPE on
   // dims 448..511 (blocks 14 and 15 swap values through DPP), then two E4M3 terms with
   // their own UE8M0 scales per block into the q tile
-  auto q_units = [&](const uint4 (&x)[4][4]) {
+  auto q_units = [&](auto nu_c, const uint4 (&x)[4][4]) {
+    constexpr int NU = decltype(nu_c)::value;
     const int tid = (int)threadIdx.x + opaque_zero(), qb = tid & 15;
     const auto& K = karg();
     const float qscale = K.sm_scale * 1.4426950408889634f, eps = K.rms_eps;
@@ -1224,8 +1228,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
       wv[4 * j] = w4.x; wv[4 * j + 1] = w4.y; wv[4 * j + 2] = w4.z; wv[4 * j + 3] = w4.w;
     }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int head = (tid >> 4) + 16 * k;
+    for (int k = 0; k < NU; ++k) {
+      const int head = (tid >> 4) + (64 / NU) * k;
       float y[32];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -1320,7 +1324,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
     int raw_cur, raw_next;
     // an item's prologue (its ids and q loads already issued): first-tile DMA (all of it),
     // cos / sin table, q tile
-    auto transition = [&](const uint4 (&x)[4][4]) {
+    auto transition = [&](auto nu_c, const uint4 (&x)[4][4]) {
       if (I.n > 0) {
         const int id0 = valid_id(I, I.tb, raw_cur);
 #pragma unroll
@@ -1331,14 +1335,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
         dma_part(4, w, id0, raw_buf(0), sc_buf(0));
       }
       rope_tab(I);
-      q_units(x);
+      q_units(nu_c, x);
     };
     {
       raw_cur = fetch_id(I, I.tb);
       raw_next = fetch_id(I, I.tb + 1);
       uint4 x[4][4];
-      q_load(I, x);
-      transition(x);
+      q_load(I, std::integral_constant<int, 2>{}, x);
+      transition(std::integral_constant<int, 2>{}, x);
     }
     while (true) {
       __syncthreads();  // B_A: q tile complete
@@ -1515,8 +1519,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
       }
       item = next;
       if (item >= total) break;
-      q_load(I, x);
-      transition(x);  // waits for the q loads, and so for the touch loads before them
+      q_load(I, std::integral_constant<int, 4>{}, x);
+      transition(std::integral_constant<int, 4>{}, x);  // waits for the q loads, and so for the touch loads before them
       asm volatile("" ::"v"(touch0), "v"(touch1));
     }
   } else {
@@ -1525,7 +1529,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
     unsigned char* vt = smem + C::OFF_VT + v * C::VTW_BYTES;
     int item = blockIdx.x;
     Item I = info(item);
-    rope_tab(I);  // this wave's table, for the epilogue's inverse RoPE
+    {
+      // the first item's prologue is shared with the QK waves (heads 16..31, 48..63);
+      // this wave's table also serves the epilogue's inverse RoPE
+      uint4 x[4][4];
+      q_load(I, std::integral_constant<int, 2>{}, x);
+      rope_tab(I);
+      q_units(std::integral_constant<int, 2>{}, x);
+    }
     while (true) {
       __syncthreads();  // B_A
       __syncthreads();  // B_B
