@@ -166,7 +166,7 @@ def measure(name, steps, warmup, torch, device, timed_steps=None):
     mean_us = float(us.mean())
     res = dict(
         workload=name, description=inp["description"], s_q=s_q, num_splits=ns,
-        kernels="smla_main" + (" + smla_combine" if ns > 1 else ""),
+        kernels="smla_ws" + (" + smla_combine" if ns > 1 else ""),
         us_per_call_mean=mean_us, us_per_call_median=float(np.median(us)),
         us_per_call_p10=float(np.percentile(us, 10)), us_per_call_p90=float(np.percentile(us, 90)),
         us_per_call_cold_median=float(np.median(cold)),
@@ -304,7 +304,7 @@ def traffic_from(folder, copy_mib):
         factor = (copy_mib * 1024.0) / float(np.median(crow))
         out[f"{counter}_copy_factor"] = factor
         rows = _counter_rows(os.path.join(folder, sub), counter)
-        for kname in ("smla_main", "smla_combine"):
+        for kname in ("smla_ws", "smla_combine"):
             vals = [v for k, v in rows if kname in k]
             if not vals:
                 continue

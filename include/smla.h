@@ -78,7 +78,9 @@ typedef struct smla_params {
   float sm_scale;   /* softmax scale, finite and > 0 (typically 1/sqrt(d)) */
   float rms_eps;    /* RMSNorm epsilon, finite and > 0 */
   float rope_theta; /* RoPE base, finite and > 0 */
-  int32_t num_splits; /* 0 = automatic; else split each token's entries over this many
+  int32_t num_splits; /* 0 = automatic (as many splits as keep s_q x splits within one
+                         round of the device's compute units, at most one per 64 index
+                         entries); else split each token's entries over this many
                          workgroups (1..64) and combine */
   float* out_f32;   /* optional f32 [s_q][h_q][d]: o after inverse RoPE, before the FP8
                        cast (NULL = not written) */
@@ -120,8 +122,9 @@ int sparse_mla_fwd(const void* q, const void* kv_pool, const uint8_t* kv_scales,
 
 /*
  * Bytes of device workspace sparse_mla_fwd needs for these parameters (0 when the
- * call runs unsplit).  Depends on s_q, h_q, d, topk and num_splits only.  Returns 0
- * for parameters sparse_mla_fwd would reject.
+ * call runs unsplit).  Depends on s_q, h_q, d, topk and num_splits, and with
+ * num_splits = 0 on the current device's compute-unit count.  Returns 0 for parameters
+ * sparse_mla_fwd would reject.
  */
 size_t sparse_mla_workspace_size(const smla_params* params);
 

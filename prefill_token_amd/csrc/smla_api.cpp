@@ -58,14 +58,15 @@ int check_params(const smla_params* p) {
 
 int tiles_of(const smla_params* p) { return (p->topk + smla::kTileRows - 1) / smla::kTileRows; }
 
-// Splits per token: enough workgroups to cover the 256 compute units when few tokens
-// are in flight, never more splits than tiles.
+// Splits per token: as many as keep the work items (token, split) within one round of the
+// device's compute units (one persistent workgroup each), never more splits than tiles.
+// Splitting past one round only adds a second round of items and the combine pass.
 int choose_splits(const smla_params* p) {
   const int tiles = tiles_of(p) > 0 ? tiles_of(p) : 1;
   int ns = p->num_splits;
   if (ns == 0) {
-    const int target = 256;
-    ns = p->s_q > 0 ? (target + p->s_q - 1) / p->s_q : 1;
+    const int cus = smla::device_cus();
+    ns = p->s_q > 0 ? cus / p->s_q : 1;
   }
   if (ns > tiles) ns = tiles;
   if (ns < 1) ns = 1;

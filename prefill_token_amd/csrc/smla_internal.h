@@ -34,4 +34,7 @@ inline size_t partial_floats(int h_q, int d) { return (size_t)h_q * (size_t)(d +
 // Enqueue the step; returns the HIP error of the first failed launch (hipSuccess if none).
 hipError_t launch(const LaunchArgs& a);
 
+// Compute units of the current device (256 if it cannot be queried).
+int device_cus();
+
 }  // namespace smla

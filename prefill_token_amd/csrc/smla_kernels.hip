@@ -1888,6 +1888,8 @@ __global__ __launch_bounds__(CTHREADS) void smla_combine(KArgs a) {
   epilogue<D, CTHREADS>(o_l, OSTR, 1, h, t, a, cs, sn);
 }
 
+}  // namespace
+
 // compute units of the current device (one persistent workgroup each)
 int device_cus() {
   static int cached[64] = {0};
@@ -1900,6 +1902,8 @@ int device_cus() {
   }
   return cached[dev];
 }
+
+namespace {
 
 template <int D, int EB>
 hipError_t launch_t(const LaunchArgs& x, const KArgs& k) {
