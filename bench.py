@@ -94,7 +94,7 @@ def measure(name, steps, warmup, torch, device, timed_steps=None):
                     kv_format=inp["kv_format"], sm_scale=inp["sm_scale"])
     ns = sparse_mla_num_splits(p)
     need = sparse_mla_workspace_size(p)
-    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=device)  # counters start at zero
 
     def call():
         sparse_mla_fwd(t["q"], t["kv_pool"], t["kv_scales"], t["indices"], t["topk_length"], t["positions"],

@@ -84,9 +84,12 @@ typedef struct smla_params {
                          workgroups (1..64) and combine */
   float* out_f32;   /* optional f32 [s_q][h_q][d]: o after inverse RoPE, before the FP8
                        cast (NULL = not written) */
-  void* workspace;  /* device scratch of >= sparse_mla_workspace_size(params) bytes, or
-                       NULL when that size is 0; contents need no initialization and
-                       are clobbered */
+  void* workspace;  /* device scratch of >= sparse_mla_workspace_size(params) bytes
+                       (NULL only when that size is 0).  Its first 256 bytes hold the
+                       work-item scheduler's counters: they must be zero before the
+                       first call on this workspace, and every call leaves them zero
+                       (zero-fill a new workspace once).  The rest (split partials) is
+                       clobbered.  Calls sharing a workspace must not overlap. */
   size_t workspace_bytes;
   void* stream;     /* hipStream_t */
 } smla_params;
@@ -121,10 +124,10 @@ int sparse_mla_fwd(const void* q, const void* kv_pool, const uint8_t* kv_scales,
                    const smla_params* params);
 
 /*
- * Bytes of device workspace sparse_mla_fwd needs for these parameters (0 when the
- * call runs unsplit).  Depends on s_q, h_q, d, topk and num_splits, and with
- * num_splits = 0 on the current device's compute-unit count.  Returns 0 for parameters
- * sparse_mla_fwd would reject.
+ * Bytes of device workspace sparse_mla_fwd needs for these parameters: 256 bytes of
+ * scheduler state, plus the split partials when the call is split (0 when s_q = 0).
+ * Depends on s_q, h_q, d, topk and num_splits, and with num_splits = 0 on the current
+ * device's compute-unit count.  Returns 0 for parameters sparse_mla_fwd would reject.
  */
 size_t sparse_mla_workspace_size(const smla_params* params);
 

@@ -75,8 +75,10 @@ def sparse_mla_fwd(q, kv_pool, kv_scales, indices, topk_length, positions, norm_
     kv_scales uint8 [n, d/32]) or bf16 [n, d] (kv_scales None); indices / topk_length /
     positions int32; norm_w float32 [d]; out_fp8 uint8 / float8_e4m3fn [s_q, h_q, d];
     out_scales uint8 [s_q, h_q, d/32]; out_f32 optional float32 [s_q, h_q, d].
-    ``workspace`` (a uint8 device tensor) is allocated here when the call needs one and
-    none is given.  Raises SmlaError with the library's message on failure.
+    ``workspace`` (a uint8 device tensor of at least sparse_mla_workspace_size bytes,
+    zero-filled before its first use; each call leaves its scheduler counters zero) is
+    allocated here, zero-filled, when none is given.  Calls sharing a workspace must not
+    overlap.  Raises SmlaError with the library's message on failure.
     """
     import torch
 
@@ -96,7 +98,8 @@ def sparse_mla_fwd(q, kv_pool, kv_scales, indices, topk_length, positions, norm_
                          out_f32=out_f32, workspace=workspace, stream=stream)
     need = sparse_mla_workspace_size(params)
     if need > 0 and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        # its scheduler counters must start at zero (every call leaves them zero)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
         params.workspace = _ptr(workspace)
         params.workspace_bytes = need
     rc = _lib.load().sparse_mla_fwd(_ptr(q), _ptr(kv_pool), _ptr(kv_scales), _ptr(indices), _ptr(topk_length),

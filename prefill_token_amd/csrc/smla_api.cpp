@@ -74,8 +74,9 @@ int choose_splits(const smla_params* p) {
 }
 
 size_t workspace_bytes_for(const smla_params* p, int ns) {
-  if (ns <= 1) return 0;
-  return (size_t)p->s_q * (size_t)ns * smla::partial_floats(p->h_q, p->d) * sizeof(float);
+  if (p->s_q <= 0) return 0;
+  const size_t part = ns <= 1 ? 0 : (size_t)p->s_q * (size_t)ns * smla::partial_floats(p->h_q, p->d) * sizeof(float);
+  return smla::kSchedBytes + part;
 }
 
 }  // namespace
@@ -135,7 +136,7 @@ int sparse_mla_fwd(const void* q, const void* kv_pool, const uint8_t* kv_scales,
   a.out_fp8 = out_fp8;
   a.out_scales = out_scales;
   a.out_f32 = p->out_f32;
-  a.workspace = static_cast<float*>(p->workspace);
+  a.workspace = p->workspace;
   a.s_q = p->s_q;
   a.h_q = p->h_q;
   a.d = p->d;

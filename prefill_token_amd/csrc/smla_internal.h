@@ -18,7 +18,7 @@ struct LaunchArgs {
   uint8_t* out_fp8;           // [s_q][h_q][d]
   uint8_t* out_scales;        // [s_q][h_q][d/32]
   float* out_f32;             // [s_q][h_q][d] or null
-  float* workspace;           // partials when num_splits > 1
+  void* workspace;            // scheduler state (kSchedBytes), then partials when num_splits > 1
   int s_q, h_q, d, rope_dim, topk, kv_format, num_splits;
   int64_t n_rows;
   float sm_scale, rms_eps, rope_theta;
@@ -27,6 +27,10 @@ struct LaunchArgs {
 
 // Rows of the index row processed per tile by one workgroup.
 constexpr int kTileRows = 64;
+
+// Bytes at the start of the workspace holding the work-item scheduler's two counters
+// (zero before a call, left zero by it).
+constexpr size_t kSchedBytes = 256;
 
 // Workspace floats per (token, split): acc [h_q][d] + m [h_q] + l [h_q].
 inline size_t partial_floats(int h_q, int d) { return (size_t)h_q * (size_t)(d + 2); }

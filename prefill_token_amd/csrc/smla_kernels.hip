@@ -167,7 +167,8 @@ struct KArgs {
   uint8_t* out_fp8;
   uint8_t* out_scales;
   float* out_f32;
-  float* ws;
+  float* ws;         // split partials (after the scheduler state)
+  unsigned* sched;   // work-item scheduler: [0] next item - gridDim.x, [1] finished workgroups
   int s_q, h_q, rope_dim, topk, num_splits, tiles_per_split;
   long long n_rows;
   float sm_scale, rms_eps, rope_theta;
@@ -1325,6 +1326,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
     // an item's prologue (its ids and q loads already issued): first-tile DMA (all of it),
     // cos / sin table, q tile
     auto transition = [&](auto nu_c, const uint4 (&x)[4][4]) {
+      // the item after this one, from the workspace's counter (published before B_A)
+      if (w == 0 && (((int)threadIdx.x + opaque_zero()) & 63) == 0)
+        flag_l[12] = (int)gridDim.x + (int)atomicAdd(a.sched, 1u);
       if (I.n > 0) {
         const int id0 = valid_id(I, I.tb, raw_cur);
 #pragma unroll
@@ -1346,6 +1350,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
     }
     while (true) {
       __syncthreads();  // B_A: q tile complete
+      const int next = __builtin_amdgcn_readfirstlane(flag_l[12]);
       const int lane = ((int)threadIdx.x + opaque_zero()) & 63, lrow = lane & 31, lhalf = lane >> 5;
       const uint32_t hsel = lhalf ? 0x07050301u : 0x06040200u;
       // q of the 32 heads of group qa, all 8 k-steps: lane half h holds dims 64ks + 16h +
@@ -1372,7 +1377,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
       __syncthreads();  // B_B: q tile read (the P.V waves overwrite it), first tile visible
 
       const int n = I.n;
-      const int next = item + (int)gridDim.x;
       float m_run = -INFINITY, l_run = 0.f, l_pend = 0.f;
       f32x16 s;  // scores of the last tile, kept for a rewrite of its P
       // flag check for tile it - 1 (it >= 1): the slow path merges the block maxima,
@@ -1523,6 +1527,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
       transition(std::integral_constant<int, 4>{}, x);  // waits for the q loads, and so for the touch loads before them
       asm volatile("" ::"v"(touch0), "v"(touch1));
     }
+    // this workgroup is done; the last one to finish leaves the counters zero for the
+    // next call on this workspace
+    if (w == 0 && (((int)threadIdx.x + opaque_zero()) & 63) == 0) {
+      if (atomicAdd(a.sched + 1, 1u) == gridDim.x - 1) {
+        atomicExch(a.sched, 0u);
+        atomicExch(a.sched + 1, 0u);
+      }
+    }
   } else {
     // =============================== P.V waves
     const int v = w - 4;
@@ -1539,6 +1551,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
     }
     while (true) {
       __syncthreads();  // B_A
+      const int next = __builtin_amdgcn_readfirstlane(flag_l[12]);
       __syncthreads();  // B_B
       const int n = I.n;
       f32x16 acc[2][4];  // O[64 heads][128 dims]
@@ -1699,8 +1712,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
         pv_iter(n, std::true_type{}, std::false_type{});
       }
 
-      // ---- finish of the item; the next item's q loads go out first
-      const int next = item + (int)gridDim.x;
+      // ---- finish of the item
       const bool more = next < total;
       Item In = I;
       if (more) In = info(next);
@@ -1935,7 +1947,8 @@ hipError_t launch(const LaunchArgs& x) {
   k.out_fp8 = x.out_fp8;
   k.out_scales = x.out_scales;
   k.out_f32 = x.out_f32;
-  k.ws = x.workspace;
+  k.sched = static_cast<unsigned*>(x.workspace);
+  k.ws = reinterpret_cast<float*>(static_cast<unsigned char*>(x.workspace) + kSchedBytes);
   k.s_q = x.s_q;
   k.h_q = x.h_q;
   k.rope_dim = x.rope_dim;

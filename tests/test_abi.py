@@ -133,7 +133,7 @@ def test_workspace_required_when_split(lib):
     ns = smla.sparse_mla_num_splits(p)
     assert ns > 1
     need = smla.sparse_mla_workspace_size(p)
-    assert need == 4 * ns * 64 * (512 + 2) * 4
+    assert need == 256 + 4 * ns * 64 * (512 + 2) * 4  # scheduler counters, then partials
     assert call(lib, p) == smla.SMLA_ERR_VALUE  # no workspace given
     assert "workspace" in smla.sparse_mla_last_error()
     p.workspace, p.workspace_bytes = FAKE, need - 1
@@ -145,7 +145,7 @@ def test_split_choice():
     assert smla.sparse_mla_num_splits(good(s_q=2123)) == 1
     assert smla.sparse_mla_num_splits(good(s_q=1, num_splits=3)) == 3
     assert smla.sparse_mla_num_splits(good(s_q=1, num_splits=64)) == 10  # capped at the tile count
-    assert smla.sparse_mla_workspace_size(good(s_q=2123)) == 0
+    assert smla.sparse_mla_workspace_size(good(s_q=2123)) == 256  # the scheduler counters only
 
 
 def test_zero_tokens_is_a_noop(lib):
