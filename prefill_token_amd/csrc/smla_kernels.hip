@@ -7,8 +7,16 @@
 // beyond topk_length are never read and -1 marks an empty slot [same page, Purpose,
 // bug-fix bullet].
 //
-// Work decomposition: one 512-thread workgroup (8 wave64, two per SIMD) per token, or
-// per token split when few tokens are in flight.
+// Two main kernels compute the step:
+//   smla_ws    the production shape (d = 512, E4M3 + UE8M0 pool, rope_dim 0 or 64): a
+//              persistent grid of one 512-thread workgroup per compute unit walking the
+//              work items (token, split), with QK and P.V waves specialized per SIMD and
+//              one barrier per 64-entry tile (its own comment below has the details);
+//   smla_main  every other shape: one workgroup per work item, described here.
+// smla_combine merges the splits of a token when a call is split.
+//
+// smla_main: one 512-thread workgroup (8 wave64, two per SIMD) per token, or per token
+// split when few tokens are in flight.
 //   prologue   one thread per (head, 32-dim block): q -> RMSNorm -> RoPE (angles in
 //              fp64) -> times sm_scale*log2(e).  For the E4M3 pool q is split into two
 //              E4M3 terms (hi + lo) with their own UE8M0 scales per 32 dims (about 8

@@ -40,7 +40,8 @@ def to_device(inp: dict, device="cuda"):
     return t
 
 
-def run_gpu(inp: dict, *, num_splits: int = 0, with_f32: bool = True, device="cuda", dev_inputs=None):
+def run_gpu(inp: dict, *, num_splits: int = 0, with_f32: bool = True, device="cuda", dev_inputs=None,
+            workspace=None):
     from prefill_token_amd import sparse_mla_fwd
 
     t = dev_inputs if dev_inputs is not None else to_device(inp, device)
@@ -50,7 +51,8 @@ def run_gpu(inp: dict, *, num_splits: int = 0, with_f32: bool = True, device="cu
     out_f32 = torch.empty((s_q, h, d), dtype=torch.float32, device=device) if with_f32 else None
     sparse_mla_fwd(t["q"], t["kv_pool"], t["kv_scales"], t["indices"], t["topk_length"], t["positions"],
                    t["norm_w"], out_fp8, out_sc, sm_scale=inp["sm_scale"], rope_dim=inp["rope_dim"],
-                   eps=inp["eps"], theta=inp["theta"], out_f32=out_f32, num_splits=num_splits)
+                   eps=inp["eps"], theta=inp["theta"], out_f32=out_f32, num_splits=num_splits,
+                   workspace=workspace)
     torch.cuda.synchronize()
     return dict(codes=out_fp8.cpu().numpy(), scales=out_sc.cpu().numpy(),
                 f32=None if out_f32 is None else out_f32.cpu().numpy())

@@ -6,7 +6,9 @@ the 2123-token prefill at full size in the benchmark's launch configuration, che
 sampled tokens the oracle computes one by one.  Edge cases: every tile boundary of
 topk_length, empty and all-sentinel rows, stale ids beyond topk_length pointing at rows
 that decode to NaN, duplicates, position 0, fewer heads, no rotary dims, the E4M3 pool at
-d = 128, the ends of the exact scale range, forced split counts, and bit-reproducibility.
+d = 128, the ends of the exact scale range, forced split counts, bit-reproducibility, and
+one workspace shared by successive calls of different shapes (its scheduler counters are
+left zero by every call).
 """
 import numpy as np
 import pytest
@@ -169,3 +171,28 @@ def test_bit_reproducible():
         b = run_gpu(inp, dev_inputs=dev, num_splits=ns)
         for k in ("codes", "scales", "f32"):
             assert a[k].tobytes() == b[k].tobytes(), (ns, k)
+
+
+def test_workspace_reused_across_calls():
+    # The first 256 bytes of the workspace are the work-item counters: every call must
+    # leave them zero, so one zero-filled workspace serves successive calls of any shape.
+    from prefill_token_amd import make_params, sparse_mla_workspace_size
+
+    cases = [_decode_case(21, s_q=300), _decode_case(22, s_q=3), _decode_case(23, s_q=300)]
+    need = 0
+    for inp in cases:
+        s_q, h, d = inp["q"].shape
+        for ns in (0, 1, 4):
+            p = make_params(s_q=s_q, h_q=h, d=d, rope_dim=inp["rope_dim"], topk=inp["topk"], n_rows=inp["n_rows"],
+                            kv_format=inp["kv_format"], sm_scale=inp["sm_scale"], num_splits=ns)
+            need = max(need, sparse_mla_workspace_size(p))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for inp in cases:
+        dev = to_device(inp)
+        for ns in (0, 1, 4):
+            a = run_gpu(inp, dev_inputs=dev, num_splits=ns, workspace=ws)
+            assert int(ws[:256].count_nonzero()) == 0, ("counters not reset", ns)
+            b = run_gpu(inp, dev_inputs=dev, num_splits=ns)  # a fresh workspace
+            for k in ("codes", "scales", "f32"):
+                assert a[k].tobytes() == b[k].tobytes(), (ns, k)
+    compare(run_gpu(cases[0], workspace=ws), run_oracle(cases[0]))
