@@ -1144,11 +1144,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
     I.n = I.te > I.tb ? I.te - I.tb : 0;
     return I;
   };
-  // Index entry tile*64 + lane, fetched before it is used (clamped into the row); its
-  // value is only looked at after a vmcnt(0) wait of the tile loop.
+  // Index entry tile*64 + lane, fetched before it is used (clamped into the row, read
+  // through a range-checked buffer so that the load has no branch: with topk = 0 it reads
+  // zero, which valid_id rejects); its value is only looked at after a wait that covers it.
   auto fetch_id = [&](const Item& I, int tile) -> int {
     const int j = tile * T + (((int)threadIdx.x + opaque_zero()) & 63);
-    return a.topk > 0 ? a.indices[(size_t)I.t * a.topk + (j < a.topk ? j : a.topk - 1)] : -1;
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(a.indices + (size_t)I.t * a.topk, (uint32_t)a.topk * 4u);
+    return (int)__builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)(j < a.topk ? j : a.topk - 1) * 4u, 0, 0);
   };
   // the id if entry tile*64 + lane is read, else -1 (beyond the length, a sentinel, or
   // outside [0, n_rows))
@@ -1192,14 +1194,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
     // hoisted out of the item loop and kept live across it
     const int tid = (int)threadIdx.x + opaque_zero(), qb = tid & 15;
     const auto& K = karg();
-    const uint16_t* qp = K.q;
     const int hq = K.h_q;
+    // the token's rows as a range-checked buffer: heads >= h_q read as zeros without a
+    // branch, so every load is issued unconditionally and waits on them can count
+    const __amdgpu_buffer_rsrc_t qrs = buf_rsrc(K.q + (size_t)I.t * hq * D, (uint32_t)(hq * D * 2));
 #pragma unroll
     for (int k = 0; k < NU; ++k) {
       const int head = (tid >> 4) + (64 / NU) * k;
-      const uint4* src = reinterpret_cast<const uint4*>(qp + ((size_t)I.t * hq + head) * D + 32 * qb);
+      const uint32_t off = (uint32_t)(head * D + 32 * qb) * 2u;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) x[k][j] = head < hq ? src[j] : make_uint4(0u, 0u, 0u, 0u);
+      for (int j = 0; j < 4; ++j) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(qrs, off + 16u * j, 0, 0);
+        x[k][j] = make_uint4(v[0], v[1], v[2], v[3]);
+      }
     }
   };
   // cos / sin of angle pos * theta^(-2i/64), i < 32: the angle in fp64 (the inverse
@@ -1313,17 +1320,21 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
     }
   };
 
-  // norm_w into LDS once (block b at 36 b floats: the 16 lanes of a head read 16 distinct
-  // banks)
-  if (tid < D / 4) {
-    const float4 w4 = reinterpret_cast<const float4*>(a.norm_w)[tid];
-    *reinterpret_cast<float4*>(smem + C::OFF_NW + 4 * (36 * (tid / 8) + 4 * (tid % 8))) = w4;
-  }
-  if (rot && tid >= 448 && tid < 480) {  // inverse frequencies theta^(-2i/r) in fp64
-    const int i = tid - 448;
-    reinterpret_cast<double*>(smem + C::OFF_IFREQ)[i] = exp2(-(2.0 * i / (double)a.rope_dim) * a.log2_theta);
-  }
-  __syncthreads();
+  // Set-up shared by all waves, published by the first barrier of either branch (each
+  // branch issues its first item's loads before its share of it): norm_w into LDS once
+  // (block b at 36 b floats: the 16 lanes of a head read 16 distinct banks) and the
+  // inverse frequencies theta^(-2i/r) in fp64.
+  // The norm_w load goes out first so that its wait leaves the q loads in flight.
+  float4 nw4;
+  if (tid < D / 4) nw4 = reinterpret_cast<const float4*>(a.norm_w)[tid];
+  auto setup = [&]() __attribute__((always_inline)) {
+    if (tid < D / 4) *reinterpret_cast<float4*>(smem + C::OFF_NW + 4 * (36 * (tid / 8) + 4 * (tid % 8))) = nw4;
+    if (rot && tid >= 448 && tid < 480) {
+      const int i = tid - 448;
+      reinterpret_cast<double*>(smem + C::OFF_IFREQ)[i] = exp2(-(2.0 * i / (double)a.rope_dim) * a.log2_theta);
+    }
+    __syncthreads();
+  };
 
   if (w < 4) {
     // =============================== QK waves
@@ -1334,26 +1345,30 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
     // an item's prologue (its ids and q loads already issued): first-tile DMA (all of it),
     // cos / sin table, q tile
     auto transition = [&](auto nu_c, const uint4 (&x)[4][4]) {
-      // the item after this one, from the workspace's counter (published before B_A)
-      if (w == 0 && (((int)threadIdx.x + opaque_zero()) & 63) == 0)
-        flag_l[12] = (int)gridDim.x + (int)atomicAdd(a.sched, 1u);
-      if (I.n > 0) {
-        const int id0 = valid_id(I, I.tb, raw_cur);
+      // the item after this one, from the workspace's counter: fetched first, published
+      // (before B_A) last, so that waiting for it holds nothing up
+      const bool leader = w == 0 && (((int)threadIdx.x + opaque_zero()) & 63) == 0;
+      unsigned nx = 0;
+      if (leader) nx = atomicAdd(a.sched, 1u);
+      // the DMA is issued without a branch (an item without tiles moves zeros), so the
+      // waits for the q loads ahead of it can count
+      const int id0 = valid_id(I, I.tb, raw_cur);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          dma_part(k, w, id0, raw_buf(0), sc_buf(0));
-          dma_part(k, w + 4, id0, raw_buf(0), sc_buf(0));
-        }
-        dma_part(4, w, id0, raw_buf(0), sc_buf(0));
+      for (int k = 0; k < 4; ++k) {
+        dma_part(k, w, id0, raw_buf(0), sc_buf(0));
+        dma_part(k, w + 4, id0, raw_buf(0), sc_buf(0));
       }
+      dma_part(4, w, id0, raw_buf(0), sc_buf(0));
       rope_tab(I);
       q_units(nu_c, x);
+      if (leader) flag_l[12] = (int)gridDim.x + (int)nx;
     };
     {
       raw_cur = fetch_id(I, I.tb);
       raw_next = fetch_id(I, I.tb + 1);
       uint4 x[4][4];
       q_load(I, std::integral_constant<int, 2>{}, x);
+      setup();
       transition(std::integral_constant<int, 2>{}, x);
     }
     while (true) {
@@ -1554,6 +1569,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
       // this wave's table also serves the epilogue's inverse RoPE
       uint4 x[4][4];
       q_load(I, std::integral_constant<int, 2>{}, x);
+      setup();
       rope_tab(I);
       q_units(std::integral_constant<int, 2>{}, x);
     }
