@@ -6,7 +6,8 @@ this wrapper loads ``liboracle.so`` built from ``sparse_mla_oracle.c`` by plain 
 
 The functions mirror the steps of the C file (each cites its passage there):
 ``bf16_decode``, ``e4m3_decode``, ``e4m3_encode``, ``ue8m0_exponent``,
-``quantize_blocks``, ``rmsnorm``, ``rope`` and the whole step ``sparse_mla``.
+``quantize_blocks``, ``rmsnorm``, ``rope``, the whole step ``sparse_mla`` and the pool-row
+producer before it, ``kv_insert``.
 
 Parity pins: every function here is checked in ``tests/test_oracle_*.py`` against
 library routines (torch's CPU float8_e4m3fn cast, torch SDPA and rms_norm in fp64,
@@ -70,6 +71,9 @@ def _load():
                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_double,
                                       ctypes.c_double, P, P, P]
+    lib.oracle_kv_insert.restype = ctypes.c_int
+    lib.oracle_kv_insert.argtypes = [P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int64, ctypes.c_double, ctypes.c_double, P, P]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     _lib = lib
@@ -179,3 +183,26 @@ def sparse_mla(q_bits: np.ndarray, kv_pool: np.ndarray, kv_scales: Optional[np.n
     if rc != 0:
         raise ValueError(f"oracle_sparse_mla failed with code {rc}")
     return o, codes, scales
+
+
+def kv_insert(kv_bits: np.ndarray, positions: np.ndarray, norm_w: np.ndarray, kv_pool: np.ndarray,
+              kv_scales: np.ndarray, *, n_swa: int, eps: float, theta: float, rope_dim: int):
+    """KV insert into copies of the pool: rows ``positions mod n_swa`` get the E4M3 codes and
+    UE8M0 exponents of RoPE(RMSNorm(kv)); negative positions are skipped.
+
+    ``kv_bits`` u16 [n, d]; ``kv_pool`` u8 [n_rows, d]; ``kv_scales`` u8 [n_rows, d/32].
+    Returns ``(kv_pool, kv_scales)`` (new arrays).  Raises ``ValueError`` on bad arguments.
+    """
+    lib = _load()
+    kv_bits = np.ascontiguousarray(kv_bits, dtype=np.uint16)
+    n, d = kv_bits.shape
+    pool = np.ascontiguousarray(kv_pool, dtype=np.uint8).copy()
+    sc = np.ascontiguousarray(kv_scales, dtype=np.uint8).copy()
+    assert pool.shape[1] == d and sc.shape == (pool.shape[0], d // 32)
+    positions = np.ascontiguousarray(positions, dtype=np.int32)
+    norm_w = np.ascontiguousarray(norm_w, dtype=np.float64)
+    rc = lib.oracle_kv_insert(_ptr(kv_bits), _ptr(positions), _ptr(norm_w), n, d, int(rope_dim), int(n_swa),
+                              pool.shape[0], float(eps), float(theta), _ptr(pool), _ptr(sc))
+    if rc != 0:
+        raise ValueError(f"oracle_kv_insert failed with code {rc}")
+    return pool, sc

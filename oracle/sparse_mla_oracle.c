@@ -283,6 +283,53 @@ int oracle_sparse_mla(const uint16_t* q, const void* kv_pool, const uint8_t* kv_
   return status;
 }
 
+/* ---------------------------------------------------------------- KV insert */
+
+/*
+ * KV insert, the producer of the pool rows the step gathers
+ *   [vLLM #56344 "Deepseek V41 Attention MegaKernel", Purpose: fp8 SWA cache rows of 512
+ *    E4M3 bytes + UE8M0 scales written by an insert kernel]
+ *   [vLLM #64364 "latency_specialized decode", Details, change table: the KV cache write
+ *    happens in the kernel that normalises and quantizes q and kv]
+ * Readings: the kv latent is RMS-normalised like a q head (same formula, its own weight),
+ * its last r dims carry RoPE at the token's own position (the step's inverse RoPE on
+ * the output only undoes a rotation the stored rows carry), and it is quantized with the
+ * step's output codec; the row is the position modulo the window size n_swa, and a
+ * negative position means "no token".  Tokens are applied in order (a later token that
+ * lands on the same row overwrites an earlier one).
+ *   kv         bf16 bits [n][d]
+ *   positions  i32 [n]
+ *   norm_w     f64 [d]
+ *   kv_pool    u8 [n_rows][d] (rows pos mod n_swa overwritten)
+ *   kv_scales  u8 [n_rows][d/32]
+ */
+int oracle_kv_insert(const uint16_t* kv, const int32_t* positions, const double* norm_w, int n, int d,
+                     int rope_dim, int n_swa, int64_t n_rows, double eps, double theta, uint8_t* kv_pool,
+                     uint8_t* kv_scales) {
+  int t, i;
+  double *x, *y;
+  if (n < 0 || d < 1 || d % BLOCK != 0 || rope_dim < 0 || rope_dim > d || rope_dim % 2 != 0 || n_swa < 1 ||
+      (int64_t)n_swa > n_rows)
+    return ORACLE_ERR_ARG;
+  x = (double*)malloc(sizeof(double) * (size_t)d);
+  y = (double*)malloc(sizeof(double) * (size_t)d);
+  if (!x || !y) {
+    free(x); free(y);
+    return ORACLE_ERR_NOMEM;
+  }
+  for (t = 0; t < n; ++t) {
+    int64_t row;
+    if (positions[t] < 0) continue;
+    row = positions[t] % n_swa;
+    for (i = 0; i < d; ++i) x[i] = oracle_bf16_decode(kv[(int64_t)t * d + i]);
+    oracle_rmsnorm(x, norm_w, d, eps, y);
+    oracle_rope(y, d, rope_dim, (double)positions[t], theta, +1);
+    oracle_quantize_blocks(y, d, kv_pool + row * d, kv_scales + row * (d / BLOCK));
+  }
+  free(x); free(y);
+  return ORACLE_OK;
+}
+
 /* Number of OpenMP threads a parallel region of the oracle uses. */
 int oracle_num_threads(void) {
 #ifdef _OPENMP
