@@ -135,6 +135,51 @@ size_t sparse_mla_workspace_size(const smla_params* params);
    or 0 for parameters it would reject. */
 int sparse_mla_num_splits(const smla_params* params);
 
+/*
+ * KV insert: the producer of the pool rows sparse_mla_fwd gathers (the step before it).
+ * For every new token i with p = positions[i] >= 0:
+ *
+ *   1. x = kv[i, :] (bf16); y = x / sqrt(mean(x^2) + rms_eps) * norm_w      (RMSNorm)
+ *   2. rotate-half RoPE on the last rope_dim dims of y at angle p * rope_theta^(-2j/rope_dim)
+ *   3. per 32-element block: e = smallest integer in [0, 254] with 448 * 2^(e-127) >= max|y|,
+ *      kv_scales[p mod n_swa, block] = e,
+ *      kv_pool[p mod n_swa, block elements] = round-to-nearest-even E4M3FN(y * 2^(127-e))
+ *
+ * [vLLM #56344 "Deepseek V41 Attention MegaKernel", Purpose: the fp8 SWA cache row, 512
+ *  E4M3 bytes plus UE8M0 scales, written by an insert kernel; vLLM #64364
+ *  "latency_specialized decode", Details, change table: the KV cache write folded into the
+ *  norm + quantization kernel.]  Rows 0 .. n_swa-1 of the pool are the sliding-window ring;
+ * a token's row is its position modulo n_swa.  Tokens with a negative position are
+ * skipped (their rows are left as they are).  The arithmetic is fp64, so the codes and
+ * exponents are those of an exact-arithmetic evaluation of steps 1-3 (up to the last-bit
+ * rounding of the sum of squares and the cosine / sine).
+ *
+ *   kv          bf16 [n][512]            (device, read; 16-byte aligned)
+ *   positions   i32 [n]                  (device, read)
+ *   norm_w      f32 [512]                (device, read; 16-byte aligned)
+ *   kv_pool     u8 [n_rows][512]         (device, rows p mod n_swa written; 16-byte aligned)
+ *   kv_scales   u8 [n_rows][16]          (device, rows p mod n_swa written; 4-byte aligned)
+ *   params      host pointer, read during the call only
+ *
+ * Precondition not checked on the device: the non-negative positions of one call fall
+ * on distinct rows (distinct modulo n_swa); rows written by two tokens of one call hold
+ * an unspecified mixture.  Same conventions as sparse_mla_fwd otherwise (asynchronous on
+ * params->stream, nothing allocated, errors by return code with nothing launched).
+ */
+typedef struct smla_kv_insert_params {
+  int32_t n;        /* tokens to insert (0 = no-op) */
+  int32_t d;        /* latent dim: 512 */
+  int32_t rope_dim; /* rotary dims at the end of the row: 0..d, a multiple of 16 */
+  int32_t n_swa;    /* sliding-window rows at the start of the pool: 1..n_rows */
+  int64_t n_rows;   /* rows of kv_pool; n_rows * 512 must stay below 4 GiB */
+  float rms_eps;    /* RMSNorm epsilon, finite and > 0 */
+  float rope_theta; /* RoPE base, finite and > 0 */
+  void* stream;     /* hipStream_t */
+} smla_kv_insert_params;
+
+int sparse_mla_kv_insert(const void* kv, const int32_t* positions, const float* norm_w, uint8_t* kv_pool,
+                         uint8_t* kv_scales, const smla_kv_insert_params* params);
+
 /* Thread-local, NUL-terminated message describing the last failed call on this thread
    ("" if none).  Valid until the next call on the same thread. */
 const char* sparse_mla_last_error(void);

@@ -15,19 +15,20 @@ from typing import Optional
 
 from . import _lib
 from ._lib import (SMLA_ERR_HIP, SMLA_ERR_NULL, SMLA_ERR_SHAPE, SMLA_ERR_VALUE, SMLA_KV_BF16,
-                   SMLA_KV_E4M3_UE8M0, SMLA_OK, LibraryMissing, SmlaParams, last_error)
+                   SMLA_KV_E4M3_UE8M0, SMLA_OK, LibraryMissing, SmlaKvInsertParams, SmlaParams, last_error)
 
 __all__ = [
     "sparse_mla_fwd", "sparse_mla_workspace_size", "sparse_mla_num_splits", "sparse_mla_last_error",
-    "sparse_mla_abi_version", "make_params", "SmlaParams", "SmlaError", "LibraryMissing",
+    "sparse_mla_abi_version", "sparse_mla_kv_insert", "make_params", "make_kv_insert_params", "SmlaParams",
+    "SmlaKvInsertParams", "SmlaError", "LibraryMissing",
     "SMLA_OK", "SMLA_ERR_NULL", "SMLA_ERR_SHAPE", "SMLA_ERR_VALUE", "SMLA_ERR_HIP",
     "SMLA_KV_E4M3_UE8M0", "SMLA_KV_BF16",
 ]
 
 
 class SmlaError(RuntimeError):
-    def __init__(self, code: int, msg: str):
-        super().__init__(f"sparse_mla_fwd failed (code {code}): {msg}")
+    def __init__(self, code: int, msg: str, fn: str = "sparse_mla_fwd"):
+        super().__init__(f"{fn} failed (code {code}): {msg}")
         self.code = code
 
 
@@ -107,3 +108,37 @@ def sparse_mla_fwd(q, kv_pool, kv_scales, indices, topk_length, positions, norm_
                                     ctypes.byref(params))
     if rc != SMLA_OK:
         raise SmlaError(rc, last_error())
+
+
+def make_kv_insert_params(*, n: int, rope_dim: int, n_swa: int, n_rows: int, d: int = 512, eps: float = 1e-6,
+                          theta: float = 1e4, stream=None) -> SmlaKvInsertParams:
+    p = SmlaKvInsertParams()
+    p.n, p.d, p.rope_dim, p.n_swa, p.n_rows = n, d, rope_dim, n_swa, n_rows
+    p.rms_eps, p.rope_theta = eps, theta
+    p.stream = stream
+    return p
+
+
+def sparse_mla_kv_insert(kv, positions, norm_w, kv_pool, kv_scales, *, rope_dim: int, n_swa: int,
+                         eps: float = 1e-6, theta: float = 1e4, stream=None) -> None:
+    """Enqueue the KV insert on the current (or given) HIP stream.
+
+    kv bf16 [n, 512]; positions int32 [n] (negative = skip); norm_w float32 [512];
+    kv_pool uint8 / float8_e4m3fn [n_rows, 512] and kv_scales uint8 [n_rows, 16], whose
+    rows ``positions mod n_swa`` are overwritten.  Raises SmlaError on failure.
+    """
+    import torch
+
+    for name, t in (("kv", kv), ("positions", positions), ("norm_w", norm_w), ("kv_pool", kv_pool),
+                    ("kv_scales", kv_scales)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    n, d = kv.shape
+    if stream is None:
+        stream = torch.cuda.current_stream(kv.device).cuda_stream
+    params = make_kv_insert_params(n=n, d=d, rope_dim=rope_dim, n_swa=n_swa, n_rows=kv_pool.shape[0], eps=eps,
+                                   theta=theta, stream=stream)
+    rc = _lib.load().sparse_mla_kv_insert(_ptr(kv), _ptr(positions), _ptr(norm_w), _ptr(kv_pool), _ptr(kv_scales),
+                                          ctypes.byref(params))
+    if rc != SMLA_OK:
+        raise SmlaError(rc, last_error(), "sparse_mla_kv_insert")

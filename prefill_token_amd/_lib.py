@@ -39,6 +39,21 @@ class SmlaParams(ctypes.Structure):
     ]
 
 
+class SmlaKvInsertParams(ctypes.Structure):
+    """Mirror of ``smla_kv_insert_params``."""
+
+    _fields_ = [
+        ("n", ctypes.c_int32),
+        ("d", ctypes.c_int32),
+        ("rope_dim", ctypes.c_int32),
+        ("n_swa", ctypes.c_int32),
+        ("n_rows", ctypes.c_int64),
+        ("rms_eps", ctypes.c_float),
+        ("rope_theta", ctypes.c_float),
+        ("stream", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 
 
@@ -65,6 +80,8 @@ def load() -> ctypes.CDLL:
     lib.sparse_mla_num_splits.argtypes = [ctypes.POINTER(SmlaParams)]
     lib.sparse_mla_last_error.restype = ctypes.c_char_p
     lib.sparse_mla_last_error.argtypes = []
+    lib.sparse_mla_kv_insert.restype = ctypes.c_int
+    lib.sparse_mla_kv_insert.argtypes = [P, P, P, P, P, ctypes.POINTER(SmlaKvInsertParams)]
     lib.sparse_mla_abi_version.restype = ctypes.c_int
     lib.sparse_mla_abi_version.argtypes = []
     _lib = lib

@@ -1,5 +1,5 @@
-// C ABI of the fused sparse-MLA step (declared in include/smla.h): argument checks on
-// the host, split selection, workspace sizing and error reporting.  All checks run
+// C ABI of the fused sparse-MLA step and of the KV insert (declared in include/smla.h):
+// argument checks on the host, split selection, workspace sizing and error reporting.  All checks run
 // before any HIP call, so a rejected call enqueues nothing.
 #include <math.h>
 #include <stdarg.h>
@@ -150,6 +150,48 @@ int sparse_mla_fwd(const void* q, const void* kv_pool, const uint8_t* kv_scales,
   a.rope_theta = p->rope_theta;
   a.stream = static_cast<hipStream_t>(p->stream);
   const hipError_t e = smla::launch(a);
+  if (e != hipSuccess) return fail(SMLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return SMLA_OK;
+}
+
+int sparse_mla_kv_insert(const void* kv, const int32_t* positions, const float* norm_w, uint8_t* kv_pool,
+                         uint8_t* kv_scales, const smla_kv_insert_params* p) {
+  g_last_error.clear();
+  if (!p) return fail(SMLA_ERR_NULL, "params is NULL");
+  if (p->n < 0) return fail(SMLA_ERR_VALUE, "n must be >= 0 (got %d)", p->n);
+  if (p->d != 512) return fail(SMLA_ERR_SHAPE, "d must be 512 (got %d)", p->d);
+  if (p->rope_dim < 0 || p->rope_dim > p->d || p->rope_dim % 16 != 0)
+    return fail(SMLA_ERR_SHAPE, "rope_dim must be a multiple of 16 in [0, d] (got %d)", p->rope_dim);
+  if (p->n_rows < 1 || p->n_rows > 0xFFFFFFF0LL / p->d)
+    return fail(SMLA_ERR_SHAPE, "n_rows must be in [1, 4 GiB / 512) (got %lld)", (long long)p->n_rows);
+  if (p->n_swa < 1 || p->n_swa > p->n_rows)
+    return fail(SMLA_ERR_VALUE, "n_swa must be in [1, n_rows] (got %d)", p->n_swa);
+  if (!finite_pos(p->rms_eps)) return fail(SMLA_ERR_VALUE, "rms_eps must be finite and > 0");
+  if (!finite_pos(p->rope_theta)) return fail(SMLA_ERR_VALUE, "rope_theta must be finite and > 0");
+  if (p->n == 0) return SMLA_OK;
+  if (!kv || !positions || !norm_w || !kv_pool || !kv_scales)
+    return fail(SMLA_ERR_NULL, "a required array pointer is NULL");
+  const struct {
+    const void* ptr;
+    uintptr_t align;
+    const char* name;
+  } al[] = {{kv, 16, "kv"}, {norm_w, 16, "norm_w"}, {kv_pool, 16, "kv_pool"}, {kv_scales, 4, "kv_scales"}};
+  for (const auto& x : al)
+    if (reinterpret_cast<uintptr_t>(x.ptr) % x.align != 0)
+      return fail(SMLA_ERR_VALUE, "%s must be %u-byte aligned", x.name, (unsigned)x.align);
+  smla::KvInsertArgs a;
+  a.kv = static_cast<const uint16_t*>(kv);
+  a.positions = positions;
+  a.norm_w = norm_w;
+  a.kv_pool = kv_pool;
+  a.kv_scales = kv_scales;
+  a.n = p->n;
+  a.rope_dim = p->rope_dim;
+  a.n_swa = p->n_swa;
+  a.rms_eps = p->rms_eps;
+  a.rope_theta = p->rope_theta;
+  a.stream = static_cast<hipStream_t>(p->stream);
+  const hipError_t e = smla::launch_kv_insert(a);
   if (e != hipSuccess) return fail(SMLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return SMLA_OK;
 }

@@ -41,4 +41,18 @@ hipError_t launch(const LaunchArgs& a);
 // Compute units of the current device (256 if it cannot be queried).
 int device_cus();
 
+// KV insert (the pool-row producer): one token per wave64, d = 512.
+struct KvInsertArgs {
+  const uint16_t* kv;        // bf16 bits [n][512]
+  const int32_t* positions;  // [n]; tokens with a negative position are skipped
+  const float* norm_w;       // [512]
+  uint8_t* kv_pool;          // u8 E4M3 [n_rows][512]; row p mod n_swa is written
+  uint8_t* kv_scales;        // u8 UE8M0 [n_rows][16]
+  int n, rope_dim, n_swa;
+  float rms_eps, rope_theta;
+  hipStream_t stream;
+};
+
+hipError_t launch_kv_insert(const KvInsertArgs& a);
+
 }  // namespace smla

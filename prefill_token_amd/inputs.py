@@ -177,6 +177,41 @@ def make(workload, seed: Optional[int] = None, s_q: Optional[int] = None) -> dic
     )
 
 
+# KV insert workloads (the pool-row producer before the step): the tokens of the
+# decode / prefill workloads above, written into pools of the same sizes.
+#   name                    n     pools (SWA + compressed)   positions
+INSERT_WORKLOADS = {
+    "insert_decode_sq1": (1, 8192, 2048, "decode"),
+    "insert_decode_sq64": (64, 8192, 2048, "decode"),
+    "insert_prefill_sq2123": (2123, 8192, 16384, "prefill"),
+}
+
+
+def make_insert(name: str, seed: Optional[int] = None, n: Optional[int] = None) -> dict:
+    """Inputs of one KV-insert workload: kv latents ~ N(0, 1) in bf16, a norm weight
+    ~ N(1, 0.1), positions (decode: uniform in [0, 32768) on distinct window rows;
+    prefill: contiguous from a random offset below 30000), and a pool of random bytes
+    (its rows are only overwritten, never decoded).  Seed 20261000 + the workload's
+    position in ``INSERT_WORKLOADS`` unless ``seed`` is given."""
+    names = list(INSERT_WORKLOADS)
+    n0, n_swa, n_comp, kind = INSERT_WORKLOADS[name]
+    rng = np.random.Generator(np.random.PCG64(SEED_BASE + 1000 + names.index(name) if seed is None else seed))
+    N = n0 if n is None else int(n)
+    d = 512
+    if kind == "prefill":
+        positions = (int(rng.integers(0, 30000)) + np.arange(N)).astype(np.int32)
+    else:
+        rows = rng.choice(n_swa, size=N, replace=False)
+        positions = (rows + n_swa * rng.integers(0, 32768 // n_swa, size=N)).astype(np.int32)
+    norm_w = bf16_values(bf16_bits(rng.normal(1.0, 0.1, size=d).astype(np.float32)))
+    kv = bf16_bits(rng.standard_normal(size=(N, d), dtype=np.float32))
+    pool = rng.integers(0, 256, size=(n_swa + n_comp, d), dtype=np.uint8)
+    scales = rng.integers(100, 140, size=(n_swa + n_comp, d // 32), dtype=np.uint8)
+    return dict(name=name, n=N, d=d, rope_dim=64, n_swa=n_swa, n_rows=n_swa + n_comp,
+                eps=1e-6, theta=10000.0, kv=kv, positions=positions, norm_w=norm_w.astype(np.float32),
+                kv_pool=pool, kv_scales=scales)
+
+
 def take_tokens(inp: dict, tokens) -> dict:
     """The same inputs restricted to a subset of tokens (the pool is shared)."""
     tokens = np.asarray(tokens, dtype=np.int64)

@@ -158,3 +158,59 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(_lib.LibraryMissing):
         _lib.load()
+
+
+# ---------------------------------------------------------------- KV insert
+
+
+def good_insert(**kw):
+    base = dict(n=4, rope_dim=64, n_swa=8192, n_rows=10240)
+    base.update(kw)
+    return smla.make_kv_insert_params(**base)
+
+
+def call_insert(lib, p, null=None, off=None):
+    ptrs = [FAKE] * 5
+    if null is not None:
+        ptrs[null] = None
+    if off is not None:
+        ptrs[off[0]] = FAKE + off[1]
+    return lib.sparse_mla_kv_insert(*ptrs, ctypes.byref(p) if p is not None else None)
+
+
+def test_insert_struct_layout():
+    P = smla.SmlaKvInsertParams
+    assert P.n_rows.offset == 16 and P.rms_eps.offset == 24 and P.stream.offset == 32 and ctypes.sizeof(P) == 40
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=128), smla.SMLA_ERR_SHAPE),
+    (dict(rope_dim=24), smla.SMLA_ERR_SHAPE),
+    (dict(rope_dim=528), smla.SMLA_ERR_SHAPE),
+    (dict(n_rows=0), smla.SMLA_ERR_SHAPE),
+    (dict(n_rows=(1 << 32) // 512), smla.SMLA_ERR_SHAPE),
+    (dict(n=-1), smla.SMLA_ERR_VALUE),
+    (dict(n_swa=0), smla.SMLA_ERR_VALUE),
+    (dict(n_swa=10241), smla.SMLA_ERR_VALUE),
+    (dict(eps=0.0), smla.SMLA_ERR_VALUE),
+    (dict(theta=float("inf")), smla.SMLA_ERR_VALUE),
+])
+def test_insert_rejected_parameters(lib, kw, code):
+    assert call_insert(lib, good_insert(**kw)) == code
+    assert smla.sparse_mla_last_error() != ""
+
+
+@pytest.mark.parametrize("which", range(5))
+def test_insert_null_arrays(lib, which):
+    assert call_insert(lib, good_insert(), null=which) == smla.SMLA_ERR_NULL
+
+
+@pytest.mark.parametrize("which,off", [(0, 8), (2, 4), (3, 8), (4, 2)])
+def test_insert_misaligned(lib, which, off):
+    assert call_insert(lib, good_insert(), off=(which, off)) == smla.SMLA_ERR_VALUE
+    assert "aligned" in smla.sparse_mla_last_error()
+
+
+def test_insert_null_params_and_empty(lib):
+    assert lib.sparse_mla_kv_insert(*([FAKE] * 5), None) == smla.SMLA_ERR_NULL
+    assert lib.sparse_mla_kv_insert(*([None] * 5), ctypes.byref(good_insert(n=0))) == smla.SMLA_OK
