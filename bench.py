@@ -16,6 +16,8 @@ Prints one JSON line:
   cpu_baseline the fp64 oracle on a bounded sample of the same recipe, on the host cores
   configs      per workload: us/call (warm and after a cache flush), tokens/s, HBM and
                MFMA fractions
+  kv_insert    the KV-insert entry point (the pool-row producer) on its three workloads:
+               us/call, tokens/s, algorithmic HBM bytes / mean duration against 8 TB/s
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
@@ -184,6 +186,50 @@ def measure(name, steps, warmup, torch, device, timed_steps=None):
     return res, wall, n
 
 
+def measure_insert(name, steps, torch, device):
+    """Time the KV insert (the pool-row producer) on one insert workload.
+
+    Algorithmic bytes per token: the bf16 latent read (2 d), its position (4), the E4M3
+    row and its UE8M0 scales written (d + d/32); plus norm_w (4 d) once per call."""
+    from prefill_token_amd import inputs, sparse_mla_kv_insert
+
+    c = inputs.make_insert(name)
+    kv = torch.from_numpy(c["kv"].view(np.int16)).to(device).view(torch.bfloat16)
+    pos = torch.from_numpy(c["positions"]).to(device)
+    w = torch.from_numpy(c["norm_w"]).to(device)
+    pool = torch.from_numpy(c["kv_pool"]).to(device)
+    sc = torch.from_numpy(c["kv_scales"]).to(device)
+
+    def call():
+        sparse_mla_kv_insert(kv, pos, w, pool, sc, rope_dim=c["rope_dim"], n_swa=c["n_swa"], eps=c["eps"],
+                             theta=c["theta"])
+
+    call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(CALLS_PER_GRAPH):
+            call()
+    stream = torch.cuda.current_stream()
+    reps = max(1, steps // CALLS_PER_GRAPH)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    g.replay()
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 / CALLS_PER_GRAPH for a, b in ev])
+    n, d = c["n"], c["d"]
+    nbytes = float(n * (2 * d + 4 + d + d // 32) + 4 * d)
+    mean_us = float(us.mean())
+    return dict(workload=name, kernel="kv_insert_kernel", tokens=n, us_per_call_mean=mean_us,
+                us_per_call_median=float(np.median(us)), tokens_per_s=n / (mean_us * 1e-6),
+                bytes_per_call=nbytes, hbm_GBs=nbytes / (mean_us * 1e-6) / 1e9,
+                hbm_frac=nbytes / (mean_us * 1e-6) / 1e9 / HBM_PEAK_GBS)
+
+
 def cpu_baseline(seconds, torch, device):
     """The oracle on a bounded sample of the headline recipe, all host threads."""
     import oracle
@@ -327,6 +373,7 @@ def main():
     ap.add_argument("--workload", default="decode_sq1")
     ap.add_argument("--extra", default=",".join(EXTRA), help="comma-separated workloads after the timed region")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-insert", action="store_true", help="skip the KV-insert measurements")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB")
     ap.add_argument("--traffic-from", default="", metavar="DIR")
@@ -360,6 +407,16 @@ def main():
               f"HBM {100 * r['hbm_compulsory_frac']:.1f}%, MFMA {100 * r['mfma_frac']:.1f}%", file=sys.stderr,
               flush=True)
 
+    inserts = []
+    if not args.no_insert:
+        from prefill_token_amd import inputs
+
+        for name in inputs.INSERT_WORKLOADS:
+            r = measure_insert(name, args.steps, torch, device)
+            inserts.append(r)
+            print(f"# {name}: {r['us_per_call_mean']:.2f} us/call, {r['tokens_per_s']:.4g} tok/s, "
+                  f"HBM {100 * r['hbm_frac']:.1f}%", file=sys.stderr, flush=True)
+
     digest = source_digest()
     traffic = load_traffic(digest)
     achieved = head["compulsory_bytes"] / (head["us_per_call_mean"] * 1e-6) / 1e9
@@ -383,7 +440,7 @@ def main():
                       "MFMAs, f32 accumulation and softmax",
         "config": {"workload": head["description"], "name": head["workload"], "s_q": head["s_q"],
                    "num_splits": head["num_splits"], "graph": True},
-        "roofline": roofline, "cpu_baseline": cpu, "configs": configs,
+        "roofline": roofline, "cpu_baseline": cpu, "configs": configs, "kv_insert": inserts,
         "device": torch.cuda.get_device_name(device), "host": host_info(), "source_digest": digest,
     }
     print(json.dumps(out), flush=True)
