@@ -126,7 +126,7 @@ int sparse_mla_fwd(const void* q, const void* kv_pool, const uint8_t* kv_scales,
 /*
  * Bytes of device workspace sparse_mla_fwd needs for these parameters: 256 bytes of
  * scheduler state, plus the split partials when the call is split (0 when s_q = 0).
- * Depends on s_q, h_q, d, topk and num_splits, and with num_splits = 0 on the current
+ * Depends on s_q, d, topk and num_splits, and with num_splits = 0 on the current
  * device's compute-unit count.  Returns 0 for parameters sparse_mla_fwd would reject.
  */
 size_t sparse_mla_workspace_size(const smla_params* params);

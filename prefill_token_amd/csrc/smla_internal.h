@@ -32,8 +32,9 @@ constexpr int kTileRows = 64;
 // (zero before a call, left zero by it).
 constexpr size_t kSchedBytes = 256;
 
-// Workspace floats per (token, split): acc [h_q][d] + m [h_q] + l [h_q].
-inline size_t partial_floats(int h_q, int d) { return (size_t)h_q * (size_t)(d + 2); }
+// Workspace floats per (token, split): acc [64][d] + m [64] + l [64] (slots for the
+// largest head count, whatever h_q is).
+inline size_t partial_floats(int, int d) { return (size_t)64 * (size_t)(d + 2); }
 
 // Enqueue the step; returns the HIP error of the first failed launch (hipSuccess if none).
 hipError_t launch(const LaunchArgs& a);

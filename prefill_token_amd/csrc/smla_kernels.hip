@@ -225,7 +225,15 @@ __device__ __forceinline__ float bf16_f32(uint32_t h) { return __builtin_bit_cas
 // (bits 3-5 of the row enter through r >> 3 and r >> 6).
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3) ^ (r >> 6)) & 7; }
 
-__device__ __forceinline__ size_t partial_floats_d(int h_q, int d) { return (size_t)h_q * (size_t)(d + 2); }
+// One split's partial in the workspace: the accumulator of HP heads x d dims (rows of
+// heads >= h_q unused), then m [HP] and l [HP].  The generic kernel stores the
+// accumulator row-major [head][dim]; smla_ws stores it in its register order, so that
+// every store instruction of a wave writes 1 KB contiguously:
+__device__ __forceinline__ size_t partial_floats_d(int, int d) { return (size_t)HP * (size_t)(d + 2); }
+
+// smla_ws's order: float4 ((((v * 2 + mb) * 4 + nb) * 4 + g) * 64 + lrow + 32 lhalf holds
+// dims 128v + 32nb + 8g + 4lhalf .. + 3 of head 32mb + lrow (lane lrow + 32 lhalf of P.V
+// wave v, registers 4g .. 4g + 3 of acc[mb][nb]).
 
 // LDS DMA (buffer_load_dword[x4] ... lds): every lane writes its 4 / 16 bytes at
 // lds_base + 4*lane / 16*lane, read at byte offset voff of a buffer resource.  An
@@ -1011,8 +1019,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
     epilogue<D, NTHREADS>(o_l, C::OS, a.h_q, 0, t, a, cs, sn);
   } else {
     float* part = a.ws + ((size_t)t * ns + split) * partial_floats_d(a.h_q, D);
-    float* pm = part + (size_t)a.h_q * D;
-    float* pl = pm + a.h_q;
+    float* pm = part + (size_t)HP * D;
+    float* pl = pm + HP;
     if (tid < a.h_q) {
       pm[tid] = maxx[tid];
       pl[tid] = lsum[tid] + lsum[HP + tid];
@@ -1578,7 +1586,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
       const int next = __builtin_amdgcn_readfirstlane(flag_l[12]);
       __syncthreads();  // B_B
       const int n = I.n;
-      f32x16 acc[2][4];  // O[64 heads][128 dims]
+      // O^T of this wave's 128 dims: acc[mb][nb] is dims 32 nb .. 32 nb + 31 x heads
+      // 32 mb .. 32 mb + 31 (Vt as the A operand, P as B), so lane = head 32 mb + lrow and
+      // register i = dim 32 nb + 8 (i >> 2) + 4 lhalf + (i & 3): each 32-dim output block
+      // of a head lives in one lane pair (lane, lane ^ 32)
+      f32x16 acc[2][4];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -1654,18 +1666,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
             const int2 rf = *reinterpret_cast<const int2*>(flag_l + 8);
             if (__builtin_amdgcn_readfirstlane(rf.x | rf.y)) {
 #pragma unroll
-              for (int mb = 0; mb < 2; ++mb)
+              for (int mb = 0; mb < 2; ++mb) {
+                const float al = alpha_l[32 * mb + lrow];  // one head per lane
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                  const float4 v4 = *reinterpret_cast<const float4*>(alpha_l + 32 * mb + 8 * g + 4 * lhalf);
+                for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-                  for (int nb = 0; nb < 4; ++nb) {
-                    acc[mb][nb][4 * g + 0] *= v4.x;
-                    acc[mb][nb][4 * g + 1] *= v4.y;
-                    acc[mb][nb][4 * g + 2] *= v4.z;
-                    acc[mb][nb][4 * g + 3] *= v4.w;
-                  }
-                }
+                  for (int i = 0; i < 16; ++i) acc[mb][nb][i] *= al;
+              }
             }
           }
         }
@@ -1692,7 +1699,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
             for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
               for (int mb = 0; mb < 2; ++mb)
-                acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ap[u][mb], Bv[u][nb], acc[mb][nb], 0, 0, 0);
+                acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Bv[u][nb], Ap[u][mb], acc[mb][nb], 0, 0, 0);
           }
           if constexpr (VT) {
             const int bsh = 8 * (cl >> 1);
@@ -1744,112 +1751,93 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
       const auto& K = karg();
       const int hq = K.h_q;
       if (ns == 1) {
-        // normalize in registers (row sums of the lane's 32 heads: four float4 per half),
-        // then per pass 16 heads x 128 dims through the staging area (rows of 132 floats:
-        // the 16 heads of a read step fall in 16 distinct bank quads): lane (hl = lane & 15,
-        // block 4v + (lane >> 4)) runs inverse RoPE, block amax, UE8M0 exponent and E4M3 codes
+        // Straight from the registers: per head (lane) and 32-dim block (nb) the lane pair
+        // (lane, lane ^ 32) holds the block, 16 dims each.  Normalize by the head's row sum,
+        // inverse RoPE (blocks 14 and 15 sit in nb 2 and 3 of the last wave: the pair
+        // (448 + j, 480 + j) is the same register of the same lane), block amax over the
+        // pair, UE8M0 exponent, E4M3 codes; the pair then swaps two code words so that
+        // each lane stores 16 consecutive bytes (lhalf 0: dims 0..15 of the block, lhalf
+        // 1: dims 16..31).
         uint8_t* out_fp8 = K.out_fp8;
         uint8_t* out_scales = K.out_scales;
         float* out_f32 = K.out_f32;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < 2; ++mb) {
+          const int h = 32 * mb + lrow;
+          const float lt = lsum[h] + lsum[HP + h];
+          const float inv = lt > 0.f ? __builtin_amdgcn_rcpf(lt) : 0.f;
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int h0 = 32 * mb + 8 * g + 4 * lhalf;
-            const float4 la = *reinterpret_cast<const float4*>(lsum + h0);
-            const float4 lb = *reinterpret_cast<const float4*>(lsum + HP + h0);
-            const float lt[4] = {la.x + lb.x, la.y + lb.y, la.z + lb.z, la.w + lb.w};
+          for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              const float inv = lt[jj] > 0.f ? __builtin_amdgcn_rcpf(lt[jj]) : 0.f;
+            for (int i = 0; i < 16; ++i) acc[mb][nb][i] *= inv;
+          if (rot && v == 3) {
 #pragma unroll
-              for (int nb = 0; nb < 4; ++nb) acc[mb][nb][4 * g + jj] *= inv;
-            }
-          }
-        float* est = reinterpret_cast<float*>(smem + C::OFF_EST + v * C::EST_BYTES);
-        const int hl_u = lane & 15, blk = lane >> 4, gb = 4 * v + blk;
+            for (int g = 0; g < 4; ++g) {
+              const float4 c4 = *reinterpret_cast<const float4*>(rtab + 8 * g + 4 * lhalf);
+              const float4 s4 = *reinterpret_cast<const float4*>(rtab + 64 + 8 * g + 4 * lhalf);
+              const float cc[4] = {c4.x, c4.y, c4.z, c4.w}, sv[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
-        for (int pass = 0; pass < 4; ++pass) {
-          const int mb = pass >> 1, hb = 16 * (pass & 1);
-#pragma unroll
-          for (int g2 = 0; g2 < 2; ++g2)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              const int i = 4 * (2 * (pass & 1) + g2) + jj;
-              const int hl = 8 * g2 + 4 * lhalf + jj;
-#pragma unroll
-              for (int nb = 0; nb < 4; ++nb) est[hl * C::EST_STRIDE + 32 * nb + lrow] = acc[mb][nb][i];
-            }
-          const int h = 32 * mb + hb + hl_u;
-          const float* row = est + hl_u * C::EST_STRIDE;
-          float vv[32];
-#pragma unroll
-          for (int q4 = 0; q4 < 8; ++q4) {
-            const float4 f4 = *reinterpret_cast<const float4*>(row + 32 * blk + 4 * q4);
-            vv[4 * q4] = f4.x; vv[4 * q4 + 1] = f4.y; vv[4 * q4 + 2] = f4.z; vv[4 * q4 + 3] = f4.w;
-          }
-          if (rot && gb >= 14) {
-            // inverse rotation of (448 + e, 480 + e): block 14 takes o c + o' s, block 15
-            // o c - o' s
-            const float* st = rtab + (gb == 14 ? 64 : 32);
-#pragma unroll
-            for (int q4 = 0; q4 < 8; ++q4) {
-              const float4 f4 = *reinterpret_cast<const float4*>(row + 32 * (blk ^ 1) + 4 * q4);
-              const float4 c4 = *reinterpret_cast<const float4*>(rtab + 4 * q4);
-              const float4 s4 = *reinterpret_cast<const float4*>(st + 4 * q4);
-              const float pr[4] = {f4.x, f4.y, f4.z, f4.w}, cc[4] = {c4.x, c4.y, c4.z, c4.w},
-                          sv[4] = {s4.x, s4.y, s4.z, s4.w};
-#pragma unroll
-              for (int m = 0; m < 4; ++m) {
-                const int e = 4 * q4 + m;
-                vv[e] = __builtin_fmaf(pr[m], sv[m], vv[e] * cc[m]);
+              for (int jj = 0; jj < 4; ++jj) {
+                const float x0 = acc[mb][2][4 * g + jj], x1 = acc[mb][3][4 * g + jj];
+                acc[mb][2][4 * g + jj] = __builtin_fmaf(x1, sv[jj], x0 * cc[jj]);
+                acc[mb][3][4 * g + jj] = __builtin_fmaf(-x0, sv[jj], x1 * cc[jj]);
               }
             }
           }
-          float amax = 0.f;
 #pragma unroll
-          for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(vv[e]));
-          if (h < hq) {
-            const size_t g = ((size_t)I.t * hq + h) * D + 32 * gb;
-            if (out_f32) {
+          for (int nb = 0; nb < 4; ++nb) {
+            const int gb = 4 * v + nb;
+            float amax = 0.f;
 #pragma unroll
-              for (int q4 = 0; q4 < 8; ++q4)
-                reinterpret_cast<float4*>(out_f32 + g)[q4] =
-                    make_float4(vv[4 * q4], vv[4 * q4 + 1], vv[4 * q4 + 2], vv[4 * q4 + 3]);
-            }
+            for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(acc[mb][nb][i]));
+            amax = fmaxf(amax, __shfl_xor(amax, 32));
             const int e8 = ue8m0_exp(amax);
             const float sc = ue8m0_f32((uint32_t)e8);  // codes = RNE(o / 2^(e-127))
-            uint32_t wd[8];
+            uint32_t wd[4];
 #pragma unroll
-            for (int q4 = 0; q4 < 8; ++q4)
-              wd[q4] = enc2(enc2(0u, vv[4 * q4], vv[4 * q4 + 1], sc, false), vv[4 * q4 + 2], vv[4 * q4 + 3], sc, true);
-            reinterpret_cast<uint4*>(out_fp8 + g)[0] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-            reinterpret_cast<uint4*>(out_fp8 + g)[1] = make_uint4(wd[4], wd[5], wd[6], wd[7]);
-            out_scales[((size_t)I.t * hq + h) * (D / 32) + gb] = (uint8_t)e8;
+            for (int g = 0; g < 4; ++g)
+              wd[g] = enc2(enc2(0u, acc[mb][nb][4 * g], acc[mb][nb][4 * g + 1], sc, false), acc[mb][nb][4 * g + 2],
+                           acc[mb][nb][4 * g + 3], sc, true);
+            // word g holds dims 8g + 4 lhalf .. + 3: lhalf 0 keeps g = 0, 1 and takes the
+            // partner's, lhalf 1 keeps g = 2, 3
+            const uint32_t give0 = lhalf ? wd[0] : wd[2], give1 = lhalf ? wd[1] : wd[3];
+            const uint32_t got0 = (uint32_t)__shfl_xor((int)give0, 32), got1 = (uint32_t)__shfl_xor((int)give1, 32);
+            const uint4 st = lhalf ? make_uint4(got0, wd[2], got1, wd[3]) : make_uint4(wd[0], got0, wd[1], got1);
+            if (h < hq) {
+              const size_t g0 = ((size_t)I.t * hq + h) * D + 32 * gb;
+              *reinterpret_cast<uint4*>(out_fp8 + g0 + 16 * lhalf) = st;
+              if (lhalf == 0) out_scales[((size_t)I.t * hq + h) * (D / 32) + gb] = (uint8_t)e8;
+              if (out_f32) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                  *reinterpret_cast<float4*>(out_f32 + g0 + 8 * g + 4 * lhalf) =
+                      make_float4(acc[mb][nb][4 * g], acc[mb][nb][4 * g + 1], acc[mb][nb][4 * g + 2],
+                                  acc[mb][nb][4 * g + 3]);
+              }
+            }
           }
         }
       } else {
-        // this split's (acc, m, l) for the combine kernel
+        // this split's (acc, m, l) for the combine kernel, the accumulator in register
+        // order: each store instruction writes 1 KB contiguously
         const int split = item % ns;
         float* part = K.ws + ((size_t)I.t * ns + split) * partial_floats_d(hq, D);
-        float* pm = part + (size_t)hq * D;
-        float* pl = pm + hq;
+        float* pm = part + (size_t)HP * D;
+        float* pl = pm + HP;
         if (v == 0 && lane < hq) {
           pm[lane] = mfin[lane];
           pl[lane] = lsum[lane] + lsum[HP + lane];
         }
         if (n > 0) {
-          const int d0 = C::VW * v;
+          float4* pv4 = reinterpret_cast<float4*>(part) + 2 * 4 * 4 * 64 * v + lane;
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int h = 32 * mb + 8 * (i >> 2) + 4 * lhalf + (i & 3);
-              if (h < hq) {
+            for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb) part[(size_t)h * D + d0 + 32 * nb + lrow] = acc[mb][nb][i];
-              }
-            }
+              for (int g = 0; g < 4; ++g)
+                pv4[((mb * 4 + nb) * 4 + g) * 64] = make_float4(acc[mb][nb][4 * g], acc[mb][nb][4 * g + 1],
+                                                               acc[mb][nb][4 * g + 2], acc[mb][nb][4 * g + 3]);
         }
       }
       if (!more) break;
@@ -1878,15 +1866,16 @@ __global__ __launch_bounds__(CTHREADS) void smla_combine(KArgs a) {
   const float* base = a.ws + (size_t)t * ns * pf;
   const int f = threadIdx.x;  // float4 index within the head's D dims
   const bool act = f < D / 4;
+  const size_t slot = (size_t)h * D + 4 * f;  // this thread's float4 of the accumulator
   float4 v[SCH];
 #pragma unroll
   for (int k = 0; k < SCH; ++k)
-    v[k] = (act && k < ns) ? *reinterpret_cast<const float4*>(base + (size_t)k * pf + (size_t)h * D + 4 * f)
+    v[k] = (act && k < ns) ? *reinterpret_cast<const float4*>(base + (size_t)k * pf + slot)
                            : make_float4(0.f, 0.f, 0.f, 0.f);
   if ((int)threadIdx.x < ns) {
-    const float* st = base + (size_t)threadIdx.x * pf + (size_t)a.h_q * D;
+    const float* st = base + (size_t)threadIdx.x * pf + (size_t)HP * D;
     mm[threadIdx.x] = st[h];
-    ll[threadIdx.x] = st[a.h_q + h];
+    ll[threadIdx.x] = st[HP + h];
   }
   rope_table(a.positions[t], a, cs, sn);
   __syncthreads();
@@ -1898,9 +1887,8 @@ __global__ __launch_bounds__(CTHREADS) void smla_combine(KArgs a) {
     if (s0 > 0) {
 #pragma unroll
       for (int k = 0; k < SCH; ++k)
-        v[k] = (act && s0 + k < ns)
-                   ? *reinterpret_cast<const float4*>(base + (size_t)(s0 + k) * pf + (size_t)h * D + 4 * f)
-                   : make_float4(0.f, 0.f, 0.f, 0.f);
+        v[k] = (act && s0 + k < ns) ? *reinterpret_cast<const float4*>(base + (size_t)(s0 + k) * pf + slot)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
     for (int k = 0; k < SCH; ++k) {
@@ -1924,6 +1912,107 @@ __global__ __launch_bounds__(CTHREADS) void smla_combine(KArgs a) {
   epilogue<D, CTHREADS>(o_l, OSTR, 1, h, t, a, cs, sn);
 }
 
+// Combine of smla_ws's splits (d = 512, rope_dim 0 or 64), reading the partials in their
+// register order so that every load instruction covers 512 contiguous bytes per 32
+// threads.  Workgroup (token, y): y = 4v + 2mb + nbp selects the P.V wave v, head block
+// mb and the block pair nb = 2nbp, 2nbp + 1; thread (lrow, gp, nbl) owns dims 16gp ..
+// 16gp + 15 of block nb = 2nbp + nbl of head 32mb + lrow (slots g = 2gp, 2gp + 1, both
+// lane halves).  Then o = sum_s w_s acc_s / sum_s w_s l_s (w_s = 2^(m_s - M), in split
+// order with a running maximum M; a split that read nothing has m_s = -inf and is never
+// touched), inverse RoPE (blocks 14 and 15 are the two
+// waves of the last workgroup pair: the partner values cross through LDS), the block
+// amax over the thread pair (gp = 0, 1), UE8M0 exponent and E4M3 codes.
+__global__ __launch_bounds__(CTHREADS) void smla_combine_lm(KArgs a) {
+  constexpr int D = 512, SCH = 8;
+  __shared__ __attribute__((aligned(16))) float xch[CTHREADS * 16];
+  __shared__ float cs[32], sn[32];
+  const int t = blockIdx.x, y = blockIdx.y, v = y >> 2, mb = (y >> 1) & 1, nbp = y & 1;
+  const int tid = threadIdx.x, lrow = tid & 31, gp = (tid >> 5) & 1, nbl = tid >> 6, nb = 2 * nbp + nbl;
+  const int h = 32 * mb + lrow, hq = a.h_q, ns = a.num_splits;
+  const size_t pf = partial_floats_d(hq, D);
+  const float* base = a.ws + (size_t)t * ns * pf;
+  // float4 slots of this thread in a split: g = 2gp + k, lane half lh
+  const int s0 = ((((v * 2 + mb) * 4 + nb) * 4 + 2 * gp) * 64) + lrow;
+  const bool rot = a.rope_dim > 0 && v == 3 && nbp == 1;
+  if (rot) rope_table(a.positions[t], a, cs, sn);
+  float M = -INFINITY, den = 0.f;
+  float o[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) o[e] = 0.f;
+  for (int c0 = 0; c0 < ns; c0 += SCH) {
+    // every load of the chunk goes out before the first use
+    float4 x[SCH][4];
+    float mv[SCH], lv[SCH];
+#pragma unroll
+    for (int k = 0; k < SCH; ++k)
+      if (c0 + k < ns) {
+        const float* sp = base + (size_t)(c0 + k) * pf;
+        const float4* p4 = reinterpret_cast<const float4*>(sp) + s0;
+        x[k][0] = p4[0];
+        x[k][1] = p4[32];
+        x[k][2] = p4[64];
+        x[k][3] = p4[96];
+        mv[k] = sp[(size_t)HP * D + h];
+        lv[k] = sp[(size_t)HP * D + HP + h];
+      }
+#pragma unroll
+    for (int k = 0; k < SCH; ++k)
+      if (c0 + k < ns && mv[k] != -INFINITY) {
+        if (mv[k] > M) {
+          const float r = M == -INFINITY ? 0.f : exp2f(M - mv[k]);
+          den *= r;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[e] *= r;
+          M = mv[k];
+        }
+        const float wv = exp2f(mv[k] - M);
+        den += wv * lv[k];
+        // slot order (g = 2gp, lh 0), (2gp, 1), (2gp + 1, 0), (2gp + 1, 1): dims 0..15
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          o[4 * q] += wv * x[k][q].x;
+          o[4 * q + 1] += wv * x[k][q].y;
+          o[4 * q + 2] += wv * x[k][q].z;
+          o[4 * q + 3] += wv * x[k][q].w;
+        }
+      }
+  }
+  const float inv = den > 0.f ? 1.0f / den : 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) o[e] *= inv;
+  if (rot) {
+    // (448 + j, 480 + j), j = 16gp + e: block 14 (nbl 0) takes o c + o' s, block 15 o c - o' s
+#pragma unroll
+    for (int e = 0; e < 16; ++e) xch[tid * 16 + e] = o[e];
+    __syncthreads();
+    const float sg = nbl ? -1.f : 1.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int j = 16 * gp + e;
+      o[e] = __builtin_fmaf(sg * xch[(tid ^ 64) * 16 + e], sn[j], o[e] * cs[j]);
+    }
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(o[e]));
+  amax = fmaxf(amax, __shfl_xor(amax, 32));
+  if (h >= hq) return;
+  const int gb = 4 * v + nb;
+  const size_t g0 = ((size_t)t * hq + h) * D + 32 * gb + 16 * gp;
+  const int e8 = ue8m0_exp(amax);
+  const float sc = ue8m0_f32((uint32_t)e8);
+  uint32_t wd[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) wd[q] = enc2(enc2(0u, o[4 * q], o[4 * q + 1], sc, false), o[4 * q + 2], o[4 * q + 3], sc, true);
+  *reinterpret_cast<uint4*>(a.out_fp8 + g0) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+  if (gp == 0) a.out_scales[((size_t)t * hq + h) * (D / 32) + gb] = (uint8_t)e8;
+  if (a.out_f32) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      reinterpret_cast<float4*>(a.out_f32 + g0)[q] = make_float4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+  }
+}
+
 }  // namespace
 
 // compute units of the current device (one persistent workgroup each)
@@ -1945,7 +2034,8 @@ template <int D, int EB>
 hipError_t launch_t(const LaunchArgs& x, const KArgs& k) {
   const int ns = x.num_splits;
   const int items = x.s_q * ns;
-  if (D == 512 && EB == 1 && (x.rope_dim == 0 || x.rope_dim == 64)) {
+  const bool ws = D == 512 && EB == 1 && (x.rope_dim == 0 || x.rope_dim == 64);
+  if (ws) {
     const int cus = device_cus();
     hipLaunchKernelGGL(smla_ws, dim3((unsigned)(items < cus ? items : cus)), dim3(NTHREADS), 0, x.stream, k);
   } else {
@@ -1953,7 +2043,10 @@ hipError_t launch_t(const LaunchArgs& x, const KArgs& k) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ns == 1) return e;
-  hipLaunchKernelGGL((smla_combine<D>), dim3((unsigned)x.s_q, (unsigned)x.h_q), dim3(CTHREADS), 0, x.stream, k);
+  if (ws)
+    hipLaunchKernelGGL(smla_combine_lm, dim3((unsigned)x.s_q, 16u), dim3(CTHREADS), 0, x.stream, k);
+  else
+    hipLaunchKernelGGL((smla_combine<D>), dim3((unsigned)x.s_q, (unsigned)x.h_q), dim3(CTHREADS), 0, x.stream, k);
   return hipGetLastError();
 }
 
