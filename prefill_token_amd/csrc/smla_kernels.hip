@@ -64,6 +64,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int T = kTileRows;  // 64
 constexpr int NTHREADS = 512;  // main kernel: 8 waves, two per SIMD
@@ -1217,6 +1218,40 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
       }
     }
   };
+  // The same loads for the between-item prologue (NU = 4), from asm: the compiler does
+  // not track them, so its own waits (which also count the asm tile DMA issued after
+  // them) cannot hold q_units up until that DMA lands.  The caller waits with an explicit
+  // vmcnt that leaves the DMA in flight, then passes x through an asm fence before any
+  // use (q_fence).
+  auto q_load_asm = [&](const Item& I, uint4 (&x)[4][4]) {
+    const int tid = (int)threadIdx.x + opaque_zero(), qb = tid & 15;
+    const auto& K = karg();
+    const int hq = K.h_q;
+    const __amdgpu_buffer_rsrc_t qrs = buf_rsrc(K.q + (size_t)I.t * hq * D, (uint32_t)(hq * D * 2));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t off = (uint32_t)(((tid >> 4) + 16 * k) * D + 32 * qb) * 2u;
+      u32x4 v0, v1, v2, v3;
+      asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(v0) : "v"(off), "s"(qrs) : "memory");
+      asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen offset:16" : "=v"(v1) : "v"(off), "s"(qrs) : "memory");
+      asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen offset:32" : "=v"(v2) : "v"(off), "s"(qrs) : "memory");
+      asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen offset:48" : "=v"(v3) : "v"(off), "s"(qrs) : "memory");
+      x[k][0] = make_uint4(v0[0], v0[1], v0[2], v0[3]);
+      x[k][1] = make_uint4(v1[0], v1[1], v1[2], v1[3]);
+      x[k][2] = make_uint4(v2[0], v2[1], v2[2], v2[3]);
+      x[k][3] = make_uint4(v3[0], v3[1], v3[2], v3[3]);
+    }
+  };
+  auto q_fence = [&](uint4 (&x)[4][4]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x4 v = {x[k][j].x, x[k][j].y, x[k][j].z, x[k][j].w};
+        asm volatile("" : "+v"(v));
+        x[k][j] = make_uint4(v[0], v[1], v[2], v[3]);
+      }
+  };
   // cos / sin of angle pos * theta^(-2i/64), i < 32: the angle in fp64 (the inverse
   // frequencies are computed once per workgroup), reduced to [-pi, pi] (Cody-Waite with a
   // two-part 2*pi), then the hardware sine / cosine of the reduced angle in revolutions;
@@ -1350,17 +1385,25 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
     int item = blockIdx.x;
     Item I = info(item);
     int raw_cur, raw_next;
-    // an item's prologue (its ids and q loads already issued): first-tile DMA (all of it),
-    // cos / sin table, q tile
-    auto transition = [&](auto nu_c, const uint4 (&x)[4][4]) {
+    // an item's prologue (its first ids, id0, resolved and its q loads issued):
+    // first-tile DMA (all of it, 9 instructions per wave), cos / sin table, q tile
+    auto transition = [&](auto nu_c, uint4 (&x)[4][4], const int id0) {
       // the item after this one, from the workspace's counter: fetched first, published
       // (before B_A) last, so that waiting for it holds nothing up
       const bool leader = w == 0 && (((int)threadIdx.x + opaque_zero()) & 63) == 0;
       unsigned nx = 0;
-      if (leader) nx = atomicAdd(a.sched, 1u);
-      // the DMA is issued without a branch (an item without tiles moves zeros), so the
-      // waits for the q loads ahead of it can count
-      const int id0 = valid_id(I, I.tb, raw_cur);
+      if constexpr (decltype(nu_c)::value == 4) {
+        // from asm as well (a plain atomicAdd would be rewritten into a wave reduction
+        // that waits for its result, and so for the q loads, on the spot); its result is
+        // covered by the vmcnt(9) below, which leaves only the DMA in flight
+        if (leader) {
+          unsigned* ctr = a.sched;
+          asm volatile("global_atomic_add %0, %1, %2, off sc0" : "=v"(nx) : "v"(ctr), "v"(1u) : "memory");
+        }
+      } else {
+        if (leader) nx = atomicAdd(a.sched, 1u);
+      }
+      // the DMA is issued without a branch (an item without tiles moves zeros)
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         dma_part(k, w, id0, raw_buf(0), sc_buf(0));
@@ -1368,6 +1411,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
       }
       dma_part(4, w, id0, raw_buf(0), sc_buf(0));
       rope_tab(I);
+      if constexpr (decltype(nu_c)::value == 4) {
+        // the asm q loads (and the counter fetch) landed; the 9 DMA instructions after
+        // them may still be in flight
+        __builtin_amdgcn_s_waitcnt(0x0F79);
+        q_fence(x);
+        if (leader) asm volatile("" : "+v"(nx));
+      }
       q_units(nu_c, x);
       if (leader) flag_l[12] = (int)gridDim.x + (int)nx;
     };
@@ -1377,7 +1427,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
       uint4 x[4][4];
       q_load(I, std::integral_constant<int, 2>{}, x);
       setup();
-      transition(std::integral_constant<int, 2>{}, x);
+      transition(std::integral_constant<int, 2>{}, x, valid_id(I, I.tb, raw_cur));
     }
     while (true) {
       __syncthreads();  // B_A: q tile complete
@@ -1449,6 +1499,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
           }
         }
       };
+      // tile after which the next item's q is touched (none without a next item)
+      const int touch_it = next < total ? (n >= 2 ? n - 2 : 0) : -1;
+      uint32_t tch0 = 0, tch1 = 0;
       for (int it = 0; it < n; ++it) {
         const int tile = I.tb + it;
         const int lane = ((int)threadIdx.x + opaque_zero()) & 63, lrow = lane & 31, lhalf = lane >> 5;
@@ -1474,6 +1527,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
         if (it + 1 < n) {
 #pragma unroll
           for (int k = 0; k <= 4; ++k) dma_part(k, w, id_next, raw_buf(it + 1), sc_buf(it + 1));
+        }
+        // the next item's q rows into the L2, two tiles ahead of its prologue (one 128-byte
+        // line per load, 64 KB per workgroup; heads >= h_q read nothing).  Issued after
+        // this tile's DMA, so the end of this iteration waits for the DMA only.
+        const bool touch = it == touch_it;
+        if (touch) {
+          const __amdgpu_buffer_rsrc_t qrs =
+              buf_rsrc(a.q + (size_t)(next / ns) * a.h_q * D, (uint32_t)(a.h_q * D * 2));
+          const uint32_t off = 256u * (uint32_t)(64 * w + lane);
+          tch0 = __builtin_amdgcn_raw_buffer_load_b32(qrs, off, 0, 0);
+          tch1 = __builtin_amdgcn_raw_buffer_load_b32(qrs, off + 128u, 0, 0);
         }
         {
           const unsigned char* sc_l = sc_buf(it);
@@ -1520,7 +1584,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
           const bool over = __any(lm > m_run + 8.0f);
           if (lane == 0) flag_l[4 * (it & 1) + w] = over ? 1 : 0;
         }
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile's DMA from this wave landed
+        // next tile's DMA from this wave landed (vmcnt(0); vmcnt(2) behind the q touches)
+        if (touch)
+          __builtin_amdgcn_s_waitcnt(0x0F72);
+        else
+          __builtin_amdgcn_s_waitcnt(0x0F70);
         raw_cur = raw_next;
         raw_next = raw_next2;
         __syncthreads();  // end of iteration
@@ -1529,7 +1597,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
       // row sums and max for the epilogue, and the next item's ids, which stay in flight
       // into the next item's prologue
       uint4 x[4][4];
-      uint32_t touch0 = 0, touch1 = 0;
       {
         if (n > 0) check(n);
         const int lane = ((int)threadIdx.x + opaque_zero()) & 63, lrow = lane & 31, lhalf = lane >> 5;
@@ -1541,22 +1608,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
           I = info(next);
           raw_cur = fetch_id(I, I.tb);
           raw_next = fetch_id(I, I.tb + 1);
-          // touch the next item's q rows into the L2 (256 B per lane); the registers stay
-          // reserved until the prologue's own q loads have been waited for
-          const int tq = 64 * w + lane;
-          if (tq / 4 < a.h_q) {
-            const uint16_t* qn = a.q + ((size_t)I.t * a.h_q) * D + 128 * tq;
-            asm volatile("global_load_dword %0, %1, off" : "=v"(touch0) : "v"(qn) : "memory");
-            asm volatile("global_load_dword %0, %1, off offset:128" : "=v"(touch1) : "v"(qn) : "memory");
-          }
         }
         __syncthreads();  // end of the last iteration
       }
       item = next;
       if (item >= total) break;
-      q_load(I, std::integral_constant<int, 4>{}, x);
-      transition(std::integral_constant<int, 4>{}, x);  // waits for the q loads, and so for the touch loads before them
-      asm volatile("" ::"v"(touch0), "v"(touch1));
+      // the first ids are resolved before the q loads go out, so that the compiler's wait
+      // for them does not wait for q as well
+      const int id0 = valid_id(I, I.tb, raw_cur);
+      q_load_asm(I, x);
+      transition(std::integral_constant<int, 4>{}, x, id0);
+      asm volatile("" ::"v"(tch0), "v"(tch1));  // the touches' results are never looked at
     }
     // this workgroup is done; the last one to finish leaves the counters zero for the
     // next call on this workspace
