@@ -284,7 +284,7 @@ def host_info():
 
 def source_digest():
     h = hashlib.sha256()
-    for fn in ("smla_kernels.hip", "smla_api.cpp", "smla_internal.h"):
+    for fn in ("smla_kernels.hip", "kv_insert.hip", "smla_api.cpp", "smla_internal.h"):
         with open(os.path.join(ROOT, "prefill_token_amd", "csrc", fn), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
