@@ -13,7 +13,8 @@
 //              work items (token, split), with QK and P.V waves specialized per SIMD and
 //              one barrier per 64-entry tile (its own comment below has the details);
 //   smla_main  every other shape: one workgroup per work item, described here.
-// smla_combine merges the splits of a token when a call is split.
+// smla_combine (smla_main's splits) and smla_combine_lm (smla_ws's splits, stored in
+// the P.V waves' register order) merge the splits of a token when a call is split.
 //
 // smla_main: one 512-thread workgroup (8 wave64, two per SIMD) per token, or per token
 // split when few tokens are in flight.
@@ -1062,10 +1063,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
 // raise the running max, rewrite P from the scores they still hold and publish the
 // accumulator rescale, and a second barrier lets the P.V waves go on.  The running max
 // is therefore the same lazily raised max as in the generic kernel.
-// Between items: the P.V waves run the epilogue of the finished item from registers
-// through a private staging area, while the QK waves issue the next item's first tile DMA
-// and run its q prologue into a q tile over the V-tile area, from which they then load
-// their fragments.
+// Between items: the P.V waves run the epilogue of the finished item straight from their
+// registers (their MFMAs produce O^T, so a head's 32-dim block sits in one lane pair),
+// while the QK waves issue the next item's first tile DMA and run its q prologue into a
+// q tile over the V-tile area, from which they then load their fragments.
 struct WsCfg {
   static constexpr int kD = 512, kEB = 1;
   static constexpr int D = kD;
@@ -1085,14 +1086,9 @@ struct WsCfg {
   static constexpr int OFF_P1 = OFF_P0 + P_BYTES;
   static constexpr int LOOP_END = OFF_P1 + P_BYTES;
   // between items: the q tile [2 terms][HP][512 B] (16-byte chunk c of head h stored at
-  // c ^ (h & 15)) over the V tiles, its UE8M0 scales [2][HP][16] in P0, the P.V waves'
-  // epilogue staging (16 heads x 128 dims f32 each, rows padded to 132 floats) in the
-  // second raw tile
+  // c ^ (h & 15)) over the V tiles, its UE8M0 scales [2][HP][16] in P0
   static constexpr int OFF_QT = OFF_VT;
   static constexpr int OFF_QSC = OFF_P0;
-  static constexpr int EST_STRIDE = VW + 4;  // floats
-  static constexpr int EST_BYTES = 16 * EST_STRIDE * 4;
-  static constexpr int OFF_EST = OFF_RAW1;
   // small area
   static constexpr int OFF_MAXX = LOOP_END;                // [2 tiles][2 row halves][HP]
   static constexpr int OFF_ALPHA = OFF_MAXX + 4 * HP * 4;  // [HP]
@@ -1105,7 +1101,7 @@ struct WsCfg {
   static constexpr int SMEM = OFF_IFREQ + 32 * 8;
   static_assert(G == 2 && NSB == 16, "layout written for 512-byte rows");
   static_assert(SMEM <= 160 * 1024, "LDS budget");
-  static_assert(2 * HP * 512 <= 4 * VTW_BYTES && 2 * HP * 16 <= P_BYTES && 4 * EST_BYTES <= RAW_BYTES,
+  static_assert(2 * HP * 512 <= 4 * VTW_BYTES && 2 * HP * 16 <= P_BYTES,
                 "item transition areas");
 };
 
