@@ -13,8 +13,9 @@
 //              work items (token, split), with QK and P.V waves specialized per SIMD and
 //              one barrier per 64-entry tile (its own comment below has the details);
 //   smla_main  every other shape: one workgroup per work item, described here.
-// smla_combine (smla_main's splits) and smla_combine_lm (smla_ws's splits, stored in
-// the P.V waves' register order) merge the splits of a token when a call is split.
+// smla_combine (smla_main's splits) and smla_combine_lm4 / smla_combine_lm1 (smla_ws's
+// splits, stored in the P.V waves' register order; 4 or 1 float4 slots per thread)
+// merge the splits of a token when a call is split.
 //
 // smla_main: one 512-thread workgroup (8 wave64, two per SIMD) per token, or per token
 // split when few tokens are in flight.
@@ -1970,9 +1971,9 @@ __global__ __launch_bounds__(CTHREADS) void smla_combine(KArgs a) {
   epilogue<D, CTHREADS>(o_l, OSTR, 1, h, t, a, cs, sn);
 }
 
-// Combine of smla_ws's splits (d = 512, rope_dim 0 or 64), reading the partials in their
-// register order so that every load instruction covers 512 contiguous bytes per 32
-// threads.  Workgroup (token, y): y = 4v + 2mb + nbp selects the P.V wave v, head block
+// Combine of smla_ws's splits for up to 8 splits per token (one round of loads): the
+// partials are read in their register order so that every load instruction covers 512
+// contiguous bytes per 32 threads.  Workgroup (token, y): y = 4v + 2mb + nbp selects the P.V wave v, head block
 // mb and the block pair nb = 2nbp, 2nbp + 1; thread (lrow, gp, nbl) owns dims 16gp ..
 // 16gp + 15 of block nb = 2nbp + nbl of head 32mb + lrow (slots g = 2gp, 2gp + 1, both
 // lane halves).  Then o = sum_s w_s acc_s / sum_s w_s l_s (w_s = 2^(m_s - M), in split
@@ -1980,7 +1981,7 @@ __global__ __launch_bounds__(CTHREADS) void smla_combine(KArgs a) {
 // touched), inverse RoPE (blocks 14 and 15 are the two
 // waves of the last workgroup pair: the partner values cross through LDS), the block
 // amax over the thread pair (gp = 0, 1), UE8M0 exponent and E4M3 codes.
-__global__ __launch_bounds__(CTHREADS) void smla_combine_lm(KArgs a) {
+__global__ __launch_bounds__(CTHREADS) void smla_combine_lm4(KArgs a) {
   constexpr int D = 512, SCH = 8;
   __shared__ __attribute__((aligned(16))) float xch[CTHREADS * 16];
   __shared__ float cs[32], sn[32];
@@ -2071,6 +2072,91 @@ __global__ __launch_bounds__(CTHREADS) void smla_combine_lm(KArgs a) {
   }
 }
 
+// Combine of smla_ws's splits for more than 8 splits per token, reading the partials in
+// their register order.  Workgroup (token, y), y = 4v + 2mb + nbp, covers P.V wave v's blocks
+// nb = 2nbp, 2nbp + 1 for the 32 heads of head block mb: 512 threads, thread (nbl, g,
+// lane) owns the float4 slot (g, lane) of block nb = 2nbp + nbl, i.e. dims 8g + 4lhalf ..
+// + 3 of that block for head 32mb + (lane & 31).  A wave (fixed nbl, g) reads 1 KB
+// contiguously per split, and every split's load goes out in one round (chunks of 16).
+// Then o = sum_s w_s acc_s / sum_s w_s l_s (w_s = 2^(m_s - M), in split order with a
+// running maximum M; a split that read nothing has m_s = -inf and is never touched),
+// inverse RoPE (the two blocks of a rotary pair are the two halves of the last
+// workgroup pair: the partner value crosses through LDS), the block amax over the 8
+// threads of a (head, block) through LDS, the UE8M0 exponent and the E4M3 codes.
+constexpr int LMT = 512;  // smla_combine_lm1 threads
+__global__ __launch_bounds__(LMT) void smla_combine_lm1(KArgs a) {
+  constexpr int D = 512, SCH = 16;
+  __shared__ __attribute__((aligned(16))) float xch[LMT * 4];
+  __shared__ float red[2][32][9];
+  __shared__ float cs[32], sn[32];
+  const int t = blockIdx.x, y = blockIdx.y, v = y >> 2, mb = (y >> 1) & 1, nbp = y & 1;
+  const int tid = threadIdx.x, lane = tid & 63, g = (tid >> 6) & 3, nbl = tid >> 8;
+  const int lrow = lane & 31, lhalf = lane >> 5, nb = 2 * nbp + nbl;
+  const int h = 32 * mb + lrow, hq = a.h_q, ns = a.num_splits;
+  const size_t pf = partial_floats_d(hq, D);
+  const float* base = a.ws + (size_t)t * ns * pf;
+  const int slot = ((((v * 2 + mb) * 4 + nb) * 4 + g) * 64) + lane;  // float4 index
+  const bool rot = a.rope_dim > 0 && v == 3 && nbp == 1;
+  if (rot) rope_table(a.positions[t], a, cs, sn);
+  float M = -INFINITY, den = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c0 = 0; c0 < ns; c0 += SCH) {
+    float4 x[SCH];
+    float mv[SCH], lv[SCH];
+#pragma unroll
+    for (int k = 0; k < SCH; ++k)
+      if (c0 + k < ns) {
+        const float* sp = base + (size_t)(c0 + k) * pf;
+        x[k] = reinterpret_cast<const float4*>(sp)[slot];
+        mv[k] = sp[(size_t)HP * D + h];
+        lv[k] = sp[(size_t)HP * D + HP + h];
+      }
+#pragma unroll
+    for (int k = 0; k < SCH; ++k)
+      if (c0 + k < ns && mv[k] != -INFINITY) {
+        if (mv[k] > M) {
+          const float r = M == -INFINITY ? 0.f : exp2f(M - mv[k]);
+          den *= r;
+          o.x *= r; o.y *= r; o.z *= r; o.w *= r;
+          M = mv[k];
+        }
+        const float wv = exp2f(mv[k] - M);
+        den += wv * lv[k];
+        o.x += wv * x[k].x; o.y += wv * x[k].y; o.z += wv * x[k].z; o.w += wv * x[k].w;
+      }
+  }
+  const float inv = den > 0.f ? 1.0f / den : 0.f;
+  float ov[4] = {o.x * inv, o.y * inv, o.z * inv, o.w * inv};
+  if (rot) {
+    // (448 + j, 480 + j), j = 8g + 4lhalf + e: block 14 (nbl 0) takes o c + o' s, block 15
+    // o c - o' s
+    *reinterpret_cast<float4*>(xch + 4 * tid) = make_float4(ov[0], ov[1], ov[2], ov[3]);
+    __syncthreads();
+    const float4 pr = *reinterpret_cast<const float4*>(xch + 4 * (tid ^ 256));
+    const float pv[4] = {pr.x, pr.y, pr.z, pr.w};
+    const float sg = nbl ? -1.f : 1.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = 8 * g + 4 * lhalf + e;
+      ov[e] = __builtin_fmaf(sg * pv[e], sn[j], ov[e] * cs[j]);
+    }
+  }
+  float am = fmaxf(fmaxf(fabsf(ov[0]), fabsf(ov[1])), fmaxf(fabsf(ov[2]), fabsf(ov[3])));
+  red[nbl][lrow][2 * g + lhalf] = am;
+  __syncthreads();
+  float amax = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) amax = fmaxf(amax, red[nbl][lrow][k]);
+  if (h >= hq) return;
+  const int gb = 4 * v + nb;
+  const size_t g0 = ((size_t)t * hq + h) * D + 32 * gb + 8 * g + 4 * lhalf;
+  const int e8 = ue8m0_exp(amax);
+  const float sc = ue8m0_f32((uint32_t)e8);
+  *reinterpret_cast<uint32_t*>(a.out_fp8 + g0) = enc2(enc2(0u, ov[0], ov[1], sc, false), ov[2], ov[3], sc, true);
+  if (g == 0 && lhalf == 0) a.out_scales[((size_t)t * hq + h) * (D / 32) + gb] = (uint8_t)e8;
+  if (a.out_f32) *reinterpret_cast<float4*>(a.out_f32 + g0) = make_float4(ov[0], ov[1], ov[2], ov[3]);
+}
+
 }  // namespace
 
 // compute units of the current device (one persistent workgroup each)
@@ -2102,7 +2188,10 @@ hipError_t launch_t(const LaunchArgs& x, const KArgs& k) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ns == 1) return e;
   if (ws)
-    hipLaunchKernelGGL(smla_combine_lm, dim3((unsigned)x.s_q, 16u), dim3(CTHREADS), 0, x.stream, k);
+    if (ns <= 8)
+      hipLaunchKernelGGL(smla_combine_lm4, dim3((unsigned)x.s_q, 16u), dim3(CTHREADS), 0, x.stream, k);
+    else
+      hipLaunchKernelGGL(smla_combine_lm1, dim3((unsigned)x.s_q, 16u), dim3(LMT), 0, x.stream, k);
   else
     hipLaunchKernelGGL((smla_combine<D>), dim3((unsigned)x.s_q, (unsigned)x.h_q), dim3(CTHREADS), 0, x.stream, k);
   return hipGetLastError();
