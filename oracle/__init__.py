@@ -6,8 +6,9 @@ this wrapper loads ``liboracle.so`` built from ``sparse_mla_oracle.c`` by plain 
 
 The functions mirror the steps of the C file (each cites its passage there):
 ``bf16_decode``, ``e4m3_decode``, ``e4m3_encode``, ``ue8m0_exponent``,
-``quantize_blocks``, ``rmsnorm``, ``rope``, the whole step ``sparse_mla`` and the pool-row
-producer before it, ``kv_insert``.
+``quantize_blocks``, ``rmsnorm``, ``rope``, the whole step ``sparse_mla``, and the two
+steps before it: the pool-row producer ``kv_insert`` and the index-row builder
+``build_index`` (plain numpy, below).
 
 Parity pins: every function here is checked in ``tests/test_oracle_*.py`` against
 library routines (torch's CPU float8_e4m3fn cast, torch SDPA and rms_norm in fp64,
@@ -206,3 +207,60 @@ def kv_insert(kv_bits: np.ndarray, positions: np.ndarray, norm_w: np.ndarray, kv
     if rc != 0:
         raise ValueError(f"oracle_kv_insert failed with code {rc}")
     return pool, sc
+
+
+def select_topk(logits_bits: np.ndarray, k: int) -> np.ndarray:
+    """Columns of the k largest logits of one row, ascending.
+
+    The rule the pages give for their top-k kernel [vLLM #64364 "latency_specialized
+    decode", Validation: torch.topk's k-th value, the selected columns in ascending order,
+    ties toward the lowest column]: order by value (bf16 bits; NaN above every number, as
+    torch orders it; -0 equal to +0), break ties by the lower column, keep the first k,
+    return them sorted by column.  k larger than the row keeps the whole row.
+    """
+    bits = np.asarray(logits_bits, dtype=np.uint16)
+    n = bits.size
+    k = min(int(k), n)
+    if k <= 0:
+        return np.zeros(0, dtype=np.int64)
+    v = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    nan = np.isnan(v)
+    v = np.where(nan, 0.0, v)
+    cols = np.arange(n)
+    # np.lexsort sorts by the last key first: NaN first, then larger values, then lower columns
+    order = np.lexsort((cols, -v, -nan.astype(np.int64)))
+    return np.sort(order[:k])
+
+
+def build_index(positions: np.ndarray, logits_bits: np.ndarray, n_valid, *, topk: int, window: int,
+                self_in_window: bool, n_swa: int, cmp_base: int, k_cmp: int):
+    """Index rows of the step, the step before it [vLLM #56344 "Deepseek V41 Attention
+    MegaKernel", Purpose: combine_topk_swa_indices builds each token's row of SWA and
+    compressed-cache indices and writes its own -1 sentinels].
+
+    Row t: entries 0 .. window-1 are the sliding-window rows of positions
+    p - window + s .. p - 1 + s (s = 1 when the token's own row is in its window), each
+    ``pos mod n_swa`` or -1 for a negative position; the next k_cmp entries are
+    ``cmp_base + c`` for the columns c chosen by ``select_topk`` among the token's first
+    ``n_valid[t]`` candidate logits, ascending, then -1 where fewer were chosen; every
+    later entry is -1.  ``topk_length[t]`` = window + the number chosen.
+
+    Returns ``(indices i32 [s_q, topk], topk_length i32 [s_q])``.
+    """
+    positions = np.asarray(positions, dtype=np.int64)
+    logits_bits = np.asarray(logits_bits, dtype=np.uint16)
+    s_q, n_cand = logits_bits.shape
+    nv = np.full(s_q, n_cand, dtype=np.int64) if n_valid is None else np.clip(np.asarray(n_valid, np.int64), 0, n_cand)
+    assert window + k_cmp <= topk and window <= n_swa
+    idx = np.full((s_q, topk), -1, dtype=np.int32)
+    L = np.zeros(s_q, dtype=np.int32)
+    s = 1 if self_in_window else 0
+    for t in range(s_q):
+        p = int(positions[t])
+        for j in range(window):
+            q = p - window + s + j
+            idx[t, j] = q % n_swa if q >= 0 else -1
+        sel = select_topk(logits_bits[t, :nv[t]], k_cmp)
+        idx[t, window:window + sel.size] = cmp_base + sel
+        L[t] = window + sel.size
+    return idx, L
