@@ -180,6 +180,48 @@ typedef struct smla_kv_insert_params {
 int sparse_mla_kv_insert(const void* kv, const int32_t* positions, const float* norm_w, uint8_t* kv_pool,
                          uint8_t* kv_scales, const smla_kv_insert_params* params);
 
+/*
+ * Index-row builder: writes the index rows and lengths sparse_mla_fwd reads (the step
+ * before it).  For token t at position p, row t of `indices` holds
+ *
+ *   [0, window)             the sliding-window rows of positions p - window + s .. p - 1 + s
+ *                           (s = self_in_window), each p' mod n_swa, or -1 for p' < 0;
+ *   [window, window + k)    cmp_base + c for the k = min(k_cmp, n_valid[t]) candidate columns
+ *                           c < n_valid[t] with the largest logits, in ascending column order;
+ *   [window + k, topk)      -1 (written by the call: the row needs no pre-fill);
+ *
+ * and topk_length[t] = window + k.  The top-k rule is torch.topk's: order by value, NaN
+ * above every number, -0 equal to +0, ties toward the lowest column
+ * [vLLM #56344 "Deepseek V41 Attention MegaKernel", Purpose: combine_topk_swa_indices
+ *  must write its own -1 sentinels; vLLM #64364 "latency_specialized decode", Validation:
+ *  the top-k kernel's specified output].  The rows are exact (integer work only).
+ *
+ *   positions    i32 [s_q]               (device, read)
+ *   logits       bf16 [s_q][n_cand]      (device, read; 2-byte aligned) candidate scores
+ *   n_valid      i32 [s_q] or NULL       (device, read) candidates of each token (clamped to
+ *                                        [0, n_cand]); NULL = all n_cand
+ *   indices      i32 [s_q][topk]         (device, written)
+ *   topk_length  i32 [s_q]               (device, written)
+ *   params       host pointer, read during the call only
+ *
+ * Same conventions as sparse_mla_fwd (asynchronous on params->stream, nothing allocated,
+ * errors by return code with nothing launched).
+ */
+typedef struct smla_index_params {
+  int32_t s_q;            /* tokens (0 = no-op) */
+  int32_t n_cand;         /* candidate columns per token: 0..65536 */
+  int32_t topk;           /* row stride of indices: window + k_cmp .. 65536 */
+  int32_t window;         /* sliding-window entries: 0..n_swa */
+  int32_t self_in_window; /* 1: the window ends at the token's own position; 0: just before it */
+  int32_t n_swa;          /* sliding-window ring rows (>= 1) */
+  int32_t cmp_base;       /* pool row of candidate column 0 (>= 0; cmp_base + n_cand < 2^31) */
+  int32_t k_cmp;          /* compressed entries kept per token: 0..topk - window */
+  void* stream;           /* hipStream_t */
+} smla_index_params;
+
+int sparse_mla_build_index(const int32_t* positions, const void* logits, const int32_t* n_valid, int32_t* indices,
+                           int32_t* topk_length, const smla_index_params* params);
+
 /* Thread-local, NUL-terminated message describing the last failed call on this thread
    ("" if none).  Valid until the next call on the same thread. */
 const char* sparse_mla_last_error(void);

@@ -15,12 +15,14 @@ from typing import Optional
 
 from . import _lib
 from ._lib import (SMLA_ERR_HIP, SMLA_ERR_NULL, SMLA_ERR_SHAPE, SMLA_ERR_VALUE, SMLA_KV_BF16,
-                   SMLA_KV_E4M3_UE8M0, SMLA_OK, LibraryMissing, SmlaKvInsertParams, SmlaParams, last_error)
+                   SMLA_KV_E4M3_UE8M0, SMLA_OK, LibraryMissing, SmlaIndexParams, SmlaKvInsertParams, SmlaParams,
+                   last_error)
 
 __all__ = [
     "sparse_mla_fwd", "sparse_mla_workspace_size", "sparse_mla_num_splits", "sparse_mla_last_error",
-    "sparse_mla_abi_version", "sparse_mla_kv_insert", "make_params", "make_kv_insert_params", "SmlaParams",
-    "SmlaKvInsertParams", "SmlaError", "LibraryMissing",
+    "sparse_mla_abi_version", "sparse_mla_kv_insert", "sparse_mla_build_index", "make_params",
+    "make_kv_insert_params", "make_index_params", "SmlaParams", "SmlaKvInsertParams", "SmlaIndexParams", "SmlaError",
+    "LibraryMissing",
     "SMLA_OK", "SMLA_ERR_NULL", "SMLA_ERR_SHAPE", "SMLA_ERR_VALUE", "SMLA_ERR_HIP",
     "SMLA_KV_E4M3_UE8M0", "SMLA_KV_BF16",
 ]
@@ -142,3 +144,37 @@ def sparse_mla_kv_insert(kv, positions, norm_w, kv_pool, kv_scales, *, rope_dim:
                                           ctypes.byref(params))
     if rc != SMLA_OK:
         raise SmlaError(rc, last_error(), "sparse_mla_kv_insert")
+
+
+def make_index_params(*, s_q: int, n_cand: int, topk: int, window: int, self_in_window: bool, n_swa: int,
+                      cmp_base: int, k_cmp: int, stream=None) -> SmlaIndexParams:
+    p = SmlaIndexParams()
+    p.s_q, p.n_cand, p.topk, p.window = s_q, n_cand, topk, window
+    p.self_in_window, p.n_swa, p.cmp_base, p.k_cmp = int(bool(self_in_window)), n_swa, cmp_base, k_cmp
+    p.stream = stream
+    return p
+
+
+def sparse_mla_build_index(positions, logits, n_valid, indices, topk_length, *, window: int, self_in_window: bool,
+                           n_swa: int, cmp_base: int, k_cmp: int, stream=None) -> None:
+    """Enqueue the index-row builder on the current (or given) HIP stream.
+
+    positions int32 [s_q]; logits bf16 [s_q, n_cand]; n_valid int32 [s_q] or None;
+    indices int32 [s_q, topk] and topk_length int32 [s_q] are written.  Raises SmlaError.
+    """
+    import torch
+
+    for name, t in (("positions", positions), ("logits", logits), ("n_valid", n_valid), ("indices", indices),
+                    ("topk_length", topk_length)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    s_q, n_cand = logits.shape
+    if stream is None:
+        stream = torch.cuda.current_stream(logits.device).cuda_stream
+    params = make_index_params(s_q=s_q, n_cand=n_cand, topk=indices.shape[1], window=window,
+                               self_in_window=self_in_window, n_swa=n_swa, cmp_base=cmp_base, k_cmp=k_cmp,
+                               stream=stream)
+    rc = _lib.load().sparse_mla_build_index(_ptr(positions), _ptr(logits), _ptr(n_valid), _ptr(indices),
+                                            _ptr(topk_length), ctypes.byref(params))
+    if rc != SMLA_OK:
+        raise SmlaError(rc, last_error(), "sparse_mla_build_index")

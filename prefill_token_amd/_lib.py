@@ -54,6 +54,22 @@ class SmlaKvInsertParams(ctypes.Structure):
     ]
 
 
+class SmlaIndexParams(ctypes.Structure):
+    """Mirror of ``smla_index_params``."""
+
+    _fields_ = [
+        ("s_q", ctypes.c_int32),
+        ("n_cand", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("self_in_window", ctypes.c_int32),
+        ("n_swa", ctypes.c_int32),
+        ("cmp_base", ctypes.c_int32),
+        ("k_cmp", ctypes.c_int32),
+        ("stream", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 
 
@@ -82,6 +98,8 @@ def load() -> ctypes.CDLL:
     lib.sparse_mla_last_error.argtypes = []
     lib.sparse_mla_kv_insert.restype = ctypes.c_int
     lib.sparse_mla_kv_insert.argtypes = [P, P, P, P, P, ctypes.POINTER(SmlaKvInsertParams)]
+    lib.sparse_mla_build_index.restype = ctypes.c_int
+    lib.sparse_mla_build_index.argtypes = [P, P, P, P, P, ctypes.POINTER(SmlaIndexParams)]
     lib.sparse_mla_abi_version.restype = ctypes.c_int
     lib.sparse_mla_abi_version.argtypes = []
     _lib = lib

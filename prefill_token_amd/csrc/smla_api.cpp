@@ -1,4 +1,5 @@
-// C ABI of the fused sparse-MLA step and of the KV insert (declared in include/smla.h):
+// C ABI of the fused sparse-MLA step, the KV insert and the index-row builder (declared in
+// include/smla.h):
 // argument checks on the host, split selection, workspace sizing and error reporting.  All checks run
 // before any HIP call, so a rejected call enqueues nothing.
 #include <math.h>
@@ -192,6 +193,48 @@ int sparse_mla_kv_insert(const void* kv, const int32_t* positions, const float* 
   a.rope_theta = p->rope_theta;
   a.stream = static_cast<hipStream_t>(p->stream);
   const hipError_t e = smla::launch_kv_insert(a);
+  if (e != hipSuccess) return fail(SMLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return SMLA_OK;
+}
+
+int sparse_mla_build_index(const int32_t* positions, const void* logits, const int32_t* n_valid, int32_t* indices,
+                           int32_t* topk_length, const smla_index_params* p) {
+  g_last_error.clear();
+  if (!p) return fail(SMLA_ERR_NULL, "params is NULL");
+  if (p->s_q < 0) return fail(SMLA_ERR_VALUE, "s_q must be >= 0 (got %d)", p->s_q);
+  if (p->n_cand < 0 || p->n_cand > 65536)
+    return fail(SMLA_ERR_SHAPE, "n_cand must be in [0, 65536] (got %d)", p->n_cand);
+  if (p->n_swa < 1) return fail(SMLA_ERR_VALUE, "n_swa must be >= 1 (got %d)", p->n_swa);
+  if (p->window < 0 || p->window > p->n_swa)
+    return fail(SMLA_ERR_SHAPE, "window must be in [0, n_swa] (got %d)", p->window);
+  if (p->self_in_window != 0 && p->self_in_window != 1)
+    return fail(SMLA_ERR_VALUE, "self_in_window must be 0 or 1 (got %d)", p->self_in_window);
+  if (p->k_cmp < 0) return fail(SMLA_ERR_SHAPE, "k_cmp must be >= 0 (got %d)", p->k_cmp);
+  if (p->topk > 65536 || (long long)p->window + p->k_cmp > p->topk)
+    return fail(SMLA_ERR_SHAPE, "topk must be in [window + k_cmp, 65536] (got %d)", p->topk);
+  if (p->cmp_base < 0 || (long long)p->cmp_base + p->n_cand > 0x7FFFFFFFLL)
+    return fail(SMLA_ERR_VALUE, "cmp_base + n_cand must lie in [0, 2^31)");
+  if ((long long)p->s_q * p->topk > 0x7FFFFFFFLL) return fail(SMLA_ERR_SHAPE, "s_q * topk must fit in int32");
+  if (p->s_q == 0) return SMLA_OK;
+  if (!positions || !indices || !topk_length || (p->n_cand > 0 && !logits))
+    return fail(SMLA_ERR_NULL, "a required array pointer is NULL");
+  if (reinterpret_cast<uintptr_t>(logits) % 2 != 0) return fail(SMLA_ERR_VALUE, "logits must be 2-byte aligned");
+  smla::IndexArgs a;
+  a.positions = positions;
+  a.logits = static_cast<const uint16_t*>(logits);
+  a.n_valid = n_valid;
+  a.indices = indices;
+  a.topk_length = topk_length;
+  a.s_q = p->s_q;
+  a.n_cand = p->n_cand;
+  a.topk = p->topk;
+  a.window = p->window;
+  a.self_in_window = p->self_in_window;
+  a.n_swa = p->n_swa;
+  a.cmp_base = p->cmp_base;
+  a.k_cmp = p->k_cmp;
+  a.stream = static_cast<hipStream_t>(p->stream);
+  const hipError_t e = smla::launch_build_index(a);
   if (e != hipSuccess) return fail(SMLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return SMLA_OK;
 }

@@ -56,4 +56,17 @@ struct KvInsertArgs {
 
 hipError_t launch_kv_insert(const KvInsertArgs& a);
 
+// Index-row builder: one 256-thread workgroup per token.
+struct IndexArgs {
+  const int32_t* positions;  // [s_q]
+  const uint16_t* logits;    // bf16 bits [s_q][n_cand]
+  const int32_t* n_valid;    // [s_q] or null (all n_cand candidates valid)
+  int32_t* indices;          // [s_q][topk]
+  int32_t* topk_length;      // [s_q]
+  int s_q, n_cand, topk, window, self_in_window, n_swa, cmp_base, k_cmp;
+  hipStream_t stream;
+};
+
+hipError_t launch_build_index(const IndexArgs& a);
+
 }  // namespace smla

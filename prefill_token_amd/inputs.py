@@ -212,6 +212,43 @@ def make_insert(name: str, seed: Optional[int] = None, n: Optional[int] = None) 
                 kv_pool=pool, kv_scales=scales)
 
 
+# Index-row builder workloads: the positions of the attention workloads above, one row of
+# candidate logits per token over the compressed pool (2048 or 16384 rows), keep 512.
+#   name                  n     candidates   window / self   valid candidates
+INDEX_WORKLOADS = {
+    "index_decode_sq1": (1, 2048, "decode"),
+    "index_decode_sq64": (64, 2048, "decode"),
+    "index_decode_sq1024": (1024, 16384, "decode_ragged"),
+    "index_prefill_sq2123": (2123, 16384, "prefill"),
+}
+
+
+def make_index(name: str, seed: Optional[int] = None, n: Optional[int] = None) -> dict:
+    """Inputs of one index-row-builder workload.  Logits are N(0, 1) rounded to multiples
+    of 1/8 in bf16 (few distinct values, as indexer logits have, so the k-th value is
+    usually tied).  Valid candidates: all (decode), uniform in [256, n_cand]
+    (decode_ragged), one per 4 positions up to the token (prefill, a compression ratio of
+    4).  Window 128 rows before the token (decode) or ending at it (prefill), 8192-row
+    ring, compressed rows after it.  Seed 20262000 + the workload's position."""
+    names = list(INDEX_WORKLOADS)
+    n0, n_cand, kind = INDEX_WORKLOADS[name]
+    rng = np.random.Generator(np.random.PCG64(SEED_BASE + 2000 + names.index(name) if seed is None else seed))
+    N = n0 if n is None else int(n)
+    if kind == "prefill":
+        positions = (int(rng.integers(0, 30000)) + np.arange(N)).astype(np.int32)
+    else:
+        positions = rng.integers(0, 32768, size=N).astype(np.int32)
+    logits = bf16_bits((np.round(rng.standard_normal((N, n_cand)) * 8) / 8).astype(np.float32))
+    if kind == "prefill":
+        n_valid = np.minimum((positions.astype(np.int64) + 1) // 4, n_cand).astype(np.int32)
+    elif kind == "decode_ragged":
+        n_valid = rng.integers(256, n_cand + 1, size=N).astype(np.int32)
+    else:
+        n_valid = np.full(N, n_cand, dtype=np.int32)
+    return dict(name=name, n=N, n_cand=n_cand, positions=positions, logits=logits, n_valid=n_valid, topk=640,
+                window=128, self_in_window=kind == "prefill", n_swa=8192, cmp_base=8192, k_cmp=512)
+
+
 def take_tokens(inp: dict, tokens) -> dict:
     """The same inputs restricted to a subset of tokens (the pool is shared)."""
     tokens = np.asarray(tokens, dtype=np.int64)

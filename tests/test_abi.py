@@ -214,3 +214,52 @@ def test_insert_misaligned(lib, which, off):
 def test_insert_null_params_and_empty(lib):
     assert lib.sparse_mla_kv_insert(*([FAKE] * 5), None) == smla.SMLA_ERR_NULL
     assert lib.sparse_mla_kv_insert(*([None] * 5), ctypes.byref(good_insert(n=0))) == smla.SMLA_OK
+
+
+# ---------------------------------------------------------------- index-row builder
+
+
+def good_index(**kw):
+    base = dict(s_q=4, n_cand=2048, topk=640, window=128, self_in_window=False, n_swa=8192, cmp_base=8192, k_cmp=512)
+    base.update(kw)
+    return smla.make_index_params(**base)
+
+
+def test_index_struct_layout():
+    P = smla.SmlaIndexParams
+    assert P.k_cmp.offset == 28 and P.stream.offset == 32 and ctypes.sizeof(P) == 40
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(s_q=-1), smla.SMLA_ERR_VALUE),
+    (dict(n_cand=65537), smla.SMLA_ERR_SHAPE),
+    (dict(n_swa=0), smla.SMLA_ERR_VALUE),
+    (dict(window=8193), smla.SMLA_ERR_SHAPE),
+    (dict(k_cmp=-1), smla.SMLA_ERR_SHAPE),
+    (dict(topk=639), smla.SMLA_ERR_SHAPE),
+    (dict(topk=70000, k_cmp=60000), smla.SMLA_ERR_SHAPE),
+    (dict(cmp_base=-1), smla.SMLA_ERR_VALUE),
+    (dict(cmp_base=0x7FFFFFFF - 100), smla.SMLA_ERR_VALUE),
+])
+def test_index_rejected_parameters(lib, kw, code):
+    p = good_index(**kw)
+    assert lib.sparse_mla_build_index(FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(p)) == code
+    assert smla.sparse_mla_last_error() != ""
+
+
+def test_index_self_in_window_flag(lib):
+    p = good_index()
+    p.self_in_window = 2
+    assert lib.sparse_mla_build_index(FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(p)) == smla.SMLA_ERR_VALUE
+
+
+@pytest.mark.parametrize("which", [0, 1, 3, 4])
+def test_index_null_arrays(lib, which):
+    ptrs = [FAKE] * 5
+    ptrs[which] = None
+    assert lib.sparse_mla_build_index(*ptrs, ctypes.byref(good_index())) == smla.SMLA_ERR_NULL
+
+
+def test_index_misaligned_logits_and_empty(lib):
+    assert lib.sparse_mla_build_index(FAKE, FAKE + 1, FAKE, FAKE, FAKE, ctypes.byref(good_index())) == smla.SMLA_ERR_VALUE
+    assert lib.sparse_mla_build_index(*([None] * 5), ctypes.byref(good_index(s_q=0))) == smla.SMLA_OK
