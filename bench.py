@@ -18,6 +18,7 @@ Prints one JSON line:
                MFMA fractions
   kv_insert    the KV-insert entry point (the pool-row producer) on its three workloads:
                us/call, tokens/s, algorithmic HBM bytes / mean duration against 8 TB/s
+  build_index  the index-row builder on its four workloads, the same figures
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
@@ -230,6 +231,48 @@ def measure_insert(name, steps, torch, device):
                 hbm_frac=nbytes / (mean_us * 1e-6) / 1e9 / HBM_PEAK_GBS)
 
 
+def measure_index(name, steps, torch, device):
+    """Time the index-row builder on one workload.  Algorithmic bytes per token: the
+    valid candidate logits read (2 n_valid), the position and n_valid (8), the index row
+    and its length written (4 topk + 4)."""
+    from prefill_token_amd import inputs, sparse_mla_build_index
+
+    c = inputs.make_index(name)
+    pos = torch.from_numpy(c["positions"]).to(device)
+    lg = torch.from_numpy(c["logits"].view(np.int16)).to(device).view(torch.bfloat16)
+    nv = torch.from_numpy(c["n_valid"]).to(device)
+    idx = torch.empty((c["n"], c["topk"]), dtype=torch.int32, device=device)
+    L = torch.empty((c["n"],), dtype=torch.int32, device=device)
+
+    def call():
+        sparse_mla_build_index(pos, lg, nv, idx, L, window=c["window"], self_in_window=c["self_in_window"],
+                               n_swa=c["n_swa"], cmp_base=c["cmp_base"], k_cmp=c["k_cmp"])
+
+    call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(CALLS_PER_GRAPH):
+            call()
+    stream = torch.cuda.current_stream()
+    reps = max(1, steps // CALLS_PER_GRAPH)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    g.replay()
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 / CALLS_PER_GRAPH for a, b in ev])
+    n = c["n"]
+    nbytes = float(2 * np.minimum(c["n_valid"], c["n_cand"]).sum() + n * (8 + 4 * c["topk"] + 4))
+    mean_us = float(us.mean())
+    return dict(workload=name, kernel="build_index_kernel", tokens=n, n_cand=c["n_cand"], us_per_call_mean=mean_us,
+                us_per_call_median=float(np.median(us)), tokens_per_s=n / (mean_us * 1e-6), bytes_per_call=nbytes,
+                hbm_GBs=nbytes / (mean_us * 1e-6) / 1e9, hbm_frac=nbytes / (mean_us * 1e-6) / 1e9 / HBM_PEAK_GBS)
+
+
 def cpu_baseline(seconds, torch, device):
     """The oracle on a bounded sample of the headline recipe, all host threads."""
     import oracle
@@ -284,7 +327,7 @@ def host_info():
 
 def source_digest():
     h = hashlib.sha256()
-    for fn in ("smla_kernels.hip", "kv_insert.hip", "smla_api.cpp", "smla_internal.h"):
+    for fn in ("smla_kernels.hip", "kv_insert.hip", "index_build.hip", "smla_api.cpp", "smla_internal.h"):
         with open(os.path.join(ROOT, "prefill_token_amd", "csrc", fn), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -373,7 +416,8 @@ def main():
     ap.add_argument("--workload", default="decode_sq1")
     ap.add_argument("--extra", default=",".join(EXTRA), help="comma-separated workloads after the timed region")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-insert", action="store_true", help="skip the KV-insert measurements")
+    ap.add_argument("--no-insert", action="store_true",
+                    help="skip the KV-insert and index-row-builder measurements")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB")
     ap.add_argument("--traffic-from", default="", metavar="DIR")
@@ -417,6 +461,16 @@ def main():
             print(f"# {name}: {r['us_per_call_mean']:.2f} us/call, {r['tokens_per_s']:.4g} tok/s, "
                   f"HBM {100 * r['hbm_frac']:.1f}%", file=sys.stderr, flush=True)
 
+    builds = []
+    if not args.no_insert:
+        from prefill_token_amd import inputs
+
+        for name in inputs.INDEX_WORKLOADS:
+            r = measure_index(name, args.steps, torch, device)
+            builds.append(r)
+            print(f"# {name}: {r['us_per_call_mean']:.2f} us/call, {r['tokens_per_s']:.4g} tok/s, "
+                  f"HBM {100 * r['hbm_frac']:.1f}%", file=sys.stderr, flush=True)
+
     digest = source_digest()
     traffic = load_traffic(digest)
     achieved = head["compulsory_bytes"] / (head["us_per_call_mean"] * 1e-6) / 1e9
@@ -441,6 +495,7 @@ def main():
         "config": {"workload": head["description"], "name": head["workload"], "s_q": head["s_q"],
                    "num_splits": head["num_splits"], "graph": True},
         "roofline": roofline, "cpu_baseline": cpu, "configs": configs, "kv_insert": inserts,
+        "build_index": builds,
         "device": torch.cuda.get_device_name(device), "host": host_info(), "source_digest": digest,
     }
     print(json.dumps(out), flush=True)
