@@ -88,8 +88,9 @@ typedef struct smla_params {
                        (NULL only when that size is 0).  Its first 256 bytes hold the
                        work-item scheduler's counters: they must be zero before the
                        first call on this workspace, and every call leaves them zero
-                       (zero-fill a new workspace once).  The rest (split partials) is
-                       clobbered.  Calls sharing a workspace must not overlap. */
+                       (zero-fill a new workspace once).  The rest (the item order of
+                       an unsplit call, or the split partials) is clobbered.  Calls
+                       sharing a workspace must not overlap. */
   size_t workspace_bytes;
   void* stream;     /* hipStream_t */
 } smla_params;
@@ -125,7 +126,9 @@ int sparse_mla_fwd(const void* q, const void* kv_pool, const uint8_t* kv_scales,
 
 /*
  * Bytes of device workspace sparse_mla_fwd needs for these parameters: 256 bytes of
- * scheduler state, plus the split partials when the call is split (0 when s_q = 0).
+ * scheduler state, then either 4 * s_q bytes rounded up to 256 (the order in which an
+ * unsplit call takes its tokens) or, when the call is split, the split partials (0 when
+ * s_q = 0).
  * Depends on s_q, d, topk and num_splits, and with num_splits = 0 on the current
  * device's compute-unit count.  Returns 0 for parameters sparse_mla_fwd would reject.
  */

@@ -76,8 +76,10 @@ int choose_splits(const smla_params* p) {
 
 size_t workspace_bytes_for(const smla_params* p, int ns) {
   if (p->s_q <= 0) return 0;
-  const size_t part = ns <= 1 ? 0 : (size_t)p->s_q * (size_t)ns * smla::partial_floats(p->h_q, p->d) * sizeof(float);
-  return smla::kSchedBytes + part;
+  // one split: the item order (s_q int32, rounded up to 256 bytes); more: the partials
+  const size_t rest = ns <= 1 ? ((size_t)p->s_q * 4 + 255) / 256 * 256
+                              : (size_t)p->s_q * (size_t)ns * smla::partial_floats(p->h_q, p->d) * sizeof(float);
+  return smla::kSchedBytes + rest;
 }
 
 }  // namespace

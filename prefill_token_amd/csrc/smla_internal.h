@@ -18,7 +18,7 @@ struct LaunchArgs {
   uint8_t* out_fp8;           // [s_q][h_q][d]
   uint8_t* out_scales;        // [s_q][h_q][d/32]
   float* out_f32;             // [s_q][h_q][d] or null
-  void* workspace;            // scheduler state (kSchedBytes), then partials when num_splits > 1
+  void* workspace;            // scheduler state (kSchedBytes), then the item order (num_splits = 1) or the partials
   int s_q, h_q, d, rope_dim, topk, kv_format, num_splits;
   int64_t n_rows;
   float sm_scale, rms_eps, rope_theta;

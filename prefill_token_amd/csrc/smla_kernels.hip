@@ -180,6 +180,7 @@ struct KArgs {
   float* out_f32;
   float* ws;         // split partials (after the scheduler state)
   unsigned* sched;   // work-item scheduler: [0] next item - gridDim.x, [1] finished workgroups
+  const int* order;  // item taken in scheduling slot k (written by smla_order), or null: item k
   int s_q, h_q, rope_dim, topk, num_splits, tiles_per_split;
   long long n_rows;
   float sm_scale, rms_eps, rope_theta;
@@ -1136,8 +1137,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
   struct Item {
     int t, pos, lcap, tb, te, n;
   };
-  auto info = [&](int item) {
+  auto info = [&](int slot) {
     Item I;
+    const int item = a.order ? a.order[slot] : slot;
     I.t = item / ns;
     const int split = item % ns;
     I.pos = a.positions[I.t];
@@ -1907,6 +1909,143 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
   }
 }
 
+// Scheduling order of the persistent kernel's items when there are more items than
+// workgroups and one split per token: tokens by descending tile count, equal counts in
+// token order (longest processing time first, so that the last items a workgroup takes
+// are short ones and the workgroups finish together).  One 1024-thread workgroup takes
+// the tokens 4096 at a time, four per thread (token c * 1024 + tid, c < 4): each wave
+// counts, per tile count (key, capped at 63), its lanes with that key (lanes with the
+// same key found by six ballots), then one scan per key over (c, wave) gives each
+// token's place among the tokens of its key, and a scan over the keys (largest first)
+// the key's first slot.  Above 4096 tokens a first pass builds the key histogram.
+__global__ __launch_bounds__(1024) void smla_order(const int32_t* __restrict__ topk_length, int s_q, int topk,
+                                                   int* __restrict__ order) {
+  constexpr int NB = 64, NW = 16, CH = 4, SUPER = CH * 1024, NC = CH * NW;
+  // per key: lanes of that key per (chunk, wave), then their exclusive scan (rows padded
+  // to 65 words, so that the accesses below hit distinct banks)
+  __shared__ int cnt[NB][NC + 1];
+  __shared__ int tot[NB], off[NB], base[NB];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  // the scans: thread tid serves key kb = tid / 16 (a DPP row of 16 lanes per key) and
+  // its columns 4 ks .. 4 ks + 3
+  const int kb = tid >> 4, ks = tid & 15;
+  auto key_of = [&](int l) {
+    l = l < 0 ? 0 : (l > topk ? topk : l);
+    const int n = (l + T - 1) / T;
+    return n < NB - 1 ? n : NB - 1;
+  };
+  auto dpp = [](int v, auto ctrl) {
+    return __builtin_amdgcn_update_dpp(0, v, decltype(ctrl)::value, 0xF, 0xF, true);
+  };
+  using shr1 = std::integral_constant<int, 0x111>;
+  using shr2 = std::integral_constant<int, 0x112>;
+  using shr4 = std::integral_constant<int, 0x114>;
+  using shr8 = std::integral_constant<int, 0x118>;
+  using ror1 = std::integral_constant<int, 0x121>;
+  using ror2 = std::integral_constant<int, 0x122>;
+  using ror4 = std::integral_constant<int, 0x124>;
+  using ror8 = std::integral_constant<int, 0x128>;
+  // sum over the 16 lanes of the row, in every lane
+  auto row_sum = [&](int v) {
+    v += dpp(v, ror8{});
+    v += dpp(v, ror4{});
+    v += dpp(v, ror2{});
+    v += dpp(v, ror1{});
+    return v;
+  };
+  // off[kb] = tokens with a larger key: row kb sums tot[kb + 1 ..]
+  auto key_offsets = [&]() {
+    int v = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int b = kb + 1 + ks + 16 * r;
+      if (b < NB) v += tot[b];
+    }
+    v = row_sum(v);
+    if (ks == 0) off[kb] = v;
+  };
+  const bool multi = s_q > SUPER;
+  if (tid < NB) {
+    tot[tid] = 0;
+    base[tid] = 0;
+  }
+  __syncthreads();
+  if (multi) {
+    for (int t0 = 0; t0 < s_q; t0 += SUPER) {
+      const int nrem = s_q - t0;
+      const __amdgpu_buffer_rsrc_t rs = buf_rsrc(topk_length + t0, (uint32_t)(nrem < SUPER ? nrem : SUPER) * 4u);
+      int lraw[CH];
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+        lraw[c] = (int)__builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)(c * 1024 + tid) * 4u, 0, 0);
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+        if (c * 1024 + tid < nrem) atomicAdd(&tot[key_of(lraw[c])], 1);
+    }
+    __syncthreads();
+    key_offsets();
+  }
+  for (int s0 = 0; s0 < s_q; s0 += SUPER) {
+    // this pass's lengths through a range-checked buffer (tokens past the end read as
+    // zero), so that the four loads go out together without branches
+    const int nrem = s_q - s0;
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(topk_length + s0, (uint32_t)(nrem < SUPER ? nrem : SUPER) * 4u);
+    int lraw[CH], key[CH], rank[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+      lraw[c] = (int)__builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)(c * 1024 + tid) * 4u, 0, 0);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) cnt[kb][4 * ks + c] = 0;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) key[c] = c * 1024 + tid < nrem ? key_of(lraw[c]) : -1;
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const bool live = key[c] >= 0;
+      unsigned long long peers = __ballot(live);
+#pragma unroll
+      for (int k = 0; k < 6; ++k) {
+        const unsigned long long m = __ballot((key[c] >> k) & 1);
+        peers &= ((key[c] >> k) & 1) ? m : ~m;
+      }
+      rank[c] = __popcll(peers & ((1ull << lane) - 1ull));
+      if (live && rank[c] == 0) cnt[key[c]][c * NW + wv] = __popcll(peers);
+    }
+    __syncthreads();
+    {
+      // exclusive scan of row kb over its 64 columns: 4 per lane, then across the 16 lanes
+      int v[4], run = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        v[r] = run;
+        run += cnt[kb][4 * ks + r];
+      }
+      int incl = run;
+      incl += dpp(incl, shr1{});
+      incl += dpp(incl, shr2{});
+      incl += dpp(incl, shr4{});
+      incl += dpp(incl, shr8{});
+      const int excl = incl - run;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) cnt[kb][4 * ks + r] = excl + v[r];
+      if (ks == 15) tot[kb] = incl;
+    }
+    __syncthreads();
+    if (!multi) {
+      key_offsets();
+      __syncthreads();
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+      if (key[c] >= 0) order[off[key[c]] + base[key[c]] + cnt[key[c]][c * NW + wv] + rank[c]] = s0 + c * 1024 + tid;
+    if (multi) {
+      __syncthreads();
+      if (tid < NB) base[tid] += tot[tid];
+      __syncthreads();
+    }
+  }
+}
+
 // Combine the splits of one (token, head): o = sum_s w_s acc_s / sum_s w_s l_s with
 // w_s = 2^(m_s - M), M = max_s m_s, in split order, then the epilogue.  One memory
 // round trip: every thread issues the loads of its 4 dims for all splits (16 at a
@@ -2181,7 +2320,16 @@ hipError_t launch_t(const LaunchArgs& x, const KArgs& k) {
   const bool ws = D == 512 && EB == 1 && (x.rope_dim == 0 || x.rope_dim == 64);
   if (ws) {
     const int cus = device_cus();
-    hipLaunchKernelGGL(smla_ws, dim3((unsigned)(items < cus ? items : cus)), dim3(NTHREADS), 0, x.stream, k);
+    KArgs kw = k;
+    if (ns == 1 && items > cus) {
+      // more items than workgroups: take them longest first
+      int* order = reinterpret_cast<int*>(k.ws);
+      hipLaunchKernelGGL(smla_order, dim3(1), dim3(1024), 0, x.stream, x.topk_length, x.s_q, x.topk, order);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      kw.order = order;
+    }
+    hipLaunchKernelGGL(smla_ws, dim3((unsigned)(items < cus ? items : cus)), dim3(NTHREADS), 0, x.stream, kw);
   } else {
     hipLaunchKernelGGL((smla_main<D, EB>), dim3((unsigned)items), dim3(NTHREADS), 0, x.stream, k);
   }
@@ -2212,6 +2360,7 @@ hipError_t launch(const LaunchArgs& x) {
   k.out_scales = x.out_scales;
   k.out_f32 = x.out_f32;
   k.sched = static_cast<unsigned*>(x.workspace);
+  k.order = nullptr;
   k.ws = reinterpret_cast<float*>(static_cast<unsigned char*>(x.workspace) + kSchedBytes);
   k.s_q = x.s_q;
   k.h_q = x.h_q;

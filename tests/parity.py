@@ -46,9 +46,11 @@ def run_gpu(inp: dict, *, num_splits: int = 0, with_f32: bool = True, device="cu
 
     t = dev_inputs if dev_inputs is not None else to_device(inp, device)
     s_q, h, d = inp["q"].shape
-    out_fp8 = torch.empty((s_q, h, d), dtype=torch.uint8, device=device)
-    out_sc = torch.empty((s_q, h, d // 32), dtype=torch.uint8, device=device)
-    out_f32 = torch.empty((s_q, h, d), dtype=torch.float32, device=device) if with_f32 else None
+    # outputs start as values the step never writes (scale byte 255, f32 NaN), so a token
+    # the kernels skipped cannot pass for a computed one
+    out_fp8 = torch.full((s_q, h, d), 0xFF, dtype=torch.uint8, device=device)
+    out_sc = torch.full((s_q, h, d // 32), 0xFF, dtype=torch.uint8, device=device)
+    out_f32 = torch.full((s_q, h, d), float("nan"), dtype=torch.float32, device=device) if with_f32 else None
     sparse_mla_fwd(t["q"], t["kv_pool"], t["kv_scales"], t["indices"], t["topk_length"], t["positions"],
                    t["norm_w"], out_fp8, out_sc, sm_scale=inp["sm_scale"], rope_dim=inp["rope_dim"],
                    eps=inp["eps"], theta=inp["theta"], out_f32=out_f32, num_splits=num_splits,

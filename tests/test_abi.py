@@ -145,7 +145,8 @@ def test_split_choice():
     assert smla.sparse_mla_num_splits(good(s_q=2123)) == 1
     assert smla.sparse_mla_num_splits(good(s_q=1, num_splits=3)) == 3
     assert smla.sparse_mla_num_splits(good(s_q=1, num_splits=64)) == 10  # capped at the tile count
-    assert smla.sparse_mla_workspace_size(good(s_q=2123)) == 256  # the scheduler counters only
+    # the scheduler counters, then the unsplit call's item order (s_q int32, 256-byte units)
+    assert smla.sparse_mla_workspace_size(good(s_q=2123)) == 256 + 8704
 
 
 def test_zero_tokens_is_a_noop(lib):

@@ -50,8 +50,8 @@ def test_decode_forced_splits(ns):
     check(inputs.make("decode_sq64", seed=101, s_q=8), num_splits=ns)
 
 
-def _sampled(name, n_sample, seed=0):
-    inp = inputs.make(name)
+def _sampled(name, n_sample, seed=0, **make_kw):
+    inp = inputs.make(name, **make_kw)
     dev = to_device(inp)
     full = run_gpu(inp, dev_inputs=dev)                  # with out_f32
     bench = run_gpu(inp, dev_inputs=dev, with_f32=False)  # the benchmark's launch configuration
@@ -63,6 +63,7 @@ def _sampled(name, n_sample, seed=0):
     tok = np.array(sorted(pick))
     sub = inputs.take_tokens(inp, tok)
     ref = run_oracle(sub)
+    assert int((full["scales"] == 0xFF).sum()) == 0, "tokens left unwritten"
     g = {k: v[tok] for k, v in full.items()}
     st = compare(g, ref)
     print(name, "sampled", len(tok), st, flush=True)
@@ -76,6 +77,11 @@ def test_prefill_sq2123_sampled():
     _sampled("prefill_sq2123", 40)
 
 
+def test_ragged_more_than_4096_tokens_sampled():
+    # the item order is built in passes of 4096 tokens above that count
+    _sampled("decode_sq1024", 30, seed=5, s_q=4500)
+
+
 def _decode_case(seed, s_q=8):
     return inputs.make("decode_sq64", seed=seed, s_q=s_q)
 
@@ -86,6 +92,18 @@ def test_topk_length_edges():
     inp["indices"][inp["indices"] < 0] = 17  # no sentinels: the length alone decides
     for ns in (0, 1, 4):
         check(inp, num_splits=ns)
+
+
+def test_ragged_lengths_longest_first():
+    # More tokens than compute units, one split each: the tokens are taken in order of
+    # descending tile count.  Lengths span empty rows, every tile count and values past
+    # topk; every token is checked.
+    inp = inputs.make("decode_sq1024", seed=31, s_q=400)
+    L = inp["topk_length"].copy()
+    L[:16] = [0, -3, 1, 64, 65, 640, 700, 5000, 128, 0, 639, 2, 200, 384, 512, 576]
+    inp["topk_length"] = L
+    check(inp)
+    check(inp, num_splits=1)
 
 
 def test_empty_and_sentinel_rows():
