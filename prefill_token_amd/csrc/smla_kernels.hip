@@ -229,15 +229,41 @@ __device__ __forceinline__ float bf16_f32(uint32_t h) { return __builtin_bit_cas
 // (bits 3-5 of the row enter through r >> 3 and r >> 6).
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3) ^ (r >> 6)) & 7; }
 
-// One split's partial in the workspace: the accumulator of HP heads x d dims (rows of
-// heads >= h_q unused), then m [HP] and l [HP].  The generic kernel stores the
-// accumulator row-major [head][dim]; smla_ws stores it in its register order, so that
-// every store instruction of a wave writes 1 KB contiguously:
+// One split's partial in the workspace of the generic kernel: the f32 accumulator of HP
+// heads x d dims, row-major [head][dim] (rows of heads >= h_q unused), then m [HP] and
+// l [HP].  This is also the workspace stride the host sizes for.
 __device__ __forceinline__ size_t partial_floats_d(int, int d) { return (size_t)HP * (size_t)(d + 2); }
 
-// smla_ws's order: float4 ((((v * 2 + mb) * 4 + nb) * 4 + g) * 64 + lrow + 32 lhalf holds
-// dims 128v + 32nb + 8g + 4lhalf .. + 3 of head 32mb + lrow (lane lrow + 32 lhalf of P.V
-// wave v, registers 4g .. 4g + 3 of acc[mb][nb]).
+// One split's partial of smla_ws (d = 512), in floats; about half the bytes of the f32
+// form, so that the split's stores and the combine's loads move half as much:
+//   [0, WSP_SCL): the accumulator in the P.V waves' register order as f16, each 32-dim
+//     block of a head scaled by 2^(-E) with 2^E <= its amax < 2^(E+1), so that the values
+//     lie in (-2, 2) (f16 keeps 11 significant bits: the rounding error is at most 2^-11
+//     of the block amax).  The 16-byte slot (((v * 2 + mb) * 4 + nb) * 2 + g2) * 64 +
+//     lrow + 32 lhalf holds registers 8 g2 .. 8 g2 + 7 of acc[mb][nb] of lane lrow +
+//     32 lhalf of P.V wave v: dims 128v + 32nb + 16 g2 + 4 lhalf + {0..3, 8..11} of head
+//     32 mb + lrow.  Each store instruction of a wave writes 1 KB contiguously.
+//   [WSP_SCL, WSP_M): the decode scale 2^E (f32) of block gb of head h at gb * HP + h;
+//   [WSP_M, WSP_L): m [HP]; [WSP_L, WSP_FLOATS): l [HP].
+constexpr int WSP_SCL = HP * 512 / 2, WSP_M = WSP_SCL + HP * 16, WSP_L = WSP_M + HP, WSP_FLOATS = WSP_L + HP;
+static_assert(WSP_FLOATS <= HP * (512 + 2), "smla_ws partials fit the host's per-split stride");
+
+// 2^(-E) and 2^E for a block amax a >= 0 (E from the f32 exponent field, kept where both
+// are normal floats)
+__device__ __forceinline__ void f16_block_scale(float a, float& enc, float& dec) {
+  int eb = (int)((__builtin_bit_cast(uint32_t, a) >> 23) & 0xFFu);
+  eb = eb < 1 ? 1 : (eb > 253 ? 253 : eb);
+  enc = __builtin_bit_cast(float, (uint32_t)(254 - eb) << 23);
+  dec = __builtin_bit_cast(float, (uint32_t)eb << 23);
+}
+__device__ __forceinline__ uint32_t pack_f16(float x, float y) {
+  typedef float f2v __attribute__((ext_vector_type(2)));
+  typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+  const f2v v = {x, y};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2v));
+}
+__device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu)); }
+__device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
 
 // LDS DMA (buffer_load_dword[x4] ... lds): every lane writes its 4 / 16 bytes at
 // lds_base + 4*lane / 16*lane, read at byte offset voff of a buffer resource.  An
@@ -1883,22 +1909,36 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
         // order: each store instruction writes 1 KB contiguously
         const int split = item % ns;
         float* part = K.ws + ((size_t)I.t * ns + split) * partial_floats_d(hq, D);
-        float* pm = part + (size_t)HP * D;
-        float* pl = pm + HP;
+        float* pm = part + WSP_M;
+        float* pl = part + WSP_L;
         if (v == 0 && lane < hq) {
           pm[lane] = mfin[lane];
           pl[lane] = lsum[lane] + lsum[HP + lane];
         }
         if (n > 0) {
-          float4* pv4 = reinterpret_cast<float4*>(part) + 2 * 4 * 4 * 64 * v + lane;
+          uint4* pv4 = reinterpret_cast<uint4*>(part) + 2 * 4 * 2 * 64 * v + lane;
+          float* psc = part + WSP_SCL;
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
+            for (int nb = 0; nb < 4; ++nb) {
+              float am = 0.f;
 #pragma unroll
-              for (int g = 0; g < 4; ++g)
-                pv4[((mb * 4 + nb) * 4 + g) * 64] = make_float4(acc[mb][nb][4 * g], acc[mb][nb][4 * g + 1],
-                                                               acc[mb][nb][4 * g + 2], acc[mb][nb][4 * g + 3]);
+              for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(acc[mb][nb][i]));
+              am = fmaxf(am, __shfl_xor(am, 32));
+              float enc, dec;
+              f16_block_scale(am, enc, dec);
+              if (lane < 32) psc[(4 * v + nb) * HP + 32 * mb + lrow] = dec;
+#pragma unroll
+              for (int g2 = 0; g2 < 2; ++g2) {
+                const int r = 8 * g2;
+                pv4[((mb * 4 + nb) * 2 + g2) * 64] = make_uint4(
+                    pack_f16(acc[mb][nb][r] * enc, acc[mb][nb][r + 1] * enc),
+                    pack_f16(acc[mb][nb][r + 2] * enc, acc[mb][nb][r + 3] * enc),
+                    pack_f16(acc[mb][nb][r + 4] * enc, acc[mb][nb][r + 5] * enc),
+                    pack_f16(acc[mb][nb][r + 6] * enc, acc[mb][nb][r + 7] * enc));
+              }
+            }
         }
       }
       if (!more) break;
@@ -2129,8 +2169,11 @@ __global__ __launch_bounds__(CTHREADS) void smla_combine_lm4(KArgs a) {
   const int h = 32 * mb + lrow, hq = a.h_q, ns = a.num_splits;
   const size_t pf = partial_floats_d(hq, D);
   const float* base = a.ws + (size_t)t * ns * pf;
-  // float4 slots of this thread in a split: g = 2gp + k, lane half lh
-  const int s0 = ((((v * 2 + mb) * 4 + nb) * 4 + 2 * gp) * 64) + lrow;
+  // 16-byte slots of this thread in a split: g2 = gp, lanes lrow and lrow + 32; the
+  // thread's 16 dims 16gp .. 16gp + 15 are halves 0..3 (dims 0..3), 4..7 (8..11) of the
+  // first and 0..3 (4..7), 4..7 (12..15) of the second
+  const int s0 = ((((v * 2 + mb) * 4 + nb) * 2 + gp) * 64) + lrow;
+  const int gb = 4 * v + nb;
   const bool rot = a.rope_dim > 0 && v == 3 && nbp == 1;
   if (rot) rope_table(a.positions[t], a, cs, sn);
   float M = -INFINITY, den = 0.f;
@@ -2139,19 +2182,18 @@ __global__ __launch_bounds__(CTHREADS) void smla_combine_lm4(KArgs a) {
   for (int e = 0; e < 16; ++e) o[e] = 0.f;
   for (int c0 = 0; c0 < ns; c0 += SCH) {
     // every load of the chunk goes out before the first use
-    float4 x[SCH][4];
-    float mv[SCH], lv[SCH];
+    uint4 x[SCH][2];
+    float mv[SCH], lv[SCH], dv[SCH];
 #pragma unroll
     for (int k = 0; k < SCH; ++k)
       if (c0 + k < ns) {
         const float* sp = base + (size_t)(c0 + k) * pf;
-        const float4* p4 = reinterpret_cast<const float4*>(sp) + s0;
+        const uint4* p4 = reinterpret_cast<const uint4*>(sp) + s0;
         x[k][0] = p4[0];
         x[k][1] = p4[32];
-        x[k][2] = p4[64];
-        x[k][3] = p4[96];
-        mv[k] = sp[(size_t)HP * D + h];
-        lv[k] = sp[(size_t)HP * D + HP + h];
+        dv[k] = sp[WSP_SCL + gb * HP + h];
+        mv[k] = sp[WSP_M + h];
+        lv[k] = sp[WSP_L + h];
       }
 #pragma unroll
     for (int k = 0; k < SCH; ++k)
@@ -2165,13 +2207,16 @@ __global__ __launch_bounds__(CTHREADS) void smla_combine_lm4(KArgs a) {
         }
         const float wv = exp2f(mv[k] - M);
         den += wv * lv[k];
-        // slot order (g = 2gp, lh 0), (2gp, 1), (2gp + 1, 0), (2gp + 1, 1): dims 0..15
+        const float ws = wv * dv[k];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          o[4 * q] += wv * x[k][q].x;
-          o[4 * q + 1] += wv * x[k][q].y;
-          o[4 * q + 2] += wv * x[k][q].z;
-          o[4 * q + 3] += wv * x[k][q].w;
+        for (int u = 0; u < 2; ++u) {
+          const uint32_t xw[4] = {x[k][u].x, x[k][u].y, x[k][u].z, x[k][u].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int e = 4 * u + 8 * (q >> 1) + 2 * (q & 1);
+            o[e] += ws * f16_lo(xw[q]);
+            o[e + 1] += ws * f16_hi(xw[q]);
+          }
         }
       }
   }
@@ -2195,7 +2240,6 @@ __global__ __launch_bounds__(CTHREADS) void smla_combine_lm4(KArgs a) {
   for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(o[e]));
   amax = fmaxf(amax, __shfl_xor(amax, 32));
   if (h >= hq) return;
-  const int gb = 4 * v + nb;
   const size_t g0 = ((size_t)t * hq + h) * D + 32 * gb + 16 * gp;
   const int e8 = ue8m0_exp(amax);
   const float sc = ue8m0_f32((uint32_t)e8);
@@ -2234,21 +2278,24 @@ __global__ __launch_bounds__(LMT) void smla_combine_lm1(KArgs a) {
   const int h = 32 * mb + lrow, hq = a.h_q, ns = a.num_splits;
   const size_t pf = partial_floats_d(hq, D);
   const float* base = a.ws + (size_t)t * ns * pf;
-  const int slot = ((((v * 2 + mb) * 4 + nb) * 4 + g) * 64) + lane;  // float4 index
+  // registers 4g .. 4g + 3 of the lane: half g & 1 of the 16-byte slot g >> 1
+  const int slot = (((((v * 2 + mb) * 4 + nb) * 2 + (g >> 1)) * 64) + lane) * 2 + (g & 1);  // 8-byte index
+  const int gb = 4 * v + nb;
   const bool rot = a.rope_dim > 0 && v == 3 && nbp == 1;
   if (rot) rope_table(a.positions[t], a, cs, sn);
   float M = -INFINITY, den = 0.f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int c0 = 0; c0 < ns; c0 += SCH) {
-    float4 x[SCH];
-    float mv[SCH], lv[SCH];
+    uint2 x[SCH];
+    float mv[SCH], lv[SCH], dv[SCH];
 #pragma unroll
     for (int k = 0; k < SCH; ++k)
       if (c0 + k < ns) {
         const float* sp = base + (size_t)(c0 + k) * pf;
-        x[k] = reinterpret_cast<const float4*>(sp)[slot];
-        mv[k] = sp[(size_t)HP * D + h];
-        lv[k] = sp[(size_t)HP * D + HP + h];
+        x[k] = reinterpret_cast<const uint2*>(sp)[slot];
+        dv[k] = sp[WSP_SCL + gb * HP + h];
+        mv[k] = sp[WSP_M + h];
+        lv[k] = sp[WSP_L + h];
       }
 #pragma unroll
     for (int k = 0; k < SCH; ++k)
@@ -2261,7 +2308,8 @@ __global__ __launch_bounds__(LMT) void smla_combine_lm1(KArgs a) {
         }
         const float wv = exp2f(mv[k] - M);
         den += wv * lv[k];
-        o.x += wv * x[k].x; o.y += wv * x[k].y; o.z += wv * x[k].z; o.w += wv * x[k].w;
+        const float ws = wv * dv[k];
+        o.x += ws * f16_lo(x[k].x); o.y += ws * f16_hi(x[k].x); o.z += ws * f16_lo(x[k].y); o.w += ws * f16_hi(x[k].y);
       }
   }
   const float inv = den > 0.f ? 1.0f / den : 0.f;
@@ -2287,7 +2335,6 @@ __global__ __launch_bounds__(LMT) void smla_combine_lm1(KArgs a) {
 #pragma unroll
   for (int k = 0; k < 8; ++k) amax = fmaxf(amax, red[nbl][lrow][k]);
   if (h >= hq) return;
-  const int gb = 4 * v + nb;
   const size_t g0 = ((size_t)t * hq + h) * D + 32 * gb + 8 * g + 4 * lhalf;
   const int e8 = ue8m0_exp(amax);
   const float sc = ue8m0_f32((uint32_t)e8);
