@@ -1559,7 +1559,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
         const bool touch = it == touch_it;
         if (touch) {
           const __amdgpu_buffer_rsrc_t qrs =
-              buf_rsrc(a.q + (size_t)(next / ns) * a.h_q * D, (uint32_t)(a.h_q * D * 2));
+              buf_rsrc(a.q + (size_t)((a.order ? a.order[next] : next) / ns) * a.h_q * D, (uint32_t)(a.h_q * D * 2));
           const uint32_t off = 256u * (uint32_t)(64 * w + lane);
           tch0 = __builtin_amdgcn_raw_buffer_load_b32(qrs, off, 0, 0);
           tch1 = __builtin_amdgcn_raw_buffer_load_b32(qrs, off + 128u, 0, 0);
