@@ -84,6 +84,14 @@ def work_model(inp):
                 distinct_rows=int(distinct))
 
 
+def kernel_names(s_q, ns, torch, device):
+    """The kernels one call launches (d = 512 E4M3 pool, the persistent kernel's path)."""
+    cus = torch.cuda.get_device_properties(device).multi_processor_count
+    if ns > 1:
+        return "smla_ws + " + ("smla_combine_lm4" if ns <= 8 else "smla_combine_lm1")
+    return "smla_order + smla_ws" if s_q > cus else "smla_ws"
+
+
 def measure(name, steps, warmup, torch, device, timed_steps=None):
     """Time one workload; returns (result dict, wall seconds of the timed steps)."""
     from prefill_token_amd import inputs, make_params, sparse_mla_fwd, sparse_mla_num_splits, sparse_mla_workspace_size
@@ -169,7 +177,7 @@ def measure(name, steps, warmup, torch, device, timed_steps=None):
     mean_us = float(us.mean())
     res = dict(
         workload=name, description=inp["description"], s_q=s_q, num_splits=ns,
-        kernels="smla_ws" + (" + smla_combine" if ns > 1 else ""),
+        kernels=kernel_names(s_q, ns, torch, device),
         us_per_call_mean=mean_us, us_per_call_median=float(np.median(us)),
         us_per_call_p10=float(np.percentile(us, 10)), us_per_call_p90=float(np.percentile(us, 90)),
         us_per_call_cold_median=float(np.median(cold)),
