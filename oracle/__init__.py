@@ -8,7 +8,8 @@ The functions mirror the steps of the C file (each cites its passage there):
 ``bf16_decode``, ``e4m3_decode``, ``e4m3_encode``, ``ue8m0_exponent``,
 ``quantize_blocks``, ``rmsnorm``, ``rope``, the whole step ``sparse_mla``, and the two
 steps before it: the pool-row producer ``kv_insert`` and the index-row builder
-``build_index`` (plain numpy, below).
+``build_index`` (plain numpy, below), and the step after it, the output projection
+``wo_a`` (plain numpy).
 
 Parity pins: every function here is checked in ``tests/test_oracle_*.py`` against
 library routines (torch's CPU float8_e4m3fn cast, torch SDPA and rms_norm in fp64,
@@ -207,6 +208,35 @@ def kv_insert(kv_bits: np.ndarray, positions: np.ndarray, norm_w: np.ndarray, kv
     if rc != 0:
         raise ValueError(f"oracle_kv_insert failed with code {rc}")
     return pool, sc
+
+
+def mx_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """E4M3 codes with one UE8M0 exponent per 32 consecutive values along the last axis,
+    decoded exactly to fp64: ``e4m3(code) * 2^(scale - 127)``."""
+    v = e4m3_decode(codes)
+    sc = np.exp2(np.asarray(scales, dtype=np.float64) - 127.0)
+    return v * np.repeat(sc, 32, axis=-1)
+
+
+def wo_a(x_codes: np.ndarray, x_scales: np.ndarray, w_codes: np.ndarray, w_scales: np.ndarray,
+         heads_per_group: int = 1) -> np.ndarray:
+    """The consumer of the step's FP8 output: the per-group output projection (wo_a), fp64.
+
+    [vLLM #56344 "Deepseek V41 Attention MegaKernel", Purpose: the kernel's FP8 output is
+    fed straight into the wo_a einsum.]  The pages give no shape; the reading: the heads
+    are taken hg = heads_per_group at a time, and group g's hg * 512 dims are contracted
+    with its own weight [d_out][hg * 512]:
+
+        y[t, g, o] = sum_k x[t, g, k] * W[g, o, k],   x[t, g, h * 512 + i] = out[t, g * hg + h, i]
+
+    with x and W decoded exactly (``mx_decode``).  The contraction is numpy's einsum.
+    """
+    s, h, d = x_codes.shape
+    hg = int(heads_per_group)
+    G = h // hg
+    x = mx_decode(x_codes, x_scales).reshape(s, G, hg * d)
+    W = mx_decode(w_codes, w_scales)
+    return np.einsum("tgk,gok->tgo", x, W)
 
 
 def select_topk(logits_bits: np.ndarray, k: int) -> np.ndarray:

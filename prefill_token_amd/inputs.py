@@ -249,6 +249,37 @@ def make_index(name: str, seed: Optional[int] = None, n: Optional[int] = None) -
                 window=128, self_in_window=kind == "prefill", n_swa=8192, cmp_base=8192, k_cmp=512)
 
 
+# Output-projection (wo_a) workloads: the attention output of the decode / prefill token
+# counts in its E4M3 + UE8M0 form, projected per head (one head per group) to 128 outputs.
+#   name                  tokens  heads  heads per group  outputs per group
+WO_A_WORKLOADS = {
+    "wo_a_decode_sq1": (1, 64, 1, 128),
+    "wo_a_decode_sq64": (64, 64, 1, 128),
+    "wo_a_prefill_sq2123": (2123, 64, 1, 128),
+}
+
+
+def make_wo_a(name: str, seed: Optional[int] = None, n: Optional[int] = None, heads_per_group: Optional[int] = None,
+              d_out: Optional[int] = None) -> dict:
+    """Inputs of one wo_a workload: the attention output ~ N(0, 0.05) (the spread of a
+    softmax-weighted mean of N(0, 1) rows) and the weight ~ N(0, 1 / sqrt(hg * 512)), both
+    as E4M3 codes with one UE8M0 scale per 32 values (the generator's MX rule,
+    ``mx_pool``).  Seed 20263000 + the workload's position unless ``seed`` is given."""
+    names = list(WO_A_WORKLOADS)
+    n0, h, hg0, dout0 = WO_A_WORKLOADS[name]
+    rng = np.random.Generator(np.random.PCG64(SEED_BASE + 3000 + names.index(name) if seed is None else seed))
+    N = n0 if n is None else int(n)
+    hg = hg0 if heads_per_group is None else int(heads_per_group)
+    dout = dout0 if d_out is None else int(d_out)
+    d = 512
+    G = h // hg
+    x, xs = mx_pool((rng.standard_normal((N * h, d), dtype=np.float32) * np.float32(0.05)))
+    w, ws = mx_pool(rng.standard_normal((G * dout, hg * d), dtype=np.float32) / np.float32(np.sqrt(hg * d)))
+    return dict(name=name, n=N, h=h, d=d, heads_per_group=hg, d_out=dout,
+                x=x.reshape(N, h, d), x_scales=xs.reshape(N, h, d // 32),
+                w=w.reshape(G, dout, hg * d), w_scales=ws.reshape(G, dout, hg * d // 32))
+
+
 def take_tokens(inp: dict, tokens) -> dict:
     """The same inputs restricted to a subset of tokens (the pool is shared)."""
     tokens = np.asarray(tokens, dtype=np.int64)
