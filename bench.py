@@ -19,6 +19,8 @@ Prints one JSON line:
   kv_insert    the KV-insert entry point (the pool-row producer) on its three workloads:
                us/call, tokens/s, algorithmic HBM bytes / mean duration against 8 TB/s
   build_index  the index-row builder on its four workloads, the same figures
+  wo_a         the output projection (the step's FP8 output consumer) on its three
+               workloads: us/call, tokens/s, HBM and fp8 MFMA fractions
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
@@ -49,6 +51,7 @@ sys.path.insert(0, ROOT)
 METRIC = "sparse_mla_fwd µs/call + tokens/s and % HBM/MFMA roofline at s_q=1/64/1024"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 / fp16 MFMA
+MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 MFMA (the output projection's arithmetic)
 PAGES_US_SQ1 = 22.7            # pages' fused kernel at s_q = 1 (GB200, TP4, CUDA graph): context only
 EXTRA = ["decode_sq64", "decode_sq1024", "prefill_sq2123", "decode_sq256", "prefill_sq184"]
 FLUSH_BYTES = 512 << 20        # larger than the 256 MB MALL + 8 x 4 MB L2
@@ -281,6 +284,52 @@ def measure_index(name, steps, torch, device):
                 hbm_GBs=nbytes / (mean_us * 1e-6) / 1e9, hbm_frac=nbytes / (mean_us * 1e-6) / 1e9 / HBM_PEAK_GBS)
 
 
+def measure_wo_a(name, steps, torch, device):
+    """Time the output projection (wo_a) on one workload.  Algorithmic bytes: the E4M3
+    input and its scales (528 per token and head), the weight and its scales (read once),
+    the bf16 output; flops 2 * tokens * heads * 512 * d_out."""
+    from prefill_token_amd import inputs, sparse_mla_wo_a
+
+    c = inputs.make_wo_a(name)
+    x = torch.from_numpy(c["x"]).to(device)
+    xs = torch.from_numpy(c["x_scales"]).to(device)
+    w = torch.from_numpy(c["w"]).to(device)
+    ws = torch.from_numpy(c["w_scales"]).to(device)
+    G = c["h"] // c["heads_per_group"]
+    y = torch.empty((c["n"], G, c["d_out"]), dtype=torch.bfloat16, device=device)
+
+    def call():
+        sparse_mla_wo_a(x, xs, w, ws, y, heads_per_group=c["heads_per_group"])
+
+    call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(CALLS_PER_GRAPH):
+            call()
+    stream = torch.cuda.current_stream()
+    reps = max(1, steps // CALLS_PER_GRAPH)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    g.replay()
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 / CALLS_PER_GRAPH for a, b in ev])
+    n, h, dout = c["n"], c["h"], c["d_out"]
+    nbytes = float(n * h * 528 + G * dout * c["heads_per_group"] * 528 + n * G * dout * 2)
+    flops = 2.0 * n * h * 512 * dout
+    mean_us = float(us.mean())
+    return dict(workload=name, kernel="wo_a_kernel", tokens=n, heads=h, heads_per_group=c["heads_per_group"],
+                d_out=dout, us_per_call_mean=mean_us, us_per_call_median=float(np.median(us)),
+                tokens_per_s=n / (mean_us * 1e-6), bytes_per_call=nbytes, flops_per_call=flops,
+                hbm_GBs=nbytes / (mean_us * 1e-6) / 1e9, hbm_frac=nbytes / (mean_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                mfma_TFLOPs=flops / (mean_us * 1e-6) / 1e12,
+                mfma_frac_fp8=flops / (mean_us * 1e-6) / 1e12 / MFMA_FP8_PEAK_TFLOPS)
+
+
 def cpu_baseline(seconds, torch, device):
     """The oracle on a bounded sample of the headline recipe, all host threads."""
     import oracle
@@ -335,7 +384,7 @@ def host_info():
 
 def source_digest():
     h = hashlib.sha256()
-    for fn in ("smla_kernels.hip", "kv_insert.hip", "index_build.hip", "smla_api.cpp", "smla_internal.h"):
+    for fn in ("smla_kernels.hip", "kv_insert.hip", "index_build.hip", "wo_a.hip", "smla_api.cpp", "smla_internal.h"):
         with open(os.path.join(ROOT, "prefill_token_amd", "csrc", fn), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -479,6 +528,17 @@ def main():
             print(f"# {name}: {r['us_per_call_mean']:.2f} us/call, {r['tokens_per_s']:.4g} tok/s, "
                   f"HBM {100 * r['hbm_frac']:.1f}%", file=sys.stderr, flush=True)
 
+    projs = []
+    if not args.no_insert:
+        from prefill_token_amd import inputs
+
+        for name in inputs.WO_A_WORKLOADS:
+            r = measure_wo_a(name, args.steps, torch, device)
+            projs.append(r)
+            print(f"# {name}: {r['us_per_call_mean']:.2f} us/call, {r['tokens_per_s']:.4g} tok/s, "
+                  f"HBM {100 * r['hbm_frac']:.1f}%, MFMA(fp8) {100 * r['mfma_frac_fp8']:.1f}%", file=sys.stderr,
+                  flush=True)
+
     digest = source_digest()
     traffic = load_traffic(digest)
     achieved = head["compulsory_bytes"] / (head["us_per_call_mean"] * 1e-6) / 1e9
@@ -503,7 +563,7 @@ def main():
         "config": {"workload": head["description"], "name": head["workload"], "s_q": head["s_q"],
                    "num_splits": head["num_splits"], "graph": True},
         "roofline": roofline, "cpu_baseline": cpu, "configs": configs, "kv_insert": inserts,
-        "build_index": builds,
+        "build_index": builds, "wo_a": projs,
         "device": torch.cuda.get_device_name(device), "host": host_info(), "source_digest": digest,
     }
     print(json.dumps(out), flush=True)

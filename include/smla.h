@@ -225,6 +225,43 @@ typedef struct smla_index_params {
 int sparse_mla_build_index(const int32_t* positions, const void* logits, const int32_t* n_valid, int32_t* indices,
                            int32_t* topk_length, const smla_index_params* params);
 
+/*
+ * The consumer of the step's FP8 output: the per-group output projection (wo_a), computed
+ * from the E4M3 codes and UE8M0 block-32 scales of both operands on the scaled FP8 MFMA.
+ * With x(t, h, i) = e4m3(x_fp8[t][h][i]) * 2^(x_scales[t][h][i/32] - 127) and
+ * w(g, o, k) = e4m3(w_fp8[g][o][k]) * 2^(w_scales[g][o][k/32] - 127), hg = heads_per_group:
+ *
+ *   y[t][g][o] = bf16( sum over h < hg, i < 512 of x(t, g*hg + h, i) * w(g, o, 512*h + i) )
+ *
+ * accumulated in f32 and rounded to nearest even.  x and x_scales are the out_fp8 /
+ * out_scales of sparse_mla_fwd as they are.
+ * [vLLM #56344 "Deepseek V41 Attention MegaKernel", Purpose: the kernel's FP8 output is fed
+ *  straight into the wo_a einsum.]  The pages do not give the projection's shape: the
+ * output width d_out and the heads per group are parameters.
+ *
+ *   x_fp8      u8 [s_q][h_q][512]                       (device, read; 16-byte aligned)
+ *   x_scales   u8 [s_q][h_q][16]                        (device, read; 16-byte aligned)
+ *   w_fp8      u8 [h_q/hg][d_out][hg*512]               (device, read; 16-byte aligned)
+ *   w_scales   u8 [h_q/hg][d_out][hg*16]                (device, read; 16-byte aligned)
+ *   y          bf16 [s_q][h_q/hg][d_out]                (device, written; 8-byte aligned)
+ *   params     host pointer, read during the call only
+ *
+ * Scales are expected in [10, 246] as for the pool (products and sums stay in f32 range).
+ * Same conventions as sparse_mla_fwd (asynchronous on params->stream, nothing allocated,
+ * errors by return code with nothing launched).
+ */
+typedef struct smla_wo_a_params {
+  int32_t s_q;             /* tokens (0 = no-op) */
+  int32_t h_q;             /* heads of x: 1..128, a multiple of heads_per_group */
+  int32_t d;               /* dims per head: 512 */
+  int32_t heads_per_group; /* heads contracted together: 1..h_q */
+  int32_t d_out;           /* outputs per group: a positive multiple of 128, at most 4096 */
+  void* stream;            /* hipStream_t */
+} smla_wo_a_params;
+
+int sparse_mla_wo_a(const uint8_t* x_fp8, const uint8_t* x_scales, const uint8_t* w_fp8, const uint8_t* w_scales,
+                    void* y, const smla_wo_a_params* params);
+
 /* Thread-local, NUL-terminated message describing the last failed call on this thread
    ("" if none).  Valid until the next call on the same thread. */
 const char* sparse_mla_last_error(void);

@@ -16,11 +16,11 @@ from typing import Optional
 from . import _lib
 from ._lib import (SMLA_ERR_HIP, SMLA_ERR_NULL, SMLA_ERR_SHAPE, SMLA_ERR_VALUE, SMLA_KV_BF16,
                    SMLA_KV_E4M3_UE8M0, SMLA_OK, LibraryMissing, SmlaIndexParams, SmlaKvInsertParams, SmlaParams,
-                   last_error)
+                   SmlaWoAParams, last_error)
 
 __all__ = [
     "sparse_mla_fwd", "sparse_mla_workspace_size", "sparse_mla_num_splits", "sparse_mla_last_error",
-    "sparse_mla_abi_version", "sparse_mla_kv_insert", "sparse_mla_build_index", "make_params",
+    "sparse_mla_abi_version", "sparse_mla_kv_insert", "sparse_mla_build_index", "sparse_mla_wo_a", "make_params",
     "make_kv_insert_params", "make_index_params", "SmlaParams", "SmlaKvInsertParams", "SmlaIndexParams", "SmlaError",
     "LibraryMissing",
     "SMLA_OK", "SMLA_ERR_NULL", "SMLA_ERR_SHAPE", "SMLA_ERR_VALUE", "SMLA_ERR_HIP",
@@ -178,3 +178,27 @@ def sparse_mla_build_index(positions, logits, n_valid, indices, topk_length, *, 
                                             _ptr(topk_length), ctypes.byref(params))
     if rc != SMLA_OK:
         raise SmlaError(rc, last_error(), "sparse_mla_build_index")
+
+
+def sparse_mla_wo_a(x_fp8, x_scales, w_fp8, w_scales, y, *, heads_per_group: int = 1, stream=None) -> None:
+    """Enqueue the FP8 output consumer (wo_a) on the current (or given) HIP stream.
+
+    x_fp8 uint8 [s_q, h_q, 512] and x_scales uint8 [s_q, h_q, 16] (sparse_mla_fwd's
+    outputs); w_fp8 uint8 [h_q / hg, d_out, hg * 512], w_scales uint8 [h_q / hg, d_out,
+    hg * 16]; y bfloat16 [s_q, h_q / hg, d_out] is written.  Raises SmlaError.
+    """
+    import torch
+
+    for name, t in (("x_fp8", x_fp8), ("x_scales", x_scales), ("w_fp8", w_fp8), ("w_scales", w_scales), ("y", y)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    s_q, h_q, d = x_fp8.shape
+    if stream is None:
+        stream = torch.cuda.current_stream(x_fp8.device).cuda_stream
+    p = SmlaWoAParams()
+    p.s_q, p.h_q, p.d, p.heads_per_group, p.d_out = s_q, h_q, d, heads_per_group, w_fp8.shape[1]
+    p.stream = stream
+    rc = _lib.load().sparse_mla_wo_a(_ptr(x_fp8), _ptr(x_scales), _ptr(w_fp8), _ptr(w_scales), _ptr(y),
+                                     ctypes.byref(p))
+    if rc != SMLA_OK:
+        raise SmlaError(rc, last_error(), "sparse_mla_wo_a")

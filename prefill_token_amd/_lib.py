@@ -70,6 +70,19 @@ class SmlaIndexParams(ctypes.Structure):
     ]
 
 
+class SmlaWoAParams(ctypes.Structure):
+    """Mirror of ``smla_wo_a_params``."""
+
+    _fields_ = [
+        ("s_q", ctypes.c_int32),
+        ("h_q", ctypes.c_int32),
+        ("d", ctypes.c_int32),
+        ("heads_per_group", ctypes.c_int32),
+        ("d_out", ctypes.c_int32),
+        ("stream", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 
 
@@ -100,6 +113,8 @@ def load() -> ctypes.CDLL:
     lib.sparse_mla_kv_insert.argtypes = [P, P, P, P, P, ctypes.POINTER(SmlaKvInsertParams)]
     lib.sparse_mla_build_index.restype = ctypes.c_int
     lib.sparse_mla_build_index.argtypes = [P, P, P, P, P, ctypes.POINTER(SmlaIndexParams)]
+    lib.sparse_mla_wo_a.restype = ctypes.c_int
+    lib.sparse_mla_wo_a.argtypes = [P, P, P, P, P, ctypes.POINTER(SmlaWoAParams)]
     lib.sparse_mla_abi_version.restype = ctypes.c_int
     lib.sparse_mla_abi_version.argtypes = []
     _lib = lib

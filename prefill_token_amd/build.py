@@ -15,7 +15,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libsmla.so")
 
 SOURCES = [os.path.join(CSRC, "smla_kernels.hip"), os.path.join(CSRC, "kv_insert.hip"),
-           os.path.join(CSRC, "index_build.hip"), os.path.join(CSRC, "smla_api.cpp")]
+           os.path.join(CSRC, "index_build.hip"), os.path.join(CSRC, "wo_a.hip"), os.path.join(CSRC, "smla_api.cpp")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -241,4 +241,48 @@ int sparse_mla_build_index(const int32_t* positions, const void* logits, const i
   return SMLA_OK;
 }
 
+int sparse_mla_wo_a(const uint8_t* x_fp8, const uint8_t* x_scales, const uint8_t* w_fp8, const uint8_t* w_scales,
+                    void* y, const smla_wo_a_params* p) {
+  g_last_error.clear();
+  if (!p) return fail(SMLA_ERR_NULL, "params is NULL");
+  if (p->s_q < 0) return fail(SMLA_ERR_VALUE, "s_q must be >= 0 (got %d)", p->s_q);
+  if (p->d != 512) return fail(SMLA_ERR_SHAPE, "d must be 512 (got %d)", p->d);
+  if (p->h_q < 1 || p->h_q > 128) return fail(SMLA_ERR_SHAPE, "h_q must be in [1, 128] (got %d)", p->h_q);
+  if (p->heads_per_group < 1 || p->heads_per_group > p->h_q || p->h_q % p->heads_per_group != 0)
+    return fail(SMLA_ERR_SHAPE, "heads_per_group must divide h_q (got %d, h_q %d)", p->heads_per_group, p->h_q);
+  if (p->d_out < 128 || p->d_out > 4096 || p->d_out % 128 != 0)
+    return fail(SMLA_ERR_SHAPE, "d_out must be a multiple of 128 in [128, 4096] (got %d)", p->d_out);
+  const long long n_groups = p->h_q / p->heads_per_group;
+  if ((long long)p->s_q * p->h_q * 512 >= 0xFFFFFFFFLL)
+    return fail(SMLA_ERR_SHAPE, "s_q * h_q * 512 must stay below 4 GiB");
+  if (n_groups * p->d_out * p->heads_per_group * 512 >= 0xFFFFFFFFLL)
+    return fail(SMLA_ERR_SHAPE, "the weight must stay below 4 GiB");
+  if (p->s_q == 0) return SMLA_OK;
+  if (!x_fp8 || !x_scales || !w_fp8 || !w_scales || !y) return fail(SMLA_ERR_NULL, "a required array pointer is NULL");
+  const struct {
+    const void* ptr;
+    uintptr_t align;
+    const char* name;
+  } al[] = {{x_fp8, 16, "x_fp8"}, {x_scales, 16, "x_scales"}, {w_fp8, 16, "w_fp8"}, {w_scales, 16, "w_scales"},
+            {y, 8, "y"}};
+  for (const auto& x : al)
+    if (reinterpret_cast<uintptr_t>(x.ptr) % x.align != 0)
+      return fail(SMLA_ERR_VALUE, "%s must be %u-byte aligned", x.name, (unsigned)x.align);
+  smla::WoArgs a;
+  a.x = x_fp8;
+  a.x_scales = x_scales;
+  a.w = w_fp8;
+  a.w_scales = w_scales;
+  a.y = static_cast<uint16_t*>(y);
+  a.s_q = p->s_q;
+  a.h_q = p->h_q;
+  a.heads_per_group = p->heads_per_group;
+  a.n_groups = (int)n_groups;
+  a.d_out = p->d_out;
+  a.stream = static_cast<hipStream_t>(p->stream);
+  const hipError_t e = smla::launch_wo_a(a);
+  if (e != hipSuccess) return fail(SMLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return SMLA_OK;
+}
+
 }  // extern "C"

@@ -69,4 +69,17 @@ struct IndexArgs {
 
 hipError_t launch_build_index(const IndexArgs& a);
 
+// The FP8 output consumer (wo_a): y[t][g][o] = sum_{h < hg, i < 512} x(t, g hg + h, i) w(g, o, 512 h + i).
+struct WoArgs {
+  const uint8_t* x;         // E4M3 [s_q][h_q][512]
+  const uint8_t* x_scales;  // UE8M0 [s_q][h_q][16]
+  const uint8_t* w;         // E4M3 [n_groups][d_out][heads_per_group * 512]
+  const uint8_t* w_scales;  // UE8M0 [n_groups][d_out][heads_per_group * 16]
+  uint16_t* y;              // bf16 bits [s_q][n_groups][d_out]
+  int s_q, h_q, heads_per_group, n_groups, d_out;
+  hipStream_t stream;
+};
+
+hipError_t launch_wo_a(const WoArgs& a);
+
 }  // namespace smla

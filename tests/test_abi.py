@@ -264,3 +264,50 @@ def test_index_null_arrays(lib, which):
 def test_index_misaligned_logits_and_empty(lib):
     assert lib.sparse_mla_build_index(FAKE, FAKE + 1, FAKE, FAKE, FAKE, ctypes.byref(good_index())) == smla.SMLA_ERR_VALUE
     assert lib.sparse_mla_build_index(*([None] * 5), ctypes.byref(good_index(s_q=0))) == smla.SMLA_OK
+
+
+def good_wo_a(**kw):
+    p = smla.SmlaWoAParams()
+    base = dict(s_q=4, h_q=64, d=512, heads_per_group=1, d_out=128)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(p, k, v)
+    return p
+
+
+def test_wo_a_struct_layout():
+    P = smla.SmlaWoAParams
+    assert P.d_out.offset == 16 and P.stream.offset == 24 and ctypes.sizeof(P) == 32
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(s_q=-1), smla.SMLA_ERR_VALUE),
+    (dict(d=256), smla.SMLA_ERR_SHAPE),
+    (dict(h_q=0), smla.SMLA_ERR_SHAPE),
+    (dict(h_q=129), smla.SMLA_ERR_SHAPE),
+    (dict(heads_per_group=3), smla.SMLA_ERR_SHAPE),
+    (dict(heads_per_group=0), smla.SMLA_ERR_SHAPE),
+    (dict(heads_per_group=128), smla.SMLA_ERR_SHAPE),
+    (dict(d_out=64), smla.SMLA_ERR_SHAPE),
+    (dict(d_out=200), smla.SMLA_ERR_SHAPE),
+    (dict(d_out=4224), smla.SMLA_ERR_SHAPE),
+    (dict(s_q=140000, h_q=64), smla.SMLA_ERR_SHAPE),
+])
+def test_wo_a_rejected_parameters(lib, kw, code):
+    p = good_wo_a(**kw)
+    assert lib.sparse_mla_wo_a(FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(p)) == code
+    assert smla.sparse_mla_last_error() != ""
+
+
+@pytest.mark.parametrize("which", [0, 1, 2, 3, 4])
+def test_wo_a_null_and_misaligned(lib, which):
+    ptrs = [FAKE] * 5
+    ptrs[which] = None
+    assert lib.sparse_mla_wo_a(*ptrs, ctypes.byref(good_wo_a())) == smla.SMLA_ERR_NULL
+    ptrs[which] = FAKE + 4
+    assert lib.sparse_mla_wo_a(*ptrs, ctypes.byref(good_wo_a())) == smla.SMLA_ERR_VALUE
+
+
+def test_wo_a_null_params_and_empty(lib):
+    assert lib.sparse_mla_wo_a(*([FAKE] * 5), None) == smla.SMLA_ERR_NULL
+    assert lib.sparse_mla_wo_a(*([None] * 5), ctypes.byref(good_wo_a(s_q=0))) == smla.SMLA_OK
