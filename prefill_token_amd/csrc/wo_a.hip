@@ -17,7 +17,9 @@
 // block 2ks + hf (the MFMA's K block hf is bytes 0..15 of both lane halves' first
 // registers, i.e. row block 2ks, and block 1 the second registers, row block 2ks + 1).
 // The rows are read straight from HBM into registers through range-checked buffer loads
-// (tokens past s_q read as zeros).  Accumulator register i of a lane holds output
+// (tokens past s_q read as zeros): all of the token rows' fragments at once, then each
+// 32-output weight block's fragments at once, so that a wave waits for a few rounds of
+// loads instead of one per MFMA.  Accumulator register i of a lane holds output
 // 8 (i >> 2) + 4 hf + (i & 3) of the tile for token n, so a lane stores four runs of 4
 // consecutive bf16 outputs.
 #include <hip/hip_runtime.h>
@@ -70,27 +72,29 @@ __global__ __launch_bounds__(64) void wo_a_kernel(WoArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[b][i] = 0.f;
   for (int hh = 0; hh < hg; ++hh) {
+    // all of the token rows' fragments first (one round of loads), then per 32-output
+    // block all of its weight fragments, then that block's 8 MFMAs
     const uint32_t xrow = ((uint32_t)t * H + (uint32_t)(g * hg + hh)) * WO_D;
-    // the 16 block scales of the x row, and of the weight rows' head-hh part
     const auto xsc = __builtin_amdgcn_raw_buffer_load_b128(xs, xrow / 32, 0, 0);
-    uint32_t wsc[WO_NB][4];
+    i32x8 bx[WO_D / 64];
+#pragma unroll
+    for (int ks = 0; ks < WO_D / 64; ++ks) bx[ks] = wo_frag(xr, xrow, ks, hf);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads together, ahead of their uses
 #pragma unroll
     for (int b = 0; b < WO_NB; ++b) {
       const uint32_t wrow = (uint32_t)(g * dout + o0 + 32 * b + n) * krow + (uint32_t)hh * WO_D;
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(ws, wrow / 32, 0, 0);
-      wsc[b][0] = v[0]; wsc[b][1] = v[1]; wsc[b][2] = v[2]; wsc[b][3] = v[3];
-    }
+      const auto wsc = __builtin_amdgcn_raw_buffer_load_b128(ws, wrow / 32, 0, 0);
+      i32x8 aw[WO_D / 64];
 #pragma unroll
-    for (int ks = 0; ks < WO_D / 64; ++ks) {
-      const i32x8 bx = wo_frag(xr, xrow, ks, hf);
-      // scale byte of block 2ks + hf: word ks / 2, byte 2 (ks & 1) + hf
-      const int sx = (int)((xsc[ks >> 1] >> (8 * (2 * (ks & 1) + hf))) & 0xFFu);
+      for (int ks = 0; ks < WO_D / 64; ++ks) aw[ks] = wo_frag(wr, wrow, ks, hf);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int b = 0; b < WO_NB; ++b) {
-        const uint32_t wrow = (uint32_t)(g * dout + o0 + 32 * b + n) * krow + (uint32_t)hh * WO_D;
-        const i32x8 aw = wo_frag(wr, wrow, ks, hf);
-        const int sw = (int)((wsc[b][ks >> 1] >> (8 * (2 * (ks & 1) + hf))) & 0xFFu);
-        acc[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aw, bx, acc[b], 0, 0, 0, sw, 0, sx);
+      for (int ks = 0; ks < WO_D / 64; ++ks) {
+        // scale byte of block 2ks + hf: word ks / 2, byte 2 (ks & 1) + hf
+        const int sh = 8 * (2 * (ks & 1) + hf);
+        const int sx = (int)((xsc[ks >> 1] >> sh) & 0xFFu);
+        const int sw = (int)((wsc[ks >> 1] >> sh) & 0xFFu);
+        acc[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aw[ks], bx[ks], acc[b], 0, 0, 0, sw, 0, sx);
       }
     }
   }

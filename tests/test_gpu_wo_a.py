@@ -39,17 +39,23 @@ def bf16_round(a):
     return torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).float().numpy().astype(np.float64)
 
 
-def check(c, label=""):
+def check(c, label="", n_sample=None):
     g = run_gpu(c)
+    assert np.isfinite(g).all(), "outputs left unwritten"
     hg = c["heads_per_group"]
-    ref = oracle.wo_a(c["x"], c["x_scales"], c["w"], c["w_scales"], hg)
+    x, xs = c["x"], c["x_scales"]
+    if n_sample is not None and c["n"] > n_sample:
+        # full-size call; the oracle on sampled tokens (first and last of the ragged tiles too)
+        rng = np.random.default_rng(0)
+        tok = set(rng.choice(c["n"], size=n_sample, replace=False).tolist()) | {0, 31, 32, c["n"] - 1}
+        tok = np.array(sorted(tok))
+        g, x, xs = g[tok], x[tok], xs[tok]
+    ref = oracle.wo_a(x, xs, c["w"], c["w_scales"], hg)
     # sum |x_k w_k|: the same projection of the magnitudes (sign bits cleared)
-    mag = oracle.wo_a((c["x"] & 0x7F).astype(np.uint8), c["x_scales"], (c["w"] & 0x7F).astype(np.uint8),
-                      c["w_scales"], hg)
+    mag = oracle.wo_a((x & 0x7F).astype(np.uint8), xs, (c["w"] & 0x7F).astype(np.uint8), c["w_scales"], hg)
     K = 512 * hg
     tol = 2.0 ** -8 * np.abs(ref) + 2 * K * 2.0 ** -24 * mag
     err = np.abs(g - ref)
-    assert np.isfinite(g).all(), "outputs left unwritten"
     assert (err <= tol).all(), f"{int((err > tol).sum())} outputs beyond tolerance, worst {(err / np.maximum(tol, 1e-300)).max():.3g}x"
     same = float((g == bf16_round(ref)).mean())
     print(c["name"], label, "max err / tol", float((err / np.maximum(tol, 1e-300)).max()), "equal to rounded oracle", same,
@@ -59,7 +65,7 @@ def check(c, label=""):
 
 @pytest.mark.parametrize("name", list(inputs.WO_A_WORKLOADS))
 def test_wo_a_workloads(name):
-    check(inputs.make_wo_a(name))
+    check(inputs.make_wo_a(name), n_sample=96)
 
 
 @pytest.mark.parametrize("hg", [2, 4, 64])
