@@ -44,64 +44,106 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t wo_rsrc(const void* base, uint
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-__device__ __forceinline__ i32x8 wo_frag(__amdgpu_buffer_rsrc_t rs, uint32_t row_off, int ks, int hf) {
-  const auto lo = __builtin_amdgcn_raw_buffer_load_b128(rs, row_off + 64u * ks + 16u * hf, 0, 0);
-  const auto hi = __builtin_amdgcn_raw_buffer_load_b128(rs, row_off + 64u * ks + 32u + 16u * hf, 0, 0);
-  return (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-}
-
 __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
   const f32x2v v = {a, b};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v));
 }
 
-__global__ __launch_bounds__(64) void wo_a_kernel(WoArgs a) {
-  const int lane = threadIdx.x, n = lane & 31, hf = lane >> 5;
-  const int t0 = blockIdx.x * 32, g = blockIdx.y, o0 = blockIdx.z * WO_OT;
+// LDS tiles of one phase (256 bytes of K = 4 k-steps): rows of 256 bytes, 16-byte chunk c
+// of row r stored at chunk c ^ (r & 15), so that the 32 rows a fragment read touches spread
+// over the banks.
+constexpr int WO_TT = 64;            // tokens per workgroup
+constexpr int WO_PH = 256;           // K bytes per phase
+constexpr int WO_XT = WO_TT * WO_PH; // 16 KB
+constexpr int WO_WT = WO_OT * WO_PH; // 32 KB
+
+__device__ __forceinline__ int wo_sw(int r, int c) { return 16 * (c ^ (r & 15)); }
+
+__global__ __launch_bounds__(256) void wo_a_kernel(WoArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char xt[WO_XT];
+  __shared__ __attribute__((aligned(16))) unsigned char wt[WO_WT];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 31, hf = lane >> 5;
+  const int th = w & 1, oh = w >> 1;  // this wave: tokens 32 th .., outputs 64 oh ..
+  const int t0 = blockIdx.x * WO_TT, g = blockIdx.y, o0 = blockIdx.z * WO_OT;
   const int H = a.h_q, hg = a.heads_per_group, dout = a.d_out;
-  const int t = t0 + n;
   const uint32_t krow = (uint32_t)hg * WO_D;  // weight row length in bytes
-  // x: rows (t, head) of 512 bytes; tokens >= s_q fall outside the resource and read zeros
+  // tokens >= s_q fall outside the resources and read zeros
   const __amdgpu_buffer_rsrc_t xr = wo_rsrc(a.x, (uint32_t)a.s_q * H * WO_D);
   const __amdgpu_buffer_rsrc_t xs = wo_rsrc(a.x_scales, (uint32_t)a.s_q * H * WO_NSB);
   const __amdgpu_buffer_rsrc_t wr = wo_rsrc(a.w, (uint32_t)a.n_groups * dout * krow);
   const __amdgpu_buffer_rsrc_t ws = wo_rsrc(a.w_scales, (uint32_t)a.n_groups * dout * (krow / 32));
-  f32x16 acc[WO_NB];
+  f32x16 acc[2];
 #pragma unroll
-  for (int b = 0; b < WO_NB; ++b)
+  for (int b = 0; b < 2; ++b)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[b][i] = 0.f;
+  // tile loads: thread tid moves chunk c = tid & 15 of rows (tid >> 4) + 16 k
+  const int lc = tid & 15, lr = tid >> 4;
   for (int hh = 0; hh < hg; ++hh) {
-    // all of the token rows' fragments first (one round of loads), then per 32-output
-    // block all of its weight fragments, then that block's 8 MFMAs
-    const uint32_t xrow = ((uint32_t)t * H + (uint32_t)(g * hg + hh)) * WO_D;
-    const auto xsc = __builtin_amdgcn_raw_buffer_load_b128(xs, xrow / 32, 0, 0);
-    i32x8 bx[WO_D / 64];
+    const int head = g * hg + hh;
+    // this lane's block scales: its token row and its two weight rows (whole head)
+    const int t = t0 + 32 * th + n;
+    const auto xsc = __builtin_amdgcn_raw_buffer_load_b128(xs, ((uint32_t)t * H + head) * WO_NSB, 0, 0);
+    uint32_t wsc[2][4];
 #pragma unroll
-    for (int ks = 0; ks < WO_D / 64; ++ks) bx[ks] = wo_frag(xr, xrow, ks, hf);
-    __builtin_amdgcn_sched_barrier(0);  // keep the loads together, ahead of their uses
+    for (int b = 0; b < 2; ++b) {
+      const uint32_t o = (uint32_t)(g * dout + o0 + 64 * oh + 32 * b + n);
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(ws, o * (krow / 32) + (uint32_t)hh * WO_NSB, 0, 0);
+      wsc[b][0] = v[0]; wsc[b][1] = v[1]; wsc[b][2] = v[2]; wsc[b][3] = v[3];
+    }
 #pragma unroll
-    for (int b = 0; b < WO_NB; ++b) {
-      const uint32_t wrow = (uint32_t)(g * dout + o0 + 32 * b + n) * krow + (uint32_t)hh * WO_D;
-      const auto wsc = __builtin_amdgcn_raw_buffer_load_b128(ws, wrow / 32, 0, 0);
-      i32x8 aw[WO_D / 64];
+    for (int ph = 0; ph < WO_D / WO_PH; ++ph) {
+      // row-contiguous loads of the phase's tiles (16 threads per 256-byte row piece)
+      uint4 xv[WO_TT / 16], wv[WO_OT / 16];
 #pragma unroll
-      for (int ks = 0; ks < WO_D / 64; ++ks) aw[ks] = wo_frag(wr, wrow, ks, hf);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int k = 0; k < WO_TT / 16; ++k) {
+        const int r = lr + 16 * k;
+        const uint32_t off = ((uint32_t)(t0 + r) * H + head) * WO_D + WO_PH * ph + 16 * lc;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0);
+        xv[k] = make_uint4(v[0], v[1], v[2], v[3]);
+      }
 #pragma unroll
-      for (int ks = 0; ks < WO_D / 64; ++ks) {
+      for (int k = 0; k < WO_OT / 16; ++k) {
+        const int r = lr + 16 * k;
+        const uint32_t off = (uint32_t)(g * dout + o0 + r) * krow + (uint32_t)hh * WO_D + WO_PH * ph + 16 * lc;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 0);
+        wv[k] = make_uint4(v[0], v[1], v[2], v[3]);
+      }
+      __syncthreads();  // the previous phase's fragment reads are done
+#pragma unroll
+      for (int k = 0; k < WO_TT / 16; ++k)
+        *reinterpret_cast<uint4*>(xt + (lr + 16 * k) * WO_PH + wo_sw(lr + 16 * k, lc)) = xv[k];
+#pragma unroll
+      for (int k = 0; k < WO_OT / 16; ++k)
+        *reinterpret_cast<uint4*>(wt + (lr + 16 * k) * WO_PH + wo_sw(lr + 16 * k, lc)) = wv[k];
+      __syncthreads();  // the tiles are complete
+#pragma unroll
+      for (int kq = 0; kq < WO_PH / 64; ++kq) {
+        const int ks = 4 * ph + kq;  // k-step within the head
+        const int xrw = 32 * th + n;
+        const uint4 xlo = *reinterpret_cast<const uint4*>(xt + xrw * WO_PH + wo_sw(xrw, 4 * kq + hf));
+        const uint4 xhi = *reinterpret_cast<const uint4*>(xt + xrw * WO_PH + wo_sw(xrw, 4 * kq + 2 + hf));
+        const i32x8 bx = {(int)xlo.x, (int)xlo.y, (int)xlo.z, (int)xlo.w, (int)xhi.x, (int)xhi.y, (int)xhi.z, (int)xhi.w};
         // scale byte of block 2ks + hf: word ks / 2, byte 2 (ks & 1) + hf
         const int sh = 8 * (2 * (ks & 1) + hf);
         const int sx = (int)((xsc[ks >> 1] >> sh) & 0xFFu);
-        const int sw = (int)((wsc[ks >> 1] >> sh) & 0xFFu);
-        acc[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aw[ks], bx[ks], acc[b], 0, 0, 0, sw, 0, sx);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const int wrw = 64 * oh + 32 * b + n;
+          const uint4 wlo = *reinterpret_cast<const uint4*>(wt + wrw * WO_PH + wo_sw(wrw, 4 * kq + hf));
+          const uint4 whi = *reinterpret_cast<const uint4*>(wt + wrw * WO_PH + wo_sw(wrw, 4 * kq + 2 + hf));
+          const i32x8 aw = {(int)wlo.x, (int)wlo.y, (int)wlo.z, (int)wlo.w, (int)whi.x, (int)whi.y, (int)whi.z, (int)whi.w};
+          const int sw = (int)((wsc[b][ks >> 1] >> sh) & 0xFFu);
+          acc[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aw, bx, acc[b], 0, 0, 0, sw, 0, sx);
+        }
       }
     }
   }
+  const int t = t0 + 32 * th + n;
   if (t >= a.s_q) return;
-  uint16_t* yrow = a.y + ((size_t)t * a.n_groups + g) * dout + o0;
+  uint16_t* yrow = a.y + ((size_t)t * a.n_groups + g) * dout + o0 + 64 * oh;
 #pragma unroll
-  for (int b = 0; b < WO_NB; ++b)
+  for (int b = 0; b < 2; ++b)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int o = 32 * b + 8 * q + 4 * hf;
@@ -113,8 +155,8 @@ __global__ __launch_bounds__(64) void wo_a_kernel(WoArgs a) {
 }  // namespace
 
 hipError_t launch_wo_a(const WoArgs& a) {
-  const dim3 grid((unsigned)((a.s_q + 31) / 32), (unsigned)a.n_groups, (unsigned)(a.d_out / WO_OT));
-  hipLaunchKernelGGL(wo_a_kernel, grid, dim3(64), 0, a.stream, a);
+  const dim3 grid((unsigned)((a.s_q + WO_TT - 1) / WO_TT), (unsigned)a.n_groups, (unsigned)(a.d_out / WO_OT));
+  hipLaunchKernelGGL(wo_a_kernel, grid, dim3(256), 0, a.stream, a);
   return hipGetLastError();
 }
 
