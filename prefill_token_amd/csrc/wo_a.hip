@@ -10,18 +10,20 @@
 // [vLLM #56344 "Deepseek V41 Attention MegaKernel", Purpose: the kernel's FP8 output is fed
 //  straight into the wo_a einsum; the E4M3 + UE8M0 block-32 output format of the step.]
 //
-// One wave64 per (32-token tile, group, 128-output tile).  Lane (n = lane & 31, half
-// hf = lane >> 5).  Per 64-wide k-step, v_mfma_scale_f32_32x32x64_f8f6f4 with A = 32
-// weight rows (M = outputs) and B = 32 token rows (N = tokens): a lane holds bytes
-// [64ks + 16hf, +16) and [64ks + 32 + 16hf, +16) of its row, and its scale byte is that of
-// block 2ks + hf (the MFMA's K block hf is bytes 0..15 of both lane halves' first
-// registers, i.e. row block 2ks, and block 1 the second registers, row block 2ks + 1).
-// The rows are read straight from HBM into registers through range-checked buffer loads
-// (tokens past s_q read as zeros): all of the token rows' fragments at once, then each
-// 32-output weight block's fragments at once, so that a wave waits for a few rounds of
-// loads instead of one per MFMA.  Accumulator register i of a lane holds output
-// 8 (i >> 2) + 4 hf + (i & 3) of the tile for token n, so a lane stores four runs of 4
-// consecutive bf16 outputs.
+// One 256-thread workgroup per (64-token tile, group, 128-output tile); wave w computes
+// tokens 32 (w & 1) .. + 31 x outputs 64 (w >> 1) .. + 63.  Per head of the group, the K
+// = 512 bytes of the rows go in two phases of 256: all threads load the phase's token and
+// weight rows with row-contiguous 16-byte loads (16 threads per row piece; range-checked
+// buffer loads, tokens past s_q read zeros) into LDS tiles whose 16-byte chunk c of row r
+// sits at chunk c ^ (r & 15), then each wave reads its MFMA fragments from LDS.  Per
+// 64-wide k-step, v_mfma_scale_f32_32x32x64_f8f6f4 with A = 32 weight rows (M = outputs)
+// and B = 32 token rows (N = tokens): a lane (row n = lane & 31, half hf = lane >> 5)
+// holds bytes [64ks + 16hf, +16) and [64ks + 32 + 16hf, +16) of its row, and its scale
+// byte is that of block 2ks + hf (the MFMA's K block hf is bytes 0..15 of both lane
+// halves' first registers, i.e. row block 2ks, and block 1 the second registers, row
+// block 2ks + 1); the scales come straight from HBM into registers.  Accumulator register
+// i of a lane holds output 8 (i >> 2) + 4 hf + (i & 3) of its 32-output block for token
+// n, so a lane stores four runs of 4 consecutive bf16 outputs per block.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
