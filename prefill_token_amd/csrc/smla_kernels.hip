@@ -2175,7 +2175,6 @@ __global__ __launch_bounds__(CTHREADS) void smla_combine_lm4(KArgs a) {
   const int s0 = ((((v * 2 + mb) * 4 + nb) * 2 + gp) * 64) + lrow;
   const int gb = 4 * v + nb;
   const bool rot = a.rope_dim > 0 && v == 3 && nbp == 1;
-  if (rot) rope_table(a.positions[t], a, cs, sn);
   float M = -INFINITY, den = 0.f;
   float o[16];
 #pragma unroll
@@ -2195,6 +2194,8 @@ __global__ __launch_bounds__(CTHREADS) void smla_combine_lm4(KArgs a) {
         mv[k] = sp[WSP_M + h];
         lv[k] = sp[WSP_L + h];
       }
+    // the cos / sin table while the first chunk's loads are in flight
+    if (c0 == 0 && rot) rope_table(a.positions[t], a, cs, sn);
 #pragma unroll
     for (int k = 0; k < SCH; ++k)
       if (c0 + k < ns && mv[k] != -INFINITY) {
@@ -2282,7 +2283,6 @@ __global__ __launch_bounds__(LMT) void smla_combine_lm1(KArgs a) {
   const int slot = (((((v * 2 + mb) * 4 + nb) * 2 + (g >> 1)) * 64) + lane) * 2 + (g & 1);  // 8-byte index
   const int gb = 4 * v + nb;
   const bool rot = a.rope_dim > 0 && v == 3 && nbp == 1;
-  if (rot) rope_table(a.positions[t], a, cs, sn);
   float M = -INFINITY, den = 0.f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int c0 = 0; c0 < ns; c0 += SCH) {
@@ -2297,6 +2297,8 @@ __global__ __launch_bounds__(LMT) void smla_combine_lm1(KArgs a) {
         mv[k] = sp[WSP_M + h];
         lv[k] = sp[WSP_L + h];
       }
+    // the cos / sin table while the first chunk's loads are in flight
+    if (c0 == 0 && rot) rope_table(a.positions[t], a, cs, sn);
 #pragma unroll
     for (int k = 0; k < SCH; ++k)
       if (c0 + k < ns && mv[k] != -INFINITY) {
