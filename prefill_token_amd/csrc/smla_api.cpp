@@ -59,15 +59,23 @@ int check_params(const smla_params* p) {
 
 int tiles_of(const smla_params* p) { return (p->topk + smla::kTileRows - 1) / smla::kTileRows; }
 
-// Splits per token: as many as keep the work items (token, split) within one round of the
-// device's compute units (one persistent workgroup each), never more splits than tiles.
-// Splitting past one round only adds a second round of items and the combine pass.
+// Splits per token.  Tiles per split first: the fewest that keep the work items (token,
+// split) within one round of the device's compute units (one persistent workgroup each),
+// and at least 2 once the call has more than 64 tiles in all (then more, shorter splits
+// cost more in partials and their combine than they save); then as many splits as those
+// tiles need, so that no split is empty.  Measured on decode rows of 10 tiles: s_q = 1 and
+// 4 run best at 10 splits, s_q = 16 and 32 at 5 (19.9 / 22.9 us against 21.6 / 26.0 us at
+// 10 / 8), s_q = 64 at 4, s_q = 96 at 2; from 129 tokens on, unsplit.
 int choose_splits(const smla_params* p) {
   const int tiles = tiles_of(p) > 0 ? tiles_of(p) : 1;
   int ns = p->num_splits;
   if (ns == 0) {
-    const int cus = smla::device_cus();
-    ns = p->s_q > 0 ? cus / p->s_q : 1;
+    const long long cus = smla::device_cus();
+    const long long s_q = p->s_q > 0 ? p->s_q : 1;
+    int tps = s_q * tiles > 64 ? 2 : 1;
+    while (tps < tiles && s_q * ((tiles + tps - 1) / tps) > cus) ++tps;
+    ns = (tiles + tps - 1) / tps;
+    if (s_q * ns > cus) ns = 1;
   }
   if (ns > tiles) ns = tiles;
   if (ns < 1) ns = 1;

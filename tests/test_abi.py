@@ -142,6 +142,12 @@ def test_workspace_required_when_split(lib):
 
 def test_split_choice():
     assert smla.sparse_mla_num_splits(good(s_q=1)) == 10   # one split per 64-entry tile
+    # (these assume 256 compute units: the count without a GPU, and MI355X's)
+    assert smla.sparse_mla_num_splits(good(s_q=4)) == 10
+    assert smla.sparse_mla_num_splits(good(s_q=32)) == 5   # two tiles per split past 64 tiles of work
+    assert smla.sparse_mla_num_splits(good(s_q=64)) == 4   # three tiles: 256 items
+    assert smla.sparse_mla_num_splits(good(s_q=96)) == 2
+    assert smla.sparse_mla_num_splits(good(s_q=129)) == 1  # no split count keeps one round
     assert smla.sparse_mla_num_splits(good(s_q=2123)) == 1
     assert smla.sparse_mla_num_splits(good(s_q=1, num_splits=3)) == 3
     assert smla.sparse_mla_num_splits(good(s_q=1, num_splits=64)) == 10  # capped at the tile count
