@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert smla.sparse_mla_abi_version() == 1
+    assert smla.sparse_mla_abi_version() == 2  # 2: sparse_mla_wo_a; the item order in the workspace
 
 
 def test_struct_layout_matches_header():
