@@ -90,6 +90,20 @@ def test_index_shapes():
         check(c)
 
 
+def test_index_candidate_count_not_a_multiple_of_8():
+    # rows of 2052 candidates: even rows start 16-byte aligned and end in a partial group
+    # of 8 columns, odd rows are not aligned
+    rng = np.random.default_rng(97)
+    n_cand = 2052
+    c = dict(name="index_2052", n=4, n_cand=n_cand, positions=np.array([9, 300, 40000, 2], dtype=np.int32),
+             logits=inputs.bf16_bits((np.round(rng.standard_normal((4, n_cand)) * 8) / 8).astype(np.float32)),
+             n_valid=np.array([n_cand, 2050, 2049, 300], dtype=np.int32), topk=640, window=128,
+             self_in_window=False, n_swa=8192, cmp_base=8192, k_cmp=512)
+    # the largest logits in the last columns, so that they must be found
+    c["logits"][:, -4:] = inputs.bf16_bits(np.full((4, 4), 9.0, dtype=np.float32))
+    check(c)
+
+
 def test_index_largest_candidate_row():
     rng = np.random.default_rng(64)
     n_cand = 65536
