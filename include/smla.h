@@ -78,9 +78,11 @@ typedef struct smla_params {
   float sm_scale;   /* softmax scale, finite and > 0 (typically 1/sqrt(d)) */
   float rms_eps;    /* RMSNorm epsilon, finite and > 0 */
   float rope_theta; /* RoPE base, finite and > 0 */
-  int32_t num_splits; /* 0 = automatic (as many splits as keep s_q x splits within one
-                         round of the device's compute units, at most one per 64 index
-                         entries); else split each token's entries over this many
+  int32_t num_splits; /* 0 = automatic: tiles (64 index entries) per split are the
+                         fewest that keep s_q x splits within one round of the device's
+                         compute units, and at least 2 once s_q x tiles exceeds 64; then
+                         as many splits as those tiles need (1 when no count keeps one
+                         round).  Else split each token's entries over this many
                          workgroups (1..64) and combine */
   float* out_f32;   /* optional f32 [s_q][h_q][d]: o after inverse RoPE, before the FP8
                        cast (NULL = not written) */
