@@ -6,8 +6,9 @@ exact in f32 and the K = 512 * hg products are summed in f32 (error at most
 K * 2^-24 * sum |x_k w_k|), then rounded once to bf16 (8 significant bits: at most 2^-8
 of the value).  The test allows 2^-8 |y| + 2 K 2^-24 sum |x_k w_k|; a wrong scale,
 element or operand order is off by far more.  Also counted: outputs equal to the oracle rounded to bf16.
-Cases: the three workloads, 2 / 4 / 64 heads per group, 256 outputs, token counts that
-leave ragged 32-token tiles, all-zero input, and the step's own output fed in.
+Cases: the three workloads, 2 / 4 / 64 heads per group, 1 / 16 / 128 heads, 256 outputs,
+token counts that leave ragged token tiles, all-zero input, and the step's own output
+fed in.
 """
 import numpy as np
 import pytest
@@ -76,6 +77,18 @@ def test_wo_a_heads_per_group(hg):
 @pytest.mark.parametrize("n", [1, 31, 32, 33, 100])
 def test_wo_a_ragged_tokens_and_wider_output(n):
     check(inputs.make_wo_a("wo_a_decode_sq64", seed=72, n=n, d_out=256), f"n={n}")
+
+
+@pytest.mark.parametrize("h,hg", [(1, 1), (16, 2), (128, 8)])
+def test_wo_a_head_counts(h, hg):
+    rng = np.random.default_rng(76 + h)
+    n, d_out = 37, 128
+    G = h // hg
+    x, xs = inputs.mx_pool(rng.standard_normal((n * h, 512)).astype(np.float32) * np.float32(0.05))
+    w, ws = inputs.mx_pool(rng.standard_normal((G * d_out, hg * 512)).astype(np.float32) / np.float32(40.0))
+    c = dict(name=f"wo_a_h{h}", n=n, h=h, d=512, heads_per_group=hg, d_out=d_out, x=x.reshape(n, h, 512),
+             x_scales=xs.reshape(n, h, 16), w=w.reshape(G, d_out, hg * 512), w_scales=ws.reshape(G, d_out, hg * 16))
+    check(c, f"h={h} hg={hg}")
 
 
 def test_wo_a_zero_input_gives_zero():
