@@ -1483,7 +1483,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
       __syncthreads();  // B_B: q tile read (the P.V waves overwrite it), first tile visible
 
       const int n = I.n;
-      float m_run = -INFINITY, l_run = 0.f, l_pend = 0.f;
+      // The running max starts as a reference of 8 (scores are in log2 units; P stays at
+      // most 1 below it and at most 2^8 below the raise threshold m + 8): exp2(s - m) is
+      // exact for any reference both row halves share, so a tile needs the merge of the
+      // halves' maxima (the slow path) only when a block max exceeds m + 8, or, while no
+      // valid row has been seen yet (mref), lies below m - 64 (the reference is then
+      // replaced by the merged max; nothing has been accumulated, so the rescale is 0).
+      // mref is cleared from the merged block maxima, which both halves read, so the
+      // halves always agree on it.
+      float m_run = 8.f, l_run = 0.f, l_pend = 0.f;
+      bool mref = true;
       f32x16 s;  // scores of the last tile, kept for a rewrite of its P
       // flag check for tile it - 1 (it >= 1): the slow path merges the block maxima,
       // raises the running max and rewrites P
@@ -1497,11 +1506,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
             const float* mx = maxx + 2 * HP * ((it - 1) & 1);
             const float mt = fmaxf(mx[head], mx[HP + head]);
             float mnew = m_run;
-            if (mt > -INFINITY && (m_run == -INFINITY || mt > m_run + 8.0f)) mnew = mt;
-            const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - mnew);
-            const bool raised = __any(m_run != -INFINITY && mnew != m_run);
+            if (mt > -INFINITY && (mref || mt > m_run + 8.0f)) mnew = mt;
+            const float alpha = mref ? 0.f : __builtin_amdgcn_exp2f(m_run - mnew);
+            if (mt > -INFINITY) mref = false;
+            const bool raised = __any(mnew != m_run);
             m_run = mnew;
-            const float msafe = (mnew == -INFINITY) ? 0.f : mnew;
+            const float msafe = mnew;
             float p[16];
             float lp = 0.f;
 #pragma unroll
@@ -1521,6 +1531,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
             __syncthreads();  // B': P and alpha rewritten
           } else {
             l_run += l_pend;
+            if (mref) {
+              const float* mx = maxx + 2 * HP * ((it - 1) & 1);
+              if (fmaxf(mx[head], mx[HP + head]) > -INFINITY) mref = false;
+            }
           }
         }
       };
@@ -1590,7 +1604,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
           lm = fmaxf(lm, __shfl_xor(lm, 32));
           // P against the running max; exact unless the flag below sends the tile to the
           // slow path, which rewrites it
-          const float msafe = (m_run == -INFINITY) ? 0.f : m_run;
+          const float msafe = m_run;
           float p[16];
           float lp = 0.f;
 #pragma unroll
@@ -1606,7 +1620,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
             *reinterpret_cast<uint2*>(prow + 16 * ((4 * qc + g) ^ sw) + 8 * lhalf) =
                 make_uint2(pack_bf16(p[4 * g], p[4 * g + 1]), pack_bf16(p[4 * g + 2], p[4 * g + 3]));
           if (lhalf == 0) maxx[2 * HP * (it & 1) + qc * HP + head] = lm;
-          const bool over = __any(lm > m_run + 8.0f);
+          const bool over = __any(lm > m_run + 8.0f || (mref && lm > -INFINITY && lm < m_run - 64.0f));
           if (lane == 0) flag_l[4 * (it & 1) + w] = over ? 1 : 0;
         }
         // next tile's DMA from this wave landed (vmcnt(0); vmcnt(2) behind the q touches)
@@ -1912,8 +1926,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
         float* pm = part + WSP_M;
         float* pl = part + WSP_L;
         if (v == 0 && lane < hq) {
-          pm[lane] = mfin[lane];
-          pl[lane] = lsum[lane] + lsum[HP + lane];
+          // a split that read nothing (l = 0) reports m = -inf: the combine skips it and
+          // never reads its accumulator
+          const float lt = lsum[lane] + lsum[HP + lane];
+          pm[lane] = lt > 0.f ? mfin[lane] : -INFINITY;
+          pl[lane] = lt;
         }
         if (n > 0) {
           uint4* pv4 = reinterpret_cast<uint4*>(part) + 2 * 4 * 2 * 64 * v + lane;

@@ -106,6 +106,18 @@ def test_ragged_lengths_longest_first():
     check(inp, num_splits=1)
 
 
+def test_equal_rows_with_huge_scores():
+    # Every pool row is one row with block scale 200: a head's scores are all equal and of
+    # size ~1e26, positive for some heads (the running max is raised) and negative for
+    # others (the initial reference is lowered to them); every output is that row after
+    # inverse RoPE.
+    inp = inputs.make("decode_sq64", seed=81, s_q=6)
+    inp["kv_pool"][:] = inp["kv_pool"][5].copy()
+    inp["kv_scales"][:] = 200
+    for ns in (0, 1, 3):
+        check(inp, num_splits=ns)
+
+
 def test_empty_and_sentinel_rows():
     inp = _decode_case(12, s_q=4)
     inp["indices"][0, :] = -1
