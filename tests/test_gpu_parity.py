@@ -45,9 +45,16 @@ def test_decode_sq64():
     check(inputs.make("decode_sq64"))
 
 
-@pytest.mark.parametrize("ns", [1, 2, 3, 10])
+@pytest.mark.parametrize("ns", [1, 2, 3, 5, 7, 10])
 def test_decode_forced_splits(ns):
     check(inputs.make("decode_sq64", seed=101, s_q=8), num_splits=ns)
+
+
+@pytest.mark.parametrize("s_q,ns", [(40, 8), (30, 10)])
+def test_split_combine_kernels(s_q, ns):
+    # more (token, split) items than compute units, so the persistent kernel takes split
+    # items from its queue; then the combine for ns <= 8 and the one for ns > 8
+    check(inputs.make("decode_sq64", seed=102, s_q=s_q), num_splits=ns)
 
 
 def _sampled(name, n_sample, seed=0, **make_kw):
