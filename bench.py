@@ -2,20 +2,29 @@
 """Benchmark of the fused sparse-MLA step (sparse_mla_fwd) on one MI355X.
 
 A step is one sparse_mla_fwd call over one batch of seeded synthetic inputs (inputs
-resident in HBM).  The timed steps are replays of a HIP graph holding 10 back-to-back
-calls, so a step's time is the GPU's and not the host's graph-launch latency (which is
-reported separately as us_per_call_single_graph_median).  The headline workload is the s_q = 1 decode
-(h_q = 64, d = 512 with 64 rotary dims, topk 128 SWA + 512 compressed, E4M3 + UE8M0
-pools); the s_q = 64 / 256 / 1024 decodes and the 184 / 2123-token prefills are measured
-after the timed region and reported under "configs".
+resident in HBM).  Timing follows the pages' kernel benchmark [vLLM #58872, Test Plan:
+one captured graph per case, the L2 flushed before every replay outside the timed
+interval, the median of many replays]: each timed step flushes the caches (a 1 GiB
+fill), synchronizes, then replays a HIP graph holding ONE call between two HIP events on
+the launch stream; a short GPU spin queued before the first event keeps the host's graph
+launch latency out of the span.  The headline workload is the s_q = 1 decode (h_q = 64,
+d = 512 with 64 rotary dims, topk 128 SWA + 512 compressed, E4M3 + UE8M0 pools); the
+s_q = 64 / 1024 decodes and the 2123-token prefill (and the pages' s_q = 256 and
+184-token rows) are measured after the timed region and reported under "configs", each
+with at least 50 cold samples.  Warm figures (graphs of 10 back-to-back calls, caches
+hot) are kept beside them, labelled warm.
 
 Prints one JSON line:
-  value        tokens/s of the headline workload over the K timed steps (wall clock)
-  roofline     the headline call's compulsory HBM bytes / its mean duration (HIP events
-               on the launch stream) against 8 TB/s
-  cpu_baseline the fp64 oracle on a bounded sample of the same recipe, on the host cores
-  configs      per workload: us/call (warm and after a cache flush), tokens/s, HBM and
-               MFMA fractions
+  value        tokens/s of the headline workload: s_q / the mean cold span of the K timed
+               steps
+  roofline     the headline call's compulsory HBM bytes / its mean cold span, against
+               8 TB/s (and against the copy bandwidth measured in the same run)
+  cpu_baseline the fp64 oracle on the headline workload's own arrays (median of 3 runs),
+               on the host cores; per-config oracle medians under "cpu_oracle_configs"
+  measured_peaks  device-copy bandwidth and pure MFMA-loop rates (bf16, E4M3) measured
+               in the same run, beside the published peaks
+  configs      per workload: cold median / p10 / p90 / mean us per call, warm us per call,
+               tokens/s, HBM and MFMA fractions (cold, and warm labelled as such)
   kv_insert    the KV-insert entry point (the pool-row producer) on its three workloads:
                us/call, tokens/s, algorithmic HBM bytes / mean duration against 8 TB/s
   build_index  the index-row builder on its four workloads, the same figures
@@ -27,9 +36,10 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 Counter helpers (for the HBM traffic figure, see profiles/):
   python bench.py --copy-probe MIB    plain device-to-device copies of MIB MiB (the
                                       reference kernel for FETCH_SIZE / WRITE_SIZE)
-  python bench.py --traffic-from DIR  turn the four rocprofv3 --pmc CSVs under DIR
+  python bench.py --traffic-from DIR --workload W
+                                      turn the four rocprofv3 --pmc CSVs under DIR
                                       (fetch/, write/, copy_fetch/, copy_write/) into
-                                      profiles/traffic_decode_sq1.json
+                                      profiles/traffic_<W>.json
 """
 from __future__ import annotations
 
@@ -54,8 +64,10 @@ MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 / fp16 MFMA
 MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 MFMA (the output projection's arithmetic)
 PAGES_US_SQ1 = 22.7            # pages' fused kernel at s_q = 1 (GB200, TP4, CUDA graph): context only
 EXTRA = ["decode_sq64", "decode_sq1024", "prefill_sq2123", "decode_sq256", "prefill_sq184"]
-FLUSH_BYTES = 512 << 20        # larger than the 256 MB MALL + 8 x 4 MB L2
-CALLS_PER_GRAPH = 10           # timed replays hold this many back-to-back calls
+FLUSH_BYTES = 1 << 30          # larger than the 256 MB MALL + 8 x 4 MB L2
+CALLS_PER_GRAPH = 10           # warm replays hold this many back-to-back calls
+MIN_COLD_SAMPLES = 50          # cold single-call replays per workload, whatever --steps is
+SPIN_CYCLES = 200000           # GPU spin before each timed call (~80 us): covers the graph launch
 
 
 def upload(inp, torch, device):
@@ -95,8 +107,43 @@ def kernel_names(s_q, ns, torch, device):
     return "smla_order + smla_ws" if s_q > cus else "smla_ws"
 
 
-def measure(name, steps, warmup, torch, device, timed_steps=None):
-    """Time one workload; returns (result dict, wall seconds of the timed steps)."""
+class ColdTimer:
+    """Cold single-call timing: flush the caches (1 GiB fill), synchronize, queue a short
+    GPU spin, then an event, the replay, an event.  The spin keeps the GPU busy while the
+    host submits the event and the replay, so the span holds the call and not the launch
+    latency; the flush and the synchronization lie outside the span."""
+
+    def __init__(self, torch, device):
+        self.torch = torch
+        self.flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=device)
+        self.stream = torch.cuda.current_stream()
+        try:
+            torch.cuda._sleep(10)
+            self.spin = True
+        except Exception:  # pragma: no cover - torch builds without the spin kernel
+            self.spin = False
+
+    def run(self, replay, n):
+        torch = self.torch
+        out = []
+        for _ in range(n):
+            self.flush.zero_()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            if self.spin:
+                torch.cuda._sleep(SPIN_CYCLES)
+            a.record(self.stream)
+            replay()
+            b.record(self.stream)
+            b.synchronize()
+            out.append(a.elapsed_time(b) * 1e3)
+        return np.array(out)
+
+
+def measure(name, steps, warmup, torch, device, cold_timer, timed_steps=None):
+    """Time one workload.  Returns (result dict, wall seconds of the timed steps, number of
+    timed steps): the timed steps are cold single-call replays (timed_steps of them for the
+    headline; at least MIN_COLD_SAMPLES for every workload), then warm graphs of 10 calls."""
     from prefill_token_amd import inputs, make_params, sparse_mla_fwd, sparse_mla_num_splits, sparse_mla_workspace_size
 
     inp = inputs.make(name)
@@ -119,10 +166,10 @@ def measure(name, steps, warmup, torch, device, timed_steps=None):
         call()
     torch.cuda.synchronize()
     eager_ref = (out_fp8.clone(), out_sc.clone())
-    graph1 = torch.cuda.CUDAGraph()  # one call: launch-inclusive and cold timings
+    graph1 = torch.cuda.CUDAGraph()  # one call: the cold timed steps
     with torch.cuda.graph(graph1):
         call()
-    graphg = torch.cuda.CUDAGraph()  # CALLS_PER_GRAPH back-to-back calls: the timed steps
+    graphg = torch.cuda.CUDAGraph()  # CALLS_PER_GRAPH back-to-back calls: warm figures
     with torch.cuda.graph(graphg):
         for _ in range(CALLS_PER_GRAPH):
             call()
@@ -131,71 +178,106 @@ def measure(name, steps, warmup, torch, device, timed_steps=None):
         torch.cuda.synchronize()
         assert torch.equal(out_fp8, eager_ref[0]) and torch.equal(out_sc, eager_ref[1]), "graph replay differs"
 
-    n = max(1, timed_steps if timed_steps is not None else steps)
-    reps, rem = divmod(n, CALLS_PER_GRAPH)
-    plan = [(graphg, CALLS_PER_GRAPH)] * reps
-    if rem:  # exactly n calls: the remainder runs as one shorter graph
-        graphr = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graphr):
-            for _ in range(rem):
-                call()
-        plan.append((graphr, rem))
-    stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in plan]
+    # cold: the timed steps
+    n = max(1, timed_steps if timed_steps is not None else MIN_COLD_SAMPLES)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for (g, _), (a, b) in zip(plan, ev):
-        a.record(stream)
-        g.replay()
-        b.record(stream)
-    torch.cuda.synchronize()
+    cold = cold_timer.run(graph1.replay, n)
     wall = time.perf_counter() - t0
-    us = np.concatenate([np.full(k, a.elapsed_time(b) * 1e3 / k) for (_, k), (a, b) in zip(plan, ev)])
-
-    # one call per replay: includes the graph launch latency of a lone call
-    ev1 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
-    for a, b in ev1:
-        a.record(stream)
-        graph1.replay()
-        b.record(stream)
-    torch.cuda.synchronize()
-    us1 = np.array([a.elapsed_time(b) * 1e3 for a, b in ev1])
-
-    # cold: flush the caches before each replay (outside the event pair)
-    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=device)
-    cold = []
-    for _ in range(max(5, min(steps, 20))):
-        flush.zero_()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        graph1.replay()
-        b.record(stream)
-        b.synchronize()
-        cold.append(a.elapsed_time(b) * 1e3)
-    cold = np.array(cold)
-    del flush
+    if n < MIN_COLD_SAMPLES:  # more samples for the reported distribution
+        cold_all = np.concatenate([cold, cold_timer.run(graph1.replay, MIN_COLD_SAMPLES - n)])
+    else:
+        cold_all = cold
     assert torch.equal(out_fp8, eager_ref[0]), "replay after flush differs"
 
+    # warm: graphs of CALLS_PER_GRAPH back-to-back calls, caches hot
+    stream = torch.cuda.current_stream()
+    reps = max(2, MIN_COLD_SAMPLES // CALLS_PER_GRAPH)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        graphg.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    warm = np.array([a.elapsed_time(b) * 1e3 / CALLS_PER_GRAPH for a, b in ev])
+
     wm = work_model(inp)
-    mean_us = float(us.mean())
+    cold_mean = float(cold.mean())
+    cold_med = float(np.median(cold_all))
+    warm_mean = float(warm.mean())
     res = dict(
         workload=name, description=inp["description"], s_q=s_q, num_splits=ns,
         kernels=kernel_names(s_q, ns, torch, device),
-        us_per_call_mean=mean_us, us_per_call_median=float(np.median(us)),
-        us_per_call_p10=float(np.percentile(us, 10)), us_per_call_p90=float(np.percentile(us, 90)),
-        us_per_call_cold_median=float(np.median(cold)),
-        us_per_call_single_graph_median=float(np.median(us1)), calls_per_graph=CALLS_PER_GRAPH,
-        tokens_per_s=s_q / (mean_us * 1e-6), tokens_per_s_cold=s_q / (float(np.median(cold)) * 1e-6),
-        hbm_compulsory_GBs=wm["compulsory_bytes"] / (mean_us * 1e-6) / 1e9,
-        hbm_compulsory_frac=wm["compulsory_bytes"] / (mean_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-        gather_effective_GBs=wm["gathered_bytes"] / (mean_us * 1e-6) / 1e9,
-        mfma_TFLOPs=wm["flops"] / (mean_us * 1e-6) / 1e12,
-        mfma_frac=wm["flops"] / (mean_us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS,
-        hbm_cold_frac=wm["compulsory_bytes"] / (float(np.median(cold)) * 1e-6) / 1e9 / HBM_PEAK_GBS,
-        mfma_cold_frac=wm["flops"] / (float(np.median(cold)) * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS,
+        timing="cold: caches flushed before each single-call graph replay, HIP events on the launch stream",
+        cold_samples=int(cold_all.size),
+        us_per_call_median=cold_med, us_per_call_p10=float(np.percentile(cold_all, 10)),
+        us_per_call_p90=float(np.percentile(cold_all, 90)), us_per_call_mean=float(cold_all.mean()),
+        us_per_call_timed_mean=cold_mean,
+        us_per_call_warm_mean=warm_mean, us_per_call_warm_median=float(np.median(warm)),
+        calls_per_warm_graph=CALLS_PER_GRAPH,
+        tokens_per_s=s_q / (cold_med * 1e-6), tokens_per_s_warm=s_q / (warm_mean * 1e-6),
+        hbm_compulsory_GBs=wm["compulsory_bytes"] / (cold_med * 1e-6) / 1e9,
+        hbm_compulsory_frac=wm["compulsory_bytes"] / (cold_med * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        gather_effective_GBs=wm["gathered_bytes"] / (cold_med * 1e-6) / 1e9,
+        mfma_TFLOPs=wm["flops"] / (cold_med * 1e-6) / 1e12,
+        mfma_frac=wm["flops"] / (cold_med * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS,
+        hbm_compulsory_frac_warm=wm["compulsory_bytes"] / (warm_mean * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        mfma_frac_warm=wm["flops"] / (warm_mean * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS,
         **wm,
     )
     return res, wall, n
+
+
+def measured_peaks(torch, device):
+    """Device-copy bandwidth (bytes read + written per second, a 1 GiB torch copy) and the
+    MFMA-loop rates of libsmla_probe.so (bf16 and E4M3), median of 5 launches each."""
+    import ctypes
+
+    out = {}
+    nbytes = 1 << 30
+    src = torch.ones(nbytes, dtype=torch.uint8, device=device)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        b.synchronize()
+        ts.append(a.elapsed_time(b) * 1e-3)
+    out["copy_GBs"] = 2.0 * nbytes / float(np.median(ts)) / 1e9
+    del src, dst
+    try:
+        from prefill_token_amd.build import PROBE_LIB_PATH
+
+        lib = ctypes.CDLL(PROBE_LIB_PATH)
+        lib.smla_probe_mfma.restype = ctypes.c_double
+        lib.smla_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        cus = torch.cuda.get_device_properties(device).multi_processor_count
+        blocks = 2 * cus  # two 4-wave workgroups per CU: two waves per SIMD
+        buf = torch.empty(blocks, dtype=torch.float32, device=device)
+        stream = torch.cuda.current_stream().cuda_stream
+        for kind, key, iters in ((0, "mfma_bf16_TFLOPs", 4000), (1, "mfma_fp8_TFLOPs", 2000)):
+            flops = lib.smla_probe_mfma(kind, iters, blocks, stream, buf.data_ptr())
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(5):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                flops = lib.smla_probe_mfma(kind, iters, blocks, stream, buf.data_ptr())
+                b.record()
+                b.synchronize()
+                ts.append(a.elapsed_time(b) * 1e-3)
+            if flops > 0:
+                out[key] = flops / float(np.median(ts)) / 1e12
+    except OSError:
+        pass
+    out["note"] = ("copy: 1 GiB device copy, read + write bytes / time; MFMA: 8 independent accumulator chains per "
+                   "wave, two waves per SIMD, v_mfma_f32_32x32x16_bf16 / v_mfma_scale_f32_32x32x64_f8f6f4")
+    return out
 
 
 def measure_insert(name, steps, torch, device):
@@ -330,44 +412,71 @@ def measure_wo_a(name, steps, torch, device):
                 mfma_frac_fp8=flops / (mean_us * 1e-6) / 1e12 / MFMA_FP8_PEAK_TFLOPS)
 
 
-def cpu_baseline(seconds, torch, device):
-    """The oracle on a bounded sample of the headline recipe, all host threads."""
+def _oracle_run(inp):
     import oracle
-    from prefill_token_amd import inputs
 
-    sample_tokens = 64
-    inp = inputs.make("decode_sq1", seed=20261001, s_q=sample_tokens)
     args = (inp["q"], inp["kv_pool"], inp["kv_scales"], inp["indices"], inp["topk_length"], inp["positions"],
             inp["norm_w"])
     kw = dict(sm_scale=inp["sm_scale"], eps=inp["eps"], theta=inp["theta"], rope_dim=inp["rope_dim"])
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        o, codes, scales = oracle.sparse_mla(*args, **kw)
-        reps += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    el = time.perf_counter() - t0
-    # the same sample through the library, compared with the oracle (pre-quant error)
-    from prefill_token_amd import sparse_mla_fwd
+    return oracle.sparse_mla(*args, **kw)
 
+
+def oracle_median(inp, min_seconds=0.0):
+    """Median wall time of 3 oracle runs over a workload's own arrays; a run repeats the
+    whole workload until it lasts min_seconds (so that one-token workloads are timed over
+    many repetitions).  Returns (seconds per workload, repetitions per run, runs)."""
+    runs, reps = [], 1
+    t0 = time.perf_counter()
+    _oracle_run(inp)
+    one = time.perf_counter() - t0
+    if min_seconds > 0 and one < min_seconds:
+        reps = int(math.ceil(min_seconds / max(one, 1e-6)))
+    for _ in range(3):
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            _oracle_run(inp)
+        runs.append((time.perf_counter() - t0) / reps)
+    return float(np.median(runs)), reps, runs
+
+
+def cpu_baseline(head_name, configs, torch, device, seconds):
+    """The oracle (as it stands) on the host cores: the headline workload's own arrays
+    (median of 3 runs, each repeating the workload for about seconds / 3), and every config
+    workload's own arrays (median of 3 runs).  Also the headline's GPU-vs-oracle pre-quant
+    error on those arrays."""
+    import oracle
+    from prefill_token_amd import inputs, sparse_mla_fwd
+
+    inp = inputs.make(head_name)
+    per, reps, runs = oracle_median(inp, min_seconds=seconds / 3.0)
+    o, _, _ = _oracle_run(inp)
     t = upload(inp, torch, device)
     out_fp8 = torch.empty(inp["q"].shape, dtype=torch.uint8, device=device)
     out_sc = torch.empty(inp["q"].shape[:2] + (inp["d"] // 32,), dtype=torch.uint8, device=device)
     out_f32 = torch.empty(inp["q"].shape, dtype=torch.float32, device=device)
     sparse_mla_fwd(t["q"], t["kv_pool"], t["kv_scales"], t["indices"], t["topk_length"], t["positions"],
-                   t["norm_w"], out_fp8, out_sc, out_f32=out_f32, **kw)
+                   t["norm_w"], out_fp8, out_sc, out_f32=out_f32, sm_scale=inp["sm_scale"], eps=inp["eps"],
+                   theta=inp["theta"], rope_dim=inp["rope_dim"])
     torch.cuda.synchronize()
     g = out_f32.cpu().numpy().astype(np.float64)
     blk = o.reshape(*o.shape[:-1], -1, 32)
     amax = np.abs(blk).max(-1)
     err = np.abs(g.reshape(blk.shape) - blk).max(-1) / np.maximum(amax, 1e-300)
-    return {
-        "value": sample_tokens * reps / el, "unit": "tokens/s", "cores": min(oracle.num_threads(), sample_tokens),
-        "kind": "oracle",
-        "sample": f"{sample_tokens} decode tokens drawn with the decode s_q=1 recipe (same shapes, index mix "
-                  f"and distributions), {reps} repetition(s), {el:.1f} s",
-        "seconds": el, "gpu_vs_oracle_max_rel_block_err": float(err.max()),
+    cores = oracle.num_threads()
+    head = {
+        "value": inp["s_q"] / per, "unit": "tokens/s", "cores": min(cores, max(inp["s_q"], 1)), "kind": "oracle",
+        "sample": f"the {head_name} workload's own arrays ({inp['s_q']} token(s)); median of 3 runs of {reps} "
+                  f"repetition(s) each ({sum(runs) * reps:.1f} s in all); OpenMP over tokens",
+        "seconds_per_call": per, "gpu_vs_oracle_max_rel_block_err": float(err.max()),
     }
+    per_cfg = []
+    for name in configs:
+        c = inputs.make(name)
+        sec, _, runs = oracle_median(c)
+        per_cfg.append({"workload": name, "s_q": c["s_q"], "seconds_median_of_3": sec,
+                        "runs_s": runs, "tokens_per_s": c["s_q"] / sec,
+                        "cores": min(cores, c["s_q"])})
+    return head, per_cfg
 
 
 def host_info():
@@ -390,10 +499,10 @@ def source_digest():
     return h.hexdigest()[:16]
 
 
-def load_traffic(digest):
-    """HBM bytes per call from the committed rocprofv3 counter summary, if it was taken
-    on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", "traffic_decode_sq1.json")
+def load_traffic(digest, workload):
+    """HBM bytes per call from the committed rocprofv3 counter summary of this workload, if
+    it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     try:
         with open(path) as f:
             rec = json.load(f)
@@ -437,11 +546,11 @@ def _counter_rows(folder, counter):
     return rows
 
 
-def traffic_from(folder, copy_mib):
-    """HBM bytes per sparse_mla_fwd call at decode s_q = 1 from rocprofv3 --pmc runs:
+def traffic_from(folder, copy_mib, workload):
+    """HBM bytes per sparse_mla_fwd call of one workload from rocprofv3 --pmc runs:
     the median FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of each of its kernels, each
     scaled by (known bytes / counter reading) of a plain copy of copy_mib MiB."""
-    out = {"source_digest": source_digest(), "workload": "decode_sq1", "copy_probe_mib": copy_mib, "kernels": {}}
+    out = {"source_digest": source_digest(), "workload": workload, "copy_probe_mib": copy_mib, "kernels": {}}
     total = 0.0
     for counter, sub, csub in (("FETCH_SIZE", "fetch", "copy_fetch"), ("WRITE_SIZE", "write", "copy_write")):
         crow = [v for k, v in _counter_rows(os.path.join(folder, csub), counter) if "copy" in k.lower()]
@@ -450,7 +559,7 @@ def traffic_from(folder, copy_mib):
         factor = (copy_mib * 1024.0) / float(np.median(crow))
         out[f"{counter}_copy_factor"] = factor
         rows = _counter_rows(os.path.join(folder, sub), counter)
-        for kname in ("smla_ws", "smla_combine"):
+        for kname in ("smla_order", "smla_ws", "smla_combine"):
             vals = [v for k, v in rows if kname in k]
             if not vals:
                 continue
@@ -459,7 +568,7 @@ def traffic_from(folder, copy_mib):
             out["kernels"][kname]["dispatches"] = len(vals)
             total += kib * factor * 1024.0
     out["hbm_bytes_per_call"] = total
-    path = os.path.join(ROOT, "profiles", "traffic_decode_sq1.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out), flush=True)
@@ -483,7 +592,7 @@ def main():
         copy_probe(args.copy_probe)
         return
     if args.traffic_from:
-        traffic_from(args.traffic_from, 256)
+        traffic_from(args.traffic_from, 256, args.workload)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -498,15 +607,20 @@ def main():
     _lib.load()  # fails loudly when the HIP library has not been built
     device = torch.device("cuda:0")
     torch.cuda.set_device(device)
+    cold_timer = ColdTimer(torch, device)
 
-    head, wall, n = measure(args.workload, args.steps, args.warmup, torch, device, timed_steps=args.steps)
+    head, wall, n = measure(args.workload, args.steps, args.warmup, torch, device, cold_timer,
+                            timed_steps=args.steps)
     configs = [head]
     for name in [x for x in args.extra.split(",") if x and x != args.workload]:
-        r, _, _ = measure(name, args.steps, args.warmup, torch, device)
+        r, _, _ = measure(name, args.steps, args.warmup, torch, device, cold_timer)
         configs.append(r)
-        print(f"# {name}: {r['us_per_call_mean']:.2f} us/call, {r['tokens_per_s']:.4g} tok/s, "
-              f"HBM {100 * r['hbm_compulsory_frac']:.1f}%, MFMA {100 * r['mfma_frac']:.1f}%", file=sys.stderr,
-              flush=True)
+    for r in configs:
+        print(f"# {r['workload']}: cold {r['us_per_call_median']:.2f} us/call (p10 {r['us_per_call_p10']:.2f}, "
+              f"p90 {r['us_per_call_p90']:.2f}), warm {r['us_per_call_warm_mean']:.2f} us, "
+              f"{r['tokens_per_s']:.4g} tok/s, HBM {100 * r['hbm_compulsory_frac']:.1f}%, "
+              f"MFMA {100 * r['mfma_frac']:.1f}%", file=sys.stderr, flush=True)
+    del cold_timer
 
     inserts = []
     if not args.no_insert:
@@ -539,31 +653,40 @@ def main():
                   f"HBM {100 * r['hbm_frac']:.1f}%, MFMA(fp8) {100 * r['mfma_frac_fp8']:.1f}%", file=sys.stderr,
                   flush=True)
 
+    peaks = measured_peaks(torch, device)
+    print(f"# measured peaks: {json.dumps(peaks)}", file=sys.stderr, flush=True)
     digest = source_digest()
-    traffic = load_traffic(digest)
-    achieved = head["compulsory_bytes"] / (head["us_per_call_mean"] * 1e-6) / 1e9
+    traffic = load_traffic(digest, head["workload"])
+    mean_us = head["us_per_call_timed_mean"]
+    achieved = head["compulsory_bytes"] / (mean_us * 1e-6) / 1e9
     roofline = {
         "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-        "traffic": traffic, "kernel": head["kernels"], "scope": "whole sparse_mla_fwd call (HIP events on its stream)",
-        "bytes_per_call": head["compulsory_bytes"], "mean_us": head["us_per_call_mean"],
+        "traffic": traffic, "kernel": head["kernels"],
+        "scope": "whole sparse_mla_fwd call, cold (caches flushed before each call), HIP events on its stream",
+        "bytes_per_call": head["compulsory_bytes"], "mean_us": mean_us,
+        "peak_measured_copy_GBs": peaks.get("copy_GBs"),
+        "frac_of_measured_copy": achieved / peaks["copy_GBs"] if peaks.get("copy_GBs") else None,
     }
-    cpu = None
+    cpu, cpu_cfg = None, None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args.cpu_seconds, torch, device)
-    value = head["s_q"] * n / wall
+        cpu, cpu_cfg = cpu_baseline(args.workload, [c["workload"] for c in configs[1:4]], torch, device,
+                                    args.cpu_seconds)
+    value = head["s_q"] / (mean_us * 1e-6)
     out = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": n, "warmup": args.warmup,
         "ms_per_step": wall / n * 1e3, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": value / (1e6 / PAGES_US_SQ1),
         "vs_baseline_note": "value / (1 / 22.7 us): the pages' fused kernel at s_q=1 on GB200 TP4 (context, "
                             "another machine)",
+        "value_note": "s_q / the mean span of the K timed steps; each step flushes the caches and synchronizes "
+                      "outside the span (ms_per_step is the wall time of a whole step, flush included)",
         "dtype": "e4m3+bf16", "data": "synthetic",
         "dtype_note": "QK^T on E4M3 MFMAs (q split into two E4M3 terms with UE8M0 scales), P.V on bf16 "
                       "MFMAs, f32 accumulation and softmax",
         "config": {"workload": head["description"], "name": head["workload"], "s_q": head["s_q"],
-                   "num_splits": head["num_splits"], "graph": True},
-        "roofline": roofline, "cpu_baseline": cpu, "configs": configs, "kv_insert": inserts,
-        "build_index": builds, "wo_a": projs,
+                   "num_splits": head["num_splits"], "graph": True, "timing": "cold"},
+        "roofline": roofline, "cpu_baseline": cpu, "cpu_oracle_configs": cpu_cfg, "measured_peaks": peaks,
+        "configs": configs, "kv_insert": inserts, "build_index": builds, "wo_a": projs,
         "device": torch.cuda.get_device_name(device), "host": host_info(), "source_digest": digest,
     }
     print(json.dumps(out), flush=True)

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define SMLA_ABI_VERSION 2
+#define SMLA_ABI_VERSION 3
 
 /* return codes */
 #define SMLA_OK 0
@@ -115,9 +115,12 @@ typedef struct smla_params {
  *   params      host pointer, read during the call only
  *
  * Preconditions not checked on the device (the values are in device memory): read
- * indices lie in [-1, n_rows); kv_scales lie in [10, 246], the range in which every
- * dequantized E4M3 value is a normal bf16 number (outside it, tiny values are rounded
- * by the hardware conversion and huge ones overflow).
+ * indices lie in [-1, n_rows) (an id outside that range is read as an empty slot, never
+ * dereferenced); kv_scales of read rows lie in [SMLA_KV_SCALE_MIN, SMLA_KV_SCALE_MAX] =
+ * [10, 246], the range in which every dequantized E4M3 value is a normal bf16 number
+ * (outside it, tiny values are rounded by the hardware conversion and huge ones
+ * overflow).  sparse_mla_kv_insert writes rows in that range.  The debug build
+ * (libsmla_debug.so, see sparse_mla_debug_checks) reports violations of both.
  *
  * Returns SMLA_OK, or SMLA_ERR_* with nothing launched (SMLA_ERR_HIP: a launch failed).
  */
@@ -146,7 +149,7 @@ int sparse_mla_num_splits(const smla_params* params);
  *
  *   1. x = kv[i, :] (bf16); y = x / sqrt(mean(x^2) + rms_eps) * norm_w      (RMSNorm)
  *   2. rotate-half RoPE on the last rope_dim dims of y at angle p * rope_theta^(-2j/rope_dim)
- *   3. per 32-element block: e = smallest integer in [0, 254] with 448 * 2^(e-127) >= max|y|,
+ *   3. per 32-element block: e = smallest integer in [10, 254] with 448 * 2^(e-127) >= max|y|,
  *      kv_scales[p mod n_swa, block] = e,
  *      kv_pool[p mod n_swa, block elements] = round-to-nearest-even E4M3FN(y * 2^(127-e))
  *
@@ -166,9 +169,13 @@ int sparse_mla_num_splits(const smla_params* params);
  *   kv_scales   u8 [n_rows][16]          (device, rows p mod n_swa written; 4-byte aligned)
  *   params      host pointer, read during the call only
  *
- * Precondition not checked on the device: the non-negative positions of one call fall
+ * The exponent floor of 10 (SMLA_KV_SCALE_MIN) keeps every written row inside the scale
+ * range sparse_mla_fwd decodes exactly; the top of that range (246) holds whenever every
+ * |norm_w| is below 2^123 (|y| <= sqrt(512) max|norm_w| after the norm).
+ *
+ * Preconditions not checked on the device: the non-negative positions of one call fall
  * on distinct rows (distinct modulo n_swa); rows written by two tokens of one call hold
- * an unspecified mixture.  Same conventions as sparse_mla_fwd otherwise (asynchronous on
+ * an unspecified mixture.  |norm_w| < 2^123.  Same conventions as sparse_mla_fwd otherwise (asynchronous on
  * params->stream, nothing allocated, errors by return code with nothing launched).
  */
 typedef struct smla_kv_insert_params {
@@ -263,6 +270,25 @@ typedef struct smla_wo_a_params {
 
 int sparse_mla_wo_a(const uint8_t* x_fp8, const uint8_t* x_scales, const uint8_t* w_fp8, const uint8_t* w_scales,
                     void* y, const smla_wo_a_params* params);
+
+/*
+ * Debug build.  The library compiled with SMLA_DEBUG_CHECKS (libsmla_debug.so beside
+ * libsmla.so; same entry points) checks sparse_mla_fwd's device-side preconditions while
+ * it runs: an entry j < topk_length[t] outside [-1, n_rows) sets SMLA_DEBUG_BAD_INDEX, a
+ * read row with a kv_scales byte outside [SMLA_KV_SCALE_MIN, SMLA_KV_SCALE_MAX] sets
+ * SMLA_DEBUG_BAD_SCALE, in the u32 error word at byte SMLA_DEBUG_WORD_OFFSET of the
+ * workspace (or-ed in; the library never clears it: zero it before the calls to check).
+ * The call still completes normally (a bad id reads as an empty slot).  The production
+ * library never touches the word.  [vLLM #56344 "Deepseek V41 Attention MegaKernel",
+ * Purpose, bug-fix bullet: stale or unterminated index rows are the failure this reports.]
+ * Returns 1 in the debug build, 0 in the production build.
+ */
+#define SMLA_DEBUG_WORD_OFFSET 8
+#define SMLA_DEBUG_BAD_INDEX 1u
+#define SMLA_DEBUG_BAD_SCALE 2u
+#define SMLA_KV_SCALE_MIN 10
+#define SMLA_KV_SCALE_MAX 246
+int sparse_mla_debug_checks(void);
 
 /* Thread-local, NUL-terminated message describing the last failed call on this thread
    ("" if none).  Valid until the next call on the same thread. */

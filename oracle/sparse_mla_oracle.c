@@ -286,6 +286,34 @@ int oracle_sparse_mla(const uint16_t* q, const void* kv_pool, const uint8_t* kv_
 /* ---------------------------------------------------------------- KV insert */
 
 /*
+ * Exponent floor of the pool rows.  A pool row is consumed by the step, whose value
+ * decoding e4m3(code) * 2^(e-127) stays a normal number in bf16 / f32 arithmetic only for
+ * e >= 10 (the smallest E4M3 subnormal, 2^-9, times 2^-117 is 2^-126).  The producer
+ * therefore never writes an exponent below 10: a block whose amax is below
+ * 448 * 2^(10-127) is coded at e = 10, where its values round (RNE) onto the E4M3 grid at
+ * that scale -- to subnormal codes or to zero -- and never saturate.  (Reading: the pages
+ * fix the 528-byte row but not the producer's range; this is the range the row format is
+ * consumed in.)
+ */
+#define POOL_EXP_MIN 10
+
+static void quantize_pool_row(const double* y, int d, uint8_t* codes, uint8_t* scales) {
+  int b, i;
+  for (b = 0; b < d / BLOCK; ++b) {
+    double amax = 0.0;
+    int e;
+    for (i = 0; i < BLOCK; ++i) {
+      double a = fabs(y[b * BLOCK + i]);
+      if (a > amax) amax = a;
+    }
+    e = oracle_ue8m0_exponent(amax);
+    if (e < POOL_EXP_MIN) e = POOL_EXP_MIN;
+    scales[b] = (uint8_t)e;
+    for (i = 0; i < BLOCK; ++i) codes[b * BLOCK + i] = oracle_e4m3_encode(ldexp(y[b * BLOCK + i], 127 - e));
+  }
+}
+
+/*
  * KV insert, the producer of the pool rows the step gathers
  *   [vLLM #56344 "Deepseek V41 Attention MegaKernel", Purpose: fp8 SWA cache rows of 512
  *    E4M3 bytes + UE8M0 scales written by an insert kernel]
@@ -294,7 +322,7 @@ int oracle_sparse_mla(const uint16_t* q, const void* kv_pool, const uint8_t* kv_
  * Readings: the kv latent is RMS-normalised like a q head (same formula, its own weight),
  * its last r dims carry RoPE at the token's own position (the step's inverse RoPE on
  * the output only undoes a rotation the stored rows carry), and it is quantized with the
- * step's output codec; the row is the position modulo the window size n_swa, and a
+ * step's output codec with the exponent floored at POOL_EXP_MIN (above); the row is the position modulo the window size n_swa, and a
  * negative position means "no token".  Tokens are applied in order (a later token that
  * lands on the same row overwrites an earlier one).
  *   kv         bf16 bits [n][d]
@@ -324,7 +352,7 @@ int oracle_kv_insert(const uint16_t* kv, const int32_t* positions, const double*
     for (i = 0; i < d; ++i) x[i] = oracle_bf16_decode(kv[(int64_t)t * d + i]);
     oracle_rmsnorm(x, norm_w, d, eps, y);
     oracle_rope(y, d, rope_dim, (double)positions[t], theta, +1);
-    oracle_quantize_blocks(y, d, kv_pool + row * d, kv_scales + row * (d / BLOCK));
+    quantize_pool_row(y, d, kv_pool + row * d, kv_scales + row * (d / BLOCK));
   }
   free(x); free(y);
   return ORACLE_OK;

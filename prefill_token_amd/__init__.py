@@ -38,6 +38,55 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else int(t.data_ptr())
 
 
+class _Checker:
+    """Argument checks of one binding call: dtype, shape, contiguity and device of every
+    tensor, before anything reaches the C ABI.  The library itself only sees pointers and
+    sizes, so a tensor whose shape disagrees with the others would be read or written out
+    of bounds on the device; every such mismatch is a ValueError here instead."""
+
+    def __init__(self, fn: str):
+        self.fn = fn
+        self.seen = []
+
+    def __call__(self, name, t, dtypes, shape=None, ndim=None, optional=False):
+        if t is None:
+            if optional:
+                return None
+            raise ValueError(f"{self.fn}: {name} is required")
+        if not hasattr(t, "dtype") or not hasattr(t, "data_ptr"):
+            raise ValueError(f"{self.fn}: {name} must be a torch tensor")
+        if t.dtype not in dtypes:
+            raise ValueError(f"{self.fn}: {name} must have dtype " + " or ".join(str(d) for d in dtypes) +
+                             f" (got {t.dtype})")
+        if ndim is not None and t.dim() != ndim:
+            raise ValueError(f"{self.fn}: {name} must have {ndim} dimensions (got shape {tuple(t.shape)})")
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{self.fn}: {name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+        if not t.is_contiguous():
+            raise ValueError(f"{self.fn}: {name} must be contiguous")
+        self.seen.append((name, t))
+        return t
+
+    def done(self):
+        """Every tensor checked so far lies on one GPU (checked last, so that the dtype and
+        shape rules can be exercised with host tensors)."""
+        dev = None
+        for name, t in self.seen:
+            if t.device.type != "cuda":
+                raise ValueError(f"{self.fn}: {name} must be on a GPU (got {t.device})")
+            if dev is None:
+                dev = t.device
+            elif t.device != dev:
+                raise ValueError(f"{self.fn}: {name} is on {t.device}, other arguments on {dev}")
+
+
+def _dtypes():
+    import torch
+
+    codes = (torch.uint8, torch.float8_e4m3fn)
+    return torch, codes
+
+
 def make_params(*, s_q: int, h_q: int, d: int, rope_dim: int, topk: int, n_rows: int, kv_format: int,
                 sm_scale: float, eps: float = 1e-6, theta: float = 1e4, num_splits: int = 0,
                 out_f32=None, workspace=None, stream=None) -> SmlaParams:
@@ -83,25 +132,48 @@ def sparse_mla_fwd(q, kv_pool, kv_scales, indices, topk_length, positions, norm_
     allocated here, zero-filled, when none is given.  Calls sharing a workspace must not
     overlap.  Raises SmlaError with the library's message on failure.
     """
-    import torch
-
+    torch, codes = _dtypes()
+    ck = _Checker("sparse_mla_fwd")
+    ck("q", q, (torch.bfloat16,), ndim=3)
     s_q, h_q, d = q.shape
+    ck("kv_pool", kv_pool, (torch.bfloat16,) + codes, ndim=2)
+    n_rows = kv_pool.shape[0]
+    if kv_pool.shape[1] != d:
+        raise ValueError(f"sparse_mla_fwd: kv_pool rows must have d = {d} elements (got {kv_pool.shape[1]})")
     bf16_pool = kv_pool.dtype == torch.bfloat16
     kv_format = SMLA_KV_BF16 if bf16_pool else SMLA_KV_E4M3_UE8M0
-    for name, t in (("q", q), ("kv_pool", kv_pool), ("indices", indices), ("topk_length", topk_length),
-                    ("positions", positions), ("norm_w", norm_w), ("out_fp8", out_fp8),
-                    ("out_scales", out_scales), ("kv_scales", kv_scales), ("out_f32", out_f32)):
-        if t is not None and not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    topk = indices.shape[1] if indices.dim() == 2 else 0
+    if bf16_pool:
+        if kv_scales is not None:
+            raise ValueError("sparse_mla_fwd: kv_scales must be None for a bf16 pool")
+    else:
+        if d % 32:
+            raise ValueError(f"sparse_mla_fwd: d must be a multiple of 32 (got {d})")
+        ck("kv_scales", kv_scales, (torch.uint8,), shape=(n_rows, d // 32))
+    ck("indices", indices, (torch.int32,), ndim=2)
+    if indices.shape[0] != s_q:
+        raise ValueError(f"sparse_mla_fwd: indices must have {s_q} rows (got {indices.shape[0]})")
+    topk = indices.shape[1]
+    ck("topk_length", topk_length, (torch.int32,), shape=(s_q,))
+    ck("positions", positions, (torch.int32,), shape=(s_q,))
+    ck("norm_w", norm_w, (torch.float32,), shape=(d,))
+    ck("out_fp8", out_fp8, codes, shape=(s_q, h_q, d))
+    ck("out_scales", out_scales, (torch.uint8,), shape=(s_q, h_q, d // 32))
+    ck("out_f32", out_f32, (torch.float32,), shape=(s_q, h_q, d), optional=True)
+    ck("workspace", workspace, (torch.uint8,), ndim=1, optional=True)
+    ck.done()
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    params = make_params(s_q=s_q, h_q=h_q, d=d, rope_dim=rope_dim, topk=topk, n_rows=kv_pool.shape[0],
+    elif workspace is None:
+        # a workspace allocated here would be zero-filled and freed on torch's current
+        # stream, unordered with the kernels enqueued on `stream`
+        raise ValueError("sparse_mla_fwd: pass a workspace when enqueuing on an explicit stream")
+    params = make_params(s_q=s_q, h_q=h_q, d=d, rope_dim=rope_dim, topk=topk, n_rows=n_rows,
                          kv_format=kv_format, sm_scale=sm_scale, eps=eps, theta=theta, num_splits=num_splits,
                          out_f32=out_f32, workspace=workspace, stream=stream)
     need = sparse_mla_workspace_size(params)
     if need > 0 and workspace is None:
-        # its scheduler counters must start at zero (every call leaves them zero)
+        # its scheduler counters must start at zero (every call leaves them zero); made,
+        # used and released on torch's current stream, which the kernels run on
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
         params.workspace = _ptr(workspace)
         params.workspace_bytes = need
@@ -129,13 +201,17 @@ def sparse_mla_kv_insert(kv, positions, norm_w, kv_pool, kv_scales, *, rope_dim:
     kv_pool uint8 / float8_e4m3fn [n_rows, 512] and kv_scales uint8 [n_rows, 16], whose
     rows ``positions mod n_swa`` are overwritten.  Raises SmlaError on failure.
     """
-    import torch
-
-    for name, t in (("kv", kv), ("positions", positions), ("norm_w", norm_w), ("kv_pool", kv_pool),
-                    ("kv_scales", kv_scales)):
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
+    torch, codes = _dtypes()
+    ck = _Checker("sparse_mla_kv_insert")
+    ck("kv", kv, (torch.bfloat16,), ndim=2)
     n, d = kv.shape
+    ck("positions", positions, (torch.int32,), shape=(n,))
+    ck("norm_w", norm_w, (torch.float32,), shape=(d,))
+    ck("kv_pool", kv_pool, codes, ndim=2)
+    if kv_pool.shape[1] != d:
+        raise ValueError(f"sparse_mla_kv_insert: kv_pool rows must have {d} elements (got {kv_pool.shape[1]})")
+    ck("kv_scales", kv_scales, (torch.uint8,), shape=(kv_pool.shape[0], d // 32))
+    ck.done()
     if stream is None:
         stream = torch.cuda.current_stream(kv.device).cuda_stream
     params = make_kv_insert_params(n=n, d=d, rope_dim=rope_dim, n_swa=n_swa, n_rows=kv_pool.shape[0], eps=eps,
@@ -162,13 +238,17 @@ def sparse_mla_build_index(positions, logits, n_valid, indices, topk_length, *, 
     positions int32 [s_q]; logits bf16 [s_q, n_cand]; n_valid int32 [s_q] or None;
     indices int32 [s_q, topk] and topk_length int32 [s_q] are written.  Raises SmlaError.
     """
-    import torch
-
-    for name, t in (("positions", positions), ("logits", logits), ("n_valid", n_valid), ("indices", indices),
-                    ("topk_length", topk_length)):
-        if t is not None and not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
+    torch, _ = _dtypes()
+    ck = _Checker("sparse_mla_build_index")
+    ck("logits", logits, (torch.bfloat16,), ndim=2)
     s_q, n_cand = logits.shape
+    ck("positions", positions, (torch.int32,), shape=(s_q,))
+    ck("n_valid", n_valid, (torch.int32,), shape=(s_q,), optional=True)
+    ck("indices", indices, (torch.int32,), ndim=2)
+    if indices.shape[0] != s_q:
+        raise ValueError(f"sparse_mla_build_index: indices must have {s_q} rows (got {indices.shape[0]})")
+    ck("topk_length", topk_length, (torch.int32,), shape=(s_q,))
+    ck.done()
     if stream is None:
         stream = torch.cuda.current_stream(logits.device).cuda_stream
     params = make_index_params(s_q=s_q, n_cand=n_cand, topk=indices.shape[1], window=window,
@@ -187,16 +267,26 @@ def sparse_mla_wo_a(x_fp8, x_scales, w_fp8, w_scales, y, *, heads_per_group: int
     outputs); w_fp8 uint8 [h_q / hg, d_out, hg * 512], w_scales uint8 [h_q / hg, d_out,
     hg * 16]; y bfloat16 [s_q, h_q / hg, d_out] is written.  Raises SmlaError.
     """
-    import torch
-
-    for name, t in (("x_fp8", x_fp8), ("x_scales", x_scales), ("w_fp8", w_fp8), ("w_scales", w_scales), ("y", y)):
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
+    torch, codes = _dtypes()
+    ck = _Checker("sparse_mla_wo_a")
+    ck("x_fp8", x_fp8, codes, ndim=3)
     s_q, h_q, d = x_fp8.shape
+    hg = int(heads_per_group)
+    if hg < 1 or h_q % hg:
+        raise ValueError(f"sparse_mla_wo_a: heads_per_group must divide h_q = {h_q} (got {hg})")
+    G = h_q // hg
+    ck("x_scales", x_scales, (torch.uint8,), shape=(s_q, h_q, d // 32))
+    ck("w_fp8", w_fp8, codes, ndim=3)
+    d_out = w_fp8.shape[1]
+    if tuple(w_fp8.shape) != (G, d_out, hg * d):
+        raise ValueError(f"sparse_mla_wo_a: w_fp8 must have shape {(G, d_out, hg * d)} (got {tuple(w_fp8.shape)})")
+    ck("w_scales", w_scales, (torch.uint8,), shape=(G, d_out, hg * d // 32))
+    ck("y", y, (torch.bfloat16,), shape=(s_q, G, d_out))
+    ck.done()
     if stream is None:
         stream = torch.cuda.current_stream(x_fp8.device).cuda_stream
     p = SmlaWoAParams()
-    p.s_q, p.h_q, p.d, p.heads_per_group, p.d_out = s_q, h_q, d, heads_per_group, w_fp8.shape[1]
+    p.s_q, p.h_q, p.d, p.heads_per_group, p.d_out = s_q, h_q, d, hg, d_out
     p.stream = stream
     rc = _lib.load().sparse_mla_wo_a(_ptr(x_fp8), _ptr(x_scales), _ptr(w_fp8), _ptr(w_scales), _ptr(y),
                                      ctypes.byref(p))

@@ -6,6 +6,11 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsmla.so")
+DEBUG_LIB_PATH = os.path.join(HERE, "libsmla_debug.so")
+
+SMLA_DEBUG_WORD_OFFSET = 8
+SMLA_DEBUG_BAD_INDEX = 1
+SMLA_DEBUG_BAD_SCALE = 2
 
 SMLA_OK = 0
 SMLA_ERR_NULL = 1
@@ -90,16 +95,12 @@ class LibraryMissing(RuntimeError):
     pass
 
 
-def load() -> ctypes.CDLL:
-    """Load the in-tree libsmla.so; raises LibraryMissing if it has not been built."""
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
+def _open(path: str) -> ctypes.CDLL:
+    if not os.path.exists(path):
         raise LibraryMissing(
-            f"{LIB_PATH} is missing: build it with `python -m prefill_token_amd.build` "
+            f"{path} is missing: build it with `python -m prefill_token_amd.build` "
             "(there is no fallback implementation)")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     lib.sparse_mla_fwd.restype = ctypes.c_int
     lib.sparse_mla_fwd.argtypes = [P, P, P, P, P, P, P, P, P, ctypes.POINTER(SmlaParams)]
@@ -117,8 +118,29 @@ def load() -> ctypes.CDLL:
     lib.sparse_mla_wo_a.argtypes = [P, P, P, P, P, ctypes.POINTER(SmlaWoAParams)]
     lib.sparse_mla_abi_version.restype = ctypes.c_int
     lib.sparse_mla_abi_version.argtypes = []
-    _lib = lib
+    lib.sparse_mla_debug_checks.restype = ctypes.c_int
+    lib.sparse_mla_debug_checks.argtypes = []
     return lib
+
+
+def load() -> ctypes.CDLL:
+    """Load the in-tree libsmla.so; raises LibraryMissing if it has not been built."""
+    global _lib
+    if _lib is None:
+        _lib = _open(LIB_PATH)
+    return _lib
+
+
+_debug_lib = None
+
+
+def load_debug() -> ctypes.CDLL:
+    """Load the in-tree debug build libsmla_debug.so (same entry points, with the device-side
+    precondition checks); raises LibraryMissing if it has not been built."""
+    global _debug_lib
+    if _debug_lib is None:
+        _debug_lib = _open(DEBUG_LIB_PATH)
+    return _debug_lib
 
 
 def last_error() -> str:

@@ -1,4 +1,6 @@
-"""Builds libsmla.so (the gfx950 kernels + C ABI) in-tree with hipcc.
+"""Builds libsmla.so (the gfx950 kernels + C ABI) in-tree with hipcc, and its debug twin
+libsmla_debug.so (the same sources with SMLA_DEBUG_CHECKS: device-side precondition
+checks reported in the workspace's error word).
 
     python -m prefill_token_amd.build        # or prefill_token_amd.build.build()
 """
@@ -13,6 +15,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libsmla.so")
+DEBUG_LIB_PATH = os.path.join(HERE, "libsmla_debug.so")
+PROBE_LIB_PATH = os.path.join(HERE, "libsmla_probe.so")  # measured MFMA ceilings for bench.py
 
 SOURCES = [os.path.join(CSRC, "smla_kernels.hip"), os.path.join(CSRC, "kv_insert.hip"),
            os.path.join(CSRC, "index_build.hip"), os.path.join(CSRC, "wo_a.hip"), os.path.join(CSRC, "smla_api.cpp")]
@@ -39,9 +43,9 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", tmp, *SOURCES]
+def _build_one(path: str, extra, verbose: bool, sources=None) -> str:
+    tmp = path + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-o", tmp, *(sources or SOURCES)]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -51,7 +55,20 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+    return path
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the libraries (the hipcc runs go in parallel); returns libsmla.so's path."""
+    import concurrent.futures as cf
+
+    with cf.ThreadPoolExecutor(3) as ex:
+        jobs = [ex.submit(_build_one, LIB_PATH, [], verbose),
+                ex.submit(_build_one, DEBUG_LIB_PATH, ["-DSMLA_DEBUG_CHECKS"], verbose),
+                ex.submit(_build_one, PROBE_LIB_PATH, [], verbose, [os.path.join(CSRC, "peak_probe.hip")])]
+        for j in jobs:
+            j.result()
     return LIB_PATH
 
 

@@ -4,9 +4,11 @@
 // (bf16) is RMS-normalised with norm_w, rotated (rotate-half RoPE on the last rope_dim
 // dims at angle p * theta^(-2j/rope_dim)), cut into 32-element blocks, and stored as one
 // pool row: 512 E4M3FN codes in kv_pool[p mod n_swa] and 16 UE8M0 exponents in
-// kv_scales[p mod n_swa].  The block exponent is the smallest e in [0, 254] with
+// kv_scales[p mod n_swa].  The block exponent is the smallest e in [10, 254] with
 // 448 * 2^(e-127) >= the block's max |y|, and the codes are the round-to-nearest-even
-// E4M3FN values of y * 2^(127-e).
+// E4M3FN values of y * 2^(127-e).  The floor of 10 keeps every row inside the scale
+// range the step dequantizes exactly (a larger exponent never saturates a code: blocks
+// whose values all lie below 448 * 2^-117 only lose bits to E4M3 subnormals and zero).
 //   [vLLM #56344 "Deepseek V41 Attention MegaKernel", Purpose: the fp8 SWA cache row of
 //    512 E4M3 bytes plus UE8M0 scales (528 B), written by an insert kernel]
 //   [vLLM #64364 "latency_specialized decode", Details, change table: the KV cache write
@@ -163,7 +165,8 @@ __global__ __launch_bounds__(64 * kInsWaves) void kv_insert_kernel(KvInsertArgs 
   for (int k = 0; k < 8; ++k) amax = fmax(amax, fabs(y[k]));
   amax = fmax(amax, __shfl_xor(amax, 1));
   amax = fmax(amax, __shfl_xor(amax, 2));
-  const int e = ue8m0_block_exp(amax);
+  const int e0 = ue8m0_block_exp(amax);
+  const int e = e0 < kScaleMin ? kScaleMin : e0;
   uint32_t lo = 0, hi = 0;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {

@@ -96,6 +96,14 @@ extern "C" {
 
 int sparse_mla_abi_version(void) { return SMLA_ABI_VERSION; }
 
+int sparse_mla_debug_checks(void) {
+#ifdef SMLA_DEBUG_CHECKS
+  return 1;
+#else
+  return 0;
+#endif
+}
+
 const char* sparse_mla_last_error(void) { return g_last_error.c_str(); }
 
 int sparse_mla_num_splits(const smla_params* p) {

@@ -29,8 +29,13 @@ struct LaunchArgs {
 constexpr int kTileRows = 64;
 
 // Bytes at the start of the workspace holding the work-item scheduler's two counters
-// (zero before a call, left zero by it).
+// (zero before a call, left zero by it), then the debug build's error word.
 constexpr size_t kSchedBytes = 256;
+constexpr int kDebugWord = 2;  // u32 index of the error word (byte offset 8)
+
+// UE8M0 pool scales the step dequantizes exactly: every E4M3 value times 2^(e-127) is a
+// normal bf16 number for e in [10, 246].  The KV insert writes no exponent below 10.
+constexpr int kScaleMin = 10, kScaleMax = 246;
 
 // Workspace floats per (token, split): acc [64][d] + m [64] + l [64] (slots for the
 // largest head count, whatever h_q is).

@@ -297,6 +297,25 @@ __device__ __forceinline__ void dma4(uint32_t voff, __amdgpu_buffer_rsrc_t rsrc,
       : "memory");
 }
 
+#ifdef SMLA_DEBUG_CHECKS
+// Debug build only: entries that are read (j < topk_length) but lie outside [-1, n_rows),
+// and read rows whose UE8M0 scales lie outside [kScaleMin, kScaleMax], set bits 1 and 2 of
+// the error word after the scheduler counters (or-ed in, never cleared here).  One wave
+// covers a tile: lane l holds entry l and reads the nsb scale bytes of slot l.
+__device__ __noinline__ void debug_flag_tile(unsigned* sched, long long n_rows, bool in_len, int raw, bool valid,
+                                             const unsigned char* row_scales, int nsb) {
+  unsigned bits = 0;
+  if (in_len && (raw < -1 || (long long)raw >= n_rows)) bits |= 1u;
+  if (valid && row_scales)
+    for (int b = 0; b < nsb; ++b) {
+      const int e = row_scales[b];
+      if (e < kScaleMin || e > kScaleMax) bits |= 2u;
+    }
+  const unsigned long long m1 = __ballot(bits & 1u), m2 = __ballot(bits & 2u);
+  if ((threadIdx.x & 63) == 0 && (m1 | m2)) atomicOr(sched + kDebugWord, (m1 ? 1u : 0u) | (m2 ? 2u : 0u));
+}
+#endif
+
 // lane permutation within rows of 16 lanes (DPP control CTRL), all lanes written
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
@@ -781,6 +800,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
     const unsigned long long mask = __ballot(id_cur >= 0);
     const int id_next = valid_id(tile + 1, raw_next);
     const int raw_next2 = fetch_id(tile + 2);
+#ifdef SMLA_DEBUG_CHECKS
+    if (w == 0)
+      debug_flag_tile(a.sched, a.n_rows, tile < te && tile * T + lane < lcap, raw_cur, id_cur >= 0,
+                      EB == 1 ? sc_l + C::NSB * lane : nullptr, C::NSB);
+#endif
 
     // ---- QK^T: partial S^T[32 rows of half qc][32 heads of group qa] over dim half qd
     f32x16 s;
@@ -1562,6 +1586,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
         const unsigned long long mask = __ballot(id_cur >= 0);
         const int id_next = valid_id(I, tile + 1, raw_next);
         const int raw_next2 = fetch_id(I, tile + 2);
+#ifdef SMLA_DEBUG_CHECKS
+        if (w == 0)
+          debug_flag_tile(a.sched, a.n_rows, tile < I.te && tile * T + lane < I.lcap, raw_cur, id_cur >= 0,
+                          sc_buf(it) + C::NSB * lane, C::NSB);
+#endif
         // the next tile's DMA (the row DMAs queue behind the P.V waves' MFMAs meanwhile)
         if (it + 1 < n) {
 #pragma unroll

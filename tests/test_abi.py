@@ -40,7 +40,28 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert smla.sparse_mla_abi_version() == 2  # 2: sparse_mla_wo_a; the item order in the workspace
+    # 2: sparse_mla_wo_a, the item order in the workspace; 3: the debug build's error word
+    assert smla.sparse_mla_abi_version() == 3
+
+
+def test_debug_build_exports_the_same_symbols_and_says_so(lib):
+    dbg = _lib.load_debug()
+    for n in declared_functions():
+        assert hasattr(dbg, n), n
+    assert lib.sparse_mla_debug_checks() == 0 and dbg.sparse_mla_debug_checks() == 1
+    assert dbg.sparse_mla_abi_version() == lib.sparse_mla_abi_version()
+    # the debug build rejects bad arguments exactly as the production build does
+    p = good(h_q=65)
+    assert dbg.sparse_mla_fwd(*([FAKE] * 9), ctypes.byref(p)) == smla.SMLA_ERR_SHAPE
+
+
+def test_debug_word_constants_match_header():
+    text = open(os.path.join(ROOT, "include", "smla.h")).read()
+    for name, val in (("SMLA_DEBUG_WORD_OFFSET", _lib.SMLA_DEBUG_WORD_OFFSET),
+                      ("SMLA_DEBUG_BAD_INDEX", _lib.SMLA_DEBUG_BAD_INDEX),
+                      ("SMLA_DEBUG_BAD_SCALE", _lib.SMLA_DEBUG_BAD_SCALE)):
+        m = re.search(r"#define " + name + r" (\d+)u?", text)
+        assert m and int(m.group(1)) == val, name
 
 
 def test_struct_layout_matches_header():

@@ -109,3 +109,26 @@ def test_inserted_rows_feed_the_step():
     att["indices"][:, :64] = rows[None, :]
     st = compare(run_gpu(att), run_oracle(att))
     print("end-to-end", st, flush=True)
+
+
+@pytest.mark.parametrize("tiny", [1e-36, 1e-30])
+def test_tiny_norm_rows_feed_the_step(tiny):
+    # Rows whose first blocks are tiny (norm weight ~1e-36 on dims 0..95): the insert codes
+    # them at its exponent floor (10), the smallest scale the step decodes exactly; the
+    # step then attends over index rows made of nothing but these rows, so its output is
+    # a mix of them, and must match the oracle on the same pool bytes.
+    att = inputs.make("decode_sq64", seed=58, s_q=6)
+    c = inputs.make_insert("insert_decode_sq64", seed=59)
+    c["norm_w"][:96] = (c["norm_w"][:96] * np.float32(tiny)).astype(np.float32)
+    c["kv_pool"], c["kv_scales"] = att["kv_pool"], att["kv_scales"]
+    gp, gs = check(c)
+    rows = (c["positions"] % c["n_swa"]).astype(np.int32)
+    assert int(gs[rows, :3].min()) >= 10
+    if tiny < 1e-35:
+        assert (gs[rows, :3] == 10).any()
+    att["kv_pool"], att["kv_scales"] = gp, gs
+    att["indices"][:, :] = -1
+    att["indices"][:, :64] = rows[None, :]
+    att["indices"][:, 200:264] = rows[None, ::-1]
+    st = compare(run_gpu(att), run_oracle(att))
+    print("tiny-norm rows end to end", tiny, st, flush=True)

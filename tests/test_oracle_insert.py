@@ -2,7 +2,8 @@
 
 Independent references: torch.nn.functional.rms_norm in fp64 (library routine), the
 rotation written as complex multiplication, torch's CPU float8_e4m3fn cast (library
-routine), and the definition of the minimal power-of-two block scale.  A plausible
+routine), and the definition of the minimal power-of-two block scale, floored at 2^(10-127)
+(the smallest exponent the step decodes exactly).  A plausible
 mistake anywhere -- RoPE before the norm, a flipped rotation, a dropped weight, the
 wrong row, a wrong exponent -- moves a dequantized value by far more than half an E4M3
 step, or a code away from the library's cast, and fails here.
@@ -45,7 +46,7 @@ def _case(seed, n, n_rows=4096, n_swa=1024, r=64, w_scale=1.0):
     return kv, positions, w.astype(np.float32), pool, sc, n_swa, r
 
 
-@pytest.mark.parametrize("r,w_scale", [(64, 1.0), (0, 1.0), (512, 1.0), (16, 3e-20), (64, 5e25)])
+@pytest.mark.parametrize("r,w_scale", [(64, 1.0), (0, 1.0), (512, 1.0), (16, 3e-20), (64, 5e25), (64, 1e-36)])
 def test_insert_against_library_pipeline(oracle_mod, r, w_scale):
     kv, pos, w, pool, sc, n_swa, r = _case(30 + r, 40, r=r, w_scale=w_scale)
     eps, theta = 1e-6, 1e4
@@ -56,11 +57,14 @@ def test_insert_against_library_pipeline(oracle_mod, r, w_scale):
     assert np.array_equal(got_pool[other], pool[other]) and np.array_equal(got_sc[other], sc[other])
     y = _ref_rows(kv, pos, w, eps, theta, r)
     blocks = np.abs(y).reshape(len(pos), 16, 32).max(axis=2)
-    # exponent: the smallest e with 448 * 2^(e-127) >= amax (decided by the definition)
+    # exponent: the smallest e >= 10 with 448 * 2^(e-127) >= amax (decided by the definition)
     e = np.ceil(np.log2(blocks / 448.0)).astype(np.int64) + 127
-    e = np.clip(e, 0, 254)
-    assert (448.0 * np.exp2(e - 127.0) >= blocks).all() and (448.0 * np.exp2(e - 128.0) < blocks).all()
+    e = np.clip(e, 10, 254)
+    assert (448.0 * np.exp2(e - 127.0) >= blocks).all()
+    assert ((448.0 * np.exp2(e - 128.0) < blocks) | (e == 10)).all()
     assert np.array_equal(got_sc[rows].astype(np.int64), e)
+    if w_scale < 1e-30:
+        assert (e == 10).any()  # the floor is exercised
     # codes: within half an E4M3 step of the exact scaled value ...
     scaled = y * np.exp2(127.0 - np.repeat(e, 32, axis=1))
     deq = torch.from_numpy(got_pool[rows].copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
@@ -97,6 +101,6 @@ def test_insert_zero_row(oracle_mod):
     kv[1] = 0x8000  # -0.0 in bf16
     got_pool, got_sc = oracle_mod.kv_insert(kv, pos, w, pool, sc, n_swa=n_swa, eps=1e-6, theta=1e4, rope_dim=0)
     rows = pos % n_swa
-    assert (got_sc[rows] == 0).all()
+    assert (got_sc[rows] == 10).all()  # the exponent floor
     # y = x * inv * w: the sign of zero follows x and w (w > 0 here)
     assert (got_pool[rows[0]] == 0x00).all() and (got_pool[rows[1]] == 0x80).all()
