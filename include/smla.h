@@ -130,6 +130,37 @@ int sparse_mla_fwd(const void* q, const void* kv_pool, const uint8_t* kv_scales,
                    const smla_params* params);
 
 /*
+ * Allocation-free variant of sparse_mla_fwd, for callers that cannot allocate device memory
+ * or pass a workspace: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, layouts, results and errors as sparse_mla_fwd, except
+ * that params->workspace and workspace_bytes are ignored: the scratch (scheduler counters,
+ * item order, split partials) is a static device array of SMLA_NOALLOC_SCRATCH_BYTES that
+ * each GPU the library runs on holds until the process ends.  The call allocates nothing
+ * and calls no allocating routine.
+ *
+ * The split count is sparse_mla_fwd's for the same params when that call's scratch fits the
+ * array; with num_splits = 0 a split call too large for it runs unsplit (one split) instead
+ * (sparse_mla_noalloc_num_splits returns the count used).  A call whose scratch cannot fit
+ * (an explicit num_splits too large for the array, or more than about 8.9 M tokens) returns
+ * SMLA_ERR_VALUE with nothing launched.  The array's scheduler counters are zero when the
+ * library loads and every call leaves them zero.
+ *
+ * All calls on one GPU share its array: calls that overlap in time on one GPU (on different
+ * streams, or from different threads) race and must not be made; successive calls on one
+ * stream are fine.  In the debug build the error word sits at byte SMLA_DEBUG_WORD_OFFSET
+ * of the array, where the caller cannot read it.
+ */
+#define SMLA_NOALLOC_SCRATCH_BYTES (34u << 20)
+int sparse_mla_fwd_noalloc(const void* q, const void* kv_pool, const uint8_t* kv_scales,
+                           const int32_t* indices, const int32_t* topk_length, const int32_t* positions,
+                           const float* norm_w, uint8_t* out_fp8, uint8_t* out_scales,
+                           const smla_params* params);
+
+/* Splits per token sparse_mla_fwd_noalloc uses for these parameters (>= 1), or 0 for
+   parameters it would reject. */
+int sparse_mla_noalloc_num_splits(const smla_params* params);
+
+/*
  * Bytes of device workspace sparse_mla_fwd needs for these parameters: 256 bytes of
  * scheduler state, then either 4 * s_q bytes rounded up to 256 (the order in which an
  * unsplit call takes its tokens) or, when the call is split, the split partials (0 when

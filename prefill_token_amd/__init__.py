@@ -20,7 +20,7 @@ from ._lib import (SMLA_ERR_HIP, SMLA_ERR_NULL, SMLA_ERR_SHAPE, SMLA_ERR_VALUE, 
 
 __all__ = [
     "sparse_mla_fwd", "sparse_mla_workspace_size", "sparse_mla_num_splits", "sparse_mla_last_error",
-    "sparse_mla_abi_version", "sparse_mla_kv_insert", "sparse_mla_build_index", "sparse_mla_wo_a", "make_params",
+    "sparse_mla_abi_version", "sparse_mla_fwd_noalloc", "sparse_mla_noalloc_num_splits", "sparse_mla_kv_insert", "sparse_mla_build_index", "sparse_mla_wo_a", "make_params",
     "make_kv_insert_params", "make_index_params", "SmlaParams", "SmlaKvInsertParams", "SmlaIndexParams", "SmlaError",
     "LibraryMissing",
     "SMLA_OK", "SMLA_ERR_NULL", "SMLA_ERR_SHAPE", "SMLA_ERR_VALUE", "SMLA_ERR_HIP",
@@ -118,6 +118,68 @@ def sparse_mla_abi_version() -> int:
     return int(_lib.load().sparse_mla_abi_version())
 
 
+def sparse_mla_noalloc_num_splits(params: SmlaParams) -> int:
+    return int(_lib.load().sparse_mla_noalloc_num_splits(ctypes.byref(params)))
+
+
+def _check_fwd(fn, q, kv_pool, kv_scales, indices, topk_length, positions, norm_w, out_fp8, out_scales, out_f32,
+               workspace):
+    """Checks shared by sparse_mla_fwd and its allocation-free variant; returns
+    (s_q, h_q, d, topk, n_rows, kv_format)."""
+    torch, codes = _dtypes()
+    ck = _Checker(fn)
+    ck("q", q, (torch.bfloat16,), ndim=3)
+    s_q, h_q, d = q.shape
+    ck("kv_pool", kv_pool, (torch.bfloat16,) + codes, ndim=2)
+    n_rows = kv_pool.shape[0]
+    if kv_pool.shape[1] != d:
+        raise ValueError(f"{fn}: kv_pool rows must have d = {d} elements (got {kv_pool.shape[1]})")
+    bf16_pool = kv_pool.dtype == torch.bfloat16
+    kv_format = SMLA_KV_BF16 if bf16_pool else SMLA_KV_E4M3_UE8M0
+    if bf16_pool:
+        if kv_scales is not None:
+            raise ValueError(f"{fn}: kv_scales must be None for a bf16 pool")
+    else:
+        if d % 32:
+            raise ValueError(f"{fn}: d must be a multiple of 32 (got {d})")
+        ck("kv_scales", kv_scales, (torch.uint8,), shape=(n_rows, d // 32))
+    ck("indices", indices, (torch.int32,), ndim=2)
+    if indices.shape[0] != s_q:
+        raise ValueError(f"{fn}: indices must have {s_q} rows (got {indices.shape[0]})")
+    topk = indices.shape[1]
+    ck("topk_length", topk_length, (torch.int32,), shape=(s_q,))
+    ck("positions", positions, (torch.int32,), shape=(s_q,))
+    ck("norm_w", norm_w, (torch.float32,), shape=(d,))
+    ck("out_fp8", out_fp8, codes, shape=(s_q, h_q, d))
+    ck("out_scales", out_scales, (torch.uint8,), shape=(s_q, h_q, d // 32))
+    ck("out_f32", out_f32, (torch.float32,), shape=(s_q, h_q, d), optional=True)
+    ck("workspace", workspace, (torch.uint8,), ndim=1, optional=True)
+    ck.done()
+    return s_q, h_q, d, topk, n_rows, kv_format
+
+
+def sparse_mla_fwd_noalloc(q, kv_pool, kv_scales, indices, topk_length, positions, norm_w, out_fp8, out_scales, *,
+                           sm_scale: float, rope_dim: int, eps: float = 1e-6, theta: float = 1e4, out_f32=None,
+                           num_splits: int = 0, stream=None) -> None:
+    """sparse_mla_fwd without a workspace: the scratch is the library's static device array
+    (for callers that cannot allocate, e.g. under graph capture).  Calls that overlap in
+    time on one GPU race.  Raises SmlaError on failure."""
+    torch, _ = _dtypes()
+    s_q, h_q, d, topk, n_rows, kv_format = _check_fwd("sparse_mla_fwd_noalloc", q, kv_pool, kv_scales, indices,
+                                                      topk_length, positions, norm_w, out_fp8, out_scales, out_f32,
+                                                      None)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    params = make_params(s_q=s_q, h_q=h_q, d=d, rope_dim=rope_dim, topk=topk, n_rows=n_rows,
+                         kv_format=kv_format, sm_scale=sm_scale, eps=eps, theta=theta, num_splits=num_splits,
+                         out_f32=out_f32, stream=stream)
+    rc = _lib.load().sparse_mla_fwd_noalloc(_ptr(q), _ptr(kv_pool), _ptr(kv_scales), _ptr(indices),
+                                            _ptr(topk_length), _ptr(positions), _ptr(norm_w), _ptr(out_fp8),
+                                            _ptr(out_scales), ctypes.byref(params))
+    if rc != SMLA_OK:
+        raise SmlaError(rc, last_error(), "sparse_mla_fwd_noalloc")
+
+
 def sparse_mla_fwd(q, kv_pool, kv_scales, indices, topk_length, positions, norm_w, out_fp8, out_scales, *,
                    sm_scale: float, rope_dim: int, eps: float = 1e-6, theta: float = 1e4, out_f32=None,
                    workspace=None, num_splits: int = 0, stream=None) -> None:
@@ -132,35 +194,9 @@ def sparse_mla_fwd(q, kv_pool, kv_scales, indices, topk_length, positions, norm_
     allocated here, zero-filled, when none is given.  Calls sharing a workspace must not
     overlap.  Raises SmlaError with the library's message on failure.
     """
-    torch, codes = _dtypes()
-    ck = _Checker("sparse_mla_fwd")
-    ck("q", q, (torch.bfloat16,), ndim=3)
-    s_q, h_q, d = q.shape
-    ck("kv_pool", kv_pool, (torch.bfloat16,) + codes, ndim=2)
-    n_rows = kv_pool.shape[0]
-    if kv_pool.shape[1] != d:
-        raise ValueError(f"sparse_mla_fwd: kv_pool rows must have d = {d} elements (got {kv_pool.shape[1]})")
-    bf16_pool = kv_pool.dtype == torch.bfloat16
-    kv_format = SMLA_KV_BF16 if bf16_pool else SMLA_KV_E4M3_UE8M0
-    if bf16_pool:
-        if kv_scales is not None:
-            raise ValueError("sparse_mla_fwd: kv_scales must be None for a bf16 pool")
-    else:
-        if d % 32:
-            raise ValueError(f"sparse_mla_fwd: d must be a multiple of 32 (got {d})")
-        ck("kv_scales", kv_scales, (torch.uint8,), shape=(n_rows, d // 32))
-    ck("indices", indices, (torch.int32,), ndim=2)
-    if indices.shape[0] != s_q:
-        raise ValueError(f"sparse_mla_fwd: indices must have {s_q} rows (got {indices.shape[0]})")
-    topk = indices.shape[1]
-    ck("topk_length", topk_length, (torch.int32,), shape=(s_q,))
-    ck("positions", positions, (torch.int32,), shape=(s_q,))
-    ck("norm_w", norm_w, (torch.float32,), shape=(d,))
-    ck("out_fp8", out_fp8, codes, shape=(s_q, h_q, d))
-    ck("out_scales", out_scales, (torch.uint8,), shape=(s_q, h_q, d // 32))
-    ck("out_f32", out_f32, (torch.float32,), shape=(s_q, h_q, d), optional=True)
-    ck("workspace", workspace, (torch.uint8,), ndim=1, optional=True)
-    ck.done()
+    torch, _ = _dtypes()
+    s_q, h_q, d, topk, n_rows, kv_format = _check_fwd("sparse_mla_fwd", q, kv_pool, kv_scales, indices, topk_length,
+                                                      positions, norm_w, out_fp8, out_scales, out_f32, workspace)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     elif workspace is None:

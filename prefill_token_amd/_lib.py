@@ -8,6 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsmla.so")
 DEBUG_LIB_PATH = os.path.join(HERE, "libsmla_debug.so")
 
+SMLA_NOALLOC_SCRATCH_BYTES = 34 << 20
 SMLA_DEBUG_WORD_OFFSET = 8
 SMLA_DEBUG_BAD_INDEX = 1
 SMLA_DEBUG_BAD_SCALE = 2
@@ -120,6 +121,10 @@ def _open(path: str) -> ctypes.CDLL:
     lib.sparse_mla_abi_version.argtypes = []
     lib.sparse_mla_debug_checks.restype = ctypes.c_int
     lib.sparse_mla_debug_checks.argtypes = []
+    lib.sparse_mla_fwd_noalloc.restype = ctypes.c_int
+    lib.sparse_mla_fwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, ctypes.POINTER(SmlaParams)]
+    lib.sparse_mla_noalloc_num_splits.restype = ctypes.c_int
+    lib.sparse_mla_noalloc_num_splits.argtypes = [ctypes.POINTER(SmlaParams)]
     return lib
 
 

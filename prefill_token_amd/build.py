@@ -19,7 +19,8 @@ DEBUG_LIB_PATH = os.path.join(HERE, "libsmla_debug.so")
 PROBE_LIB_PATH = os.path.join(HERE, "libsmla_probe.so")  # measured MFMA ceilings for bench.py
 
 SOURCES = [os.path.join(CSRC, "smla_kernels.hip"), os.path.join(CSRC, "kv_insert.hip"),
-           os.path.join(CSRC, "index_build.hip"), os.path.join(CSRC, "wo_a.hip"), os.path.join(CSRC, "smla_api.cpp")]
+           os.path.join(CSRC, "index_build.hip"), os.path.join(CSRC, "wo_a.hip"), os.path.join(CSRC, "noalloc.hip"),
+           os.path.join(CSRC, "smla_api.cpp")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -90,6 +90,16 @@ size_t workspace_bytes_for(const smla_params* p, int ns) {
   return smla::kSchedBytes + rest;
 }
 
+// Split count of the allocation-free variant: the automatic (or given) count when its
+// scratch fits the static array; with num_splits = 0 and a split call too large for it,
+// one split (whose scratch is the scheduler state and the item order); 0 if nothing fits.
+int noalloc_splits(const smla_params* p) {
+  int ns = choose_splits(p);
+  if (workspace_bytes_for(p, ns) <= (size_t)SMLA_NOALLOC_SCRATCH_BYTES) return ns;
+  if (p->num_splits != 0) return 0;
+  return workspace_bytes_for(p, 1) <= (size_t)SMLA_NOALLOC_SCRATCH_BYTES ? 1 : 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -116,13 +126,15 @@ size_t sparse_mla_workspace_size(const smla_params* p) {
   return workspace_bytes_for(p, choose_splits(p));
 }
 
-int sparse_mla_fwd(const void* q, const void* kv_pool, const uint8_t* kv_scales, const int32_t* indices,
-                   const int32_t* topk_length, const int32_t* positions, const float* norm_w, uint8_t* out_fp8,
-                   uint8_t* out_scales, const smla_params* p) {
-  g_last_error.clear();
-  int rc = check_params(p);
-  if (rc != SMLA_OK) return rc;
-  if (p->s_q == 0) return SMLA_OK;
+}  // extern "C"
+
+namespace {
+
+// Argument checks of sparse_mla_fwd (and its allocation-free variant) that need the array
+// pointers: SMLA_OK or an error code with the message set.
+int check_fwd_arrays(const void* q, const void* kv_pool, const uint8_t* kv_scales, const int32_t* indices,
+                     const int32_t* topk_length, const int32_t* positions, const float* norm_w,
+                     const uint8_t* out_fp8, const uint8_t* out_scales, const smla_params* p) {
   if (!q || !kv_pool || !positions || !norm_w || !out_fp8 || !out_scales || !topk_length)
     return fail(SMLA_ERR_NULL, "a required array pointer is NULL");
   if (p->topk > 0 && !indices) return fail(SMLA_ERR_NULL, "indices is NULL");
@@ -134,16 +146,17 @@ int sparse_mla_fwd(const void* q, const void* kv_pool, const uint8_t* kv_scales,
     uintptr_t align;
     const char* name;
   } al[] = {{q, 16, "q"}, {kv_pool, 16, "kv_pool"}, {kv_scales, 4, "kv_scales"}, {norm_w, 16, "norm_w"},
-            {out_fp8, 16, "out_fp8"}, {p->out_f32, 16, "out_f32"}, {p->workspace, 16, "workspace"}};
+            {out_fp8, 16, "out_fp8"}, {p->out_f32, 16, "out_f32"}};
   for (const auto& x : al)
     if (reinterpret_cast<uintptr_t>(x.ptr) % x.align != 0)
       return fail(SMLA_ERR_VALUE, "%s must be %u-byte aligned", x.name, (unsigned)x.align);
-  const int ns = choose_splits(p);
-  const size_t need = workspace_bytes_for(p, ns);
-  if (need > 0 && (!p->workspace || p->workspace_bytes < need))
-    return fail(SMLA_ERR_VALUE, "workspace of %zu bytes needed (got %zu)", need,
-                p->workspace ? p->workspace_bytes : (size_t)0);
+  return SMLA_OK;
+}
 
+// Enqueue the step with the given scratch buffer and split count.
+int launch_fwd(const void* q, const void* kv_pool, const uint8_t* kv_scales, const int32_t* indices,
+               const int32_t* topk_length, const int32_t* positions, const float* norm_w, uint8_t* out_fp8,
+               uint8_t* out_scales, const smla_params* p, void* workspace, int ns) {
   smla::LaunchArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.kv_pool = kv_pool;
@@ -155,7 +168,7 @@ int sparse_mla_fwd(const void* q, const void* kv_pool, const uint8_t* kv_scales,
   a.out_fp8 = out_fp8;
   a.out_scales = out_scales;
   a.out_f32 = p->out_f32;
-  a.workspace = p->workspace;
+  a.workspace = workspace;
   a.s_q = p->s_q;
   a.h_q = p->h_q;
   a.d = p->d;
@@ -171,6 +184,55 @@ int sparse_mla_fwd(const void* q, const void* kv_pool, const uint8_t* kv_scales,
   const hipError_t e = smla::launch(a);
   if (e != hipSuccess) return fail(SMLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return SMLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sparse_mla_fwd(const void* q, const void* kv_pool, const uint8_t* kv_scales, const int32_t* indices,
+                   const int32_t* topk_length, const int32_t* positions, const float* norm_w, uint8_t* out_fp8,
+                   uint8_t* out_scales, const smla_params* p) {
+  g_last_error.clear();
+  int rc = check_params(p);
+  if (rc != SMLA_OK) return rc;
+  if (p->s_q == 0) return SMLA_OK;
+  rc = check_fwd_arrays(q, kv_pool, kv_scales, indices, topk_length, positions, norm_w, out_fp8, out_scales, p);
+  if (rc != SMLA_OK) return rc;
+  if (reinterpret_cast<uintptr_t>(p->workspace) % 16 != 0) return fail(SMLA_ERR_VALUE, "workspace must be 16-byte aligned");
+  const int ns = choose_splits(p);
+  const size_t need = workspace_bytes_for(p, ns);
+  if (need > 0 && (!p->workspace || p->workspace_bytes < need))
+    return fail(SMLA_ERR_VALUE, "workspace of %zu bytes needed (got %zu)", need,
+                p->workspace ? p->workspace_bytes : (size_t)0);
+  return launch_fwd(q, kv_pool, kv_scales, indices, topk_length, positions, norm_w, out_fp8, out_scales, p,
+                    p->workspace, ns);
+}
+
+int sparse_mla_fwd_noalloc(const void* q, const void* kv_pool, const uint8_t* kv_scales, const int32_t* indices,
+                           const int32_t* topk_length, const int32_t* positions, const float* norm_w,
+                           uint8_t* out_fp8, uint8_t* out_scales, const smla_params* p) {
+  g_last_error.clear();
+  int rc = check_params(p);
+  if (rc != SMLA_OK) return rc;
+  if (p->s_q == 0) return SMLA_OK;
+  rc = check_fwd_arrays(q, kv_pool, kv_scales, indices, topk_length, positions, norm_w, out_fp8, out_scales, p);
+  if (rc != SMLA_OK) return rc;
+  const int ns = noalloc_splits(p);
+  if (ns == 0)
+    return fail(SMLA_ERR_VALUE, "this call needs %zu bytes of scratch; the static scratch holds %zu",
+                workspace_bytes_for(p, p->num_splits > 0 ? choose_splits(p) : 1),
+                (size_t)SMLA_NOALLOC_SCRATCH_BYTES);
+  void* scratch = nullptr;
+  const hipError_t e = smla::noalloc_scratch(&scratch);
+  if (e != hipSuccess) return fail(SMLA_ERR_HIP, "static scratch lookup failed: %s", hipGetErrorString(e));
+  return launch_fwd(q, kv_pool, kv_scales, indices, topk_length, positions, norm_w, out_fp8, out_scales, p,
+                    scratch, ns);
+}
+
+int sparse_mla_noalloc_num_splits(const smla_params* p) {
+  if (check_params(p) != SMLA_OK) return 0;
+  return noalloc_splits(p);
 }
 
 int sparse_mla_kv_insert(const void* kv, const int32_t* positions, const float* norm_w, uint8_t* kv_pool,

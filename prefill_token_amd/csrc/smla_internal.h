@@ -44,6 +44,10 @@ inline size_t partial_floats(int, int d) { return (size_t)64 * (size_t)(d + 2); 
 // Enqueue the step; returns the HIP error of the first failed launch (hipSuccess if none).
 hipError_t launch(const LaunchArgs& a);
 
+// Device address of the allocation-free entry point's static scratch on the current device
+// (looked up once per device).
+hipError_t noalloc_scratch(void** ptr);
+
 // Compute units of the current device (256 if it cannot be queried).
 int device_cus();
 

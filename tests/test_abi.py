@@ -338,3 +338,36 @@ def test_wo_a_null_and_misaligned(lib, which):
 def test_wo_a_null_params_and_empty(lib):
     assert lib.sparse_mla_wo_a(*([FAKE] * 5), None) == smla.SMLA_ERR_NULL
     assert lib.sparse_mla_wo_a(*([None] * 5), ctypes.byref(good_wo_a(s_q=0))) == smla.SMLA_OK
+
+
+# ---------------------------------------------------------------- allocation-free variant
+
+
+def test_noalloc_split_choice_and_limits(lib):
+    scratch = _lib.SMLA_NOALLOC_SCRATCH_BYTES
+    for s_q in (1, 4, 16, 32, 64, 96, 129, 2123):
+        p = good(s_q=s_q)
+        ns = smla.sparse_mla_num_splits(p)
+        # the same count as sparse_mla_fwd whenever that call's scratch fits the static array
+        assert smla.sparse_mla_workspace_size(p) <= scratch
+        assert lib.sparse_mla_noalloc_num_splits(ctypes.byref(p)) == ns
+    # an explicit split count whose partials cannot fit is rejected before any HIP call
+    p = good(s_q=300, num_splits=4)
+    assert smla.sparse_mla_workspace_size(p) > scratch
+    assert lib.sparse_mla_noalloc_num_splits(ctypes.byref(p)) == 0
+    assert lib.sparse_mla_fwd_noalloc(*([FAKE] * 9), ctypes.byref(p)) == smla.SMLA_ERR_VALUE
+    assert "static scratch" in smla.sparse_mla_last_error()
+    # the same argument checks as sparse_mla_fwd
+    assert lib.sparse_mla_fwd_noalloc(*([FAKE] * 9), ctypes.byref(good(h_q=65))) == smla.SMLA_ERR_SHAPE
+    ptrs = [FAKE] * 9
+    ptrs[0] = None
+    assert lib.sparse_mla_fwd_noalloc(*ptrs, ctypes.byref(good())) == smla.SMLA_ERR_NULL
+    ptrs[0] = FAKE + 8
+    assert lib.sparse_mla_fwd_noalloc(*ptrs, ctypes.byref(good())) == smla.SMLA_ERR_VALUE
+    assert lib.sparse_mla_fwd_noalloc(*([None] * 9), ctypes.byref(good(s_q=0))) == smla.SMLA_OK
+
+
+def test_noalloc_scratch_constant_matches_header():
+    text = open(os.path.join(ROOT, "include", "smla.h")).read()
+    m = re.search(r"#define SMLA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.SMLA_NOALLOC_SCRATCH_BYTES
