@@ -1103,22 +1103,26 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
 //   QK waves (w = 0..3, head group qa = w & 1, row half qc = w >> 1) hold q for their
 //     32 heads over all 512 dims in VGPRs and compute S^T[32 rows][32 heads] of a tile
 //     with 16 scaled E4M3 MFMAs, then the softmax of that block.
-//   P.V waves (w = 4..7) own output dims [128v, 128v + 128) for all 64 heads and a
-//     private bf16 V tile Vt[128 dims][64 slots].  In each k-step of 16 slots they issue
-//     the 8 MFMAs of the previous tile and dequantize the same 16 slots of the current
-//     tile into Vt, interleaved so that the conversion runs under the MFMAs.
-// Iteration i: QK waves compute S and P of tile i, P.V waves P.V of tile i - 1 and the V
-// tile of tile i; one barrier per iteration.  The softmax is taken against the running
-// max of the previous tiles: a QK wave flags its head group when its block max exceeds
-// that max by more than 2^8.  The flags are read after the barrier; if any is set
-// (always on the first tile), the QK waves merge the block maxima of both row halves,
-// raise the running max, rewrite P from the scores they still hold and publish the
-// accumulator rescale, and a second barrier lets the P.V waves go on.  The running max
-// is therefore the same lazily raised max as in the generic kernel.
+//   P.V waves (w = 4..7) own output dims [128v, 128v + 128) for all 64 heads.  They take
+//     V straight from the raw E4M3 rows: one scaled E4M3 MFMA of 32 rows x 64 dims against
+//     an identity operand yields a 32 x 32 block of V dequantized exactly and transposed
+//     (lane = dim, registers = slots), which, packed to bf16, is the A operand of the
+//     P.V MFMAs; the P.V contraction visits the slots in that register order and the QK
+//     waves store P in the same order (details at the P.V iteration below).  They also
+//     issue all row DMA of the next tile.
+// Iteration i: QK waves compute S and P of tile i, P.V waves P.V of tile i - 1 and the DMA
+// of tile i + 1 (three raw tile buffers); one barrier per iteration.  The softmax is taken
+// against the running max of the previous tiles: a QK wave flags its head group when its
+// block max exceeds that max by more than 2^8.  The flags are read after the barrier; if
+// any is set (always on the first tile), the QK waves merge the block maxima of both row
+// halves, raise the running max, rewrite P from the scores they still hold and publish
+// the accumulator rescale, and a second barrier lets the P.V waves go on.  The running
+// max is therefore the same lazily raised max as in the generic kernel.
 // Between items: the P.V waves run the epilogue of the finished item straight from their
 // registers (their MFMAs produce O^T, so a head's 32-dim block sits in one lane pair),
 // while the QK waves issue the next item's first tile DMA and run its q prologue into a
-// q tile over the V-tile area, from which they then load their fragments.
+// q tile over the second and third raw tile buffers, from which they then load their
+// fragments.
 struct WsCfg {
   static constexpr int kD = 512, kEB = 1;
   static constexpr int D = kD;
@@ -1126,20 +1130,22 @@ struct WsCfg {
   static constexpr int GS = 1024 + 16 * G;
   static constexpr int RAW_BYTES = (T / G) * GS;
   static constexpr int SC_BYTES = T * NSB;
-  static constexpr int VW = 128;                    // dims per P.V wave
-  static constexpr int VTW_BYTES = VW * T * 2;      // one P.V wave's Vt
   static constexpr int P_BYTES = HP * T * 2;
+  // three raw tiles (and their scale rows): tile i in buffer i mod 3, so that the QK waves
+  // read tile i, the P.V waves tile i - 1 and the DMA fills tile i + 1 at once
   static constexpr int OFF_RAW0 = 0;
   static constexpr int OFF_RAW1 = RAW_BYTES;
-  static constexpr int OFF_SC0 = 2 * RAW_BYTES;
+  static constexpr int OFF_RAW2 = 2 * RAW_BYTES;
+  static constexpr int OFF_SC0 = 3 * RAW_BYTES;
   static constexpr int OFF_SC1 = OFF_SC0 + SC_BYTES;
-  static constexpr int OFF_VT = align16(OFF_SC1 + SC_BYTES);
-  static constexpr int OFF_P0 = OFF_VT + 4 * VTW_BYTES;
+  static constexpr int OFF_SC2 = OFF_SC1 + SC_BYTES;
+  static constexpr int OFF_P0 = align16(OFF_SC2 + SC_BYTES);
   static constexpr int OFF_P1 = OFF_P0 + P_BYTES;
   static constexpr int LOOP_END = OFF_P1 + P_BYTES;
   // between items: the q tile [2 terms][HP][512 B] (16-byte chunk c of head h stored at
-  // c ^ (h & 15)) over the V tiles, its UE8M0 scales [2][HP][16] in P0
-  static constexpr int OFF_QT = OFF_VT;
+  // c ^ (h & 15)) over raw tiles 1 and 2 (an item's first tile lands in tile 0), its UE8M0
+  // scales [2][HP][16] in P0
+  static constexpr int OFF_QT = OFF_RAW1;
   static constexpr int OFF_QSC = OFF_P0;
   // small area
   static constexpr int OFF_MAXX = LOOP_END;                // [2 tiles][2 row halves][HP]
@@ -1153,8 +1159,7 @@ struct WsCfg {
   static constexpr int SMEM = OFF_IFREQ + 32 * 8;
   static_assert(G == 2 && NSB == 16, "layout written for 512-byte rows");
   static_assert(SMEM <= 160 * 1024, "LDS budget");
-  static_assert(2 * HP * 512 <= 4 * VTW_BYTES && 2 * HP * 16 <= P_BYTES,
-                "item transition areas");
+  static_assert(2 * HP * 512 <= 2 * RAW_BYTES && 2 * HP * 16 <= P_BYTES, "item transition areas");
 };
 
 __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
@@ -1237,8 +1242,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
       dma4(id >= 0 ? (uint32_t)id * C::NSB + 4 * (f % 4) : kNoRow, scale_rs, dst);
     }
   };
-  auto raw_buf = [&](int i) { return smem + ((i & 1) ? C::OFF_RAW1 : C::OFF_RAW0); };
-  auto sc_buf = [&](int i) { return smem + ((i & 1) ? C::OFF_SC1 : C::OFF_SC0); };
+  // tile i's raw rows and scales in buffer i mod 3 (i >= -1: the P.V waves ask for i - 1)
+  auto raw_buf = [&](int i) {
+    const int b = (i + 3) % 3;
+    return smem + (b == 0 ? C::OFF_RAW0 : (b == 1 ? C::OFF_RAW1 : C::OFF_RAW2));
+  };
+  auto sc_buf = [&](int i) {
+    const int b = (i + 3) % 3;
+    return smem + (b == 0 ? C::OFF_SC0 : (b == 1 ? C::OFF_SC1 : C::OFF_SC2));
+  };
   auto p_buf = [&](int i) { return smem + ((i & 1) ? C::OFF_P1 : C::OFF_P0); };
 
   // ---------------- q prologue of an item (in two steps)
@@ -1547,9 +1559,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
             unsigned char* prow = p_buf(it - 1) + head * 128;
             const int sw = swz(head);
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
-              *reinterpret_cast<uint2*>(prow + 16 * ((4 * qc + g) ^ sw) + 8 * lhalf) =
-                  make_uint2(pack_bf16(p[4 * g], p[4 * g + 1]), pack_bf16(p[4 * g + 2], p[4 * g + 3]));
+            for (int kk = 0; kk < 2; ++kk)
+              *reinterpret_cast<uint4*>(prow + 16 * ((4 * qc + 2 * kk + lhalf) ^ sw)) =
+                  make_uint4(pack_bf16(p[8 * kk], p[8 * kk + 1]), pack_bf16(p[8 * kk + 2], p[8 * kk + 3]),
+                             pack_bf16(p[8 * kk + 4], p[8 * kk + 5]), pack_bf16(p[8 * kk + 6], p[8 * kk + 7]));
             if (qc == 0 && lhalf == 0) alpha_l[head] = alpha;
             if (qc == 0 && lane == 0) flag_l[8 + qa] = raised ? 1 : 0;
             __syncthreads();  // B': P and alpha rewritten
@@ -1584,18 +1597,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
         if (it > 0) check(it);
         const int id_cur = valid_id(I, tile, raw_cur);
         const unsigned long long mask = __ballot(id_cur >= 0);
-        const int id_next = valid_id(I, tile + 1, raw_next);
         const int raw_next2 = fetch_id(I, tile + 2);
 #ifdef SMLA_DEBUG_CHECKS
         if (w == 0)
           debug_flag_tile(a.sched, a.n_rows, tile < I.te && tile * T + lane < I.lcap, raw_cur, id_cur >= 0,
                           sc_buf(it) + C::NSB * lane, C::NSB);
 #endif
-        // the next tile's DMA (the row DMAs queue behind the P.V waves' MFMAs meanwhile)
-        if (it + 1 < n) {
-#pragma unroll
-          for (int k = 0; k <= 4; ++k) dma_part(k, w, id_next, raw_buf(it + 1), sc_buf(it + 1));
-        }
+        // (the next tile's DMA is issued by the P.V waves, whose loop has more slack)
         // the next item's q rows into the L2, two tiles ahead of its prologue (one 128-byte
         // line per load, 64 KB per workgroup; heads >= h_q read nothing).  Issued after
         // this tile's DMA, so the end of this iteration waits for the DMA only.
@@ -1645,14 +1653,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
           unsigned char* prow = p_buf(it) + head * 128;
           const int sw = swz(head);
 #pragma unroll
-          for (int g = 0; g < 4; ++g)
-            *reinterpret_cast<uint2*>(prow + 16 * ((4 * qc + g) ^ sw) + 8 * lhalf) =
-                make_uint2(pack_bf16(p[4 * g], p[4 * g + 1]), pack_bf16(p[4 * g + 2], p[4 * g + 3]));
+          for (int kk = 0; kk < 2; ++kk)
+            *reinterpret_cast<uint4*>(prow + 16 * ((4 * qc + 2 * kk + lhalf) ^ sw)) =
+                make_uint4(pack_bf16(p[8 * kk], p[8 * kk + 1]), pack_bf16(p[8 * kk + 2], p[8 * kk + 3]),
+                           pack_bf16(p[8 * kk + 4], p[8 * kk + 5]), pack_bf16(p[8 * kk + 6], p[8 * kk + 7]));
           if (lhalf == 0) maxx[2 * HP * (it & 1) + qc * HP + head] = lm;
           const bool over = __any(lm > m_run + 8.0f || (mref && lm > -INFINITY && lm < m_run - 64.0f));
           if (lane == 0) flag_l[4 * (it & 1) + w] = over ? 1 : 0;
         }
-        // next tile's DMA from this wave landed (vmcnt(0); vmcnt(2) behind the q touches)
+        // this wave's index loads landed (vmcnt(0); vmcnt(2) behind the q touches)
         if (touch)
           __builtin_amdgcn_s_waitcnt(0x0F72);
         else
@@ -1699,7 +1708,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
   } else {
     // =============================== P.V waves
     const int v = w - 4;
-    unsigned char* vt = smem + C::OFF_VT + v * C::VTW_BYTES;
     int item = blockIdx.x;
     Item I = info(item);
     {
@@ -1729,66 +1737,41 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
           for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
       int raw_next = fetch_id(I, I.tb + 1);
 
-      // one iteration: P.V of tile it - 1 (PV) and / or the V tile of tile it (VT)
-      auto pv_iter = [&](const int it, auto pv_c, auto vt_c) __attribute__((always_inline)) {
-        constexpr bool PV = decltype(pv_c)::value, VT = decltype(vt_c)::value;
+      // One iteration: P.V of tile it - 1 (PV) and / or this wave's DMA parts of tile it + 1
+      // (DM).  V is never written back to LDS: the scaled E4M3 MFMA of the raw rows (A,
+      // with their UE8M0 block scales) against an identity (B, E4M3 1.0, scale 1) gives the
+      // dequantized block exactly in f32, in the MFMA output layout lane = dim, register i
+      // = slot 8 (i >> 2) + 4 lhalf + (i & 3) of a 32-slot half.  The P.V contraction takes
+      // the slots in that order: k-step ks, lane half kg holds slots 16 ks + 4 kg + {0..3}
+      // and 16 ks + 8 + 4 kg + {0..3} (registers 0..7 of the half's output for the even
+      // k-step, 8..15 for the odd one, rounded to bf16, which is exact), and the QK waves
+      // store P in the same order.  So the transposition costs one MFMA per 32 x 32 block and
+      // a bf16 pack per value pair, and no LDS traffic beyond reading the raw rows once.
+      auto pv_iter = [&](const int it, auto pv_c, auto dm_c) __attribute__((always_inline)) {
+        constexpr bool PV = decltype(pv_c)::value, DM = decltype(dm_c)::value;
         const int tile = I.tb + it;
         const int lane = ((int)threadIdx.x + opaque_zero()) & 63, lrow = lane & 31, lhalf = lane >> 5;
         const unsigned char* p_l = p_buf(it - 1);
-        const unsigned char* raw_l = raw_buf(it);
-        const unsigned char* sc_l = sc_buf(it);
-        // Address bases.  Row n of Vt (dim) or P (head) is 128 bytes, its 16-byte chunk ch
-        // stored at chunk ch ^ swz(n).  For the P.V reads n = 32b + lrow (b = n-block or
-        // m-block) and ch = 2ks + lhalf, so the stored chunk is nu ^ (2ks ^ kb(b)) with the
-        // lane part nu = swz(lrow) ^ lhalf and kb(b) = 4(b & 1) ^ (b >> 1): eight lane offsets
-        // rd[c] = 128 lrow + 16 (nu ^ c) cover every read, the rest is an immediate.
+        const unsigned char* raw_l = raw_buf(it - 1);
+        const unsigned char* sc_l = sc_buf(it - 1);
+        // P rows (heads) are 128 bytes, 16-byte chunk ch stored at ch ^ swz(head); for head
+        // 32 mb + lrow and ch = 2 ks + lhalf that is nu ^ 2ks ^ 4mb (nu = swz(lrow) ^ lhalf)
         const int nu = (lrow & 7) ^ (lrow >> 3) ^ lhalf;
         uint32_t rd[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) rd[c] = 128 * lrow + 16 * (nu ^ c);
-        // V tile roles: lane = 8c' + j converts rows 16ks + 2j, 16ks + 2j + 1 (one DMA group,
-        // adjacent 16-byte pieces) of chunk 8v + c' (tile dims 16c' .. 16c' + 15 of this
-        // wave).  Dim n = 16c' + e takes the two slots at chunk 2ks + (j >> 2) of its row,
-        // stored at chunk lam ^ (2ks ^ E(e)) with lam = K0(c') ^ (j >> 2), K0(c') = (2c' ^
-        // (c' >> 2)) & 7, E(e) = (e & 7) ^ (e >> 3): lane offsets wr0 + 16 (lam ^ c), plus 128 e.
-        const int j = lane & 7, cl = lane >> 3;
-        const int lam = ((2 * cl) ^ (cl >> 2) ^ (j >> 2)) & 7;
-        const uint32_t wr0 = 2048 * cl + 4 * (j & 3);
-        const uint32_t rsrc = (uint32_t)(j * C::GS + 32 * cl);  // + group 8ks, + chunk 8v
-        const uint32_t ssrc = (uint32_t)(32 * j);               // + 256 ks + 4v
         const int raw_next2 = fetch_id(I, tile + 2);
-        // operands double-buffered by k-step parity: the reads of k-step ks + 1 go out at
-        // the start of k-step ks, a full k-step of MFMAs ahead of their use
-        bf16x8 Ap[2][2], Bv[2][4];
-        uint4 ra[2], rb[2];
-        uint32_t wa[2], wb[2];
-        auto load_p = [&](int ks) {
+        const int id_next = valid_id(I, tile + 1, raw_next);
+        bf16x8 Ap[2][2];  // P of k-steps 2 sh + kk, head blocks mb
+        auto load_p = [&](int sh) {
 #pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-            Ap[ks & 1][mb] = *reinterpret_cast<const bf16x8*>(p_l + 4096 * mb + rd[(2 * ks) ^ (4 * mb)]);
-        };
-        auto load_v = [&](int ks) {
+          for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-          for (int nb = 0; nb < 4; ++nb)
-            Bv[ks & 1][nb] =
-                *reinterpret_cast<const bf16x8*>(vt + 4096 * nb + rd[(2 * ks) ^ (4 * (nb & 1)) ^ (nb >> 1)]);
+            for (int mb = 0; mb < 2; ++mb)
+              Ap[kk][mb] = *reinterpret_cast<const bf16x8*>(p_l + 4096 * mb + rd[(2 * (2 * sh + kk)) ^ (4 * mb)]);
         };
-        auto load_vt = [&](int ks, int u) {
-          const unsigned char* src = raw_l + rsrc + 8 * ks * C::GS + 256 * v;
-          ra[u] = *reinterpret_cast<const uint4*>(src);
-          rb[u] = *reinterpret_cast<const uint4*>(src + 16);
-          const unsigned char* ssp = sc_l + ssrc + 256 * ks + 4 * v;
-          wa[u] = *reinterpret_cast<const uint32_t*>(ssp);
-          wb[u] = *reinterpret_cast<const uint32_t*>(ssp + C::NSB);
-        };
-        // first k-step's operands before the flag check (P is read again if the slow path
-        // rewrites it)
         if constexpr (PV) {
           load_p(0);
-          load_v(0);
-        }
-        if constexpr (VT) load_vt(0, 0);
-        if constexpr (PV) {
           const int4 fl = *reinterpret_cast<const int4*>(flag_l + 4 * ((it - 1) & 1));
           if (__builtin_amdgcn_readfirstlane(fl.x | fl.y | fl.z | fl.w)) {
             __syncthreads();  // B': P and alpha rewritten
@@ -1805,61 +1788,74 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
               }
             }
           }
+          // identity operands: lane (column n = lrow, half h) holds K = 16 h + p (p < 16)
+          // and K = 32 + 16 h + (p - 16) (p >= 16); E4M3 1.0 where K = n (block 0 of the
+          // 64-dim step) or K = 32 + n (block 1)
+          int i4[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int idx = lrow - 16 * lhalf - 4 * q;
+            i4[q] = (idx >= 0 && idx < 4) ? (0x38 << (8 * idx)) : 0;
+          }
+          const i32x8 ilo = {i4[0], i4[1], i4[2], i4[3], 0, 0, 0, 0};
+          const i32x8 ihi = {0, 0, 0, 0, i4[0], i4[1], i4[2], i4[3]};
+          const int unit = 0x7F7F7F7F;
+          __builtin_amdgcn_s_setprio(2);
+#pragma unroll
+          for (int sh = 0; sh < 2; ++sh) {
+            if (sh == 1) load_p(1);
+            // raw rows 32 sh + lrow; their scales of blocks 4v .. 4v + 3, byte j of the word
+            // for lane half h = block 4v + 2j + h (the A scale of k-block h of chunk j)
+            const int r = 32 * sh + lrow;
+            const uint32_t w4 = *reinterpret_cast<const uint32_t*>(sc_l + r * C::NSB + 4 * v);
+            const uint32_t asc = __builtin_amdgcn_perm(w4, w4, lhalf ? 0x07050301u : 0x06040200u);
+            static_for<2>([&](auto kc_c) {
+              constexpr int kc = decltype(kc_c)::value;
+              // this wave's share of the next tile's DMA and that of its SIMD's QK wave
+              // (w - 4): rows 32 (w - 4) + 8 (2 sh + kc) .. + 7 and 128 + ..., scales last
+              if constexpr (DM) {
+                dma_part(2 * sh + kc, w, id_next, raw_buf(it + 1), sc_buf(it + 1));
+                dma_part(2 * sh + kc, w - 4, id_next, raw_buf(it + 1), sc_buf(it + 1));
+                if (sh == 1 && kc == 1) dma_part(4, w - 4, id_next, raw_buf(it + 1), sc_buf(it + 1));
+              }
+              const int ks8 = 2 * v + kc;  // 64-dim step of the row
+              const uint4 lo = *reinterpret_cast<const uint4*>(raw_l + raw_off<C>(r, 4 * ks8 + lhalf));
+              const uint4 hi = *reinterpret_cast<const uint4*>(raw_l + raw_off<C>(r, 4 * ks8 + 2 + lhalf));
+              const i32x8 A = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+              const f32x16 zero = {};
+              f32x16 tv[2];
+              tv[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, ilo, zero, 0, 0, kc, (int)asc, 0, unit);
+              tv[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, ihi, zero, 0, 0, kc, (int)asc, 0, unit);
+#pragma unroll
+              for (int t = 0; t < 2; ++t) {
+                const int nb = 2 * kc + t;
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                  const f32x16& x = tv[t];
+                  // bf16 of exactly representable values (4 significant bits): the RNE pack
+                  // is exact.  (A v_perm of the f32 high halves would be as exact, but the
+                  // compiler folds a perm of two elements of an MFMA result into one.)
+                  const uint32_t b0 = pack_bf16(x[8 * kk], x[8 * kk + 1]);
+                  const uint32_t b1 = pack_bf16(x[8 * kk + 2], x[8 * kk + 3]);
+                  const uint32_t b2 = pack_bf16(x[8 * kk + 4], x[8 * kk + 5]);
+                  const uint32_t b3 = pack_bf16(x[8 * kk + 6], x[8 * kk + 7]);
+                  const bf16x8 bv = __builtin_bit_cast(bf16x8, make_uint4(b0, b1, b2, b3));
+#pragma unroll
+                  for (int mb = 0; mb < 2; ++mb)
+                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv, Ap[kk][mb], acc[mb][nb], 0, 0, 0);
+                }
+              }
+            });
+          }
+          __builtin_amdgcn_s_setprio(0);
+        } else if constexpr (DM) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            dma_part(k, w, id_next, raw_buf(it + 1), sc_buf(it + 1));
+            dma_part(k, w - 4, id_next, raw_buf(it + 1), sc_buf(it + 1));
+          }
+          dma_part(4, w - 4, id_next, raw_buf(it + 1), sc_buf(it + 1));
         }
-        const int id_next = valid_id(I, tile + 1, raw_next);
-        // the k-step loop at raised wave priority: when both waves of a SIMD are ready,
-        // this wave's MFMA / conversion stream goes first (the QK wave is then usually
-        // waiting on its own MFMA chain)
-        __builtin_amdgcn_s_setprio(2);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int u = ks & 1;
-          __builtin_amdgcn_sched_barrier(0);
-          // next k-step's operands first
-          if (VT && ks + 1 < 4) load_vt(ks + 1, u ^ 1);
-          if (PV && ks + 1 < 4) {
-            load_p(ks + 1);
-            load_v(ks + 1);
-          }
-          // one of this wave's row DMAs for the next tile per k-step (zero rows past the
-          // end of the range)
-          if constexpr (VT) dma_part(ks, w, id_next, raw_buf(it + 1), sc_buf(it + 1));
-          if constexpr (PV) {
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-              for (int mb = 0; mb < 2; ++mb)
-                acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Bv[u][nb], Ap[u][mb], acc[mb][nb], 0, 0, 0);
-          }
-          if constexpr (VT) {
-            const int bsh = 8 * (cl >> 1);
-            const float sa = ue8m0_f32((wa[u] >> bsh) & 0xFFu), sb = ue8m0_f32((wb[u] >> bsh) & 0xFFu);
-            const uint4 xa = ra[u], xb = rb[u];
-            const uint32_t pa[8] = {cvt_lo(xa.x, sa), cvt_hi(xa.x, sa), cvt_lo(xa.y, sa), cvt_hi(xa.y, sa),
-                                    cvt_lo(xa.z, sa), cvt_hi(xa.z, sa), cvt_lo(xa.w, sa), cvt_hi(xa.w, sa)};
-            const uint32_t pb[8] = {cvt_lo(xb.x, sb), cvt_hi(xb.x, sb), cvt_lo(xb.y, sb), cvt_hi(xb.y, sb),
-                                    cvt_lo(xb.z, sb), cvt_hi(xb.z, sb), cvt_lo(xb.w, sb), cvt_hi(xb.w, sb)};
-            // (the reads of this k-step's slots were issued before: LDS ops of a wave are
-            // processed in order)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const int k = e >> 1;
-              const uint32_t val = __builtin_amdgcn_perm(pb[k], pa[k], (e & 1) ? 0x07060302u : 0x05040100u);
-              const int c = (2 * ks) ^ (e & 7) ^ (e >> 3);
-              *reinterpret_cast<uint32_t*>(vt + wr0 + 16 * (lam ^ c) + 128 * e) = val;
-            }
-          }
-          if constexpr (PV && VT) {
-            // the conversion and its LDS writes spread between the 8 MFMAs
-#pragma unroll
-            for (int m = 0; m < 8; ++m) {
-              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-              __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
-              __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);  // DS write
-            }
-          }
-        }
-        __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_s_waitcnt(0x0F70);
         raw_next = raw_next2;
         __syncthreads();  // end of iteration
