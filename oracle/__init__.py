@@ -6,7 +6,9 @@ this wrapper loads ``liboracle.so`` built from ``sparse_mla_oracle.c`` by plain 
 
 The functions mirror the steps of the C file (each cites its passage there):
 ``bf16_decode``, ``e4m3_decode``, ``e4m3_encode``, ``ue8m0_exponent``,
-``quantize_blocks``, ``rmsnorm``, ``rope``, the whole step ``sparse_mla``, and the two
+``quantize_blocks``, ``rmsnorm``, ``rope``, the whole step ``sparse_mla`` (and over the
+two-pool nvfp4_ds_mla cache, ``sparse_mla_ds_nvfp4`` with ``e2m1_decode`` /
+``nvfp4_decode``), and the two
 steps before it: the pool-row producer ``kv_insert`` and the index-row builder
 ``build_index`` (plain numpy, below), and the step after it, the output projection
 ``wo_a`` (plain numpy).
@@ -76,6 +78,13 @@ def _load():
     lib.oracle_kv_insert.restype = ctypes.c_int
     lib.oracle_kv_insert.argtypes = [P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_int64, ctypes.c_double, ctypes.c_double, P, P]
+    lib.oracle_e2m1_decode.restype = ctypes.c_double
+    lib.oracle_e2m1_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_sparse_mla_ds_nvfp4.restype = ctypes.c_int
+    lib.oracle_sparse_mla_ds_nvfp4.argtypes = [P, P, P, P, P, P, P, P, P,
+                                               ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                               ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+                                               ctypes.c_double, ctypes.c_double, P, P, P]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     _lib = lib
@@ -106,6 +115,23 @@ def e4m3_encode(x) -> np.ndarray:
     lib = _load()
     v = np.asarray(x, dtype=np.float64)
     return np.array([lib.oracle_e4m3_encode(float(z)) for z in v.ravel()], dtype=np.uint8).reshape(v.shape)
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    """OCP E2M1 (FP4) codes (low 4 bits) -> exact fp64 values."""
+    lib = _load()
+    c = np.asarray(codes, dtype=np.uint8)
+    return np.array([lib.oracle_e2m1_decode(int(x)) for x in c.ravel()], dtype=np.float64).reshape(c.shape)
+
+
+def nvfp4_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Rows of the NVFP4 pool decoded exactly: ``codes`` u8 [..., d/2] (element 2i in the low
+    nibble of byte i), ``scales`` u8 [..., d/16] E4M3: value = e2m1(code) * e4m3(scale)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    nib = np.stack([c & 15, c >> 4], axis=-1).reshape(*c.shape[:-1], 2 * c.shape[-1])
+    lut = e2m1_decode(np.arange(16, dtype=np.uint8))
+    sc = e4m3_decode(np.asarray(scales, dtype=np.uint8))
+    return lut[nib] * np.repeat(sc, 16, axis=-1)
 
 
 def ue8m0_exponent(amax) -> np.ndarray:
@@ -184,6 +210,41 @@ def sparse_mla(q_bits: np.ndarray, kv_pool: np.ndarray, kv_scales: Optional[np.n
                                _ptr(o), _ptr(codes), _ptr(scales))
     if rc != 0:
         raise ValueError(f"oracle_sparse_mla failed with code {rc}")
+    return o, codes, scales
+
+
+def sparse_mla_ds_nvfp4(q_bits: np.ndarray, swa_codes: np.ndarray, swa_scales: np.ndarray, cmp_codes: np.ndarray,
+                        cmp_scales: np.ndarray, indices: np.ndarray, topk_length: np.ndarray,
+                        positions: np.ndarray, norm_w: np.ndarray, *, swa_entries: int, sm_scale: float,
+                        eps: float, theta: float, rope_dim: int):
+    """The step over the two-pool nvfp4_ds_mla cache: entries j < ``swa_entries`` of each index
+    row name rows of the E4M3 + UE8M0 pool (``swa_codes`` u8 [n_swa, d], ``swa_scales`` u8
+    [n_swa, d/32]), the later entries rows of the NVFP4 pool (``cmp_codes`` u8 [n_cmp, d/2],
+    ``cmp_scales`` u8 [n_cmp, d/16]).  Returns ``(o, codes, scales)`` as ``sparse_mla``."""
+    lib = _load()
+    q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
+    s_q, h, d = q_bits.shape
+    sw = np.ascontiguousarray(swa_codes, dtype=np.uint8)
+    ss = np.ascontiguousarray(swa_scales, dtype=np.uint8)
+    cc = np.ascontiguousarray(cmp_codes, dtype=np.uint8)
+    cs = np.ascontiguousarray(cmp_scales, dtype=np.uint8)
+    assert sw.shape[1] == d and ss.shape == (sw.shape[0], d // 32)
+    assert cc.shape[1] == d // 2 and cs.shape == (cc.shape[0], d // 16)
+    indices = np.ascontiguousarray(indices, dtype=np.int32)
+    topk = indices.shape[1] if indices.ndim == 2 else 0
+    topk_length = np.ascontiguousarray(topk_length, dtype=np.int32)
+    positions = np.ascontiguousarray(positions, dtype=np.int32)
+    norm_w = np.ascontiguousarray(norm_w, dtype=np.float64)
+    o = np.zeros((s_q, h, d), dtype=np.float64)
+    codes = np.zeros((s_q, h, d), dtype=np.uint8)
+    scales = np.zeros((s_q, h, d // 32), dtype=np.uint8)
+    rc = lib.oracle_sparse_mla_ds_nvfp4(_ptr(q_bits), _ptr(sw), _ptr(ss), _ptr(cc), _ptr(cs), _ptr(indices),
+                                        _ptr(topk_length), _ptr(positions), _ptr(norm_w), s_q, h, d,
+                                        int(rope_dim), topk, int(swa_entries), sw.shape[0], cc.shape[0],
+                                        float(sm_scale), float(eps), float(theta), _ptr(o), _ptr(codes),
+                                        _ptr(scales))
+    if rc != 0:
+        raise ValueError(f"oracle_sparse_mla_ds_nvfp4 failed with code {rc}")
     return o, codes, scales
 
 

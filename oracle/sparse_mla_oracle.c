@@ -85,6 +85,16 @@ double oracle_e4m3_decode(uint8_t code) {
   return sign ? -v : v;
 }
 
+/*
+ * OCP E2M1 (FP4) code (low 4 bits) -> exact double: sign bit 3, exponent bits 2-1 (bias 1),
+ * mantissa bit 0; exponent 0 is subnormal (m * 0.5).  Magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+ */
+double oracle_e2m1_decode(uint8_t code) {
+  int sign = (code >> 3) & 1, ex = (code >> 1) & 3, man = code & 1;
+  double v = ex == 0 ? 0.5 * man : ldexp(1.0 + 0.5 * man, ex - 1);
+  return sign ? -v : v;
+}
+
 /* ---------------------------------------------------------------- encoders */
 
 /*
@@ -178,30 +188,115 @@ void oracle_rope(double* y, int d, int r, double pos, double base, int direction
 
 /* ---------------------------------------------------------------- the step */
 
+#define KV_DS_NVFP4 2
+
 /*
- * Full step for s_q tokens.
- *   q           bf16 bits [s_q][h][d]
- *   kv_pool     kv_format 0: u8 E4M3 codes [n_rows][d];  1: bf16 bits [n_rows][d]
- *   kv_scales   kv_format 0: u8 UE8M0 [n_rows][d/32];   1: unused (may be NULL)
- *   indices     i32 [s_q][topk] rows of kv_pool, -1 = empty
- *   topk_length i32 [s_q]: only entries j < min(topk_length, topk) are read
- *   positions   i32 [s_q]
- *   norm_w      f64 [d]
- *   outputs: out_f64 [s_q][h][d] (pre-quant, after inverse RoPE), out_fp8 [s_q][h][d],
- *            out_scales [s_q][h][d/32]; out_f64 may be NULL.
- * Returns ORACLE_OK or a negative error.
+ * Where an index entry's row comes from.  kv_format 0 / 1: one pool (E4M3 + UE8M0, or
+ * bf16).  KV_DS_NVFP4, the two-pool cache of the pages' nvfp4_ds_mla layout [vLLM #56344
+ * "Deepseek V41 Attention MegaKernel", Purpose: fp8 528 B SWA rows + fp4 288 B compressed
+ * rows]: entries j < swa_entries of an index row name rows of the E4M3 + UE8M0 pool (512
+ * codes + 16 scales), entries j >= swa_entries name rows of the NVFP4 pool, 256 bytes of
+ * E2M1 codes (element 2i in the low nibble of byte i, 2i + 1 in the high nibble) and 32
+ * E4M3 scales, one per 16 elements: value = e2m1(code) * e4m3(scale).  (Reading: the
+ * pages give the row sizes only; this is the OCP E2M1 / E4M3-scale-per-16 format that
+ * fills 288 bytes, with no per-tensor scale.)
  */
+typedef struct {
+  int fmt, d, swa_entries;
+  const void* pool;          /* fmt 0 / 1 / SWA: codes or bf16 bits */
+  const uint8_t* scales;     /* fmt 0 / SWA: UE8M0 per 32 */
+  const uint8_t* cmp_codes;  /* NVFP4 pool: E2M1 pairs [n_cmp][d/2] */
+  const uint8_t* cmp_scales; /* NVFP4 pool: E4M3 per 16 [n_cmp][d/16] */
+  int64_t n_rows, n_cmp;
+} row_source;
+
+/* Bounds of the ids entry j may hold: [-1, n) of the pool it names. */
+static int64_t rows_of(const row_source* R, int j) {
+  return (R->fmt == KV_DS_NVFP4 && j >= R->swa_entries) ? R->n_cmp : R->n_rows;
+}
+
+/* Decode row r named by entry j into v[d], exactly. */
+static void decode_row(const row_source* R, int j, int32_t r, double* v) {
+  int i, d = R->d;
+  if (R->fmt == KV_BF16) {
+    const uint16_t* bits = (const uint16_t*)R->pool;
+    for (i = 0; i < d; ++i) v[i] = oracle_bf16_decode(bits[(int64_t)r * d + i]);
+  } else if (R->fmt == KV_DS_NVFP4 && j >= R->swa_entries) {
+    for (i = 0; i < d; ++i) {
+      uint8_t byte = R->cmp_codes[(int64_t)r * (d / 2) + i / 2];
+      uint8_t code = (i & 1) ? (byte >> 4) : (byte & 15);
+      v[i] = oracle_e2m1_decode(code) * oracle_e4m3_decode(R->cmp_scales[(int64_t)r * (d / 16) + i / 16]);
+    }
+  } else {
+    const uint8_t* codes = (const uint8_t*)R->pool;
+    for (i = 0; i < d; ++i) {
+      int e = R->scales[(int64_t)r * (d / BLOCK) + i / BLOCK];
+      v[i] = oracle_e4m3_decode(codes[(int64_t)r * d + i]) * ldexp(1.0, e - 127);
+    }
+  }
+}
+
+static int step(const uint16_t* q, const row_source* R, const int32_t* indices, const int32_t* topk_length,
+                const int32_t* positions, const double* norm_w, int s_q, int h, int d, int rope_dim, int topk,
+                double sm_scale, double eps, double theta, double* out_f64, uint8_t* out_fp8,
+                uint8_t* out_scales);
+
 int oracle_sparse_mla(const uint16_t* q, const void* kv_pool, const uint8_t* kv_scales,
                       const int32_t* indices, const int32_t* topk_length, const int32_t* positions,
                       const double* norm_w, int s_q, int h, int d, int rope_dim, int topk,
                       int64_t n_rows, int kv_format, double sm_scale, double eps, double theta,
                       double* out_f64, uint8_t* out_fp8, uint8_t* out_scales) {
+  row_source R;
+  if (kv_format != KV_E4M3_UE8M0 && kv_format != KV_BF16) return ORACLE_ERR_ARG;
+  if (kv_format == KV_E4M3_UE8M0 && kv_scales == NULL) return ORACLE_ERR_ARG;
+  memset(&R, 0, sizeof R);
+  R.fmt = kv_format;
+  R.d = d;
+  R.pool = kv_pool;
+  R.scales = kv_scales;
+  R.n_rows = n_rows;
+  return step(q, &R, indices, topk_length, positions, norm_w, s_q, h, d, rope_dim, topk, sm_scale, eps, theta,
+              out_f64, out_fp8, out_scales);
+}
+
+/*
+ * The step over the two-pool nvfp4_ds_mla cache (see row_source): swa_codes / swa_scales
+ * u8 [n_swa][d] / [n_swa][d/32], cmp_codes / cmp_scales u8 [n_cmp][d/2] / [n_cmp][d/16];
+ * entries j < swa_entries of each index row are SWA rows, the rest compressed rows.  The
+ * rest as oracle_sparse_mla.
+ */
+int oracle_sparse_mla_ds_nvfp4(const uint16_t* q, const uint8_t* swa_codes, const uint8_t* swa_scales,
+                               const uint8_t* cmp_codes, const uint8_t* cmp_scales, const int32_t* indices,
+                               const int32_t* topk_length, const int32_t* positions, const double* norm_w,
+                               int s_q, int h, int d, int rope_dim, int topk, int swa_entries, int64_t n_swa,
+                               int64_t n_cmp, double sm_scale, double eps, double theta, double* out_f64,
+                               uint8_t* out_fp8, uint8_t* out_scales) {
+  row_source R;
+  if (!swa_codes || !swa_scales || !cmp_codes || !cmp_scales || d % 16 != 0 || swa_entries < 0 || n_cmp < 1)
+    return ORACLE_ERR_ARG;
+  memset(&R, 0, sizeof R);
+  R.fmt = KV_DS_NVFP4;
+  R.d = d;
+  R.swa_entries = swa_entries;
+  R.pool = swa_codes;
+  R.scales = swa_scales;
+  R.cmp_codes = cmp_codes;
+  R.cmp_scales = cmp_scales;
+  R.n_rows = n_swa;
+  R.n_cmp = n_cmp;
+  return step(q, &R, indices, topk_length, positions, norm_w, s_q, h, d, rope_dim, topk, sm_scale, eps, theta,
+              out_f64, out_fp8, out_scales);
+}
+
+static int step(const uint16_t* q, const row_source* R, const int32_t* indices, const int32_t* topk_length,
+                const int32_t* positions, const double* norm_w, int s_q, int h, int d, int rope_dim, int topk,
+                double sm_scale, double eps, double theta, double* out_f64, uint8_t* out_fp8,
+                uint8_t* out_scales) {
   int t;
   int status = ORACLE_OK;
-  if (s_q < 0 || h < 1 || d < 1 || d % BLOCK != 0 || rope_dim < 0 || rope_dim > d ||
-      rope_dim % 2 != 0 || topk < 0 || n_rows < 1 || (kv_format != KV_E4M3_UE8M0 && kv_format != KV_BF16))
+  if (s_q < 0 || h < 1 || d < 1 || d % BLOCK != 0 || rope_dim < 0 || rope_dim > d || rope_dim % 2 != 0 ||
+      topk < 0 || R->n_rows < 1)
     return ORACLE_ERR_ARG;
-  if (kv_format == KV_E4M3_UE8M0 && kv_scales == NULL) return ORACLE_ERR_ARG;
 
   /* validate the read prefix of every row first */
   for (t = 0; t < s_q; ++t) {
@@ -209,7 +304,7 @@ int oracle_sparse_mla(const uint16_t* q, const void* kv_pool, const uint8_t* kv_
     int j;
     for (j = 0; j < L; ++j) {
       int32_t r = indices[(int64_t)t * topk + j];
-      if (r < -1 || (int64_t)r >= n_rows) return ORACLE_ERR_INDEX;
+      if (r < -1 || (int64_t)r >= rows_of(R, j)) return ORACLE_ERR_INDEX;
     }
   }
 
@@ -234,18 +329,7 @@ int oracle_sparse_mla(const uint16_t* q, const void* kv_pool, const uint8_t* kv_
     for (j = 0; j < L; ++j) {
       int32_t r = indices[(int64_t)t * topk + j];
       if (r < 0) continue;
-      for (i = 0; i < d; ++i) {
-        double v;
-        if (kv_format == KV_E4M3_UE8M0) {
-          const uint8_t* codes = (const uint8_t*)kv_pool;
-          int e = kv_scales[(int64_t)r * (d / BLOCK) + i / BLOCK];
-          v = oracle_e4m3_decode(codes[(int64_t)r * d + i]) * ldexp(1.0, e - 127);
-        } else {
-          const uint16_t* bits = (const uint16_t*)kv_pool;
-          v = oracle_bf16_decode(bits[(int64_t)r * d + i]);
-        }
-        V[(int64_t)nv * d + i] = v;
-      }
+      decode_row(R, j, r, V + (int64_t)nv * d);
       ++nv;
     }
     for (hh = 0; hh < h; ++hh) {

@@ -35,6 +35,7 @@ import torch
 
 KV_E4M3_UE8M0 = 0
 KV_BF16 = 1
+KV_DS_NVFP4 = 2  # two pools: E4M3 + UE8M0 SWA rows, NVFP4 (E2M1 + E4M3 per 16) compressed rows
 
 SEED_BASE = 20260000
 
@@ -105,6 +106,56 @@ def mx_pool(latents: np.ndarray):
     scaled = np.clip(scaled, -448.0, 448.0)
     codes = torch.from_numpy(np.ascontiguousarray(scaled.reshape(n, d))).to(torch.float8_e4m3fn)
     return codes.view(torch.uint8).numpy().copy(), (X + 127).astype(np.uint8)
+
+
+E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def nvfp4_pool(latents: np.ndarray):
+    """Stand-in producer of NVFP4 rows: per 16 elements an E4M3 scale amax / 6 (torch's RNE
+    cast), E2M1 codes round-to-nearest-even of x / scale on the grid 0 .. 6 (clipped at 6),
+    element 2i in the low nibble of byte i.  Returns ``(codes u8 [n, d/2], scales u8 [n, d/16])``."""
+    n, d = latents.shape
+    blk = latents.reshape(n, d // 16, 16).astype(np.float64)
+    amax = np.abs(blk).max(axis=2)
+    sc = torch.from_numpy(amax / 6.0).to(torch.float8_e4m3fn)
+    sc_codes = sc.view(torch.uint8).numpy().copy()
+    sv = sc.double().numpy()
+    x = np.where(sv[..., None] > 0, np.abs(blk) / np.where(sv > 0, sv, 1.0)[..., None], 0.0)
+    x = np.minimum(x, 6.0)
+    dist = np.abs(x[..., None] - E2M1_GRID)
+    mag = np.argmin(dist, axis=-1)  # the lower code on a tie ...
+    tie = np.isclose(np.take_along_axis(dist, np.minimum(mag + 1, 7)[..., None], -1)[..., 0],
+                     np.take_along_axis(dist, mag[..., None], -1)[..., 0], rtol=0, atol=0) & (mag < 7)
+    mag = np.where(tie & (mag % 2 == 1), mag + 1, mag)  # ... unless it is odd: ties to even
+    code = (mag | np.where(blk < 0, 8, 0)).astype(np.uint8).reshape(n, d)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
+    return packed, sc_codes.reshape(n, d // 16)
+
+
+def make_ds_nvfp4(name: str = "decode_sq64", seed: Optional[int] = None, s_q: Optional[int] = None) -> dict:
+    """A workload over the two-pool nvfp4_ds_mla cache: the recipe of workload ``name``
+    (positions, q, norm_w, window and compressed entries, sentinels, lengths) with the
+    compressed rows in an NVFP4 pool of their own (``nvfp4_pool`` of N(0, 1) latents) and
+    index entries 128 .. 639 naming rows of that pool (0 .. n_comp - 1) instead of rows
+    n_swa + c of one concatenated pool.  Seed 20265000 + the workload's index unless
+    ``seed`` is given."""
+    w = BY_NAME[name]
+    base = make(name, seed=(SEED_BASE + 5000 + w.index) if seed is None else seed, s_q=s_q)
+    rng = np.random.Generator(np.random.PCG64((SEED_BASE + 5500 + w.index) if seed is None else seed + 1))
+    lat = rng.standard_normal(size=(w.n_comp, w.d), dtype=np.float32)
+    cmp_codes, cmp_scales = nvfp4_pool(lat)
+    idx = base["indices"].copy()
+    seg = idx[:, 128:]
+    idx[:, 128:] = np.where(seg >= 0, seg - w.n_swa, -1)
+    out = dict(base)
+    out.update(name=name + "_nvfp4", description=base["description"] + ", compressed rows NVFP4 (288 B)",
+               kv_format=KV_DS_NVFP4, swa_codes=base["kv_pool"][:w.n_swa].copy(),
+               swa_scales=base["kv_scales"][:w.n_swa].copy(), cmp_codes=cmp_codes, cmp_scales=cmp_scales,
+               indices=idx, swa_entries=128, n_swa_rows=w.n_swa, n_cmp_rows=w.n_comp)
+    for k in ("kv_pool", "kv_scales"):
+        out.pop(k)
+    return out
 
 
 def _rng(index: int, seed: Optional[int]) -> np.random.Generator:
