@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define SMLA_ABI_VERSION 3
+#define SMLA_ABI_VERSION 4
 
 /* return codes */
 #define SMLA_OK 0
@@ -128,6 +128,43 @@ int sparse_mla_fwd(const void* q, const void* kv_pool, const uint8_t* kv_scales,
                    const int32_t* indices, const int32_t* topk_length, const int32_t* positions,
                    const float* norm_w, uint8_t* out_fp8, uint8_t* out_scales,
                    const smla_params* params);
+
+/*
+ * The step over the two-pool nvfp4_ds_mla cache [vLLM #56344 "Deepseek V41 Attention
+ * MegaKernel", Purpose: fp8 528 B SWA rows + fp4 288 B compressed rows, index segments of
+ * their own; Performance: 1.38x the KV token capacity at 8k context].  Steps 1-7 above with
+ * the rows of entry j of an index row taken from
+ *   j <  swa_entries:  the SWA pool, E4M3 + UE8M0 as kv_format 0 (swa_pool u8 [n_rows][512],
+ *                      swa_scales u8 [n_rows][16]; the same scale range as sparse_mla_fwd);
+ *   j >= swa_entries:  the compressed pool, NVFP4: cmp_pool u8 [n_cmp_rows][256] holds the
+ *                      E2M1 codes of a row, element 2i in the low nibble of byte i and 2i + 1
+ *                      in the high nibble; cmp_scales u8 [n_cmp_rows][32] one E4M3 scale per
+ *                      16 elements; value = e2m1(code) * e4m3(scale)  (OCP E2M1: sign, two
+ *                      exponent bits with bias 1, one mantissa bit; no per-tensor scale).
+ * An id that is negative or outside the pool its segment names is read as an empty slot
+ * (never dereferenced).  Arithmetic: rows are dequantized
+ * exactly to bf16, q' (after norm and RoPE, times sm_scale) is rounded to bf16, QK^T and
+ * P.V accumulate in f32; the output codec is the same.
+ *
+ *   base          the shapes and scalars as for sparse_mla_fwd: d = 512, kv_format
+ *                 SMLA_KV_E4M3_UE8M0 (the SWA pool), n_rows = SWA rows, rope_dim <= 96;
+ *                 workspace of sparse_mla_workspace_size(&base) bytes (the same split rule)
+ *   n_cmp_rows    rows of the compressed pool (>= 1; n_cmp_rows * 256 below 4 GiB)
+ *   swa_entries   the segment boundary, a multiple of 64 in [0, 65536]
+ * cmp_pool must be 16-byte aligned, cmp_scales 4-byte aligned; the rest as sparse_mla_fwd.
+ * Returns SMLA_OK or SMLA_ERR_* with nothing launched.
+ */
+typedef struct smla_ds_params {
+  smla_params base;
+  int64_t n_cmp_rows;
+  int32_t swa_entries;
+  int32_t reserved; /* 0 */
+} smla_ds_params;
+
+int sparse_mla_fwd_ds_nvfp4(const void* q, const uint8_t* swa_pool, const uint8_t* swa_scales,
+                            const uint8_t* cmp_pool, const uint8_t* cmp_scales, const int32_t* indices,
+                            const int32_t* topk_length, const int32_t* positions, const float* norm_w,
+                            uint8_t* out_fp8, uint8_t* out_scales, const smla_ds_params* params);
 
 /*
  * Allocation-free variant of sparse_mla_fwd, for callers that cannot allocate device memory

@@ -15,12 +15,12 @@ from typing import Optional
 
 from . import _lib
 from ._lib import (SMLA_ERR_HIP, SMLA_ERR_NULL, SMLA_ERR_SHAPE, SMLA_ERR_VALUE, SMLA_KV_BF16,
-                   SMLA_KV_E4M3_UE8M0, SMLA_OK, LibraryMissing, SmlaIndexParams, SmlaKvInsertParams, SmlaParams,
-                   SmlaWoAParams, last_error)
+                   SMLA_KV_E4M3_UE8M0, SMLA_OK, LibraryMissing, SmlaDsParams, SmlaIndexParams, SmlaKvInsertParams,
+                   SmlaParams, SmlaWoAParams, last_error)
 
 __all__ = [
     "sparse_mla_fwd", "sparse_mla_workspace_size", "sparse_mla_num_splits", "sparse_mla_last_error",
-    "sparse_mla_abi_version", "sparse_mla_fwd_noalloc", "sparse_mla_noalloc_num_splits", "sparse_mla_kv_insert", "sparse_mla_build_index", "sparse_mla_wo_a", "make_params",
+    "sparse_mla_abi_version", "sparse_mla_fwd_ds_nvfp4", "SmlaDsParams", "sparse_mla_fwd_noalloc", "sparse_mla_noalloc_num_splits", "sparse_mla_kv_insert", "sparse_mla_build_index", "sparse_mla_wo_a", "make_params",
     "make_kv_insert_params", "make_index_params", "SmlaParams", "SmlaKvInsertParams", "SmlaIndexParams", "SmlaError",
     "LibraryMissing",
     "SMLA_OK", "SMLA_ERR_NULL", "SMLA_ERR_SHAPE", "SMLA_ERR_VALUE", "SMLA_ERR_HIP",
@@ -218,6 +218,51 @@ def sparse_mla_fwd(q, kv_pool, kv_scales, indices, topk_length, positions, norm_
                                     ctypes.byref(params))
     if rc != SMLA_OK:
         raise SmlaError(rc, last_error())
+
+
+def sparse_mla_fwd_ds_nvfp4(q, swa_pool, swa_scales, cmp_pool, cmp_scales, indices, topk_length, positions, norm_w,
+                            out_fp8, out_scales, *, swa_entries: int, sm_scale: float, rope_dim: int,
+                            eps: float = 1e-6, theta: float = 1e4, out_f32=None, workspace=None,
+                            num_splits: int = 0, stream=None) -> None:
+    """Enqueue the step over the two-pool nvfp4_ds_mla cache on the current (or given) stream.
+
+    swa_pool uint8 / float8_e4m3fn [n_swa, 512] + swa_scales uint8 [n_swa, 16] (E4M3 +
+    UE8M0); cmp_pool uint8 [n_cmp, 256] (E2M1 pairs, low nibble first) + cmp_scales uint8
+    [n_cmp, 32] (E4M3 per 16); index entries j < swa_entries name SWA rows, later entries
+    compressed rows.  The rest as sparse_mla_fwd.  Raises SmlaError on failure."""
+    torch, _ = _dtypes()
+    s_q, h_q, d, topk, n_swa, kv_format = _check_fwd("sparse_mla_fwd_ds_nvfp4", q, swa_pool, swa_scales, indices,
+                                                     topk_length, positions, norm_w, out_fp8, out_scales, out_f32,
+                                                     workspace)
+    if kv_format != SMLA_KV_E4M3_UE8M0:
+        raise ValueError("sparse_mla_fwd_ds_nvfp4: the SWA pool must hold E4M3 codes")
+    ck = _Checker("sparse_mla_fwd_ds_nvfp4")
+    ck("cmp_pool", cmp_pool, (torch.uint8,), ndim=2)
+    n_cmp = cmp_pool.shape[0]
+    if cmp_pool.shape[1] != d // 2:
+        raise ValueError(f"sparse_mla_fwd_ds_nvfp4: cmp_pool rows must have {d // 2} bytes (got {cmp_pool.shape[1]})")
+    ck("cmp_scales", cmp_scales, (torch.uint8,), shape=(n_cmp, d // 16))
+    ck("q", q, (torch.bfloat16,), ndim=3)
+    ck.done()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif workspace is None:
+        raise ValueError("sparse_mla_fwd_ds_nvfp4: pass a workspace when enqueuing on an explicit stream")
+    dp = SmlaDsParams()
+    dp.base = make_params(s_q=s_q, h_q=h_q, d=d, rope_dim=rope_dim, topk=topk, n_rows=n_swa, kv_format=kv_format,
+                          sm_scale=sm_scale, eps=eps, theta=theta, num_splits=num_splits, out_f32=out_f32,
+                          workspace=workspace, stream=stream)
+    dp.n_cmp_rows, dp.swa_entries, dp.reserved = n_cmp, swa_entries, 0
+    need = sparse_mla_workspace_size(dp.base)
+    if need > 0 and workspace is None:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+        dp.base.workspace = _ptr(workspace)
+        dp.base.workspace_bytes = need
+    rc = _lib.load().sparse_mla_fwd_ds_nvfp4(_ptr(q), _ptr(swa_pool), _ptr(swa_scales), _ptr(cmp_pool),
+                                             _ptr(cmp_scales), _ptr(indices), _ptr(topk_length), _ptr(positions),
+                                             _ptr(norm_w), _ptr(out_fp8), _ptr(out_scales), ctypes.byref(dp))
+    if rc != SMLA_OK:
+        raise SmlaError(rc, last_error(), "sparse_mla_fwd_ds_nvfp4")
 
 
 def make_kv_insert_params(*, n: int, rope_dim: int, n_swa: int, n_rows: int, d: int = 512, eps: float = 1e-6,

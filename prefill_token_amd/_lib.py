@@ -8,6 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsmla.so")
 DEBUG_LIB_PATH = os.path.join(HERE, "libsmla_debug.so")
 
+SMLA_ABI_VERSION = 4  # the layout of the structures below
 SMLA_NOALLOC_SCRATCH_BYTES = 34 << 20
 SMLA_DEBUG_WORD_OFFSET = 8
 SMLA_DEBUG_BAD_INDEX = 1
@@ -42,6 +43,17 @@ class SmlaParams(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
+    ]
+
+
+class SmlaDsParams(ctypes.Structure):
+    """Mirror of ``smla_ds_params`` (the two-pool nvfp4_ds_mla step)."""
+
+    _fields_ = [
+        ("base", SmlaParams),
+        ("n_cmp_rows", ctypes.c_int64),
+        ("swa_entries", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -123,8 +135,14 @@ def _open(path: str) -> ctypes.CDLL:
     lib.sparse_mla_debug_checks.argtypes = []
     lib.sparse_mla_fwd_noalloc.restype = ctypes.c_int
     lib.sparse_mla_fwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, ctypes.POINTER(SmlaParams)]
+    lib.sparse_mla_fwd_ds_nvfp4.restype = ctypes.c_int
+    lib.sparse_mla_fwd_ds_nvfp4.argtypes = [P, P, P, P, P, P, P, P, P, P, P, ctypes.POINTER(SmlaDsParams)]
     lib.sparse_mla_noalloc_num_splits.restype = ctypes.c_int
     lib.sparse_mla_noalloc_num_splits.argtypes = [ctypes.POINTER(SmlaParams)]
+    got = lib.sparse_mla_abi_version()
+    if got != SMLA_ABI_VERSION:
+        raise LibraryMissing(f"{path} has ABI version {got}, this binding needs {SMLA_ABI_VERSION}: rebuild it with "
+                             "`python -m prefill_token_amd.build`")
     return lib
 
 

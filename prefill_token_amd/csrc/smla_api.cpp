@@ -230,6 +230,70 @@ int sparse_mla_fwd_noalloc(const void* q, const void* kv_pool, const uint8_t* kv
                     scratch, ns);
 }
 
+int sparse_mla_fwd_ds_nvfp4(const void* q, const uint8_t* swa_pool, const uint8_t* swa_scales,
+                            const uint8_t* cmp_pool, const uint8_t* cmp_scales, const int32_t* indices,
+                            const int32_t* topk_length, const int32_t* positions, const float* norm_w,
+                            uint8_t* out_fp8, uint8_t* out_scales, const smla_ds_params* dp) {
+  g_last_error.clear();
+  if (!dp) return fail(SMLA_ERR_NULL, "params is NULL");
+  const smla_params* p = &dp->base;
+  int rc = check_params(p);
+  if (rc != SMLA_OK) return rc;
+  if (p->d != 512 || p->kv_format != SMLA_KV_E4M3_UE8M0)
+    return fail(SMLA_ERR_SHAPE, "the two-pool step needs d = 512 and an E4M3 + UE8M0 SWA pool");
+  if (p->rope_dim > smla::kNvMaxRope)
+    return fail(SMLA_ERR_SHAPE, "rope_dim must be at most %d for the two-pool step (got %d)", smla::kNvMaxRope,
+                p->rope_dim);
+  if (dp->n_cmp_rows < 1 || dp->n_cmp_rows > 0xFFFFFFF0LL / 256)
+    return fail(SMLA_ERR_SHAPE, "n_cmp_rows must be in [1, 4 GiB / 256) (got %lld)", (long long)dp->n_cmp_rows);
+  if (dp->swa_entries < 0 || dp->swa_entries > 65536 || dp->swa_entries % smla::kTileRows != 0)
+    return fail(SMLA_ERR_SHAPE, "swa_entries must be a multiple of 64 in [0, 65536] (got %d)", dp->swa_entries);
+  if (dp->reserved != 0) return fail(SMLA_ERR_VALUE, "reserved must be 0");
+  if (p->s_q == 0) return SMLA_OK;
+  rc = check_fwd_arrays(q, swa_pool, swa_scales, indices, topk_length, positions, norm_w, out_fp8, out_scales, p);
+  if (rc != SMLA_OK) return rc;
+  if (!cmp_pool || !cmp_scales) return fail(SMLA_ERR_NULL, "cmp_pool and cmp_scales are required");
+  if (reinterpret_cast<uintptr_t>(cmp_pool) % 16 != 0 || reinterpret_cast<uintptr_t>(cmp_scales) % 4 != 0)
+    return fail(SMLA_ERR_VALUE, "cmp_pool must be 16-byte and cmp_scales 4-byte aligned");
+  if (reinterpret_cast<uintptr_t>(p->workspace) % 16 != 0) return fail(SMLA_ERR_VALUE, "workspace must be 16-byte aligned");
+  const int ns = choose_splits(p);
+  const size_t need = workspace_bytes_for(p, ns);
+  if (need > 0 && (!p->workspace || p->workspace_bytes < need))
+    return fail(SMLA_ERR_VALUE, "workspace of %zu bytes needed (got %zu)", need,
+                p->workspace ? p->workspace_bytes : (size_t)0);
+  smla::LaunchArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.kv_pool = swa_pool;
+  a.kv_scales = swa_scales;
+  a.indices = indices;
+  a.topk_length = topk_length;
+  a.positions = positions;
+  a.norm_w = norm_w;
+  a.out_fp8 = out_fp8;
+  a.out_scales = out_scales;
+  a.out_f32 = p->out_f32;
+  a.workspace = p->workspace;
+  a.s_q = p->s_q;
+  a.h_q = p->h_q;
+  a.d = p->d;
+  a.rope_dim = p->rope_dim;
+  a.topk = p->topk;
+  a.kv_format = p->kv_format;
+  a.num_splits = ns;
+  a.n_rows = p->n_rows;
+  a.sm_scale = p->sm_scale;
+  a.rms_eps = p->rms_eps;
+  a.rope_theta = p->rope_theta;
+  a.stream = static_cast<hipStream_t>(p->stream);
+  a.cmp_pool = cmp_pool;
+  a.cmp_scales = cmp_scales;
+  a.n_cmp = dp->n_cmp_rows;
+  a.swa_entries = dp->swa_entries;
+  const hipError_t e = smla::launch(a);
+  if (e != hipSuccess) return fail(SMLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return SMLA_OK;
+}
+
 int sparse_mla_noalloc_num_splits(const smla_params* p) {
   if (check_params(p) != SMLA_OK) return 0;
   return noalloc_splits(p);

@@ -23,7 +23,16 @@ struct LaunchArgs {
   int64_t n_rows;
   float sm_scale, rms_eps, rope_theta;
   hipStream_t stream;
+  // two-pool (nvfp4_ds_mla) calls: the NVFP4 pool of the compressed rows (null otherwise);
+  // kv_pool / kv_scales are then the E4M3 SWA pool
+  const uint8_t* cmp_pool = nullptr;    // E2M1 pairs [n_cmp][d/2]
+  const uint8_t* cmp_scales = nullptr;  // E4M3 [n_cmp][d/16]
+  int64_t n_cmp = 0;
+  int swa_entries = 0;                  // index entries [0, swa_entries) name SWA rows
 };
+
+// Largest rotary width the two-pool kernel stages (its q prologue's staging area).
+constexpr int kNvMaxRope = 96;
 
 // Rows of the index row processed per tile by one workgroup.
 constexpr int kTileRows = 64;

@@ -185,6 +185,12 @@ struct KArgs {
   long long n_rows;
   float sm_scale, rms_eps, rope_theta;
   double log2_theta;  // log2(rope_theta), computed on the host
+  // two-pool (nvfp4_ds_mla) calls only: the NVFP4 pool of the compressed rows and where
+  // an index row switches to it (pool / scales above are then the E4M3 SWA pool)
+  const uint8_t* cmp_pool;    // E2M1 pairs [n_cmp][256]
+  const uint8_t* cmp_scales;  // E4M3 [n_cmp][32], one per 16 elements
+  long long n_cmp;
+  int swa_entries;
 };
 
 __device__ __forceinline__ uint32_t cvt_lo(uint32_t src, float sc) {
@@ -1991,6 +1997,360 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// The step over the two-pool nvfp4_ds_mla cache, d = 512: entries j < swa_entries of an
+// index row name rows of the E4M3 + UE8M0 SWA pool (512 codes + 16 scales), the later
+// entries rows of the NVFP4 pool (256 bytes of E2M1 pairs + 32 E4M3 scales, one per 16
+// elements) [vLLM #56344 "Deepseek V41 Attention MegaKernel", Purpose: fp8 528 B SWA rows
+// + fp4 288 B compressed rows].  An E2M1 value times an E4M3 scale has up to six
+// significant bits and its scale is not a power of two, so neither the scaled FP8 MFMA nor
+// an E4M3 re-encoding holds it exactly; both kinds of rows are decoded exactly to bf16
+// instead, and q' is bf16, with QK^T and P.V on bf16 MFMAs.
+//
+// One 512-thread workgroup per (token, split).  Per 64-entry tile (each tile lies in one
+// segment: swa_entries is a multiple of 64):
+//   gather    thread (row gr = tid / 8, part gp = tid % 8) loads dims 64 gp .. 64 gp + 63 of
+//             its row (64 E4M3 bytes + 2 UE8M0 scales, or 32 bytes of E2M1 pairs + 4 E4M3
+//             scales) through range-checked buffer loads (rows that are not read come in as
+//             zeros), one tile ahead, and writes them as bf16 into the V tile [slot][dim];
+//   QK^T      wave (qa, qc, qd) computes the partial S^T[32 slots of half qc][32 heads of
+//             group qa] over dim half qd (16 bf16 MFMAs, q' fragments in VGPRs); the qd = 1
+//             halves meet the qd = 0 halves through LDS;
+//   softmax   the qd = 0 waves mask, take the tile max of each head over both slot halves
+//             (LDS), raise the running max, write P = exp2(s - m) in bf16 and the rescale;
+//   P.V       wave w owns output dims [64 w, 64 w + 64) of all 64 heads: O^T += V^T P^T with
+//             the V^T operand read by the 16-bit transpose load (ds_read_b64_tr_b16: lane
+//             i of a 16-lane group receives element i % 4 of the 8-byte pieces addressed by
+//             lanes i / 4, i / 4 + 4, i / 4 + 8, i / 4 + 12, which turns four row-major slots
+//             of 16 dims into 16 lanes of four slots each).
+// Then the same epilogue as the generic kernel, or the split partials in its format for
+// smla_combine.
+struct NvCfg {
+  static constexpr int kD = 512, kEB = 2;  // the q prologue writes a bf16 q' tile
+  static constexpr int D = kD;
+  static constexpr int QS = D + 8;         // bf16 stride of the q' tile and of the V tile
+  static constexpr int VS = QS;
+  static constexpr int OFF_Q = 0, OFF_V = 0;
+  static constexpr int V_BYTES = T * VS * 2;
+  static constexpr int OFF_SX = V_BYTES;                 // partial S^T of the qd = 1 waves
+  static constexpr int PS = T + 8;                       // bf16 stride of the P tile
+  static constexpr int OFF_P = OFF_SX + 4 * 64 * 16 * 4;
+  static constexpr int LOOP_END = OFF_P + HP * PS * 2;
+  static constexpr int OS = D + 4;                       // f32 stride of the epilogue's o tile
+  static constexpr int O_BYTES = HP * OS * 4;
+  static constexpr int OFF_SMALL = align16(cmax(O_BYTES, LOOP_END));
+  static constexpr int OFF_COS = OFF_SMALL;
+  static constexpr int OFF_SIN = OFF_COS + (D / 2) * 4;
+  static constexpr int OFF_W = OFF_SIN + (D / 2) * 4;   // norm_w of the q prologue
+  static constexpr int OFF_MAXX = OFF_W + (D / 32) * 36 * 4;  // [2 slot halves][HP]
+  static constexpr int OFF_ALPHA = OFF_MAXX + 2 * HP * 4;     // [HP]
+  static constexpr int OFF_LSUM = OFF_ALPHA + HP * 4;         // [2 slot halves][HP]
+  static constexpr int OFF_VALID = OFF_LSUM + 2 * HP * 4;     // [T]: the tile's entry is read
+  static constexpr int SMEM = OFF_VALID + T * 4;
+  static constexpr int MAX_ROPE = (LOOP_END - OFF_SX) / (HP * 4) - 4;  // the prologue's staging over SX + P
+  static_assert(HP * QS * 2 <= OFF_SX && SMEM <= 160 * 1024, "LDS layout");
+  static_assert(MAX_ROPE >= 64, "rotary staging");
+};
+
+__global__ __launch_bounds__(NTHREADS, 1) void smla_nv(KArgs a) {
+  using C = NvCfg;
+  constexpr int D = C::D;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM];
+  float* cs = reinterpret_cast<float*>(smem + C::OFF_COS);
+  float* sn = reinterpret_cast<float*>(smem + C::OFF_SIN);
+  float* maxx = reinterpret_cast<float*>(smem + C::OFF_MAXX);
+  float* alpha_l = reinterpret_cast<float*>(smem + C::OFF_ALPHA);
+  float* lsum = reinterpret_cast<float*>(smem + C::OFF_LSUM);
+  int* valid_l = reinterpret_cast<int*>(smem + C::OFF_VALID);
+  unsigned char* vt = smem + C::OFF_V;
+  unsigned char* pt = smem + C::OFF_P;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  const int qa = w & 1, qc = (w >> 1) & 1, qd = w >> 2;  // QK roles
+  const int ns = a.num_splits;
+  const int t = blockIdx.x / ns, split = blockIdx.x % ns;
+  const int pos = a.positions[t];
+  const int lraw = a.topk_length[t];
+  const int lcap = lraw < 0 ? 0 : (lraw > a.topk ? a.topk : lraw);
+  const int ntile = (lcap + T - 1) / T;
+  const int tb = split * a.tiles_per_split;
+  const int te_raw = tb + a.tiles_per_split;
+  const int te = te_raw < ntile ? te_raw : ntile;
+
+  // gather role: row gr of the tile, dims 64 gp .. 64 gp + 63
+  const int gr = tid >> 3, gp = tid & 7;
+  const __amdgpu_buffer_rsrc_t idx_rs = buf_rsrc(a.indices + (size_t)t * a.topk, (uint32_t)a.topk * 4u);
+  const __amdgpu_buffer_rsrc_t swa_rs = buf_rsrc(a.pool, (uint32_t)(a.n_rows * D));
+  const __amdgpu_buffer_rsrc_t swa_srs = buf_rsrc(a.scales, (uint32_t)(a.n_rows * (D / 32)));
+  const __amdgpu_buffer_rsrc_t cmp_rs = buf_rsrc(a.cmp_pool, (uint32_t)(a.n_cmp * (D / 2)));
+  const __amdgpu_buffer_rsrc_t cmp_srs = buf_rsrc(a.cmp_scales, (uint32_t)(a.n_cmp * (D / 16)));
+  // the raw id of entry tile * 64 + gr (an entry past the row reads 0; decided in row_of)
+  auto fetch_id = [&](int tile) -> int {
+    const int j = tile * T + gr;
+    return (int)__builtin_amdgcn_raw_buffer_load_b32(idx_rs, (uint32_t)(j < a.topk ? j : a.topk) * 4u, 0, 0);
+  };
+  // the row entry tile * 64 + gr reads, or -1 (past the length, a sentinel, out of its pool)
+  auto row_of = [&](int tile, int raw) -> int {
+    const int j = tile * T + gr;
+    const long long n = j < a.swa_entries ? a.n_rows : a.n_cmp;
+    return (tile < te && j < lcap && raw >= 0 && (long long)raw < n) ? raw : -1;
+  };
+  struct Raw {
+    uint4 c[4];
+    uint32_t s;
+  };
+  auto gather = [&](int tile, int id, Raw& g) {
+    if (tile * T < a.swa_entries) {
+      // every chunk's offset is selected on its own: kNoRow plus a chunk offset would wrap
+      // round to the start of the pool
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t off = id >= 0 ? (uint32_t)id * D + 64u * gp + 16u * k : kNoRow;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(swa_rs, off, 0, 0);
+        g.c[k] = make_uint4(v[0], v[1], v[2], v[3]);
+      }
+      g.s = __builtin_amdgcn_raw_buffer_load_b16(swa_srs, id >= 0 ? (uint32_t)id * (D / 32) + 2u * gp : kNoRow, 0, 0);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const uint32_t off = id >= 0 ? (uint32_t)id * (D / 2) + 32u * gp + 16u * k : kNoRow;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(cmp_rs, off, 0, 0);
+        g.c[k] = make_uint4(v[0], v[1], v[2], v[3]);
+      }
+      g.c[2] = g.c[3] = make_uint4(0u, 0u, 0u, 0u);
+      g.s = __builtin_amdgcn_raw_buffer_load_b32(cmp_srs, id >= 0 ? (uint32_t)id * (D / 16) + 4u * gp : kNoRow, 0, 0);
+    }
+  };
+  // the gathered part of row gr as bf16 into the V tile (exact: an E4M3 value times a
+  // power of two in the range the ABI admits, or an E2M1 value times an E4M3 scale)
+  auto dequant = [&](int tile, const Raw& g) {
+    uint4* dst = reinterpret_cast<uint4*>(vt + (gr * C::VS + 64 * gp) * 2);
+    if (tile * T < a.swa_entries) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float sc = ue8m0_f32((g.s >> (k < 2 ? 0 : 8)) & 0xFFu);
+        const uint32_t u[4] = {g.c[k].x, g.c[k].y, g.c[k].z, g.c[k].w};
+        dst[2 * k] = make_uint4(cvt_lo(u[0], sc), cvt_hi(u[0], sc), cvt_lo(u[1], sc), cvt_hi(u[1], sc));
+        dst[2 * k + 1] = make_uint4(cvt_lo(u[2], sc), cvt_hi(u[2], sc), cvt_lo(u[3], sc), cvt_hi(u[3], sc));
+      }
+    } else {
+      // the four E4M3 block scales, decoded exactly
+      const f32x2 s01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(g.s, 1.0f, false);
+      const f32x2 s23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(g.s, 1.0f, true);
+      const float scv[4] = {s01[0], s01[1], s23[0], s23[1]};
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const uint32_t u[4] = {g.c[k].x, g.c[k].y, g.c[k].z, g.c[k].w};
+        // bytes 16k .. 16k + 15: elements 32k .. 32k + 31, blocks 2k, 2k + 1
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float sc = scv[2 * k + (q >> 1)];
+          uint32_t pk[4];
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            // byte b of word q: elements 2b (low nibble) and 2b + 1 (high nibble), exact at
+            // scale 1; the block scale is a plain f32 product (exact: 2 x 4 significant bits)
+            f32x2 e2;
+            if (b == 0) e2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u[q], 1.0f, 0);
+            else if (b == 1) e2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u[q], 1.0f, 1);
+            else if (b == 2) e2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u[q], 1.0f, 2);
+            else e2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u[q], 1.0f, 3);
+            pk[b] = pack_bf16(e2[0] * sc, e2[1] * sc);
+          }
+          dst[4 * k + q] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+        }
+      }
+    }
+  };
+
+  // ---------------- prologue: q' (bf16, times sm_scale log2 e) into the q tile
+  int raw_cur = tb < te ? fetch_id(tb) : -1;
+  Raw g;
+  float* ystage = reinterpret_cast<float*>(smem + C::OFF_SX);
+  q_prologue<C>(smem, t, pos, a, cs, sn, ystage, [&]() {});
+  __syncthreads();
+  // q' fragments (B operand of S^T = K q'^T): head 32 qa + lrow, k-steps 16 qd .. 16 qd + 15,
+  // lane half h holding dims 16 ks + 8 h .. + 7
+  bf16x8 qf[16];
+  {
+    const unsigned short* qrow = reinterpret_cast<const unsigned short*>(smem + C::OFF_Q) + (32 * qa + lrow) * C::QS;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) qf[j] = *reinterpret_cast<const bf16x8*>(qrow + 16 * (16 * qd + j) + 8 * lhalf);
+  }
+  // the first tile's rows (after the q tile is read: the V tile shares its space)
+  if (tb < te) gather(tb, row_of(tb, raw_cur), g);
+  int raw_next = tb + 1 < te ? fetch_id(tb + 1) : -1;
+  __syncthreads();  // q fragments loaded: the V tile may overwrite the q tile
+
+  // P.V accumulators of this wave's 64 dims: acc[mb][nb] = O^T rows (dims 64 w + 32 nb ..)
+  // x columns (heads 32 mb ..): lane = head, register i = dim 8 (i >> 2) + 4 lhalf + (i & 3)
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;  // qd = 0 waves: per head (lane), this slot half
+
+  for (int tile = tb; tile < te; ++tile) {
+    const int lane = ((int)threadIdx.x + opaque_zero()) & 63, lrow = lane & 31, lhalf = lane >> 5;
+    dequant(tile, g);
+    if (gp == 0) valid_l[gr] = row_of(tile, raw_cur) >= 0;
+    __syncthreads();  // V tile and the read mask complete
+    // next tile's rows, landing during this tile's arithmetic
+    if (tile + 1 < te) gather(tile + 1, row_of(tile + 1, raw_next), g);
+    const int raw_next2 = tile + 2 < te ? fetch_id(tile + 2) : -1;
+
+    // ---- QK^T: partial S^T[32 slots of half qc][32 heads of group qa] over dim half qd
+    f32x16 s;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = 0.f;
+    {
+      const unsigned short* krow = reinterpret_cast<const unsigned short*>(vt) + (32 * qc + lrow) * C::VS;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + 16 * (16 * qd + j) + 8 * lhalf);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[j], s, 0, 0, 0);
+      }
+    }
+    float* sx = reinterpret_cast<float*>(smem + C::OFF_SX) + (2 * qa + qc) * 1024;
+    if (qd == 1) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sx[i * 64 + lane] = s[i];
+    }
+    __syncthreads();  // partial S^T of the qd = 1 waves visible
+    if (qd == 0) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] += sx[i * 64 + lane];
+      // slot 32 qc + 8 (i >> 2) + 4 lhalf + (i & 3) counts only if its entry is read
+      float lm = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int slot = 32 * qc + 8 * (i >> 2) + 4 * lhalf + (i & 3);
+        s[i] = valid_l[slot] ? s[i] : -INFINITY;
+        lm = fmaxf(lm, s[i]);
+      }
+      lm = fmaxf(lm, __shfl_xor(lm, 32));
+      if (lhalf == 0) maxx[qc * HP + 32 * qa + lrow] = lm;
+    }
+    __syncthreads();  // block maxima of both slot halves visible
+    if (qd == 0) {
+      const int head = 32 * qa + lrow;
+      const float mt = fmaxf(maxx[head], maxx[HP + head]);
+      const float mnew = fmaxf(m_run, mt);
+      const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - mnew);
+      const float msafe = mnew == -INFINITY ? 0.f : mnew;
+      float p[16], lp = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(s[i] - msafe);
+        lp += p[i];
+      }
+      l_run = l_run * alpha + lp;
+      m_run = mnew;
+      // P [head][slot] in bf16, natural slot order
+      unsigned short* prow = reinterpret_cast<unsigned short*>(pt) + head * C::PS + 32 * qc + 4 * lhalf;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<uint2*>(prow + 8 * g4) =
+            make_uint2(pack_bf16(p[4 * g4], p[4 * g4 + 1]), pack_bf16(p[4 * g4 + 2], p[4 * g4 + 3]));
+      if (qc == 0 && lhalf == 0) alpha_l[head] = alpha;
+    }
+    __syncthreads();  // P and the rescale visible
+    // ---- P.V: O^T[dims 64 w .. 64 w + 63][heads] += V^T P^T
+    {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const float al = alpha_l[32 * mb + lrow];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[mb][nb][i] *= al;
+      }
+      const int grp = lane >> 4, p16 = lane & 15;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        bf16x8 bp[2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          bp[mb] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const unsigned short*>(pt) +
+                                                    (32 * mb + lrow) * C::PS + 16 * ks + 8 * lhalf);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          // V^T fragment of dims 64 w + 32 nb .. + 31, slots 16 ks + 8 lhalf .. + 7: lane p of
+          // 16-lane group g points at slot k0 + p / 4, dims 16 (g & 1) + 4 (p & 3) .. + 3
+          const int dim0 = 64 * w + 32 * nb + 16 * (grp & 1) + 4 * (p16 & 3);
+          uint2 h0, h1;
+          {
+            const int slot = 16 * ks + 8 * lhalf + (p16 >> 2);
+            const uint32_t ad = lds_addr(vt + (slot * C::VS + dim0) * 2);
+            asm volatile("ds_read_b64_tr_b16 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(h0) : "v"(ad) : "memory");
+            const uint32_t ad1 = ad + 4 * C::VS * 2;
+            asm volatile("ds_read_b64_tr_b16 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(h1) : "v"(ad1) : "memory");
+          }
+          const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(h0.x, h0.y, h1.x, h1.y));
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, bp[mb], acc[mb][nb], 0, 0, 0);
+        }
+      }
+    }
+    raw_cur = raw_next;
+    raw_next = raw_next2;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // next tile's rows landed
+    __syncthreads();  // V tile and P read: the next tile may overwrite them
+  }
+
+  // ---------------- finish: l and m per head, then normalize + epilogue, or the partials
+  if (qd == 0) {
+    const float lw = l_run + __shfl_xor(l_run, 32);
+    if (lhalf == 0) lsum[qc * HP + 32 * qa + lrow] = lw;
+    if (qc == 0 && lhalf == 0) maxx[32 * qa + lrow] = m_run;
+  }
+  __syncthreads();
+  const int d0 = 64 * w;
+  if (ns == 1) {
+    float* o_l = reinterpret_cast<float*>(smem);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int h = 32 * mb + lrow;
+      const float lt = lsum[h] + lsum[HP + h];
+      const float inv = lt > 0.f ? __builtin_amdgcn_rcpf(lt) : 0.f;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          o_l[h * C::OS + d0 + 32 * nb + 8 * (i >> 2) + 4 * lhalf + (i & 3)] = acc[mb][nb][i] * inv;
+    }
+    __syncthreads();
+    epilogue<D, NTHREADS>(o_l, C::OS, a.h_q, 0, t, a, cs, sn);
+  } else {
+    float* part = a.ws + ((size_t)t * ns + split) * partial_floats_d(a.h_q, D);
+    float* pm = part + (size_t)HP * D;
+    float* pl = pm + HP;
+    if (tid < a.h_q) {
+      pm[tid] = maxx[tid];
+      pl[tid] = lsum[tid] + lsum[HP + tid];
+    }
+    if (te > tb) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int h = 32 * mb + lrow;
+        if (h < a.h_q) {
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              part[(size_t)h * D + d0 + 32 * nb + 8 * (i >> 2) + 4 * lhalf + (i & 3)] = acc[mb][nb][i];
+        }
+      }
+    }
+  }
+}
+
 // Scheduling order of the persistent kernel's items when there are more items than
 // workgroups and one split per token: tokens by descending tile count, equal counts in
 // token order (longest processing time first, so that the last items a workgroup takes
@@ -2439,7 +2799,7 @@ hipError_t launch_t(const LaunchArgs& x, const KArgs& k) {
 }  // namespace
 
 hipError_t launch(const LaunchArgs& x) {
-  KArgs k;
+  KArgs k = {};
   k.q = x.q;
   k.pool = static_cast<const uint8_t*>(x.kv_pool);
   k.scales = x.kv_scales;
@@ -2466,6 +2826,19 @@ hipError_t launch(const LaunchArgs& x) {
   k.rms_eps = x.rms_eps;
   k.rope_theta = x.rope_theta;
   k.log2_theta = std::log2((double)x.rope_theta);
+  k.cmp_pool = x.cmp_pool;
+  k.cmp_scales = x.cmp_scales;
+  k.n_cmp = x.n_cmp;
+  k.swa_entries = x.swa_entries;
+  if (x.cmp_pool) {
+    static_assert(NvCfg::MAX_ROPE >= kNvMaxRope, "the host's rotary limit for the two-pool kernel");
+    if (x.d != 512 || x.kv_format != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(smla_nv, dim3((unsigned)(x.s_q * x.num_splits)), dim3(NTHREADS), 0, x.stream, k);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || x.num_splits == 1) return e;
+    hipLaunchKernelGGL((smla_combine<512>), dim3((unsigned)x.s_q, (unsigned)x.h_q), dim3(CTHREADS), 0, x.stream, k);
+    return hipGetLastError();
+  }
   if (x.d == 512 && x.kv_format == 0) return launch_t<512, 1>(x, k);
   if (x.d == 128 && x.kv_format == 0) return launch_t<128, 1>(x, k);
   if (x.d == 128 && x.kv_format == 1) return launch_t<128, 2>(x, k);

@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_abi_version(lib):
     # 2: sparse_mla_wo_a, the item order in the workspace; 3: the debug build's error word
-    assert smla.sparse_mla_abi_version() == 3
+    assert smla.sparse_mla_abi_version() == 4 == smla._lib.SMLA_ABI_VERSION
 
 
 def test_debug_build_exports_the_same_symbols_and_says_so(lib):
@@ -371,3 +371,65 @@ def test_noalloc_scratch_constant_matches_header():
     text = open(os.path.join(ROOT, "include", "smla.h")).read()
     m = re.search(r"#define SMLA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == _lib.SMLA_NOALLOC_SCRATCH_BYTES
+
+
+# ---------------------------------------------------------------- two-pool (nvfp4_ds_mla) step
+
+
+def good_ds(**kw):
+    n_cmp = kw.pop("n_cmp_rows", 2048)
+    swa_entries = kw.pop("swa_entries", 128)
+    reserved = kw.pop("reserved", 0)
+    dp = smla.SmlaDsParams()
+    dp.base = good(**kw)
+    dp.n_cmp_rows, dp.swa_entries, dp.reserved = n_cmp, swa_entries, reserved
+    return dp
+
+
+def call_ds(lib, dp, null=None, off=None):
+    ptrs = [FAKE] * 11
+    if null is not None:
+        ptrs[null] = None
+    if off is not None:
+        ptrs[off[0]] = FAKE + off[1]
+    return lib.sparse_mla_fwd_ds_nvfp4(*ptrs, ctypes.byref(dp) if dp is not None else None)
+
+
+def test_ds_struct_layout():
+    P = smla.SmlaDsParams
+    assert P.n_cmp_rows.offset == 80 and P.swa_entries.offset == 88 and ctypes.sizeof(P) == 96
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=128), smla.SMLA_ERR_SHAPE),
+    (dict(d=128, kv_format=1), smla.SMLA_ERR_SHAPE),
+    (dict(rope_dim=128), smla.SMLA_ERR_SHAPE),
+    (dict(n_cmp_rows=0), smla.SMLA_ERR_SHAPE),
+    (dict(n_cmp_rows=(1 << 32) // 256), smla.SMLA_ERR_SHAPE),
+    (dict(swa_entries=100), smla.SMLA_ERR_SHAPE),
+    (dict(swa_entries=-64), smla.SMLA_ERR_SHAPE),
+    (dict(reserved=1), smla.SMLA_ERR_VALUE),
+    (dict(h_q=65), smla.SMLA_ERR_SHAPE),
+    (dict(sm_scale=0.0), smla.SMLA_ERR_VALUE),
+])
+def test_ds_rejected_parameters(lib, kw, code):
+    assert call_ds(lib, good_ds(num_splits=1, **kw)) == code
+    assert smla.sparse_mla_last_error() != ""
+
+
+@pytest.mark.parametrize("which", [0, 1, 2, 3, 4, 6, 7, 8, 9, 10])
+def test_ds_null_arrays(lib, which):
+    assert call_ds(lib, good_ds(num_splits=1), null=which) == smla.SMLA_ERR_NULL
+
+
+@pytest.mark.parametrize("which,off", [(0, 8), (1, 4), (3, 8), (4, 2), (9, 1)])
+def test_ds_misaligned(lib, which, off):
+    assert call_ds(lib, good_ds(num_splits=1), off=(which, off)) == smla.SMLA_ERR_VALUE
+    assert "aligned" in smla.sparse_mla_last_error()
+
+
+def test_ds_null_params_workspace_and_empty(lib):
+    assert lib.sparse_mla_fwd_ds_nvfp4(*([FAKE] * 11), None) == smla.SMLA_ERR_NULL
+    assert call_ds(lib, good_ds(s_q=4)) == smla.SMLA_ERR_VALUE  # a split call without a workspace
+    assert "workspace" in smla.sparse_mla_last_error()
+    assert lib.sparse_mla_fwd_ds_nvfp4(*([None] * 11), ctypes.byref(good_ds(s_q=0))) == smla.SMLA_OK
