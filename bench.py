@@ -28,6 +28,8 @@ Prints one JSON line:
   kv_insert    the KV-insert entry point (the pool-row producer) on its three workloads:
                us/call, tokens/s, algorithmic HBM bytes / mean duration against 8 TB/s
   build_index  the index-row builder on its four workloads, the same figures
+  two_pool_nvfp4  the step over the two-pool nvfp4_ds_mla cache (sparse_mla_fwd_ds_nvfp4) on
+               the decode s_q = 1 / 64 / 1024 and 2123-token prefill workloads, the same figures
   wo_a         the output projection (the step's FP8 output consumer) on its three
                workloads: us/call, tokens/s, HBM and fp8 MFMA fractions
 
@@ -64,6 +66,7 @@ MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 / fp16 MFMA
 MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 MFMA (the output projection's arithmetic)
 PAGES_US_SQ1 = 22.7            # pages' fused kernel at s_q = 1 (GB200, TP4, CUDA graph): context only
 EXTRA = ["decode_sq64", "decode_sq1024", "prefill_sq2123", "decode_sq256", "prefill_sq184"]
+TWO_POOL = ["decode_sq1", "decode_sq64", "decode_sq1024", "prefill_sq2123"]
 FLUSH_BYTES = 1 << 30          # larger than the 256 MB MALL + 8 x 4 MB L2
 CALLS_PER_GRAPH = 10           # warm replays hold this many back-to-back calls
 MIN_COLD_SAMPLES = 50          # cold single-call replays per workload, whatever --steps is
@@ -97,6 +100,36 @@ def work_model(inp):
     compulsory = float(s_q * per_tok_fixed + row_bytes * distinct)
     return dict(flops=flops, gathered_bytes=gathered, compulsory_bytes=compulsory, valid_rows=int(nv.sum()),
                 distinct_rows=int(distinct))
+
+
+def upload_ds(inp, torch, device):
+    t = {"q": torch.from_numpy(inp["q"].view(np.int16)).to(device).view(torch.bfloat16)}
+    for k in ("swa_codes", "swa_scales", "cmp_codes", "cmp_scales"):
+        t[k] = torch.from_numpy(np.ascontiguousarray(inp[k])).to(device)
+    for k in ("indices", "topk_length", "positions"):
+        t[k] = torch.from_numpy(np.ascontiguousarray(inp[k], dtype=np.int32)).to(device)
+    t["norm_w"] = torch.from_numpy(np.ascontiguousarray(inp["norm_w"], dtype=np.float32)).to(device)
+    return t
+
+
+def work_model_ds(inp):
+    """Algorithmic flops and bytes of one two-pool call: SWA rows 512 + 16 bytes, compressed
+    rows 256 + 32 bytes, distinct rows counted per pool."""
+    s_q, h, d = inp["q"].shape
+    L = np.minimum(inp["topk_length"], inp["topk"])
+    cols = np.arange(inp["topk"])[None, :]
+    valid = (cols < L[:, None]) & (inp["indices"] >= 0)
+    swa = valid & (cols < inp["swa_entries"])
+    cmp_ = valid & (cols >= inp["swa_entries"])
+    swa_b, cmp_b = d + d // 32, d // 2 + d // 16
+    nv = int(valid.sum())
+    per_tok_fixed = 2 * h * d + 4 * inp["topk"] + 8 + h * d + h * d // 32
+    gathered = float(s_q * per_tok_fixed + swa_b * swa.sum() + cmp_b * cmp_.sum())
+    distinct_swa = np.unique(inp["indices"][swa]).size
+    distinct_cmp = np.unique(inp["indices"][cmp_]).size
+    compulsory = float(s_q * per_tok_fixed + swa_b * distinct_swa + cmp_b * distinct_cmp)
+    return dict(flops=4.0 * h * d * nv, gathered_bytes=gathered, compulsory_bytes=compulsory, valid_rows=nv,
+                distinct_rows=int(distinct_swa + distinct_cmp), swa_row_bytes=swa_b, cmp_row_bytes=cmp_b)
 
 
 def kernel_names(s_q, ns, torch, device):
@@ -140,27 +173,37 @@ class ColdTimer:
         return np.array(out)
 
 
-def measure(name, steps, warmup, torch, device, cold_timer, timed_steps=None):
+def measure(name, steps, warmup, torch, device, cold_timer, timed_steps=None, two_pool=False):
     """Time one workload.  Returns (result dict, wall seconds of the timed steps, number of
     timed steps): the timed steps are cold single-call replays (timed_steps of them for the
-    headline; at least MIN_COLD_SAMPLES for every workload), then warm graphs of 10 calls."""
-    from prefill_token_amd import inputs, make_params, sparse_mla_fwd, sparse_mla_num_splits, sparse_mla_workspace_size
+    headline; at least MIN_COLD_SAMPLES for every workload), then warm graphs of 10 calls.
+    two_pool: the same workload over the two-pool nvfp4_ds_mla cache (sparse_mla_fwd_ds_nvfp4)."""
+    from prefill_token_amd import (inputs, make_params, sparse_mla_fwd, sparse_mla_fwd_ds_nvfp4,
+                                   sparse_mla_num_splits, sparse_mla_workspace_size)
 
-    inp = inputs.make(name)
-    t = upload(inp, torch, device)
+    inp = inputs.make_ds_nvfp4(name) if two_pool else inputs.make(name)
+    t = upload_ds(inp, torch, device) if two_pool else upload(inp, torch, device)
     s_q, h, d = inp["q"].shape
     out_fp8 = torch.empty((s_q, h, d), dtype=torch.uint8, device=device)
     out_sc = torch.empty((s_q, h, d // 32), dtype=torch.uint8, device=device)
-    p = make_params(s_q=s_q, h_q=h, d=d, rope_dim=inp["rope_dim"], topk=inp["topk"], n_rows=inp["n_rows"],
-                    kv_format=inp["kv_format"], sm_scale=inp["sm_scale"])
+    p = make_params(s_q=s_q, h_q=h, d=d, rope_dim=inp["rope_dim"], topk=inp["topk"],
+                    n_rows=inp["n_swa_rows"] if two_pool else inp["n_rows"],
+                    kv_format=inputs.KV_E4M3_UE8M0 if two_pool else inp["kv_format"], sm_scale=inp["sm_scale"])
     ns = sparse_mla_num_splits(p)
     need = sparse_mla_workspace_size(p)
     ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=device)  # counters start at zero
 
     def call():
-        sparse_mla_fwd(t["q"], t["kv_pool"], t["kv_scales"], t["indices"], t["topk_length"], t["positions"],
-                       t["norm_w"], out_fp8, out_sc, sm_scale=inp["sm_scale"], rope_dim=inp["rope_dim"],
-                       eps=inp["eps"], theta=inp["theta"], workspace=ws if need else None)
+        if two_pool:
+            sparse_mla_fwd_ds_nvfp4(t["q"], t["swa_codes"], t["swa_scales"], t["cmp_codes"], t["cmp_scales"],
+                                    t["indices"], t["topk_length"], t["positions"], t["norm_w"], out_fp8, out_sc,
+                                    swa_entries=inp["swa_entries"], sm_scale=inp["sm_scale"],
+                                    rope_dim=inp["rope_dim"], eps=inp["eps"], theta=inp["theta"],
+                                    workspace=ws if need else None)
+        else:
+            sparse_mla_fwd(t["q"], t["kv_pool"], t["kv_scales"], t["indices"], t["topk_length"], t["positions"],
+                           t["norm_w"], out_fp8, out_sc, sm_scale=inp["sm_scale"], rope_dim=inp["rope_dim"],
+                           eps=inp["eps"], theta=inp["theta"], workspace=ws if need else None)
 
     for _ in range(max(warmup, 1)):
         call()
@@ -202,13 +245,14 @@ def measure(name, steps, warmup, torch, device, cold_timer, timed_steps=None):
     torch.cuda.synchronize()
     warm = np.array([a.elapsed_time(b) * 1e3 / CALLS_PER_GRAPH for a, b in ev])
 
-    wm = work_model(inp)
+    wm = work_model_ds(inp) if two_pool else work_model(inp)
     cold_mean = float(cold.mean())
     cold_med = float(np.median(cold_all))
     warm_mean = float(warm.mean())
     res = dict(
         workload=name, description=inp["description"], s_q=s_q, num_splits=ns,
-        kernels=kernel_names(s_q, ns, torch, device),
+        kernels=("smla_nv" + (" + smla_combine<512>" if ns > 1 else "")) if two_pool
+        else kernel_names(s_q, ns, torch, device),
         timing="cold: caches flushed before each single-call graph replay, HIP events on the launch stream",
         cold_samples=int(cold_all.size),
         us_per_call_median=cold_med, us_per_call_p10=float(np.percentile(cold_all, 10)),
@@ -581,6 +625,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_sq1")
     ap.add_argument("--extra", default=",".join(EXTRA), help="comma-separated workloads after the timed region")
+    ap.add_argument("--two-pool", default=",".join(TWO_POOL),
+                    help="comma-separated workloads measured over the two-pool nvfp4_ds_mla cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-insert", action="store_true",
                     help="skip the KV-insert and index-row-builder measurements")
@@ -620,6 +666,14 @@ def main():
               f"p90 {r['us_per_call_p90']:.2f}), warm {r['us_per_call_warm_mean']:.2f} us, "
               f"{r['tokens_per_s']:.4g} tok/s, HBM {100 * r['hbm_compulsory_frac']:.1f}%, "
               f"MFMA {100 * r['mfma_frac']:.1f}%", file=sys.stderr, flush=True)
+    two_pool = []
+    for name in [x for x in args.two_pool.split(",") if x]:
+        r, _, _ = measure(name, args.steps, args.warmup, torch, device, cold_timer, two_pool=True)
+        two_pool.append(r)
+        print(f"# {name} two-pool nvfp4: cold {r['us_per_call_median']:.2f} us/call, warm "
+              f"{r['us_per_call_warm_mean']:.2f} us, {r['tokens_per_s']:.4g} tok/s, "
+              f"HBM {100 * r['hbm_compulsory_frac']:.1f}%, MFMA {100 * r['mfma_frac']:.1f}%", file=sys.stderr,
+              flush=True)
     del cold_timer
 
     inserts = []
@@ -686,7 +740,12 @@ def main():
         "config": {"workload": head["description"], "name": head["workload"], "s_q": head["s_q"],
                    "num_splits": head["num_splits"], "graph": True, "timing": "cold"},
         "roofline": roofline, "cpu_baseline": cpu, "cpu_oracle_configs": cpu_cfg, "measured_peaks": peaks,
-        "configs": configs, "kv_insert": inserts, "build_index": builds, "wo_a": projs,
+        "configs": configs,
+        "two_pool_nvfp4": two_pool,
+        "two_pool_note": "the same workloads over the nvfp4_ds_mla cache: SWA rows E4M3 + UE8M0 (528 B), "
+                         "compressed rows NVFP4 (256 B of E2M1 pairs + 32 E4M3 scales = 288 B), one smla_nv "
+                         "launch (bf16 MFMAs) plus the split combine",
+        "kv_insert": inserts, "build_index": builds, "wo_a": projs,
         "device": torch.cuda.get_device_name(device), "host": host_info(), "source_digest": digest,
     }
     print(json.dumps(out), flush=True)

@@ -14,43 +14,12 @@ import torch
 import oracle
 from prefill_token_amd import inputs
 
-from parity import compare
+from parity import compare, run_gpu_ds, run_oracle_ds
 
 pytestmark = pytest.mark.gpu
 
 if not torch.cuda.is_available():  # pragma: no cover - CPU containers
     pytest.skip("needs a GPU", allow_module_level=True)
-
-
-def run_gpu_ds(inp, num_splits=0, with_f32=True):
-    from prefill_token_amd import sparse_mla_fwd_ds_nvfp4
-
-    dev = "cuda"
-    s_q, h, d = inp["q"].shape
-    q = torch.from_numpy(inp["q"].view(np.int16)).to(dev).view(torch.bfloat16)
-    t = {k: torch.from_numpy(np.ascontiguousarray(inp[k])).to(dev)
-         for k in ("swa_codes", "swa_scales", "cmp_codes", "cmp_scales")}
-    for k in ("indices", "topk_length", "positions"):
-        t[k] = torch.from_numpy(np.ascontiguousarray(inp[k], dtype=np.int32)).to(dev)
-    w = torch.from_numpy(np.ascontiguousarray(inp["norm_w"], dtype=np.float32)).to(dev)
-    out_fp8 = torch.full((s_q, h, d), 0xFF, dtype=torch.uint8, device=dev)
-    out_sc = torch.full((s_q, h, d // 32), 0xFF, dtype=torch.uint8, device=dev)
-    out_f32 = torch.full((s_q, h, d), float("nan"), dtype=torch.float32, device=dev) if with_f32 else None
-    sparse_mla_fwd_ds_nvfp4(q, t["swa_codes"], t["swa_scales"], t["cmp_codes"], t["cmp_scales"], t["indices"],
-                            t["topk_length"], t["positions"], w, out_fp8, out_sc, swa_entries=inp["swa_entries"],
-                            sm_scale=inp["sm_scale"], rope_dim=inp["rope_dim"], eps=inp["eps"], theta=inp["theta"],
-                            out_f32=out_f32, num_splits=num_splits)
-    torch.cuda.synchronize()
-    return dict(codes=out_fp8.cpu().numpy(), scales=out_sc.cpu().numpy(),
-                f32=None if out_f32 is None else out_f32.cpu().numpy())
-
-
-def run_oracle_ds(inp):
-    o, codes, scales = oracle.sparse_mla_ds_nvfp4(
-        inp["q"], inp["swa_codes"], inp["swa_scales"], inp["cmp_codes"], inp["cmp_scales"], inp["indices"],
-        inp["topk_length"], inp["positions"], inp["norm_w"], swa_entries=inp["swa_entries"], sm_scale=inp["sm_scale"],
-        eps=inp["eps"], theta=inp["theta"], rope_dim=inp["rope_dim"])
-    return dict(o=o, codes=codes, scales=scales)
 
 
 def check(inp, **kw):
