@@ -427,7 +427,9 @@ def measure_index(name, steps, torch, device):
     n = c["n"]
     nbytes = float(2 * np.minimum(c["n_valid"], c["n_cand"]).sum() + n * (8 + 4 * c["topk"] + 4))
     mean_us = float(us.mean())
-    return dict(workload=name, kernel="build_index_kernel", tokens=n, n_cand=c["n_cand"], us_per_call_mean=mean_us,
+    kernel = ("build_index_reg<16, 256>" if c["n_cand"] <= 4096 else
+              "build_index_reg<64, 256>" if c["n_cand"] <= 16384 else "build_index_kernel")
+    return dict(workload=name, kernel=kernel, tokens=n, n_cand=c["n_cand"], us_per_call_mean=mean_us,
                 us_per_call_median=float(np.median(us)), tokens_per_s=n / (mean_us * 1e-6), bytes_per_call=nbytes,
                 hbm_GBs=nbytes / (mean_us * 1e-6) / 1e9, hbm_frac=nbytes / (mean_us * 1e-6) / 1e9 / HBM_PEAK_GBS)
 
@@ -559,8 +561,9 @@ def host_info():
 
 def source_digest():
     h = hashlib.sha256()
-    for fn in ("smla_kernels.hip", "kv_insert.hip", "index_build.hip", "wo_a.hip", "smla_api.cpp", "smla_internal.h"):
-        with open(os.path.join(ROOT, "prefill_token_amd", "csrc", fn), "rb") as f:
+    csrc = os.path.join(ROOT, "prefill_token_amd", "csrc")
+    for fn in sorted(f for f in os.listdir(csrc) if f.endswith((".hip", ".cpp", ".h"))):
+        with open(os.path.join(csrc, fn), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 

@@ -4,8 +4,9 @@ Cases: the four builder workloads at full size (1 and 64 decode tokens over 2048
 candidates, 1024 ragged decode tokens and the 2123-token prefill chunk over 16384), ties
 everywhere (few distinct logits), NaN / -0 / +-inf logits, all-equal rows, no valid
 candidates, fewer candidates than k, no candidate row at all (n_valid NULL), an empty
-window, k = 0, positions before the window fills, 65536 candidates (the largest LDS
-case), a wide -1 tail, and an end-to-end check: rows built on the GPU drive
+window, k = 0, positions before the window fills, candidate counts around 8192 and
+16384 (a thread's share doubles; the last count whose keys stay in registers), 65536
+candidates (the largest LDS case), a wide -1 tail, and an end-to-end check: rows built on the GPU drive
 sparse_mla_fwd against the oracle.
 """
 import numpy as np
@@ -101,6 +102,21 @@ def test_index_candidate_count_not_a_multiple_of_8():
              self_in_window=False, n_swa=8192, cmp_base=8192, k_cmp=512)
     # the largest logits in the last columns, so that they must be found
     c["logits"][:, -4:] = inputs.bf16_bits(np.full((4, 4), 9.0, dtype=np.float32))
+    check(c)
+
+
+@pytest.mark.parametrize("n_cand", [4095, 4096, 8191, 8192, 8193, 16383, 16384, 16385])
+def test_index_candidate_count_boundaries(n_cand):
+    # around the valid counts where a thread's share of the row grows from 8 to 16 columns
+    # (8192) and where the builder moves from keys in registers (up to 16384 candidates) to
+    # keys in LDS; counts that are not a multiple of 8 read the row column by column
+    rng = np.random.default_rng(n_cand)
+    n = 5
+    c = dict(name=f"index_{n_cand}", n=n, n_cand=n_cand, positions=rng.integers(0, 40000, size=n).astype(np.int32),
+             logits=inputs.bf16_bits((np.round(rng.standard_normal((n, n_cand)) * 8) / 8).astype(np.float32)),
+             n_valid=np.array([n_cand, n_cand - 1, n_cand // 2 + 3, 513, 64], dtype=np.int32), topk=640,
+             window=128, self_in_window=False, n_swa=8192, cmp_base=8192, k_cmp=512)
+    c["logits"][0, -3:] = inputs.bf16_bits(np.full(3, 9.0, dtype=np.float32))  # the largest in the last columns
     check(c)
 
 
