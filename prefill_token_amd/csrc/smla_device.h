@@ -232,11 +232,14 @@ __device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bi
 // LDS DMA (buffer_load_dword[x4] ... lds): every lane writes its 4 / 16 bytes at
 // lds_base + 4*lane / 16*lane, read at byte offset voff of a buffer resource.  An
 // offset at or beyond the resource's size reads as zeros, which is how entries that are
-// not read (sentinels, beyond the length) become zero rows without a branch.  Issued
-// from asm so that the compiler does not make its own LDS reads wait for it; the tile
-// loop waits (vmcnt 0) before the barrier that publishes the data.  Vector loads retire
-// in order, so the compiler's own vmcnt waits stay correct (they can only over-wait).
-// M0 is saved and restored around the DMA (the compiler reserves it for its own use).
+// not read (sentinels, beyond the length) become zero rows without a branch.  Whoever
+// reads the rows waits for them (vmcnt 0) before the barrier that publishes them.
+// dma16 / dma4 are issued from asm (no register results; M0 saved and restored), which the
+// compiler schedules as written and does not count: the tile loops use them.  Vector
+// loads retire in order, so the compiler's own waits stay correct (they can only
+// over-wait).  dma16c / dma4c are the compiler's own LDS-DMA loads, which it counts like
+// any other: an item's prologue issues its first tile with them after its q loads, so
+// that the compiler's wait for q leaves the DMA in flight.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -259,6 +262,14 @@ __device__ __forceinline__ void dma4(uint32_t voff, __amdgpu_buffer_rsrc_t rsrc,
       : "=&s"(save)
       : "v"(voff), "s"(rsrc), "s"(lds_base)
       : "memory");
+}
+__device__ __forceinline__ void dma16c(uint32_t voff, __amdgpu_buffer_rsrc_t rsrc, uint32_t lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(size_t)lds_base, 16, voff,
+                                           0, 0, 0);
+}
+__device__ __forceinline__ void dma4c(uint32_t voff, __amdgpu_buffer_rsrc_t rsrc, uint32_t lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(size_t)lds_base, 4, voff,
+                                           0, 0, 0);
 }
 
 #ifdef SMLA_DEBUG_CHECKS

@@ -637,20 +637,24 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
   // One part of the LDS DMA of a tile, as if issued by wave vw: part k < 4 moves DMA group
   // 4vw + k (two rows, one 1 KB instruction; the rows' ids come from two lanes by
   // readlane), part 4 the scale rows of 16 ids (vw < 4, one shuffle).  Rows that are not
-  // read come in as zeros.
-  auto dma_part = [&](int k, int vw, int id_vec, unsigned char* raw, unsigned char* sc) {
+  // read come in as zeros.  counted: the compiler's own DMA loads (an item's first tile),
+  // else the asm ones (the tile loop).
+  auto dma_part = [&](int k, int vw, int id_vec, unsigned char* raw, unsigned char* sc, auto counted_c) {
+    constexpr bool counted = decltype(counted_c)::value;
     const int lane = ((int)threadIdx.x + opaque_zero()) & 63;
     if (k < 4) {
       const int gi = 4 * vw + k;
       const int i0 = __builtin_amdgcn_readlane(id_vec, 2 * gi), i1 = __builtin_amdgcn_readlane(id_vec, 2 * gi + 1);
       const int id = (lane & 1) ? i1 : i0;
       const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(raw + gi * C::GS));
-      dma16(id >= 0 ? (uint32_t)id * C::RB + 16 * (lane >> 1) : kNoRow, pool_rs, dst);
+      const uint32_t off = id >= 0 ? (uint32_t)id * C::RB + 16 * (lane >> 1) : kNoRow;
+      if constexpr (counted) dma16c(off, pool_rs, dst); else dma16(off, pool_rs, dst);
     } else {
       const int f = 64 * vw + lane;
       const int id = __shfl(id_vec, (f / 4) & 63);
       const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(sc + 256 * vw));
-      dma4(id >= 0 ? (uint32_t)id * C::NSB + 4 * (f % 4) : kNoRow, scale_rs, dst);
+      const uint32_t off = id >= 0 ? (uint32_t)id * C::NSB + 4 * (f % 4) : kNoRow;
+      if constexpr (counted) dma4c(off, scale_rs, dst); else dma4(off, scale_rs, dst);
     }
   };
   // tile i's raw rows and scales in buffer i mod 3 (i >= -1: the P.V waves ask for i - 1)
@@ -689,40 +693,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
         x[k][j] = make_uint4(v[0], v[1], v[2], v[3]);
       }
     }
-  };
-  // The same loads for the between-item prologue (NU = 4), from asm: the compiler does
-  // not track them, so its own waits (which also count the asm tile DMA issued after
-  // them) cannot hold q_units up until that DMA lands.  The caller waits with an explicit
-  // vmcnt that leaves the DMA in flight, then passes x through an asm fence before any
-  // use (q_fence).
-  auto q_load_asm = [&](const Item& I, uint4 (&x)[4][4]) {
-    const int tid = (int)threadIdx.x + opaque_zero(), qb = tid & 15;
-    const auto& K = karg();
-    const int hq = K.h_q;
-    const __amdgpu_buffer_rsrc_t qrs = buf_rsrc(K.q + (size_t)I.t * hq * D, (uint32_t)(hq * D * 2));
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t off = (uint32_t)(((tid >> 4) + 16 * k) * D + 32 * qb) * 2u;
-      u32x4 v0, v1, v2, v3;
-      asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(v0) : "v"(off), "s"(qrs) : "memory");
-      asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen offset:16" : "=v"(v1) : "v"(off), "s"(qrs) : "memory");
-      asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen offset:32" : "=v"(v2) : "v"(off), "s"(qrs) : "memory");
-      asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen offset:48" : "=v"(v3) : "v"(off), "s"(qrs) : "memory");
-      x[k][0] = make_uint4(v0[0], v0[1], v0[2], v0[3]);
-      x[k][1] = make_uint4(v1[0], v1[1], v1[2], v1[3]);
-      x[k][2] = make_uint4(v2[0], v2[1], v2[2], v2[3]);
-      x[k][3] = make_uint4(v3[0], v3[1], v3[2], v3[3]);
-    }
-  };
-  auto q_fence = [&](uint4 (&x)[4][4]) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x4 v = {x[k][j].x, x[k][j].y, x[k][j].z, x[k][j].w};
-        asm volatile("" : "+v"(v));
-        x[k][j] = make_uint4(v[0], v[1], v[2], v[3]);
-      }
   };
   // cos / sin of angle pos * theta^(-2i/64), i < 32: the angle in fp64 (the inverse
   // frequencies are computed once per workgroup), reduced to [-pi, pi] (Cody-Waite with a
@@ -861,35 +831,22 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
     // first-tile DMA (all of it, 9 instructions per wave), cos / sin table, q tile
     auto transition = [&](auto nu_c, uint4 (&x)[4][4], const int id0) {
       // the item after this one, from the workspace's counter: fetched first, published
-      // (before B_A) last, so that waiting for it holds nothing up
+      // (before B_A) last, so that waiting for it holds nothing up.  The address is made
+      // opaque so that the compiler issues a plain returning atomic (a wave reduction
+      // around it would wait for its result, and so for the q loads, on the spot).
       const bool leader = w == 0 && (((int)threadIdx.x + opaque_zero()) & 63) == 0;
       unsigned nx = 0;
-      if constexpr (decltype(nu_c)::value == 4) {
-        // from asm as well (a plain atomicAdd would be rewritten into a wave reduction
-        // that waits for its result, and so for the q loads, on the spot); its result is
-        // covered by the vmcnt(9) below, which leaves only the DMA in flight
-        if (leader) {
-          unsigned* ctr = a.sched;
-          asm volatile("global_atomic_add %0, %1, %2, off sc0" : "=v"(nx) : "v"(ctr), "v"(1u) : "memory");
-        }
-      } else {
-        if (leader) nx = atomicAdd(a.sched, 1u);
-      }
+      if (leader) nx = atomicAdd(a.sched + opaque_zero(), 1u);
       // the DMA is issued without a branch (an item without tiles moves zeros)
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        dma_part(k, w, id0, raw_buf(0), sc_buf(0));
-        dma_part(k, w + 4, id0, raw_buf(0), sc_buf(0));
+        dma_part(k, w, id0, raw_buf(0), sc_buf(0), std::true_type{});
+        dma_part(k, w + 4, id0, raw_buf(0), sc_buf(0), std::true_type{});
       }
-      dma_part(4, w, id0, raw_buf(0), sc_buf(0));
+      dma_part(4, w, id0, raw_buf(0), sc_buf(0), std::true_type{});
       rope_tab(I);
-      if constexpr (decltype(nu_c)::value == 4) {
-        // the asm q loads (and the counter fetch) landed; the 9 DMA instructions after
-        // them may still be in flight
-        __builtin_amdgcn_s_waitcnt(0x0F79);
-        q_fence(x);
-        if (leader) asm volatile("" : "+v"(nx));
-      }
+      // (the compiler's wait for q counts the counter fetch and the 9 DMA loads issued
+      // after it, which stay in flight)
       q_units(nu_c, x);
       if (leader) flag_l[12] = (int)gridDim.x + (int)nx;
     };
@@ -1104,7 +1061,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
       // the first ids are resolved before the q loads go out, so that the compiler's wait
       // for them does not wait for q as well
       const int id0 = valid_id(I, I.tb, raw_cur);
-      q_load_asm(I, x);
+      q_load(I, std::integral_constant<int, 4>{}, x);
       transition(std::integral_constant<int, 4>{}, x, id0);
       asm volatile("" ::"v"(tch0), "v"(tch1));  // the touches' results are never looked at
     }
@@ -1225,9 +1182,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
               // this wave's share of the next tile's DMA and that of its SIMD's QK wave
               // (w - 4): rows 32 (w - 4) + 8 (2 sh + kc) .. + 7 and 128 + ..., scales last
               if constexpr (DM) {
-                dma_part(2 * sh + kc, w, id_next, raw_buf(it + 1), sc_buf(it + 1));
-                dma_part(2 * sh + kc, w - 4, id_next, raw_buf(it + 1), sc_buf(it + 1));
-                if (sh == 1 && kc == 1) dma_part(4, w - 4, id_next, raw_buf(it + 1), sc_buf(it + 1));
+                dma_part(2 * sh + kc, w, id_next, raw_buf(it + 1), sc_buf(it + 1), std::false_type{});
+                dma_part(2 * sh + kc, w - 4, id_next, raw_buf(it + 1), sc_buf(it + 1), std::false_type{});
+                if (sh == 1 && kc == 1) dma_part(4, w - 4, id_next, raw_buf(it + 1), sc_buf(it + 1), std::false_type{});
               }
               const int ks8 = 2 * v + kc;  // 64-dim step of the row
               const uint4 lo = *reinterpret_cast<const uint4*>(raw_l + raw_off<C>(r, 4 * ks8 + lhalf));
@@ -1262,10 +1219,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
         } else if constexpr (DM) {
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
-            dma_part(k, w, id_next, raw_buf(it + 1), sc_buf(it + 1));
-            dma_part(k, w - 4, id_next, raw_buf(it + 1), sc_buf(it + 1));
+            dma_part(k, w, id_next, raw_buf(it + 1), sc_buf(it + 1), std::false_type{});
+            dma_part(k, w - 4, id_next, raw_buf(it + 1), sc_buf(it + 1), std::false_type{});
           }
-          dma_part(4, w - 4, id_next, raw_buf(it + 1), sc_buf(it + 1));
+          dma_part(4, w - 4, id_next, raw_buf(it + 1), sc_buf(it + 1), std::false_type{});
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);
         raw_next = raw_next2;
