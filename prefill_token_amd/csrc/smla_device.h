@@ -299,6 +299,23 @@ __device__ __forceinline__ float dpp_f32(float v) {
 
 // A zero the compiler cannot see through: lane-dependent address math derived from it
 // is recomputed where it is used instead of being hoisted (and kept live) across loops.
+// Lane pair (l, l ^ 32) exchanges through v_permlane32_swap (one VALU op, no LDS round
+// trip): swapping a register with itself leaves lanes 0..31 of the first result and lanes
+// 32..63 of the second holding their own value, the other lanes their partner's, so each
+// lane sees both values of its pair in the two results.
+__device__ __forceinline__ uint32_t xor32_u32(uint32_t v) {  // the value of lane l ^ 32
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, true, false);
+  return (threadIdx.x & 32) ? (uint32_t)r[0] : (uint32_t)r[1];
+}
+__device__ __forceinline__ float pair_max(float v) {  // max over the pair, in both lanes
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v), __builtin_bit_cast(uint32_t, v), true, false);
+  return fmaxf(__uint_as_float((uint32_t)r[0]), __uint_as_float((uint32_t)r[1]));
+}
+__device__ __forceinline__ float pair_sum(float v) {  // sum over the pair, in both lanes
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v), __builtin_bit_cast(uint32_t, v), true, false);
+  return __uint_as_float((uint32_t)r[0]) + __uint_as_float((uint32_t)r[1]);
+}
+
 __device__ __forceinline__ int opaque_zero() {
   int z;
   asm volatile("v_mov_b32 %0, 0" : "=v"(z));

@@ -370,7 +370,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
         s[i] = __builtin_amdgcn_inverse_ballot_w64(lm) ? s[i] : -INFINITY;
         mloc = fmaxf(mloc, s[i]);
       }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+      mloc = pair_max(mloc);
       if (lhalf == 0) maxx[qc * HP + 32 * qa + lrow] = mloc;
     }
     __syncthreads();  // B2: maxima exchanged
@@ -460,7 +460,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_main(KArgs a) {
 
   // ---------------- finish: l per head, then normalize + epilogue, or write partials
   if (qd == 0) {
-    const float lw = l_run + __shfl_xor(l_run, 32);
+    const float lw = pair_sum(l_run);
     if (lhalf == 0) lsum[qc * HP + 32 * qa + lrow] = lw;
     if (qc == 0 && lhalf == 0) maxx[32 * qa + lrow] = m_run;
   }
@@ -1006,7 +1006,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
             s[i] = __builtin_amdgcn_inverse_ballot_w64(lmk) ? s[i] : -INFINITY;
             lm = fmaxf(lm, s[i]);
           }
-          lm = fmaxf(lm, __shfl_xor(lm, 32));
+          lm = pair_max(lm);
           // P against the running max; exact unless the flag below sends the tile to the
           // slow path, which rewrites it
           const float msafe = m_run;
@@ -1046,7 +1046,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
         if (n > 0) check(n);
         const int lane = ((int)threadIdx.x + opaque_zero()) & 63, lrow = lane & 31, lhalf = lane >> 5;
         const int head = 32 * qa + lrow;
-        const float lw = l_run + __shfl_xor(l_run, 32);
+        const float lw = pair_sum(l_run);
         if (lhalf == 0) lsum[qc * HP + head] = lw;
         if (qc == 0 && lhalf == 0) mfin[head] = m_run;
         if (next < total) {
@@ -1284,7 +1284,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
             float amax = 0.f;
 #pragma unroll
             for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(acc[mb][nb][i]));
-            amax = fmaxf(amax, __shfl_xor(amax, 32));
+            amax = pair_max(amax);
             const int e8 = ue8m0_exp(amax);
             const float sc = ue8m0_f32((uint32_t)e8);  // codes = RNE(o / 2^(e-127))
             uint32_t wd[4];
@@ -1295,7 +1295,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
             // word g holds dims 8g + 4 lhalf .. + 3: lhalf 0 keeps g = 0, 1 and takes the
             // partner's, lhalf 1 keeps g = 2, 3
             const uint32_t give0 = lhalf ? wd[0] : wd[2], give1 = lhalf ? wd[1] : wd[3];
-            const uint32_t got0 = (uint32_t)__shfl_xor((int)give0, 32), got1 = (uint32_t)__shfl_xor((int)give1, 32);
+            const uint32_t got0 = xor32_u32(give0), got1 = xor32_u32(give1);
             const uint4 st = lhalf ? make_uint4(got0, wd[2], got1, wd[3]) : make_uint4(wd[0], got0, wd[1], got1);
             if (h < hq) {
               const size_t g0 = ((size_t)I.t * hq + h) * D + 32 * gb;
@@ -1335,7 +1335,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
               float am = 0.f;
 #pragma unroll
               for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(acc[mb][nb][i]));
-              am = fmaxf(am, __shfl_xor(am, 32));
+              am = pair_max(am);
               float enc, dec;
               f16_block_scale(am, enc, dec);
               if (lane < 32) psc[(4 * v + nb) * HP + 32 * mb + lrow] = dec;
@@ -1594,7 +1594,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_nv(KArgs a) {
         s[i] = valid_l[slot] ? s[i] : -INFINITY;
         lm = fmaxf(lm, s[i]);
       }
-      lm = fmaxf(lm, __shfl_xor(lm, 32));
+      lm = pair_max(lm);
       if (lhalf == 0) maxx[qc * HP + 32 * qa + lrow] = lm;
     }
     __syncthreads();  // block maxima of both slot halves visible
@@ -1667,7 +1667,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_nv(KArgs a) {
 
   // ---------------- finish: l and m per head, then normalize + epilogue, or the partials
   if (qd == 0) {
-    const float lw = l_run + __shfl_xor(l_run, 32);
+    const float lw = pair_sum(l_run);
     if (lhalf == 0) lsum[qc * HP + 32 * qa + lrow] = lw;
     if (qc == 0 && lhalf == 0) maxx[32 * qa + lrow] = m_run;
   }
@@ -2002,7 +2002,7 @@ __global__ __launch_bounds__(CTHREADS) void smla_combine_lm4(KArgs a) {
   float amax = 0.f;
 #pragma unroll
   for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(o[e]));
-  amax = fmaxf(amax, __shfl_xor(amax, 32));
+  amax = pair_max(amax);
   if (h >= hq) return;
   const size_t g0 = ((size_t)t * hq + h) * D + 32 * gb + 16 * gp;
   const int e8 = ue8m0_exp(amax);
