@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define SMLA_ABI_VERSION 4
+#define SMLA_ABI_VERSION 5
 
 /* return codes */
 #define SMLA_OK 0
@@ -364,6 +364,16 @@ const char* sparse_mla_last_error(void);
 
 /* SMLA_ABI_VERSION of the loaded library. */
 int sparse_mla_abi_version(void);
+
+/* Per-kernel timing of the next step call (sparse_mla_fwd, sparse_mla_fwd_noalloc or
+ * sparse_mla_fwd_ds_nvfp4) made on this thread: each non-NULL argument is a hipEvent_t the
+ * caller created, recorded on that call's stream.  before_main: just before the main kernel
+ * (after the item-order kernel, if any); after_main: just after it, i.e. before the split
+ * combine when there is one; after_all: after the call's last kernel.  Every step call on
+ * this thread consumes the armed events, whether it launches or fails its checks (then
+ * nothing is recorded); calls with s_q = 0 record nothing.  For measurement tools: the
+ * records become graph nodes when the call is captured.  Always returns SMLA_OK. */
+int sparse_mla_profile_events(void* before_main, void* after_main, void* after_all);
 
 #ifdef __cplusplus
 }

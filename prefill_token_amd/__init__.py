@@ -20,7 +20,7 @@ from ._lib import (SMLA_ERR_HIP, SMLA_ERR_NULL, SMLA_ERR_SHAPE, SMLA_ERR_VALUE, 
 
 __all__ = [
     "sparse_mla_fwd", "sparse_mla_workspace_size", "sparse_mla_num_splits", "sparse_mla_last_error",
-    "sparse_mla_abi_version", "sparse_mla_fwd_ds_nvfp4", "SmlaDsParams", "sparse_mla_fwd_noalloc", "sparse_mla_noalloc_num_splits", "sparse_mla_kv_insert", "sparse_mla_build_index", "sparse_mla_wo_a", "make_params",
+    "sparse_mla_abi_version", "sparse_mla_profile_events", "sparse_mla_fwd_ds_nvfp4", "SmlaDsParams", "sparse_mla_fwd_noalloc", "sparse_mla_noalloc_num_splits", "sparse_mla_kv_insert", "sparse_mla_build_index", "sparse_mla_wo_a", "make_params",
     "make_kv_insert_params", "make_index_params", "SmlaParams", "SmlaKvInsertParams", "SmlaIndexParams", "SmlaError",
     "LibraryMissing",
     "SMLA_OK", "SMLA_ERR_NULL", "SMLA_ERR_SHAPE", "SMLA_ERR_VALUE", "SMLA_ERR_HIP",
@@ -116,6 +116,20 @@ def sparse_mla_last_error() -> str:
 
 def sparse_mla_abi_version() -> int:
     return int(_lib.load().sparse_mla_abi_version())
+
+
+def sparse_mla_profile_events(before_main=None, after_main=None, after_all=None) -> None:
+    """Arm torch.cuda.Event objects (created with enable_timing=True and recorded once, so
+    that they exist) to be recorded by this thread's next step call: before its main kernel,
+    after it, and after its last kernel."""
+    def handle(ev):
+        if ev is None:
+            return None
+        h = int(ev.cuda_event)
+        if h == 0:
+            raise ValueError("record the event once before arming it (torch creates events lazily)")
+        return h
+    _lib.load().sparse_mla_profile_events(handle(before_main), handle(after_main), handle(after_all))
 
 
 def sparse_mla_noalloc_num_splits(params: SmlaParams) -> int:

@@ -8,7 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsmla.so")
 DEBUG_LIB_PATH = os.path.join(HERE, "libsmla_debug.so")
 
-SMLA_ABI_VERSION = 4  # the layout of the structures below
+SMLA_ABI_VERSION = 5  # the layout of the structures below and the exported functions
 SMLA_NOALLOC_SCRATCH_BYTES = 34 << 20
 SMLA_DEBUG_WORD_OFFSET = 8
 SMLA_DEBUG_BAD_INDEX = 1
@@ -139,6 +139,8 @@ def _open(path: str) -> ctypes.CDLL:
     lib.sparse_mla_fwd_ds_nvfp4.argtypes = [P, P, P, P, P, P, P, P, P, P, P, ctypes.POINTER(SmlaDsParams)]
     lib.sparse_mla_noalloc_num_splits.restype = ctypes.c_int
     lib.sparse_mla_noalloc_num_splits.argtypes = [ctypes.POINTER(SmlaParams)]
+    lib.sparse_mla_profile_events.restype = ctypes.c_int
+    lib.sparse_mla_profile_events.argtypes = [P, P, P]
     got = lib.sparse_mla_abi_version()
     if got != SMLA_ABI_VERSION:
         raise LibraryMissing(f"{path} has ABI version {got}, this binding needs {SMLA_ABI_VERSION}: rebuild it with "

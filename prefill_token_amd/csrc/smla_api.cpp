@@ -14,6 +14,16 @@
 namespace {
 
 thread_local std::string g_last_error;
+// events armed by sparse_mla_profile_events for this thread's next step call
+thread_local void* g_prof_events[3] = {nullptr, nullptr, nullptr};
+
+// the armed events, disarmed (every step call consumes them, launched or not)
+void take_prof_events(smla::LaunchArgs& a) {
+  a.ev_main = static_cast<hipEvent_t>(g_prof_events[0]);
+  a.ev_split = static_cast<hipEvent_t>(g_prof_events[1]);
+  a.ev_end = static_cast<hipEvent_t>(g_prof_events[2]);
+  g_prof_events[0] = g_prof_events[1] = g_prof_events[2] = nullptr;
+}
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -106,6 +116,13 @@ extern "C" {
 
 int sparse_mla_abi_version(void) { return SMLA_ABI_VERSION; }
 
+int sparse_mla_profile_events(void* before_main, void* after_main, void* after_all) {
+  g_prof_events[0] = before_main;
+  g_prof_events[1] = after_main;
+  g_prof_events[2] = after_all;
+  return SMLA_OK;
+}
+
 int sparse_mla_debug_checks(void) {
 #ifdef SMLA_DEBUG_CHECKS
   return 1;
@@ -156,8 +173,11 @@ int check_fwd_arrays(const void* q, const void* kv_pool, const uint8_t* kv_scale
 // Enqueue the step with the given scratch buffer and split count.
 int launch_fwd(const void* q, const void* kv_pool, const uint8_t* kv_scales, const int32_t* indices,
                const int32_t* topk_length, const int32_t* positions, const float* norm_w, uint8_t* out_fp8,
-               uint8_t* out_scales, const smla_params* p, void* workspace, int ns) {
+               uint8_t* out_scales, const smla_params* p, void* workspace, int ns, const smla::LaunchArgs& ev) {
   smla::LaunchArgs a;
+  a.ev_main = ev.ev_main;
+  a.ev_split = ev.ev_split;
+  a.ev_end = ev.ev_end;
   a.q = static_cast<const uint16_t*>(q);
   a.kv_pool = kv_pool;
   a.kv_scales = kv_scales;
@@ -194,6 +214,8 @@ int sparse_mla_fwd(const void* q, const void* kv_pool, const uint8_t* kv_scales,
                    const int32_t* topk_length, const int32_t* positions, const float* norm_w, uint8_t* out_fp8,
                    uint8_t* out_scales, const smla_params* p) {
   g_last_error.clear();
+  smla::LaunchArgs ev;
+  take_prof_events(ev);
   int rc = check_params(p);
   if (rc != SMLA_OK) return rc;
   if (p->s_q == 0) return SMLA_OK;
@@ -206,13 +228,15 @@ int sparse_mla_fwd(const void* q, const void* kv_pool, const uint8_t* kv_scales,
     return fail(SMLA_ERR_VALUE, "workspace of %zu bytes needed (got %zu)", need,
                 p->workspace ? p->workspace_bytes : (size_t)0);
   return launch_fwd(q, kv_pool, kv_scales, indices, topk_length, positions, norm_w, out_fp8, out_scales, p,
-                    p->workspace, ns);
+                    p->workspace, ns, ev);
 }
 
 int sparse_mla_fwd_noalloc(const void* q, const void* kv_pool, const uint8_t* kv_scales, const int32_t* indices,
                            const int32_t* topk_length, const int32_t* positions, const float* norm_w,
                            uint8_t* out_fp8, uint8_t* out_scales, const smla_params* p) {
   g_last_error.clear();
+  smla::LaunchArgs ev;
+  take_prof_events(ev);
   int rc = check_params(p);
   if (rc != SMLA_OK) return rc;
   if (p->s_q == 0) return SMLA_OK;
@@ -227,7 +251,7 @@ int sparse_mla_fwd_noalloc(const void* q, const void* kv_pool, const uint8_t* kv
   const hipError_t e = smla::noalloc_scratch(&scratch);
   if (e != hipSuccess) return fail(SMLA_ERR_HIP, "static scratch lookup failed: %s", hipGetErrorString(e));
   return launch_fwd(q, kv_pool, kv_scales, indices, topk_length, positions, norm_w, out_fp8, out_scales, p,
-                    scratch, ns);
+                    scratch, ns, ev);
 }
 
 int sparse_mla_fwd_ds_nvfp4(const void* q, const uint8_t* swa_pool, const uint8_t* swa_scales,
@@ -235,6 +259,8 @@ int sparse_mla_fwd_ds_nvfp4(const void* q, const uint8_t* swa_pool, const uint8_
                             const int32_t* topk_length, const int32_t* positions, const float* norm_w,
                             uint8_t* out_fp8, uint8_t* out_scales, const smla_ds_params* dp) {
   g_last_error.clear();
+  smla::LaunchArgs a;
+  take_prof_events(a);
   if (!dp) return fail(SMLA_ERR_NULL, "params is NULL");
   const smla_params* p = &dp->base;
   int rc = check_params(p);
@@ -261,7 +287,6 @@ int sparse_mla_fwd_ds_nvfp4(const void* q, const uint8_t* swa_pool, const uint8_
   if (need > 0 && (!p->workspace || p->workspace_bytes < need))
     return fail(SMLA_ERR_VALUE, "workspace of %zu bytes needed (got %zu)", need,
                 p->workspace ? p->workspace_bytes : (size_t)0);
-  smla::LaunchArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.kv_pool = swa_pool;
   a.kv_scales = swa_scales;

@@ -29,6 +29,9 @@ struct LaunchArgs {
   const uint8_t* cmp_scales = nullptr;  // E4M3 [n_cmp][d/16]
   int64_t n_cmp = 0;
   int swa_entries = 0;                  // index entries [0, swa_entries) name SWA rows
+  // optional events recorded on the stream: before the main kernel, between it and the
+  // split combine (or after it when there is none), and after the last kernel
+  hipEvent_t ev_main = nullptr, ev_split = nullptr, ev_end = nullptr;
 };
 
 // Largest rotary width the two-pool kernel stages (its q prologue's staging area).

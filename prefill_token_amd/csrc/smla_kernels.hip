@@ -2141,12 +2141,18 @@ hipError_t launch_t(const LaunchArgs& x, const KArgs& k) {
       if (e != hipSuccess) return e;
       kw.order = order;
     }
+    if (x.ev_main) (void)hipEventRecord(x.ev_main, x.stream);
     hipLaunchKernelGGL(smla_ws, dim3((unsigned)(items < cus ? items : cus)), dim3(NTHREADS), 0, x.stream, kw);
   } else {
+    if (x.ev_main) (void)hipEventRecord(x.ev_main, x.stream);
     hipLaunchKernelGGL((smla_main<D, EB>), dim3((unsigned)items), dim3(NTHREADS), 0, x.stream, k);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || ns == 1) return e;
+  if (x.ev_split) (void)hipEventRecord(x.ev_split, x.stream);
+  if (e != hipSuccess || ns == 1) {
+    if (x.ev_end) (void)hipEventRecord(x.ev_end, x.stream);
+    return e;
+  }
   if (ws)
     if (ns <= 8)
       hipLaunchKernelGGL(smla_combine_lm4, dim3((unsigned)x.s_q, 16u), dim3(CTHREADS), 0, x.stream, k);
@@ -2154,7 +2160,9 @@ hipError_t launch_t(const LaunchArgs& x, const KArgs& k) {
       hipLaunchKernelGGL(smla_combine_lm1, dim3((unsigned)x.s_q, 16u), dim3(LMT), 0, x.stream, k);
   else
     hipLaunchKernelGGL((smla_combine<D>), dim3((unsigned)x.s_q, (unsigned)x.h_q), dim3(CTHREADS), 0, x.stream, k);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (x.ev_end) (void)hipEventRecord(x.ev_end, x.stream);
+  return e;
 }
 
 }  // namespace
@@ -2164,11 +2172,16 @@ hipError_t launch(const LaunchArgs& x) {
   if (x.cmp_pool) {
     static_assert(NvCfg::MAX_ROPE >= kNvMaxRope, "the host's rotary limit for the two-pool kernel");
     if (x.d != 512 || x.kv_format != 0) return hipErrorInvalidValue;
+    if (x.ev_main) (void)hipEventRecord(x.ev_main, x.stream);
     hipLaunchKernelGGL(smla_nv, dim3((unsigned)(x.s_q * x.num_splits)), dim3(NTHREADS), 0, x.stream, k);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || x.num_splits == 1) return e;
-    hipLaunchKernelGGL((smla_combine<512>), dim3((unsigned)x.s_q, (unsigned)x.h_q), dim3(CTHREADS), 0, x.stream, k);
-    return hipGetLastError();
+    if (x.ev_split) (void)hipEventRecord(x.ev_split, x.stream);
+    if (e == hipSuccess && x.num_splits > 1) {
+      hipLaunchKernelGGL((smla_combine<512>), dim3((unsigned)x.s_q, (unsigned)x.h_q), dim3(CTHREADS), 0, x.stream, k);
+      e = hipGetLastError();
+    }
+    if (x.ev_end) (void)hipEventRecord(x.ev_end, x.stream);
+    return e;
   }
   if (x.d == 512 && x.kv_format == 0) return launch_t<512, 1>(x, k);
   if (x.d == 128 && x.kv_format == 0) return launch_t<128, 1>(x, k);

@@ -40,8 +40,19 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    # 2: sparse_mla_wo_a, the item order in the workspace; 3: the debug build's error word
-    assert smla.sparse_mla_abi_version() == 4 == smla._lib.SMLA_ABI_VERSION
+    # 2: sparse_mla_wo_a, the item order in the workspace; 3: the debug build's error word;
+    # 5: sparse_mla_profile_events
+    assert smla.sparse_mla_abi_version() == 5 == smla._lib.SMLA_ABI_VERSION
+
+
+def test_profile_events_arm_and_disarm_without_a_gpu(lib):
+    # arming takes plain handles; a step call that fails its checks consumes them without
+    # touching them (fake handles are never dereferenced)
+    assert lib.sparse_mla_profile_events(None, None, None) == smla.SMLA_OK
+    assert lib.sparse_mla_profile_events(FAKE, FAKE, FAKE) == smla.SMLA_OK
+    p = good(h_q=65)
+    assert lib.sparse_mla_fwd(*([FAKE] * 9), ctypes.byref(p)) == smla.SMLA_ERR_SHAPE
+    assert lib.sparse_mla_profile_events(None, None, None) == smla.SMLA_OK
 
 
 def test_debug_build_exports_the_same_symbols_and_says_so(lib):

@@ -11,8 +11,10 @@ topk_length, empty and all-sentinel rows, stale ids beyond topk_length pointing 
 that decode to NaN, duplicates, position 0, fewer heads, no rotary dims, the E4M3 pool at
 d = 128, the ends of the exact scale range, forced split counts, bit-reproducibility, and
 one workspace shared by successive calls of different shapes (its scheduler counters are
-left zero by every call).
+left zero by every call), and the per-kernel profiling events (no effect on the outputs).
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -266,3 +268,38 @@ def test_workspace_reused_across_calls():
             for k in ("codes", "scales", "f32"):
                 assert a[k].tobytes() == b[k].tobytes(), (ns, k)
     compare(run_gpu(cases[0], workspace=ws), run_oracle(cases[0]))
+
+
+def test_profile_events_time_each_kernel():
+    # sparse_mla_profile_events arms three events for this thread's next step call: before
+    # its main kernel, after it, after its last kernel.  Arming changes no output, and every
+    # step call consumes the armed events, also one that fails its checks.
+    from prefill_token_amd import _lib, make_params, sparse_mla_profile_events
+
+    inp = _decode_case(24, s_q=16)
+    dev = to_device(inp)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in evs:
+        e.record()  # torch creates its events on first record
+    torch.cuda.synchronize()
+    whole = {}
+    for ns in (1, 4):
+        ref = run_gpu(inp, dev_inputs=dev, num_splits=ns)
+        evs[3].record()
+        sparse_mla_profile_events(evs[0], evs[1], evs[2])
+        got = run_gpu(inp, dev_inputs=dev, num_splits=ns)
+        main, tail, whole[ns] = evs[0].elapsed_time(evs[1]), evs[1].elapsed_time(evs[2]), evs[3].elapsed_time(evs[2])
+        assert main > 0 and tail >= 0 and main + tail <= whole[ns] + 1e-3, (ns, main, tail, whole[ns])
+        if ns == 4:
+            assert tail > 0  # the split combine runs between the second and the third event
+        for k in ("codes", "scales", "f32"):
+            assert got[k].tobytes() == ref[k].tobytes(), (ns, k)
+    # a call that fails its checks consumes the armed events: the next call records none
+    for e in evs[:3]:
+        e.record()
+    torch.cuda.synchronize()
+    sparse_mla_profile_events(evs[0], evs[1], evs[2])
+    bad = make_params(s_q=1, h_q=65, d=512, rope_dim=64, topk=640, n_rows=10, kv_format=0, sm_scale=0.1)
+    assert _lib.load().sparse_mla_fwd(*([None] * 9), ctypes.byref(bad)) != 0
+    run_gpu(inp, dev_inputs=dev, num_splits=4)
+    assert evs[0].elapsed_time(evs[2]) < 0.5 * whole[4]
