@@ -296,6 +296,13 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
+// The same for a permutation that reads only lanes of the row itself (quad_perm): no
+// "old" value to materialize, so the compiler can fold the move into the instruction that
+// uses it (v_fmac_f32_dpp and the like).
+template <int CTRL>
+__device__ __forceinline__ float dpp_perm_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
 
 // A zero the compiler cannot see through: lane-dependent address math derived from it
 // is recomputed where it is used instead of being hoisted (and kept live) across loops.
@@ -547,10 +554,7 @@ __device__ void q_prologue(unsigned char* smem, int t, int pos, const KArgs& a, 
     const bool lo_lane = (b & 1) == 0;
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-      float pv[32];
-#pragma unroll
-      for (int e = 0; e < 32; ++e) pv[e] = dpp_f32<0xB1>(y[it][e]);
-      if (rotb) {
+      if (rotb) {  // (both lanes of a pair are rotary lanes: the swap reads active lanes only)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const float4 c4 = *reinterpret_cast<const float4*>(cs + 4 * j);
@@ -559,7 +563,10 @@ __device__ void q_prologue(unsigned char* smem, int t, int pos, const KArgs& a, 
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int e = 4 * j + i;
-            y[it][e] = lo_lane ? y[it][e] * cc[i] - pv[e] * ssn[i] : y[it][e] * cc[i] + pv[e] * ssn[i];
+            // the partner times the sine (the lane swap folded into the multiply), then
+            // y c - p s on the lower lane of the pair, y c + p s on the upper one
+            const float ps = dpp_perm_f32<0xB1>(y[it][e]) * ssn[i];
+            y[it][e] = __builtin_fmaf(y[it][e], cc[i], lo_lane ? -ps : ps);
           }
         }
       }

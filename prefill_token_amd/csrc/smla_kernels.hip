@@ -764,8 +764,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
             const int e = 4 * q4 + m;
-            const float pe = dpp_f32<0xB4>(y[e]);  // quad_perm [0,1,3,2]: lanes 14 <-> 15
-            y[e] = __builtin_fmaf(pe, sv[m], y[e] * cc[m]);
+            // the partner (quad_perm [0,1,3,2]: lanes 14 <-> 15) times the sine: one v_mul
+            // with the lane swap folded in, then one fma
+            const float ps = dpp_perm_f32<0xB4>(y[e]) * sv[m];
+            y[e] = __builtin_fmaf(y[e], cc[m], ps);
           }
         }
       }
