@@ -567,7 +567,8 @@ struct WsCfg {
   static constexpr int OFF_ROPE = OFF_FLAG + 64;           // per wave: cos[32], -sin[32], sin[32]
   static constexpr int OFF_NW = OFF_ROPE + NWAVES * 96 * 4; // norm_w, block b at 36 b floats
   static constexpr int OFF_IFREQ = OFF_NW + (D / 32) * 36 * 4;  // theta^(-2i/r), i < 32, fp64
-  static constexpr int SMEM = OFF_IFREQ + 32 * 8;
+  static constexpr int OFF_ID = OFF_IFREQ + 32 * 8;               // cos 1 [32], sin 0 [32]
+  static constexpr int SMEM = OFF_ID + 64 * 4;
   static_assert(G == 2 && NSB == 16, "layout written for 512-byte rows");
   static_assert(SMEM <= 160 * 1024, "LDS budget");
   static_assert(2 * HP * 512 <= 2 * RAW_BYTES && 2 * HP * 16 <= P_BYTES, "item transition areas");
@@ -753,12 +754,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
       const float inv = qscale * __builtin_amdgcn_rsqf(ss / (float)D + eps);
 #pragma unroll
       for (int e = 0; e < 32; ++e) y[e] = y[e] * inv * wv[e];
-      if (rot && qb >= 14) {
-        // (448 + e, 480 + e) pairs: block 14 takes y c - y' s, block 15 y c + y' s
-        const float* st = rtab + (qb == 14 ? 32 : 64);
+      {
+        // (448 + e, 480 + e) pairs: block 14 takes y c - y' s, block 15 y c + y' s.  The
+        // other lanes run the same instructions with cos 1 and sin 0, an exact identity, so
+        // the row needs no branch (a divergent one costs the same issue slots plus copies
+        // of y at its join)
+        const bool rl = rot && qb >= 14;
+        const float* ct = rl ? rtab : reinterpret_cast<const float*>(smem + C::OFF_ID);
+        const float* st = rl ? rtab + (qb == 14 ? 32 : 64) : reinterpret_cast<const float*>(smem + C::OFF_ID) + 32;
 #pragma unroll
         for (int q4 = 0; q4 < 8; ++q4) {
-          const float4 c4 = *reinterpret_cast<const float4*>(rtab + 4 * q4);
+          const float4 c4 = *reinterpret_cast<const float4*>(ct + 4 * q4);
           const float4 s4 = *reinterpret_cast<const float4*>(st + 4 * q4);
           const float cc[4] = {c4.x, c4.y, c4.z, c4.w}, sv[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
@@ -820,6 +826,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
       const int i = tid - 448;
       reinterpret_cast<double*>(smem + C::OFF_IFREQ)[i] = exp2(-(2.0 * i / (double)a.rope_dim) * a.log2_theta);
     }
+    if (tid >= 384 && tid < 448) reinterpret_cast<float*>(smem + C::OFF_ID)[tid - 384] = tid < 416 ? 1.f : 0.f;
     __syncthreads();
   };
 
