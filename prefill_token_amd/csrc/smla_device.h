@@ -208,8 +208,11 @@ __device__ __forceinline__ size_t partial_floats_d(int, int d) { return (size_t)
 //     32 lhalf of P.V wave v: dims 128v + 32nb + 16 g2 + 4 lhalf + {0..3, 8..11} of head
 //     32 mb + lrow.  Each store instruction of a wave writes 1 KB contiguously.
 //   [WSP_SCL, WSP_M): the decode scale 2^E (f32) of block gb of head h at gb * HP + h;
-//   [WSP_M, WSP_L): m [HP]; [WSP_L, WSP_FLOATS): l [HP].
-constexpr int WSP_SCL = HP * 512 / 2, WSP_M = WSP_SCL + HP * 16, WSP_L = WSP_M + HP, WSP_FLOATS = WSP_L + HP;
+//   [WSP_M, WSP_L): m [HP]; [WSP_L, WSP_ROPE): l [HP];
+//   [WSP_ROPE, WSP_FLOATS): the token's cos [32] and sin [32] of its rotary angles (every
+//     split writes the same table), for the combine's inverse RoPE.
+constexpr int WSP_SCL = HP * 512 / 2, WSP_M = WSP_SCL + HP * 16, WSP_L = WSP_M + HP, WSP_ROPE = WSP_L + HP,
+              WSP_FLOATS = WSP_ROPE + 64;
 static_assert(WSP_FLOATS <= HP * (512 + 2), "smla_ws partials fit the host's per-split stride");
 
 // 2^(-E) and 2^E for a block amax a >= 0 (E from the f32 exponent field, kept where both

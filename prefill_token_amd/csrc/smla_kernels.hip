@@ -1334,6 +1334,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
           pm[lane] = lt > 0.f ? mfin[lane] : -INFINITY;
           pl[lane] = lt;
         }
+        // the token's cos / sin table (this wave's, the one its epilogue would use)
+        if (rot && v == 3 && lane < 32) {
+          part[WSP_ROPE + lane] = rtab[lane];
+          part[WSP_ROPE + 32 + lane] = rtab[64 + lane];
+        }
         if (n > 0) {
           uint4* pv4 = reinterpret_cast<uint4*>(part) + 2 * 4 * 2 * 64 * v + lane;
           float* psc = part + WSP_SCL;
@@ -1927,15 +1932,15 @@ __global__ __launch_bounds__(CTHREADS) void smla_combine(KArgs a) {
 // contiguous bytes per 32 threads.  Workgroup (token, y): y = 4v + 2mb + nbp selects the P.V wave v, head block
 // mb and the block pair nb = 2nbp, 2nbp + 1; thread (lrow, gp, nbl) owns dims 16gp ..
 // 16gp + 15 of block nb = 2nbp + nbl of head 32mb + lrow (slots g = 2gp, 2gp + 1, both
-// lane halves).  Then o = sum_s w_s acc_s / sum_s w_s l_s (w_s = 2^(m_s - M), in split
-// order with a running maximum M; a split that read nothing has m_s = -inf and is never
-// touched), inverse RoPE (blocks 14 and 15 are the two
-// waves of the last workgroup pair: the partner values cross through LDS), the block
-// amax over the thread pair (gp = 0, 1), UE8M0 exponent and E4M3 codes.
+// lane halves).  Then o = sum_s w_s acc_s / sum_s w_s l_s (w_s = 2^(m_s - M), M the largest
+// m_s, taken before the weights so that they do not depend on one another, the sums in
+// split order; a split that read nothing has m_s = -inf and is never touched), inverse
+// RoPE with the cos / sin table the splits wrote (blocks 14 and 15 are the two waves of
+// the last workgroup pair: the partner values cross through LDS), the block amax over the
+// thread pair (gp = 0, 1), UE8M0 exponent and E4M3 codes.
 __global__ __launch_bounds__(CTHREADS) void smla_combine_lm4(KArgs a) {
   constexpr int D = 512, SCH = 8;
   __shared__ __attribute__((aligned(16))) float xch[CTHREADS * 16];
-  __shared__ float cs[32], sn[32];
   const int t = blockIdx.x, y = blockIdx.y, v = y >> 2, mb = (y >> 1) & 1, nbp = y & 1;
   const int tid = threadIdx.x, lrow = tid & 31, gp = (tid >> 5) & 1, nbl = tid >> 6, nb = 2 * nbp + nbl;
   const int h = 32 * mb + lrow, hq = a.h_q, ns = a.num_splits;
@@ -1947,6 +1952,16 @@ __global__ __launch_bounds__(CTHREADS) void smla_combine_lm4(KArgs a) {
   const int s0 = ((((v * 2 + mb) * 4 + nb) * 2 + gp) * 64) + lrow;
   const int gb = 4 * v + nb;
   const bool rot = a.rope_dim > 0 && v == 3 && nbp == 1;
+  // the rotary workgroups' cos / sin of dims 16 gp .. 16 gp + 15 of the pair, written by
+  // the splits (split 0's copy), loaded with the first chunk
+  float4 rc[4], rs[4];
+  if (rot) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      rc[q] = reinterpret_cast<const float4*>(base + WSP_ROPE + 16 * gp)[q];
+      rs[q] = reinterpret_cast<const float4*>(base + WSP_ROPE + 32 + 16 * gp)[q];
+    }
+  }
   float M = -INFINITY, den = 0.f;
   float o[16];
 #pragma unroll
@@ -1966,19 +1981,23 @@ __global__ __launch_bounds__(CTHREADS) void smla_combine_lm4(KArgs a) {
         mv[k] = sp[WSP_M + h];
         lv[k] = sp[WSP_L + h];
       }
-    // the cos / sin table while the first chunk's loads are in flight
-    if (c0 == 0 && rot) rope_table(a.positions[t], a, cs, sn);
+    // the chunk's largest m first (one rescale of the running sums per chunk), then every
+    // split's weight on its own: no chain from split to split
+    float Mc = M;
+#pragma unroll
+    for (int k = 0; k < SCH; ++k)
+      if (c0 + k < ns) Mc = fmaxf(Mc, mv[k]);
+    if (Mc > M) {
+      const float r = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mc);
+      den *= r;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[e] *= r;
+      M = Mc;
+    }
 #pragma unroll
     for (int k = 0; k < SCH; ++k)
       if (c0 + k < ns && mv[k] != -INFINITY) {
-        if (mv[k] > M) {
-          const float r = M == -INFINITY ? 0.f : exp2f(M - mv[k]);
-          den *= r;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) o[e] *= r;
-          M = mv[k];
-        }
-        const float wv = exp2f(mv[k] - M);
+        const float wv = __builtin_amdgcn_exp2f(mv[k] - M);
         den += wv * lv[k];
         const float ws = wv * dv[k];
 #pragma unroll
@@ -2002,11 +2021,12 @@ __global__ __launch_bounds__(CTHREADS) void smla_combine_lm4(KArgs a) {
     for (int e = 0; e < 16; ++e) xch[tid * 16 + e] = o[e];
     __syncthreads();
     const float sg = nbl ? -1.f : 1.f;
+    const float cv[16] = {rc[0].x, rc[0].y, rc[0].z, rc[0].w, rc[1].x, rc[1].y, rc[1].z, rc[1].w,
+                          rc[2].x, rc[2].y, rc[2].z, rc[2].w, rc[3].x, rc[3].y, rc[3].z, rc[3].w};
+    const float sv[16] = {rs[0].x, rs[0].y, rs[0].z, rs[0].w, rs[1].x, rs[1].y, rs[1].z, rs[1].w,
+                          rs[2].x, rs[2].y, rs[2].z, rs[2].w, rs[3].x, rs[3].y, rs[3].z, rs[3].w};
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int j = 16 * gp + e;
-      o[e] = __builtin_fmaf(sg * xch[(tid ^ 64) * 16 + e], sn[j], o[e] * cs[j]);
-    }
+    for (int e = 0; e < 16; ++e) o[e] = __builtin_fmaf(sg * xch[(tid ^ 64) * 16 + e], sv[e], o[e] * cv[e]);
   }
   float amax = 0.f;
 #pragma unroll
@@ -2034,17 +2054,18 @@ __global__ __launch_bounds__(CTHREADS) void smla_combine_lm4(KArgs a) {
 // lane) owns the float4 slot (g, lane) of block nb = 2nbp + nbl, i.e. dims 8g + 4lhalf ..
 // + 3 of that block for head 32mb + (lane & 31).  A wave (fixed nbl, g) reads 1 KB
 // contiguously per split, and every split's load goes out in one round (chunks of 16).
-// Then o = sum_s w_s acc_s / sum_s w_s l_s (w_s = 2^(m_s - M), in split order with a
-// running maximum M; a split that read nothing has m_s = -inf and is never touched),
-// inverse RoPE (the two blocks of a rotary pair are the two halves of the last
-// workgroup pair: the partner value crosses through LDS), the block amax over the 8
-// threads of a (head, block) through LDS, the UE8M0 exponent and the E4M3 codes.
+// Then o = sum_s w_s acc_s / sum_s w_s l_s (w_s = 2^(m_s - M), M the running maximum,
+// raised once per chunk of 16 splits before that chunk's weights, which then do not depend
+// on one another; the sums in split order; a split that read nothing has m_s = -inf and
+// is never touched), inverse RoPE with the cos / sin table the splits wrote (the two
+// blocks of a rotary pair are the two halves of the last workgroup pair: the partner value
+// crosses through LDS), the block amax over the 8 threads of a (head, block) through LDS,
+// the UE8M0 exponent and the E4M3 codes.
 constexpr int LMT = 512;  // smla_combine_lm1 threads
 __global__ __launch_bounds__(LMT) void smla_combine_lm1(KArgs a) {
   constexpr int D = 512, SCH = 16;
   __shared__ __attribute__((aligned(16))) float xch[LMT * 4];
   __shared__ float red[2][32][9];
-  __shared__ float cs[32], sn[32];
   const int t = blockIdx.x, y = blockIdx.y, v = y >> 2, mb = (y >> 1) & 1, nbp = y & 1;
   const int tid = threadIdx.x, lane = tid & 63, g = (tid >> 6) & 3, nbl = tid >> 8;
   const int lrow = lane & 31, lhalf = lane >> 5, nb = 2 * nbp + nbl;
@@ -2055,6 +2076,13 @@ __global__ __launch_bounds__(LMT) void smla_combine_lm1(KArgs a) {
   const int slot = (((((v * 2 + mb) * 4 + nb) * 2 + (g >> 1)) * 64) + lane) * 2 + (g & 1);  // 8-byte index
   const int gb = 4 * v + nb;
   const bool rot = a.rope_dim > 0 && v == 3 && nbp == 1;
+  // the rotary workgroups' cos / sin of pair dims 8g + 4lhalf .. + 3, written by the
+  // splits (split 0's copy), loaded with the first chunk
+  float4 rc = make_float4(0.f, 0.f, 0.f, 0.f), rs = rc;
+  if (rot) {
+    rc = *reinterpret_cast<const float4*>(base + WSP_ROPE + 8 * g + 4 * lhalf);
+    rs = *reinterpret_cast<const float4*>(base + WSP_ROPE + 32 + 8 * g + 4 * lhalf);
+  }
   float M = -INFINITY, den = 0.f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int c0 = 0; c0 < ns; c0 += SCH) {
@@ -2069,18 +2097,22 @@ __global__ __launch_bounds__(LMT) void smla_combine_lm1(KArgs a) {
         mv[k] = sp[WSP_M + h];
         lv[k] = sp[WSP_L + h];
       }
-    // the cos / sin table while the first chunk's loads are in flight
-    if (c0 == 0 && rot) rope_table(a.positions[t], a, cs, sn);
+    // the chunk's largest m first (one rescale of the running sums per chunk), then every
+    // split's weight on its own: no chain from split to split
+    float Mc = M;
+#pragma unroll
+    for (int k = 0; k < SCH; ++k)
+      if (c0 + k < ns) Mc = fmaxf(Mc, mv[k]);
+    if (Mc > M) {
+      const float r = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mc);
+      den *= r;
+      o.x *= r; o.y *= r; o.z *= r; o.w *= r;
+      M = Mc;
+    }
 #pragma unroll
     for (int k = 0; k < SCH; ++k)
       if (c0 + k < ns && mv[k] != -INFINITY) {
-        if (mv[k] > M) {
-          const float r = M == -INFINITY ? 0.f : exp2f(M - mv[k]);
-          den *= r;
-          o.x *= r; o.y *= r; o.z *= r; o.w *= r;
-          M = mv[k];
-        }
-        const float wv = exp2f(mv[k] - M);
+        const float wv = __builtin_amdgcn_exp2f(mv[k] - M);
         den += wv * lv[k];
         const float ws = wv * dv[k];
         o.x += ws * f16_lo(x[k].x); o.y += ws * f16_hi(x[k].x); o.z += ws * f16_lo(x[k].y); o.w += ws * f16_hi(x[k].y);
@@ -2096,11 +2128,9 @@ __global__ __launch_bounds__(LMT) void smla_combine_lm1(KArgs a) {
     const float4 pr = *reinterpret_cast<const float4*>(xch + 4 * (tid ^ 256));
     const float pv[4] = {pr.x, pr.y, pr.z, pr.w};
     const float sg = nbl ? -1.f : 1.f;
+    const float cv[4] = {rc.x, rc.y, rc.z, rc.w}, sv[4] = {rs.x, rs.y, rs.z, rs.w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int j = 8 * g + 4 * lhalf + e;
-      ov[e] = __builtin_fmaf(sg * pv[e], sn[j], ov[e] * cs[j]);
-    }
+    for (int e = 0; e < 4; ++e) ov[e] = __builtin_fmaf(sg * pv[e], sv[e], ov[e] * cv[e]);
   }
   float am = fmaxf(fmaxf(fabsf(ov[0]), fabsf(ov[1])), fmaxf(fabsf(ov[2]), fabsf(ov[3])));
   red[nbl][lrow][2 * g + lhalf] = am;

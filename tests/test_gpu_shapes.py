@@ -4,7 +4,7 @@ the split choice and the persistent grid work in, rotary widths other than 64 (t
 general kernel, its rotary staging above the raw tiles or at offset 0), index rows whose
 width is not a multiple of the 64-entry tile, no entries at all, and rows whose scores
 rise tile after tile (the running reference raised mid-row, past its lazy-rescale
-margin)."""
+margin), and more than 16 splits per token (the combine's chunks of 16)."""
 import math
 
 import numpy as np
@@ -88,3 +88,29 @@ def test_scores_rising_slab_after_slab(seed):
     inp["topk_length"] = np.array([topk, topk, 500, 321], dtype=np.int32)
     inp["sm_scale"] = 4.0 / math.sqrt(512)
     check(inp, extra=tie_aware_tolerance(inp))
+
+
+@pytest.mark.parametrize("ns", [17, 20, 32])
+def test_many_splits(ns):
+    # more than 16 splits per token: the combine merges them in chunks of 16, raising its
+    # running maximum (and rescaling the sums so far) between chunks.  Rows of 2000 random
+    # entries, and rows whose scores rise along the row (entry j reads pool row j, scaled
+    # by 1 + j / 400), so that a later chunk holds the largest m
+    inp = inputs.make("decode_sq64", seed=360 + ns, s_q=3)
+    rng = np.random.default_rng(ns)
+    topk = 2000
+    n_rows = inp["kv_pool"].shape[0]
+    idx = rng.integers(0, n_rows, (3, topk)).astype(np.int32)
+    idx[rng.random(idx.shape) < 0.1] = -1
+    inp["indices"], inp["topk"] = idx, topk
+    inp["topk_length"] = np.array([topk, 1500, 1100], dtype=np.int32)
+    check(inp, num_splits=ns)
+    rising = inputs.make("decode_sq64", seed=370 + ns, s_q=2)
+    lat = rng.standard_normal((topk, 512)).astype(np.float32)
+    lat *= (1.0 + np.arange(topk) / 400.0)[:, None].astype(np.float32)
+    rising["kv_pool"], rising["kv_scales"] = inputs.mx_pool(lat)
+    rising["n_rows"] = topk
+    rising["indices"] = np.tile(np.arange(topk, dtype=np.int32), (2, 1))
+    rising["topk"] = topk
+    rising["topk_length"] = np.array([topk, 1300], dtype=np.int32)
+    check(rising, extra=tie_aware_tolerance(rising), num_splits=ns)
