@@ -595,18 +595,23 @@ def source_digest():
     return h.hexdigest()[:16]
 
 
-def load_traffic(digest, workload):
-    """HBM bytes per call from the committed rocprofv3 counter summary of this workload, if
-    it was taken on the current kernel sources."""
+def load_traffic(digest, workload, kernel=None):
+    """HBM bytes per launch of one kernel (or per call, all kernels) from the committed
+    rocprofv3 counter summary of this workload, if it was taken on the current kernel
+    sources: scaled FETCH_SIZE + WRITE_SIZE medians."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     try:
         with open(path) as f:
             rec = json.load(f)
-        if rec.get("source_digest") == digest:
+        if rec.get("source_digest") != digest:
+            return None
+        if kernel is None:
             return float(rec["hbm_bytes_per_call"])
+        k = rec["kernels"][kernel]
+        return 1024.0 * (k["FETCH_SIZE_KiB_median"] * rec["FETCH_SIZE_copy_factor"] +
+                         k["WRITE_SIZE_KiB_median"] * rec["WRITE_SIZE_copy_factor"])
     except Exception:
-        pass
-    return None
+        return None
 
 
 COPY_PROBE_REPS = 8
@@ -764,7 +769,7 @@ def main():
     peaks = measured_peaks(torch, device)
     print(f"# measured peaks: {json.dumps(peaks)}", file=sys.stderr, flush=True)
     digest = source_digest()
-    traffic = load_traffic(digest, head["workload"])
+    traffic = load_traffic(digest, head["workload"], head["main_kernel"])
     mean_us = head["us_per_call_timed_mean"]
     k_us, k_bytes = head["main_kernel_cold_us_mean"], head["main_kernel_bytes"]
     achieved = k_bytes / (k_us * 1e-6) / 1e9
@@ -778,7 +783,8 @@ def main():
                  "just before and just after it (the span includes the event overhead, timing_overheads)",
         "bytes_per_launch": k_bytes, "mean_us": k_us,
         "whole_call": {"kernels": head["kernels"], "bytes": head["compulsory_bytes"], "mean_us": mean_us,
-                       "achieved_GBs": call_gbs, "frac": call_gbs / HBM_PEAK_GBS},
+                       "achieved_GBs": call_gbs, "frac": call_gbs / HBM_PEAK_GBS,
+                       "traffic": load_traffic(digest, head["workload"])},
         "peak_measured_copy_GBs": peaks.get("copy_GBs"),
         "frac_of_measured_copy": achieved / peaks["copy_GBs"] if peaks.get("copy_GBs") else None,
     }
