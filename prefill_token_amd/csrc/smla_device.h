@@ -321,6 +321,14 @@ __device__ __forceinline__ float pair_max(float v) {  // max over the pair, in b
   const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v), __builtin_bit_cast(uint32_t, v), true, false);
   return fmaxf(__uint_as_float((uint32_t)r[0]), __uint_as_float((uint32_t)r[1]));
 }
+__device__ __forceinline__ float xor32_f32(float v) {  // the value of lane l ^ 32
+  return __uint_as_float(xor32_u32(__float_as_uint(v)));
+}
+// the same for rows of 16 lanes: v_permlane16_swap exchanges rows 0 <-> 1 and 2 <-> 3
+__device__ __forceinline__ float xor16_max(float v) {  // max over lanes l and l ^ 16
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v), __builtin_bit_cast(uint32_t, v), true, false);
+  return fmaxf(__uint_as_float((uint32_t)r[0]), __uint_as_float((uint32_t)r[1]));
+}
 __device__ __forceinline__ float pair_sum(float v) {  // sum over the pair, in both lanes
   const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v), __builtin_bit_cast(uint32_t, v), true, false);
   return __uint_as_float((uint32_t)r[0]) + __uint_as_float((uint32_t)r[1]);

@@ -2050,32 +2050,32 @@ __global__ __launch_bounds__(CTHREADS) void smla_combine_lm4(KArgs a) {
 
 // Combine of smla_ws's splits for more than 8 splits per token, reading the partials in
 // their register order.  Workgroup (token, y), y = 4v + 2mb + nbp, covers P.V wave v's blocks
-// nb = 2nbp, 2nbp + 1 for the 32 heads of head block mb: 512 threads, thread (nbl, g,
-// lane) owns the float4 slot (g, lane) of block nb = 2nbp + nbl, i.e. dims 8g + 4lhalf ..
-// + 3 of that block for head 32mb + (lane & 31).  A wave (fixed nbl, g) reads 1 KB
-// contiguously per split, and every split's load goes out in one round (chunks of 16).
-// Then o = sum_s w_s acc_s / sum_s w_s l_s (w_s = 2^(m_s - M), M the running maximum,
-// raised once per chunk of 16 splits before that chunk's weights, which then do not depend
-// on one another; the sums in split order; a split that read nothing has m_s = -inf and
-// is never touched), inverse RoPE with the cos / sin table the splits wrote (the two
-// blocks of a rotary pair are the two halves of the last workgroup pair: the partner value
-// crosses through LDS), the block amax over the 8 threads of a (head, block) through LDS,
-// the UE8M0 exponent and the E4M3 codes.
+// nb = 2nbp, 2nbp + 1 for the 32 heads of head block mb: 512 threads.  Wave wv holds heads
+// 32mb + 4wv .. + 3 and lane (nbl, g, lhalf, lq) (bits 5, 4..3, 2, 1..0) the float4 slot
+// (g, lhalf) of block nb = 2nbp + nbl of head 32mb + 4wv + lq, i.e. its dims 8g + 4lhalf ..
+// + 3, so that the 8 threads of a (head, block) and the two blocks of a rotary pair share a
+// wave: the block amax and the pair exchange go through DPP and lane swaps, with no LDS and
+// no barrier.  A wave reads 64-byte runs of each split's partials, and every split's load
+// goes out in one round (chunks of 16).  Then o = sum_s w_s acc_s / sum_s w_s l_s (w_s =
+// 2^(m_s - M), M the running maximum, raised once per chunk of 16 splits before that
+// chunk's weights, which then do not depend on one another; the sums in split order; a
+// split that read nothing has m_s = -inf and is never touched), inverse RoPE with the
+// cos / sin table the splits wrote, the UE8M0 exponent and the E4M3 codes.
 constexpr int LMT = 512;  // smla_combine_lm1 threads
 __global__ __launch_bounds__(LMT) void smla_combine_lm1(KArgs a) {
   constexpr int D = 512, SCH = 16;
-  __shared__ __attribute__((aligned(16))) float xch[LMT * 4];
-  __shared__ float red[2][32][9];
   const int t = blockIdx.x, y = blockIdx.y, v = y >> 2, mb = (y >> 1) & 1, nbp = y & 1;
-  const int tid = threadIdx.x, lane = tid & 63, g = (tid >> 6) & 3, nbl = tid >> 8;
-  const int lrow = lane & 31, lhalf = lane >> 5, nb = 2 * nbp + nbl;
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  const int lq = lane & 3, lhalf = (lane >> 2) & 1, g = (lane >> 3) & 3, nbl = lane >> 5;
+  const int lrow = 4 * wv + lq, nb = 2 * nbp + nbl;
   const int h = 32 * mb + lrow, hq = a.h_q, ns = a.num_splits;
   const size_t pf = partial_floats_d(hq, D);
   const float* base = a.ws + (size_t)t * ns * pf;
-  // registers 4g .. 4g + 3 of the lane: half g & 1 of the 16-byte slot g >> 1
-  const int slot = (((((v * 2 + mb) * 4 + nb) * 2 + (g >> 1)) * 64) + lane) * 2 + (g & 1);  // 8-byte index
+  // registers 4g .. 4g + 3 of lane lrow + 32 lhalf of the P.V wave: half g & 1 of its
+  // 16-byte slot g >> 1
+  const int slot = (((((v * 2 + mb) * 4 + nb) * 2 + (g >> 1)) * 64) + lrow + 32 * lhalf) * 2 + (g & 1);  // 8-byte index
   const int gb = 4 * v + nb;
-  const bool rot = a.rope_dim > 0 && v == 3 && nbp == 1;
+  const bool rot = a.rope_dim > 0 && v == 3 && nbp == 1;  // (uniform over the workgroup)
   // the rotary workgroups' cos / sin of pair dims 8g + 4lhalf .. + 3, written by the
   // splits (split 0's copy), loaded with the first chunk
   float4 rc = make_float4(0.f, 0.f, 0.f, 0.f), rs = rc;
@@ -2112,9 +2112,9 @@ __global__ __launch_bounds__(LMT) void smla_combine_lm1(KArgs a) {
 #pragma unroll
     for (int k = 0; k < SCH; ++k)
       if (c0 + k < ns && mv[k] != -INFINITY) {
-        const float wv = __builtin_amdgcn_exp2f(mv[k] - M);
-        den += wv * lv[k];
-        const float ws = wv * dv[k];
+        const float wv_ = __builtin_amdgcn_exp2f(mv[k] - M);
+        den += wv_ * lv[k];
+        const float ws = wv_ * dv[k];
         o.x += ws * f16_lo(x[k].x); o.y += ws * f16_hi(x[k].x); o.z += ws * f16_lo(x[k].y); o.w += ws * f16_hi(x[k].y);
       }
   }
@@ -2122,22 +2122,21 @@ __global__ __launch_bounds__(LMT) void smla_combine_lm1(KArgs a) {
   float ov[4] = {o.x * inv, o.y * inv, o.z * inv, o.w * inv};
   if (rot) {
     // (448 + j, 480 + j), j = 8g + 4lhalf + e: block 14 (nbl 0) takes o c + o' s, block 15
-    // o c - o' s
-    *reinterpret_cast<float4*>(xch + 4 * tid) = make_float4(ov[0], ov[1], ov[2], ov[3]);
-    __syncthreads();
-    const float4 pr = *reinterpret_cast<const float4*>(xch + 4 * (tid ^ 256));
-    const float pv[4] = {pr.x, pr.y, pr.z, pr.w};
+    // o c - o' s; the partner is lane l ^ 32
+    float pv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pv[e] = xor32_f32(ov[e]);
     const float sg = nbl ? -1.f : 1.f;
     const float cv[4] = {rc.x, rc.y, rc.z, rc.w}, sv[4] = {rs.x, rs.y, rs.z, rs.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) ov[e] = __builtin_fmaf(sg * pv[e], sv[e], ov[e] * cv[e]);
   }
-  float am = fmaxf(fmaxf(fabsf(ov[0]), fabsf(ov[1])), fmaxf(fabsf(ov[2]), fabsf(ov[3])));
-  red[nbl][lrow][2 * g + lhalf] = am;
-  __syncthreads();
-  float amax = 0.f;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) amax = fmaxf(amax, red[nbl][lrow][k]);
+  // block amax over the 8 lanes of the (head, block): bits 2..3 by two rotations within the
+  // 16-lane row, bit 4 by the row swap
+  float amax = fmaxf(fmaxf(fabsf(ov[0]), fabsf(ov[1])), fmaxf(fabsf(ov[2]), fabsf(ov[3])));
+  amax = fmaxf(amax, dpp_perm_f32<0x124>(amax));  // row_ror:4
+  amax = fmaxf(amax, dpp_perm_f32<0x128>(amax));  // row_ror:8
+  amax = xor16_max(amax);
   if (h >= hq) return;
   const size_t g0 = ((size_t)t * hq + h) * D + 32 * gb + 8 * g + 4 * lhalf;
   const int e8 = ue8m0_exp(amax);
