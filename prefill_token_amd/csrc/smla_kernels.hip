@@ -564,11 +564,13 @@ struct WsCfg {
   static constexpr int OFF_LSUM = OFF_ALPHA + HP * 4;      // [2 row halves][HP]
   static constexpr int OFF_MFIN = OFF_LSUM + 2 * HP * 4;   // [HP]
   static constexpr int OFF_FLAG = OFF_MFIN + HP * 4;       // overflow [2 tiles][4], rescale [2]
-  static constexpr int OFF_ROPE = OFF_FLAG + 64;           // per wave: cos[32], -sin[32], sin[32]
-  static constexpr int OFF_NW = OFF_ROPE + NWAVES * 96 * 4; // norm_w, block b at 36 b floats
+  // per wave: cos[32], sin[32], then the rotary blocks' q factors A14, B14, A15, B15 [32]
+  static constexpr int OFF_ROPE = OFF_FLAG + 64;
+  static constexpr int ROPE_FLOATS = 192;
+  static constexpr int OFF_NW = OFF_ROPE + NWAVES * ROPE_FLOATS * 4;  // norm_w, block b at 36 b floats
   static constexpr int OFF_IFREQ = OFF_NW + (D / 32) * 36 * 4;  // theta^(-2i/r), i < 32, fp64
-  static constexpr int OFF_ID = OFF_IFREQ + 32 * 8;               // cos 1 [32], sin 0 [32]
-  static constexpr int SMEM = OFF_ID + 64 * 4;
+  static constexpr int OFF_ZERO = OFF_IFREQ + 32 * 8;             // 32 zeros
+  static constexpr int SMEM = OFF_ZERO + 32 * 4;
   static_assert(G == 2 && NSB == 16, "layout written for 512-byte rows");
   static_assert(SMEM <= 160 * 1024, "LDS budget");
   static_assert(2 * HP * 512 <= 2 * RAW_BYTES && 2 * HP * 16 <= P_BYTES, "item transition areas");
@@ -599,7 +601,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
   const int ns = a.num_splits;
   const int total = a.s_q * ns;
   const bool rot = a.rope_dim > 0;  // 0 or 64 on this path
-  float* rtab = reinterpret_cast<float*>(smem + C::OFF_ROPE) + 96 * w;  // this wave's table
+  float* rtab = reinterpret_cast<float*>(smem + C::OFF_ROPE) + C::ROPE_FLOATS * w;  // this wave's table
 
   struct Item {
     int t, pos, lcap, tb, te, n;
@@ -698,7 +700,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
   // cos / sin of angle pos * theta^(-2i/64), i < 32: the angle in fp64 (the inverse
   // frequencies are computed once per workgroup), reduced to [-pi, pi] (Cody-Waite with a
   // two-part 2*pi), then the hardware sine / cosine of the reduced angle in revolutions;
-  // lane i of every wave computes entry i of the wave's own table (cos, -sin, sin).
+  // lane i of every wave computes entry i of the wave's own table: cos, sin, and the q
+  // prologue's factors of the rotary pair (448 + i, 480 + i) with norm_w w folded in,
+  // A14 = w448 c, B14 = -w480 s, A15 = w480 c, B15 = w448 s.
   const double* ifreq = reinterpret_cast<const double*>(smem + C::OFF_IFREQ);
   auto rope_tab = [&](const Item& I) {
     const int lane = ((int)threadIdx.x + opaque_zero()) & 63;
@@ -709,30 +713,37 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
       const double r = fma(-nn, k2PiLo, fma(-nn, k2PiHi, ang));
       const float rev = (float)(r * kInv2Pi);  // in [-1/2, 1/2]
       const float sv = __builtin_amdgcn_sinf(rev), cv = __builtin_amdgcn_cosf(rev);
+      const float* nw = reinterpret_cast<const float*>(smem + C::OFF_NW);
+      const float w0 = nw[36 * 14 + lane], w1 = nw[36 * 15 + lane];
       rtab[lane] = cv;
-      rtab[32 + lane] = -sv;
-      rtab[64 + lane] = sv;
+      rtab[32 + lane] = sv;
+      rtab[64 + lane] = w0 * cv;
+      rtab[96 + lane] = -(w1 * sv);
+      rtab[128 + lane] = w1 * cv;
+      rtab[160 + lane] = w0 * sv;
     }
   };
   // RMSNorm (f32), times sm_scale * log2(e) (the scores come out ready for exp2), RoPE on
-  // dims 448..511 (blocks 14 and 15 swap values through DPP), then two E4M3 terms with
-  // their own UE8M0 scales per block into the q tile
+  // dims 448..511, then two E4M3 terms with their own UE8M0 scales per block into the q
+  // tile.  Norm and RoPE are one step per dim, y' = (A y + B y_partner) * qscale / rms: on
+  // the rotary blocks 14 and 15 A and B are the wave table's norm_w * cos / sin products
+  // (the partner, the same dim of the other block, comes through DPP), elsewhere A =
+  // norm_w and B = 0, an exact identity, so the row needs no branch (a divergent one costs
+  // the same issue slots plus copies of y at its join).
   auto q_units = [&](auto nu_c, const uint4 (&x)[4][4]) {
     constexpr int NU = decltype(nu_c)::value;
     const int tid = (int)threadIdx.x + opaque_zero(), qb = tid & 15;
     const auto& K = karg();
     const float qscale = K.sm_scale * 1.4426950408889634f, eps = K.rms_eps;
-    float wv[32];
-    const float* nw = reinterpret_cast<const float*>(smem + C::OFF_NW) + 36 * qb;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float4 w4 = *reinterpret_cast<const float4*>(nw + 4 * j);
-      wv[4 * j] = w4.x; wv[4 * j + 1] = w4.y; wv[4 * j + 2] = w4.z; wv[4 * j + 3] = w4.w;
-    }
+    const bool rl = rot && qb >= 14;
+    const float* at = rl ? rtab + (qb == 14 ? 64 : 128) : reinterpret_cast<const float*>(smem + C::OFF_NW) + 36 * qb;
+    const float* bt = rl ? rtab + (qb == 14 ? 96 : 160) : reinterpret_cast<const float*>(smem + C::OFF_ZERO);
 #pragma unroll
     for (int k = 0; k < NU; ++k) {
       const int head = (tid >> 4) + (64 / NU) * k;
       float y[32];
+      // the sum of squares straight from the bf16 pairs (products exact in f32)
+      float ss = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t uu[4] = {x[k][j].x, x[k][j].y, x[k][j].z, x[k][j].w};
@@ -740,11 +751,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
         for (int m = 0; m < 4; ++m) {
           y[8 * j + 2 * m] = bf16_f32(uu[m] & 0xFFFFu);
           y[8 * j + 2 * m + 1] = bf16_f32(uu[m] >> 16);
+          const bf16x2 p = __builtin_bit_cast(bf16x2, uu[m]);
+          ss = __builtin_amdgcn_fdot2_f32_bf16(p, p, ss, false);
         }
       }
-      float ss = 0.f;
-#pragma unroll
-      for (int e = 0; e < 32; ++e) ss += y[e] * y[e];
       // lane pairs i^1, i^2, then i <-> 7-i, i <-> 15-i: every lane of the row ends with
       // the same sum
       ss += dpp_f32<0xB1>(ss);
@@ -753,28 +763,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
       ss += dpp_f32<0x140>(ss);
       const float inv = qscale * __builtin_amdgcn_rsqf(ss / (float)D + eps);
 #pragma unroll
-      for (int e = 0; e < 32; ++e) y[e] = y[e] * inv * wv[e];
-      {
-        // (448 + e, 480 + e) pairs: block 14 takes y c - y' s, block 15 y c + y' s.  The
-        // other lanes run the same instructions with cos 1 and sin 0, an exact identity, so
-        // the row needs no branch (a divergent one costs the same issue slots plus copies
-        // of y at its join)
-        const bool rl = rot && qb >= 14;
-        const float* ct = rl ? rtab : reinterpret_cast<const float*>(smem + C::OFF_ID);
-        const float* st = rl ? rtab + (qb == 14 ? 32 : 64) : reinterpret_cast<const float*>(smem + C::OFF_ID) + 32;
+      for (int q4 = 0; q4 < 8; ++q4) {
+        const float4 a4 = *reinterpret_cast<const float4*>(at + 4 * q4);
+        const float4 b4 = *reinterpret_cast<const float4*>(bt + 4 * q4);
+        const float av[4] = {a4.x, a4.y, a4.z, a4.w}, bv[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
-        for (int q4 = 0; q4 < 8; ++q4) {
-          const float4 c4 = *reinterpret_cast<const float4*>(ct + 4 * q4);
-          const float4 s4 = *reinterpret_cast<const float4*>(st + 4 * q4);
-          const float cc[4] = {c4.x, c4.y, c4.z, c4.w}, sv[4] = {s4.x, s4.y, s4.z, s4.w};
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const int e = 4 * q4 + m;
-            // the partner (quad_perm [0,1,3,2]: lanes 14 <-> 15) times the sine: one v_mul
-            // with the lane swap folded in, then one fma
-            const float ps = dpp_perm_f32<0xB4>(y[e]) * sv[m];
-            y[e] = __builtin_fmaf(y[e], cc[m], ps);
-          }
+        for (int m = 0; m < 4; ++m) {
+          const int e = 4 * q4 + m;
+          // the partner (quad_perm [0,1,3,2]: lanes 14 <-> 15) times B: one v_mul with the
+          // lane swap folded in, then one fma and the scale
+          const float ps = dpp_perm_f32<0xB4>(y[e]) * bv[m];
+          y[e] = __builtin_fmaf(y[e], av[m], ps) * inv;
         }
       }
       unsigned char* qt = smem + C::OFF_QT + head * 512;
@@ -826,7 +825,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
       const int i = tid - 448;
       reinterpret_cast<double*>(smem + C::OFF_IFREQ)[i] = exp2(-(2.0 * i / (double)a.rope_dim) * a.log2_theta);
     }
-    if (tid >= 384 && tid < 448) reinterpret_cast<float*>(smem + C::OFF_ID)[tid - 384] = tid < 416 ? 1.f : 0.f;
+    if (tid >= 384 && tid < 416) reinterpret_cast<float*>(smem + C::OFF_ZERO)[tid - 384] = 0.f;
     __syncthreads();
   };
 
@@ -1277,7 +1276,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
               const float4 c4 = *reinterpret_cast<const float4*>(rtab + 8 * g + 4 * lhalf);
-              const float4 s4 = *reinterpret_cast<const float4*>(rtab + 64 + 8 * g + 4 * lhalf);
+              const float4 s4 = *reinterpret_cast<const float4*>(rtab + 32 + 8 * g + 4 * lhalf);
               const float cc[4] = {c4.x, c4.y, c4.z, c4.w}, sv[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
               for (int jj = 0; jj < 4; ++jj) {
@@ -1337,7 +1336,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
         // the token's cos / sin table (this wave's, the one its epilogue would use)
         if (rot && v == 3 && lane < 32) {
           part[WSP_ROPE + lane] = rtab[lane];
-          part[WSP_ROPE + 32 + lane] = rtab[64 + lane];
+          part[WSP_ROPE + 32 + lane] = rtab[32 + lane];
         }
         if (n > 0) {
           uint4* pv4 = reinterpret_cast<uint4*>(part) + 2 * 4 * 2 * 64 * v + lane;
