@@ -13,9 +13,10 @@
 //              work items (token, split), with QK and P.V waves specialized per SIMD and
 //              one barrier per 64-entry tile (its own comment below has the details);
 //   smla_main  every other shape: one workgroup per work item, described here.
-// smla_combine (smla_main's splits) and smla_combine_lm4 / smla_combine_lm1 (smla_ws's
-// splits, stored in the P.V waves' register order; 4 or 1 float4 slots per thread)
-// merge the splits of a token when a call is split.
+// smla_combine (smla_main's splits, and the two-pool smla_nv's at rotary widths other
+// than 0 and 64) and smla_combine_lm4 / smla_combine_lm1 (smla_ws's splits, stored in
+// the P.V waves' register order, and smla_nv's in the same format; 4 or 1 float4 slots
+// per thread) merge the splits of a token when a call is split.
 //
 // smla_main: one 512-thread workgroup (8 wave64, two per SIMD) per token, or per token
 // split when few tokens are in flight.
@@ -1398,8 +1399,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
 //             i of a 16-lane group receives element i % 4 of the 8-byte pieces addressed by
 //             lanes i / 4, i / 4 + 4, i / 4 + 8, i / 4 + 12, which turns four row-major slots
 //             of 16 dims into 16 lanes of four slots each).
-// Then the same epilogue as the generic kernel, or the split partials in its format for
-// smla_combine.
+// Then the same epilogue as the generic kernel, or the split partials: at rotary widths 0
+// and 64 in smla_ws's f16 register-order format for smla_combine_lm4 / lm1, else in the
+// generic f32 format for smla_combine.
 struct NvCfg {
   static constexpr int kD = 512, kEB = 2;  // the q prologue writes a bf16 q' tile
   static constexpr int D = kD;
@@ -1657,13 +1659,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_nv(KArgs a) {
           // V^T fragment of dims 64 w + 32 nb .. + 31, slots 16 ks + 8 lhalf .. + 7: lane p of
           // 16-lane group g points at slot k0 + p / 4, dims 16 (g & 1) + 4 (p & 3) .. + 3
           const int dim0 = 64 * w + 32 * nb + 16 * (grp & 1) + 4 * (p16 & 3);
+          // (the compiler's own transpose loads: it counts their waits, so the sixteen
+          // loads of a tile need not each wait for the last)
           uint2 h0, h1;
           {
+            typedef short s16x4 __attribute__((ext_vector_type(4)));
+            typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
             const int slot = 16 * ks + 8 * lhalf + (p16 >> 2);
-            const uint32_t ad = lds_addr(vt + (slot * C::VS + dim0) * 2);
-            asm volatile("ds_read_b64_tr_b16 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(h0) : "v"(ad) : "memory");
-            const uint32_t ad1 = ad + 4 * C::VS * 2;
-            asm volatile("ds_read_b64_tr_b16 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(h1) : "v"(ad1) : "memory");
+            lds_s16x4* ad = (lds_s16x4*)(vt + (slot * C::VS + dim0) * 2);
+            h0 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(ad));
+            h1 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(ad + C::VS));
           }
           const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(h0.x, h0.y, h1.x, h1.y));
 #pragma unroll
@@ -1701,7 +1706,49 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_nv(KArgs a) {
     }
     __syncthreads();
     epilogue<D, NTHREADS>(o_l, C::OS, a.h_q, 0, t, a, cs, sn);
+  } else if (a.rope_dim == 0 || a.rope_dim == 64) {
+    // smla_ws's partial format (f16 blocks in its P.V waves' register order), read by
+    // smla_combine_lm4 / lm1: this wave's acc[mb][nb] (dims 64 w + 32 nb ..) is acc[mb]
+    // [2 (w & 1) + nb] of P.V wave w / 2 there, with the same element order in the block
+    float* part = a.ws + ((size_t)t * ns + split) * partial_floats_d(a.h_q, D);
+    if (tid < a.h_q) {
+      // a split that read nothing reports m = -inf: the combine never reads its accumulator
+      const float lt = lsum[tid] + lsum[HP + tid];
+      part[WSP_M + tid] = lt > 0.f ? maxx[tid] : -INFINITY;
+      part[WSP_L + tid] = lt;
+    }
+    if (a.rope_dim == 64 && tid < 32) {
+      part[WSP_ROPE + tid] = cs[tid];
+      part[WSP_ROPE + 32 + tid] = sn[tid];
+    }
+    if (te > tb) {
+      uint4* pv4 = reinterpret_cast<uint4*>(part) + lane;
+      float* psc = part + WSP_SCL;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          float am = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(acc[mb][nb][i]));
+          am = pair_max(am);
+          float enc, dec;
+          f16_block_scale(am, enc, dec);
+          if (lane < 32) psc[(2 * w + nb) * HP + 32 * mb + lrow] = dec;
+          const int slot0 = (((w >> 1) * 2 + mb) * 4 + 2 * (w & 1) + nb) * 2;
+#pragma unroll
+          for (int g2 = 0; g2 < 2; ++g2) {
+            const int r = 8 * g2;
+            pv4[(slot0 + g2) * 64] = make_uint4(
+                pack_f16(acc[mb][nb][r] * enc, acc[mb][nb][r + 1] * enc),
+                pack_f16(acc[mb][nb][r + 2] * enc, acc[mb][nb][r + 3] * enc),
+                pack_f16(acc[mb][nb][r + 4] * enc, acc[mb][nb][r + 5] * enc),
+                pack_f16(acc[mb][nb][r + 6] * enc, acc[mb][nb][r + 7] * enc));
+          }
+        }
+    }
   } else {
+    // other rotary widths: the generic f32 partials, read by smla_combine
     float* part = a.ws + ((size_t)t * ns + split) * partial_floats_d(a.h_q, D);
     float* pm = part + (size_t)HP * D;
     float* pl = pm + HP;
@@ -2214,7 +2261,13 @@ hipError_t launch(const LaunchArgs& x) {
     hipError_t e = hipGetLastError();
     if (x.ev_split) (void)hipEventRecord(x.ev_split, x.stream);
     if (e == hipSuccess && x.num_splits > 1) {
-      hipLaunchKernelGGL((smla_combine<512>), dim3((unsigned)x.s_q, (unsigned)x.h_q), dim3(CTHREADS), 0, x.stream, k);
+      // the split partials are in smla_ws's format for rotary widths 0 and 64
+      if (x.rope_dim != 0 && x.rope_dim != 64)
+        hipLaunchKernelGGL((smla_combine<512>), dim3((unsigned)x.s_q, (unsigned)x.h_q), dim3(CTHREADS), 0, x.stream, k);
+      else if (x.num_splits <= 8)
+        hipLaunchKernelGGL(smla_combine_lm4, dim3((unsigned)x.s_q, 16u), dim3(CTHREADS), 0, x.stream, k);
+      else
+        hipLaunchKernelGGL(smla_combine_lm1, dim3((unsigned)x.s_q, 16u), dim3(LMT), 0, x.stream, k);
       e = hipGetLastError();
     }
     if (x.ev_end) (void)hipEventRecord(x.ev_end, x.stream);

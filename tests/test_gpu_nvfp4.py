@@ -6,7 +6,8 @@ Workloads in the two-pool form (E4M3 + UE8M0 SWA rows, NVFP4 compressed rows, en
 the 1024-token ragged decode and the 2123-token prefill with every token checked; forced
 split counts; all entries in one segment (swa_entries 0 and 640); empty, all-sentinel and
 short rows; stale ids past the length pointing outside either pool; fewer heads; no
-rotary dims; tiny and huge compressed-row scales."""
+rotary dims; split calls at rotary widths 0, 32 and 96 (both combine formats); tiny and
+huge compressed-row scales."""
 import numpy as np
 import pytest
 import torch
@@ -85,6 +86,16 @@ def test_fewer_heads_and_no_rope():
     check(inp)
     inp["rope_dim"] = 0
     check(inp, num_splits=1)
+
+
+@pytest.mark.parametrize("rope", [0, 32, 96])
+@pytest.mark.parametrize("ns", [3, 10])
+def test_split_combines_by_rotary_width(rope, ns):
+    # rotary widths 0 and 64 send the split partials to the register-order combines (3
+    # splits: four per thread, 10: one per thread), other widths to the generic combine
+    inp = inputs.make_ds_nvfp4("decode_sq64", seed=206 + rope, s_q=3)
+    inp["rope_dim"] = rope
+    check(inp, num_splits=ns)
 
 
 @pytest.mark.parametrize("lo,hi", [(0x10, 0x20), (0x60, 0x70)])
