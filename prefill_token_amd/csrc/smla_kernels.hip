@@ -1446,7 +1446,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_nv(KArgs a) {
   const int lrow = lane & 31, lhalf = lane >> 5;
   const int qa = w & 1, qc = (w >> 1) & 1, qd = w >> 2;  // QK roles
   const int ns = a.num_splits;
-  const int t = blockIdx.x / ns, split = blockIdx.x % ns;
+  // the item of this workgroup: in the order smla_order wrote (tokens by descending tile
+  // count, so that the dispatcher, which starts workgroups in id order as compute units
+  // free up, takes the long ones first), or item = id
+  const int item = a.order ? a.order[blockIdx.x] : (int)blockIdx.x;
+  const int t = item / ns, split = item % ns;
   const int pos = a.positions[t];
   const int lraw = a.topk_length[t];
   const int lcap = lraw < 0 ? 0 : (lraw > a.topk ? a.topk : lraw);
@@ -2256,8 +2260,17 @@ hipError_t launch(const LaunchArgs& x) {
   if (x.cmp_pool) {
     static_assert(NvCfg::MAX_ROPE >= kNvMaxRope, "the host's rotary limit for the two-pool kernel");
     if (x.d != 512 || x.kv_format != 0) return hipErrorInvalidValue;
+    KArgs kn = k;
+    if (x.num_splits == 1 && x.s_q > device_cus()) {
+      // more tokens than compute units: longest first
+      int* order = reinterpret_cast<int*>(k.ws);
+      hipLaunchKernelGGL(smla_order, dim3(1), dim3(1024), 0, x.stream, x.topk_length, x.s_q, x.topk, order);
+      const hipError_t eo = hipGetLastError();
+      if (eo != hipSuccess) return eo;
+      kn.order = order;
+    }
     if (x.ev_main) (void)hipEventRecord(x.ev_main, x.stream);
-    hipLaunchKernelGGL(smla_nv, dim3((unsigned)(x.s_q * x.num_splits)), dim3(NTHREADS), 0, x.stream, k);
+    hipLaunchKernelGGL(smla_nv, dim3((unsigned)(x.s_q * x.num_splits)), dim3(NTHREADS), 0, x.stream, kn);
     hipError_t e = hipGetLastError();
     if (x.ev_split) (void)hipEventRecord(x.ev_split, x.stream);
     if (e == hipSuccess && x.num_splits > 1) {
