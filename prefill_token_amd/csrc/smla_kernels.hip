@@ -1388,7 +1388,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_ws(KArgs a) {
 //   gather    thread (row gr = tid / 8, part gp = tid % 8) loads dims 64 gp .. 64 gp + 63 of
 //             its row (64 E4M3 bytes + 2 UE8M0 scales, or 32 bytes of E2M1 pairs + 4 E4M3
 //             scales) through range-checked buffer loads (rows that are not read come in as
-//             zeros), one tile ahead, and writes them as bf16 into the V tile [slot][dim];
+//             zeros), one tile ahead, and writes them as bf16 into the V tile [slot][dim]
+//             (16-byte chunk c of a slot's row stored at chunk c ^ ((c >> 3) & 7), so that
+//             the eight threads of a row write distinct banks);
 //   QK^T      wave (qa, qc, qd) computes the partial S^T[32 slots of half qc][32 heads of
 //             group qa] over dim half qd (16 bf16 MFMAs, q' fragments in VGPRs); the qd = 1
 //             halves meet the qd = 0 halves through LDS;
@@ -1506,14 +1508,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_nv(KArgs a) {
   // the gathered part of row gr as bf16 into the V tile (exact: an E4M3 value times a
   // power of two in the range the ABI admits, or an E2M1 value times an E4M3 scale)
   auto dequant = [&](int tile, const Raw& g) {
+    // 16-byte chunk i of this thread's part (chunk 8 gp + i of the row) at i ^ gp: the
+    // eight threads of a row then write eight different bank groups at each step
     uint4* dst = reinterpret_cast<uint4*>(vt + (gr * C::VS + 64 * gp) * 2);
+    auto at = [&](int i) -> uint4& { return dst[i ^ gp]; };
     if (tile * T < a.swa_entries) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const float sc = ue8m0_f32((g.s >> (k < 2 ? 0 : 8)) & 0xFFu);
         const uint32_t u[4] = {g.c[k].x, g.c[k].y, g.c[k].z, g.c[k].w};
-        dst[2 * k] = make_uint4(cvt_lo(u[0], sc), cvt_hi(u[0], sc), cvt_lo(u[1], sc), cvt_hi(u[1], sc));
-        dst[2 * k + 1] = make_uint4(cvt_lo(u[2], sc), cvt_hi(u[2], sc), cvt_lo(u[3], sc), cvt_hi(u[3], sc));
+        at(2 * k) = make_uint4(cvt_lo(u[0], sc), cvt_hi(u[0], sc), cvt_lo(u[1], sc), cvt_hi(u[1], sc));
+        at(2 * k + 1) = make_uint4(cvt_lo(u[2], sc), cvt_hi(u[2], sc), cvt_lo(u[3], sc), cvt_hi(u[3], sc));
       }
     } else {
       // the four E4M3 block scales, decoded exactly
@@ -1539,7 +1544,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_nv(KArgs a) {
             else e2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u[q], 1.0f, 3);
             pk[b] = pack_bf16(e2[0] * sc, e2[1] * sc);
           }
-          dst[4 * k + q] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+          at(4 * k + q) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
         }
       }
     }
@@ -1592,7 +1597,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_nv(KArgs a) {
       const unsigned short* krow = reinterpret_cast<const unsigned short*>(vt) + (32 * qc + lrow) * C::VS;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + 16 * (16 * qd + j) + 8 * lhalf);
+        // chunk c = 2 (16 qd + j) + lhalf of the row, stored at c ^ ((c >> 3) & 7)
+        const int c = 2 * (16 * qd + j) + lhalf;
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + 8 * (c ^ ((c >> 3) & 7)));
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[j], s, 0, 0, 0);
       }
     }
@@ -1670,7 +1677,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void smla_nv(KArgs a) {
             typedef short s16x4 __attribute__((ext_vector_type(4)));
             typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
             const int slot = 16 * ks + 8 * lhalf + (p16 >> 2);
-            lds_s16x4* ad = (lds_s16x4*)(vt + (slot * C::VS + dim0) * 2);
+            const int c = dim0 >> 3;  // its 16-byte chunk, stored at c ^ ((c >> 3) & 7)
+            lds_s16x4* ad = (lds_s16x4*)(vt + (slot * C::VS + 8 * (c ^ ((c >> 3) & 7)) + (dim0 & 7)) * 2);
             h0 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(ad));
             h1 = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(ad + C::VS));
           }
