@@ -6,8 +6,9 @@ Workloads in the two-pool form (E4M3 + UE8M0 SWA rows, NVFP4 compressed rows, en
 the 1024-token ragged decode and the 2123-token prefill with every token checked; forced
 split counts; all entries in one segment (swa_entries 0 and 640); empty, all-sentinel and
 short rows; stale ids past the length pointing outside either pool; fewer heads; no
-rotary dims; split calls at rotary widths 0, 32 and 96 (both combine formats); tiny and
-huge compressed-row scales."""
+rotary dims; split calls at rotary widths 0, 32 and 96 (both combine formats); 17 and 32
+splits of 2000-entry rows (the combine's chunks of 16); tiny and huge compressed-row
+scales."""
 import numpy as np
 import pytest
 import torch
@@ -95,6 +96,22 @@ def test_split_combines_by_rotary_width(rope, ns):
     # splits: four per thread, 10: one per thread), other widths to the generic combine
     inp = inputs.make_ds_nvfp4("decode_sq64", seed=206 + rope, s_q=3)
     inp["rope_dim"] = rope
+    check(inp, num_splits=ns)
+
+
+@pytest.mark.parametrize("ns", [17, 32])
+def test_many_splits(ns):
+    # more than 16 splits per token: the two-pool kernel's register-order partials merged
+    # by the combine in chunks of 16.  Rows of 2000 entries: 128 SWA, then 1872 compressed
+    inp = inputs.make_ds_nvfp4("decode_sq64", seed=230 + ns, s_q=3)
+    rng = np.random.default_rng(ns)
+    topk = 2000
+    idx = np.empty((3, topk), dtype=np.int32)
+    idx[:, :128] = rng.integers(0, inp["swa_codes"].shape[0], (3, 128))
+    idx[:, 128:] = rng.integers(0, inp["cmp_codes"].shape[0], (3, topk - 128))
+    idx[rng.random(idx.shape) < 0.1] = -1
+    inp["indices"], inp["topk"] = idx, topk
+    inp["topk_length"] = np.array([topk, 1500, 1100], dtype=np.int32)
     check(inp, num_splits=ns)
 
 
